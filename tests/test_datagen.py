@@ -18,7 +18,7 @@ def test_bf16_generator_is_rne_of_fp32():
     b = datagen.bf16_bits_from_f32(f)
     back = datagen.bf16_bits_to_f32(b)
     # within half a bf16 ulp
-    ulp = np.spacing(back.astype(np.float32)) * 2 ** 16
+    ulp = np.abs(np.spacing(back.astype(np.float32))) * 2 ** 16
     assert np.all(np.abs(back - f) <= ulp / 2)
 
 
