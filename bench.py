@@ -1,0 +1,383 @@
+"""Benchmark of the binary-weight hot path on one MI355X.
+
+Headline (value): decode-shaped binary GEMV at M=1 -- one step is y = x . Wq^T
+for both decode matrices, W 4096x14336 and 14336x4096 in the group-128 sign +
+fp16 scale format, bf16 activations, bf16 outputs. Throughput is algorithmic
+HBM bytes (packed weights + activations in + outputs out) per second. The
+weights rotate through a ring of copies larger than twice the 256 MB
+Infinity Cache, so every call streams its weights from HBM.
+
+Also reported (extra): the same product at M = 4, 16, 64; the routed MoE layer
+(256 experts, top-8, hidden 2048, intermediate 512) at T = 1 and 64 decode
+tokens; the DBF chain (4096x4096, r = 2048) at M = 1 and 512; the prefill
+product at M = 4096 (4096 -> 14336) with the Kronecker rotation before it.
+
+The CPU baseline is the fp64 numpy oracle on the host cores, timed on a bounded
+sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "binary GEMV/MoE decode HBM GB/s (% of peak) at M=1; prefill TFLOP/s at M=4096"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def packed_bytes(N, K):
+    return N * K // 8 + 2 * (N * K // 128)
+
+
+class EventTimer:
+    """Per-launch HIP event pairs on the stream the library launches on
+    (torch's current stream)."""
+
+    def __init__(self, n):
+        import torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.i = 0
+
+    def __enter__(self):
+        self.ev[self.i][0].record()
+        return self
+
+    def __exit__(self, *exc):
+        self.ev[self.i][1].record()
+        self.i += 1
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.ev[: self.i])
+
+
+def dev_np(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def ring_copies(per_copy_bytes):
+    return max(2, int(np.ceil(2 * MALL_BYTES / per_copy_bytes)))
+
+
+# ---------------------------------------------------------------------------
+# headline: C2 decode at M (default 1)
+# ---------------------------------------------------------------------------
+
+def setup_c2(brq, torch, M):
+    import datagen
+    mats = []
+    for which in (0, 1):
+        N, K = datagen.C2_SHAPES[which]
+        w = torch.from_numpy(datagen.C2_weight(which)).cuda()
+        s, sc = brq.pack(w)
+        del w
+        mats.append((N, K, s, sc))
+    torch.cuda.synchronize()
+    per_step = sum(packed_bytes(N, K) for N, K, _, _ in mats)
+    copies = ring_copies(per_step)
+    ring = []
+    for c in range(copies):
+        ring.append([(N, K, s.clone(), sc.clone()) for N, K, s, sc in mats])
+    xs = [dev_np(datagen.C2_x(which, M)) for which in (0, 1)]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N, K, _, _ in mats]
+    wss = [torch.empty(max(brq.gemm_workspace_bytes(M, N, K), 256), dtype=torch.uint8, device="cuda")
+           for N, K, _, _ in mats]
+    step_bytes = sum(packed_bytes(N, K) + M * K * 2 + M * N * 2 for N, K, _, _ in mats)
+    return ring, xs, ys, wss, step_bytes
+
+
+def run_c2(brq, torch, M, steps, warmup, timer_launches=True):
+    ring, xs, ys, wss, step_bytes = setup_c2(brq, torch, M)
+    n = len(ring)
+
+    def step(i, timer=None):
+        for j, (N, K, s, sc) in enumerate(ring[i % n]):
+            if timer is not None:
+                with timer:
+                    brq.gemm(xs[j], s, sc, N, K, out_dtype=torch.bfloat16, y=ys[j], ws=wss[j])
+            else:
+                brq.gemm(xs[j], s, sc, N, K, out_dtype=torch.bfloat16, y=ys[j], ws=wss[j])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # wall-clock region: back-to-back launches
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    # per-launch event pairs (kernel duration of each call)
+    timer = EventTimer(2 * steps) if timer_launches else None
+    if timer is not None:
+        for i in range(steps):
+            step(warmup + i, timer)
+        torch.cuda.synchronize()
+    res = dict(M=M, ms_per_step=ms / steps, step_bytes=step_bytes, gbs=step_bytes * steps / (ms * 1e-3) / 1e9,
+               tflops=2.0 * M * sum(N * K for N, K, _, _ in ring[0]) * steps / (ms * 1e-3) / 1e12,
+               ring_copies=n)
+    if timer is not None:
+        per_launch = timer.total_ms() / timer.i
+        res["launch_ms"] = per_launch
+        res["launch_gbs"] = (step_bytes / 2) / (per_launch * 1e-3) / 1e9
+    del ring
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# extras
+# ---------------------------------------------------------------------------
+
+def run_moe(brq, torch, Ts, iters=50):
+    import datagen
+    cfg = datagen.C4()
+    E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.top_k
+    gs = torch.empty((E, I, H // 64), dtype=torch.int64, device="cuda")
+    gsc = torch.empty((E, I, H // 128), dtype=torch.float16, device="cuda")
+    us, usc = torch.empty_like(gs), torch.empty_like(gsc)
+    ds = torch.empty((E, H, I // 64), dtype=torch.int64, device="cuda")
+    dsc = torch.empty((E, H, I // 128), dtype=torch.float16, device="cuda")
+    for e in range(E):
+        for f, (a, b) in ((cfg.gate, (gs, gsc)), (cfg.up, (us, usc)), (cfg.down, (ds, dsc))):
+            brq.pack(torch.from_numpy(f(e)).cuda(), out=(a[e], b[e]))
+    torch.cuda.synchronize()
+    layer_bytes = 3 * E * packed_bytes(I, H)
+    copies = ring_copies(layer_bytes)
+    ring = [(gs.clone(), gsc.clone(), us.clone(), usc.clone(), ds.clone(), dsc.clone()) for _ in range(copies)]
+    out = {}
+    for T in Ts:
+        x = dev_np(cfg.x(T))
+        lgs = [dev_np(cfg.logits(T, it)) for it in range(iters)]
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(brq.moe_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device="cuda")
+        # algorithmic bytes: distinct selected experts' packed weights + x + logits + y
+        nbytes = 0
+        for it in range(iters):
+            ids = np.argsort(-cfg.logits(T, it), axis=1, kind="stable")[:, :k]
+            nbytes += len(np.unique(ids)) * 3 * packed_bytes(I, H) + T * (H * 2 * 2 + E * 4)
+        for it in range(5):
+            brq.moe_ffn(x, lgs[it], *ring[it % copies], E, H, I, k, y=y, ws=ws)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for it in range(iters):
+            brq.moe_ffn(x, lgs[it], *ring[it % copies], E, H, I, k, y=y, ws=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / iters
+        out[f"T={T}"] = dict(us_per_layer=ms * 1e3, gbs=nbytes / iters / (ms * 1e-3) / 1e9,
+                             tokens_per_s=T / (ms * 1e-3), ring_copies=copies)
+    del ring, gs, gsc, us, usc, ds, dsc
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_dbf(brq, torch, Ms, iters=50):
+    import datagen
+    out = {}
+    for M in Ms:
+        d = datagen.C3(M)
+        m, n, r = d["m"], d["n"], d["r"]
+        v, _ = brq.pack(torch.from_numpy(d["v"]).cuda(), scales=False)
+        u, _ = brq.pack(torch.from_numpy(d["u"]).cuda(), scales=False)
+        wbytes = (r * n + m * r) // 8 + 2 * (n + r + m)
+        copies = ring_copies(wbytes) if M == 1 else 1
+        ring = [(v.clone(), u.clone()) for _ in range(copies)]
+        x = dev_np(d["x"])
+        di, dm, do = (torch.from_numpy(d[k]).cuda() for k in ("d_in", "d_mid", "d_out"))
+        y = torch.empty((M, m), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(brq.dbf_workspace_bytes(M, m, n, r), dtype=torch.uint8, device="cuda")
+        for i in range(5):
+            brq.dbf_gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(iters):
+            brq.dbf_gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / iters
+        nbytes = wbytes + M * n * 2 + M * m * 2
+        flops = 2.0 * M * (r * n + m * r)
+        out[f"M={M}"] = dict(us=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
+                             bpe=(r * (m + n) + 16 * (m + n + r)) / (m * n))
+        del ring
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_prefill(brq, torch, iters=10):
+    import datagen
+    d = datagen.C5()
+    N, K = d["N"], d["K"]
+    w = torch.from_numpy(datagen.C5_weight(N, K)).cuda()
+    s, sc = brq.pack(w)
+    del w
+    x = dev_np(d["x"])
+    H, R = dev_np(d["H"]), dev_np(d["R"])
+    xr = torch.empty_like(x)
+    y = torch.empty((x.shape[0], N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        brq.kron_rotate(x, H, R, y=xr)
+        brq.gemm(xr, s, sc, N, K, y=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    rot_ms = gemm_ms = 0.0
+    for _ in range(iters):
+        ev[0].record()
+        brq.kron_rotate(x, H, R, y=xr)
+        ev[1].record()
+        brq.gemm(xr, s, sc, N, K, y=y)
+        ev[2].record()
+        torch.cuda.synchronize()
+        rot_ms += ev[0].elapsed_time(ev[1])
+        gemm_ms += ev[1].elapsed_time(ev[2])
+    rot_ms /= iters
+    gemm_ms /= iters
+    M = x.shape[0]
+    flops = 2.0 * M * N * K
+    res = dict(M=M, N=N, K=K, gemm_us=gemm_ms * 1e3, gemm_tflops=flops / (gemm_ms * 1e-3) / 1e12,
+               gemm_frac_of_f16_peak=flops / (gemm_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+               rotate_us=rot_ms * 1e3, rotate_gbs=(2 * M * K * 2) / (rot_ms * 1e-3) / 1e9,
+               tokens_per_s=M / ((rot_ms + gemm_ms) * 1e-3))
+    del s, sc, x, xr, y
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores, bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(budget_s=12.0):
+    import datagen
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        ncores = len(os.sched_getaffinity(0))
+        limiter = threadpool_limits(limits=ncores, user_api="blas")
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        limiter, threads = None, os.cpu_count()
+    mats = []
+    for which in (0, 1):
+        N, K = datagen.C2_SHAPES[which]
+        words, scales = oracle.pack_sign1(datagen.C2_weight(which))
+        x = oracle.bf16_to_f64(datagen.C2_x(which, 1))
+        mats.append((N, K, words, scales, x))
+    step_bytes = sum(packed_bytes(N, K) + K * 2 + N * 2 for N, K, _, _, _ in mats)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for N, K, words, scales, x in mats:
+            oracle.bin_gemm(x, words, scales, N, K)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return dict(value=step_bytes * steps / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{steps} steps of the headline workload (both C2 matrices at M=1, fp64 numpy "
+                       f"dequantise + matmul) in {el:.1f} s")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import binary_weight_gemm_amd as brq
+    brq.lib()
+    torch.cuda.set_device(0)
+
+    log("[bench] headline C2 decode M=1")
+    head = run_c2(brq, torch, 1, args.steps, args.warmup)
+    log(f"[bench] headline {head}")
+    extra = {}
+    if not args.no_extra:
+        extra["c2"] = {}
+        for M in (4, 16, 64):
+            log(f"[bench] C2 M={M}")
+            r = run_c2(brq, torch, M, 50, 10, timer_launches=False)
+            extra["c2"][f"M={M}"] = {k: r[k] for k in ("ms_per_step", "gbs", "tflops")}
+        log("[bench] MoE")
+        extra["moe"] = run_moe(brq, torch, (1, 64))
+        log("[bench] DBF")
+        extra["dbf"] = run_dbf(brq, torch, (1, 512))
+        log("[bench] prefill")
+        extra["prefill"] = run_prefill(brq, torch)
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] cpu baseline")
+        cpu = cpu_baseline()
+
+    achieved = head.get("launch_gbs", head["gbs"])
+    out = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode binary GEMV: W 4096x14336 and 14336x4096 group-128 sign + fp16 scale, "
+                        "x bf16 M=1, y bf16; one step = both matrices",
+            "M": 1, "shapes_NxK": [[4096, 14336], [14336, 4096]], "ring_copies": head["ring_copies"],
+            "step_bytes": head["step_bytes"],
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "brq_gemm decode (M=1), per-launch HIP events",
+            "launch_us": round(head.get("launch_ms", 0.0) * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+// C-ABI entry points of libbrq: argument validation on the host, then dispatch
+// to the gfx950 kernels. Every check that can fail runs before the first HIP
+// call, so invalid arguments never touch the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/brq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+brq_status fail(brq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+brq_status ok() {
+  g_last_error.clear();
+  return BRQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every index inside 32-bit element counts per row
+
+// gfx950 check, cached per device id
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+brq_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(BRQ_E_DEVICE, "no current HIP device");
+  }
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 1) return BRQ_OK;
+    if (g_dev_state[dev] == 2) return fail(BRQ_E_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BRQ_E_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+  }
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_dev_state[dev] = good ? 1 : 2;
+  }
+  if (!good) return fail(BRQ_E_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return BRQ_OK;
+}
+
+brq_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BRQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
+
+size_t gemm_ws(int64_t M, int64_t K) { return M <= 64 ? brq::align256((size_t)M * K * 2) : 0; }
+
+}  // namespace
+
+extern "C" {
+
+int brq_abi_version(void) { return BRQ_ABI_VERSION; }
+
+const char* brq_status_str(brq_status s) {
+  switch (s) {
+    case BRQ_OK: return "BRQ_OK";
+    case BRQ_E_NULL: return "BRQ_E_NULL";
+    case BRQ_E_SHAPE: return "BRQ_E_SHAPE";
+    case BRQ_E_ALIGN: return "BRQ_E_ALIGN";
+    case BRQ_E_DTYPE: return "BRQ_E_DTYPE";
+    case BRQ_E_WORKSPACE: return "BRQ_E_WORKSPACE";
+    case BRQ_E_DEVICE: return "BRQ_E_DEVICE";
+    case BRQ_E_HIP: return "BRQ_E_HIP";
+  }
+  return "BRQ_E_UNKNOWN";
+}
+
+const char* brq_last_error(void) { return g_last_error.c_str(); }
+
+size_t brq_sign_words(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 64 || cols % 64) return 0;
+  return (size_t)rows * (size_t)(cols / 64);
+}
+
+size_t brq_scale_count(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 128 || cols % 128) return 0;
+  return (size_t)rows * (size_t)(cols / 128);
+}
+
+brq_status brq_pack(const float* w, int64_t rows, int64_t cols, uint64_t* signs, uint16_t* scales,
+                    void* stream) {
+  if (!w || !signs) return fail(BRQ_E_NULL, "brq_pack: w and signs must not be NULL");
+  if (rows < 1 || rows > kMaxDim) return fail(BRQ_E_SHAPE, "brq_pack: rows=%lld out of range", (long long)rows);
+  const int64_t mult = scales ? 128 : 64;
+  if (cols < mult || cols > kMaxDim || cols % mult)
+    return fail(BRQ_E_SHAPE, "brq_pack: cols=%lld must be a positive multiple of %lld", (long long)cols,
+                (long long)mult);
+  if (!aligned(w, 16) || !aligned(signs, 16) || (scales && !aligned(scales, 16)))
+    return fail(BRQ_E_ALIGN, "brq_pack: buffers must be 16-byte aligned");
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  return hip_result(brq::launch_pack(w, rows, cols, signs, scales, (hipStream_t)stream), "brq_pack");
+}
+
+size_t brq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  if (M < 1 || K < 128 || K % 128) return 0;
+  return gemm_ws(M, K);
+}
+
+brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint64_t* signs,
+                    const uint16_t* scales, void* y, brq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !signs || !scales || !y) return fail(BRQ_E_NULL, "brq_gemm: x, signs, scales and y must not be NULL");
+  if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim)
+    return fail(BRQ_E_SHAPE, "brq_gemm: M=%lld N=%lld out of range", (long long)M, (long long)N);
+  if (K < 128 || K > kMaxDim || K % 128)
+    return fail(BRQ_E_SHAPE, "brq_gemm: K=%lld must be a positive multiple of 128", (long long)K);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm: unknown y_dtype %d", (int)y_dtype);
+  if (!aligned(x, 16) || !aligned(signs, 16) || !aligned(scales, 16) || !aligned(y, 16))
+    return fail(BRQ_E_ALIGN, "brq_gemm: x, signs, scales and y must be 16-byte aligned");
+  const size_t need = gemm_ws(M, K);
+  if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(BRQ_E_WORKSPACE, "brq_gemm: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int yb = y_dtype == BRQ_BF16;
+  if (M <= 64) {
+    uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
+    hipError_t e = brq::launch_prep_bf16(x, M, K, xp, st);
+    if (e != hipSuccess) return hip_result(e, "brq_gemm (stage activations)");
+    return hip_result(brq::launch_gemm_dec(xp, (int)M, (int)N, (int)K, signs, scales, y, yb, st), "brq_gemm");
+  }
+  return hip_result(brq::launch_gemm_tile(x, (int)M, (int)N, (int)K, signs, scales, y, yb, st), "brq_gemm");
+}
+
+size_t brq_dbf_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
+  if (M < 1 || m < 1 || n < 128 || r < 128 || n % 128 || r % 128) return 0;
+  return brq::dbf_ws_bytes(M, m, n, r);
+}
+
+brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int64_t r, const uint16_t* d_in,
+                        const uint64_t* v, const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out,
+                        void* y, brq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !d_in || !v || !d_mid || !u || !d_out || !y)
+    return fail(BRQ_E_NULL, "brq_dbf_gemm: x, d_in, v, d_mid, u, d_out and y must not be NULL");
+  if (M < 1 || m < 1 || M > kMaxDim || m > kMaxDim)
+    return fail(BRQ_E_SHAPE, "brq_dbf_gemm: M=%lld m=%lld out of range", (long long)M, (long long)m);
+  if (n < 128 || r < 128 || n > kMaxDim || r > kMaxDim || n % 128 || r % 128)
+    return fail(BRQ_E_SHAPE, "brq_dbf_gemm: n=%lld and r=%lld must be positive multiples of 128", (long long)n,
+                (long long)r);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm: unknown y_dtype %d", (int)y_dtype);
+  if (!aligned(x, 16) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, 16) || !aligned(d_in, 16) ||
+      !aligned(d_mid, 2) || !aligned(d_out, 2))
+    return fail(BRQ_E_ALIGN, "brq_dbf_gemm: x, v, u, y and d_in must be 16-byte aligned");
+  const size_t need = brq::dbf_ws_bytes(M, m, n, r);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(BRQ_E_WORKSPACE, "brq_dbf_gemm: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  return hip_result(brq::launch_dbf(x, (int)M, (int)m, (int)n, (int)r, d_in, v, d_mid, u, d_out, y,
+                                    y_dtype == BRQ_BF16, ws, (hipStream_t)stream),
+                    "brq_dbf_gemm");
+}
+
+size_t brq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
+  if (T < 1 || T > 256 || H < 128 || I < 128 || H % 128 || I % 128 || E < 1 || E > 1024 || top_k < 1 ||
+      top_k > 16 || top_k > E)
+    return 0;
+  return brq::moe_ws_bytes(T, H, I, E, top_k);
+}
+
+brq_status brq_moe_ffn(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I, int64_t E,
+                       int64_t top_k, const uint64_t* gate_s, const uint16_t* gate_sc, const uint64_t* up_s,
+                       const uint16_t* up_sc, const uint64_t* down_s, const uint16_t* down_sc, void* y,
+                       brq_dtype y_dtype, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !logits || !gate_s || !gate_sc || !up_s || !up_sc || !down_s || !down_sc || !y)
+    return fail(BRQ_E_NULL, "brq_moe_ffn: inputs, weights and y must not be NULL");
+  if (T < 1 || T > 256) return fail(BRQ_E_SHAPE, "brq_moe_ffn: T=%lld must be in [1, 256]", (long long)T);
+  if (E < 1 || E > 1024) return fail(BRQ_E_SHAPE, "brq_moe_ffn: E=%lld must be in [1, 1024]", (long long)E);
+  if (top_k < 1 || top_k > 16 || top_k > E)
+    return fail(BRQ_E_SHAPE, "brq_moe_ffn: top_k=%lld must be in [1, min(E, 16)]", (long long)top_k);
+  if (H < 128 || I < 128 || H > 65536 || I > 65536 || H % 128 || I % 128)
+    return fail(BRQ_E_SHAPE, "brq_moe_ffn: H=%lld and I=%lld must be multiples of 128 in [128, 65536]",
+                (long long)H, (long long)I);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_ffn: unknown y_dtype %d", (int)y_dtype);
+  if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(gate_s, 16) || !aligned(up_s, 16) || !aligned(down_s, 16) ||
+      !aligned(gate_sc, 16) || !aligned(up_sc, 16) || !aligned(down_sc, 16) || !aligned(y, 16) ||
+      (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
+    return fail(BRQ_E_ALIGN, "brq_moe_ffn: weight planes, scales, x and y must be 16-byte aligned");
+  const size_t need = brq::moe_ws_bytes(T, H, I, E, top_k);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(BRQ_E_WORKSPACE, "brq_moe_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  return hip_result(brq::launch_moe(x, logits, (int)T, (int)H, (int)I, (int)E, (int)top_k, gate_s, gate_sc, up_s,
+                                    up_sc, down_s, down_sc, y, y_dtype == BRQ_BF16, ids, w, ws, (hipStream_t)stream),
+                    "brq_moe_ffn");
+}
+
+brq_status brq_kron_rotate(const uint16_t* x, int64_t M, const float* H, int64_t n1, const float* R, int64_t n2,
+                           uint16_t* y, void* stream) {
+  if (!x || !H || !R || !y) return fail(BRQ_E_NULL, "brq_kron_rotate: x, H, R and y must not be NULL");
+  if (M < 1 || M > kMaxDim) return fail(BRQ_E_SHAPE, "brq_kron_rotate: M=%lld out of range", (long long)M);
+  if (n1 != 64 || n2 != 64)
+    return fail(BRQ_E_SHAPE, "brq_kron_rotate: n1=%lld n2=%lld, only 64 x 64 factors are supported", (long long)n1,
+                (long long)n2);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(H, 4) || !aligned(R, 4))
+    return fail(BRQ_E_ALIGN, "brq_kron_rotate: x and y must be 16-byte aligned");
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* yb = reinterpret_cast<const char*>(y);
+  const size_t bytes = (size_t)M * 4096 * 2;
+  if (xb < yb + bytes && yb < xb + bytes) return fail(BRQ_E_SHAPE, "brq_kron_rotate: x and y overlap");
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  return hip_result(brq::launch_kron(x, (int)M, H, R, y, (hipStream_t)stream), "brq_kron_rotate");
+}
+
+}  // extern "C"

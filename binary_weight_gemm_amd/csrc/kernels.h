@@ -1,0 +1,52 @@
+// Internal launchers of libbrq (host side). Arguments are validated by the
+// C-ABI layer before any of these is called; each returns hipGetLastError()
+// after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace brq {
+
+// ---- S1 quantiser --------------------------------------------------------
+hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, uint64_t* signs,
+                       uint16_t* scales /* NULL: SIGN1 plane only */, hipStream_t st);
+
+// ---- activation staging --------------------------------------------------
+// bf16 [rows][K] -> fp16 [rows][K] in the permuted operand order.
+hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st);
+// fp16 vector [K] -> fp16 [K] in the permuted operand order.
+hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream_t st);
+
+// ---- group-128 product ----------------------------------------------------
+// Few activation rows (M <= 64): split-K inside a workgroup, 16 output columns
+// per workgroup. xp: permuted fp16 activations [M][K].
+hipError_t launch_gemm_dec(const uint16_t* xp, int M, int N, int K, const uint64_t* signs,
+                           const uint16_t* scales, void* y, int y_bf16, hipStream_t st);
+// Many activation rows: LDS-tiled matrix-core kernel, bf16 activations read directly.
+hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
+                            const uint16_t* scales, void* y, int y_bf16, hipStream_t st);
+
+// ---- DBF chain -------------------------------------------------------------
+// stage 1: hp[2M][r] (fp16 hi/lo pairs, permuted) = D_mid (V (D_in x))
+// stage 2: y[M][m] = D_out (U h_s)
+hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in,
+                      const uint64_t* v, const uint16_t* d_mid, const uint64_t* u,
+                      const uint16_t* d_out, void* y, int y_bf16, void* ws, hipStream_t st);
+size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
+
+// ---- routed MoE ------------------------------------------------------------
+size_t moe_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
+hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int I, int E,
+                      int top_k, const uint64_t* gate_s, const uint16_t* gate_sc,
+                      const uint64_t* up_s, const uint16_t* up_sc, const uint64_t* down_s,
+                      const uint16_t* down_sc, void* y, int y_bf16, int32_t* ids, float* w,
+                      void* ws, hipStream_t st);
+
+// ---- Kronecker rotation ----------------------------------------------------
+hipError_t launch_kron(const uint16_t* x, int M, const float* H, const float* R, uint16_t* y,
+                       hipStream_t st);
+
+static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace brq

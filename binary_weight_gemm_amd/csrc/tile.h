@@ -1,0 +1,26 @@
+// Arguments of the LDS-tiled matrix-core kernel (internal).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace brq {
+
+enum { EPI_Y = 0, EPI_HSPLIT = 1, EPI_PAIRSUM = 2 };
+
+struct TileArgs {
+  const void* a;            // activations: bf16 [M][K] (AMODE 0) or permuted fp16 [M][K] (AMODE 1)
+  int M, N, K;              // A rows, output columns, reduction length
+  const uint64_t* signs;    // SIGN1 plane [N][K/64]
+  const uint16_t* scales;   // group-128 scales [N][K/128] (BM_GROUP)
+  const uint16_t* kperm;    // permuted fp16 per-k magnitudes [K] (BM_PERK)
+  const uint16_t* diag;     // fp16 per-column diagonal (EPI_HSPLIT, EPI_PAIRSUM)
+  void* out;
+  int out_bf16;
+};
+
+hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st);
+hipError_t launch_tile_dbf2(const TileArgs& a, hipStream_t st);
+
+}  // namespace brq

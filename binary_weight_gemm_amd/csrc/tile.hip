@@ -1,0 +1,249 @@
+// Many-row binary product on the matrix cores (the prefill regime: one matrix
+// applied to many vectors, so the weight unpack is amortised over a tile of
+// rows; "LLM binarization, Episode 01: DBF", section 4).
+//
+// Block tile BM x BN x 64 on 4 waves (2 x 2), each wave (BM/2) x (BN/2) of
+// v_mfma_f32_32x32x16_f16 tiles. Per k-step of 64:
+//   A: activations, bf16 read from global (AMODE 0) and converted to fp16, or
+//      fp16 already in the permuted order (AMODE 1); written to LDS in the
+//      permuted order.
+//   B: one 64-bit sign word per column; each pair of signs becomes an fp16
+//      pair +-c (c = group scale, per-k value or 1) with one shift and one
+//      and-or, written to LDS.
+// Two LDS stages: the global loads of step k+1 are issued before the matrix
+// products of step k, and land in the other stage afterwards.
+//
+// Layout facts of the 32x32x16 MFMA used here: A lane l supplies row l%32 and
+// 8 consecutive k of block l/32; B lane l supplies column l%32 and the same k
+// block; D lane l holds, in item r, row 8*(r/4) + 4*(l/32) + r%4 of column l%32.
+//
+// Epilogues: EPI_Y writes y (fp32 or bf16); EPI_HSPLIT multiplies by a per-column
+// fp16 diagonal and writes fp16 hi/lo pairs in the permuted order (the DBF
+// intermediate h_s); EPI_PAIRSUM adds the two piece rows of every token and
+// multiplies by a per-column diagonal (the DBF output).
+#include "common.h"
+#include "dec_core.h"
+#include "kernels.h"
+#include "tile.h"
+
+namespace brq {
+
+template <int BM, int BN, int AMODE, int BMODE, int EPI>
+__global__ __launch_bounds__(256) void k_tile(TileArgs p) {
+  constexpr int BK = 64, LDK = BK + 8;  // +16 bytes per LDS row against bank conflicts
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int A_UNITS = BM * 4 / 256;  // per thread: 16 activations (8 pairs)
+  constexpr int B_UNITS = BN * 4 / 256;  // per thread: 8 pairs of one column
+  static_assert(A_UNITS >= 1 && B_UNITS >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+
+  // tile id -> (tm, tn); contiguous ranges of tile ids per XCD so the
+  // workgroups sharing an activation row-block share one L2
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = p.K / BK;
+
+  // ---- global -> register staging --------------------------------------
+  uint4 ra[A_UNITS][2];
+  uint2 rb[B_UNITS];   // .x = sign dword, .y = magnitude pair (BM_GROUP / BM_ONE)
+  u32x4 rk[B_UNITS][2];  // BM_PERK magnitudes: 8 pairs
+
+  auto load_stage = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int u = 0; u < A_UNITS; ++u) {
+      const int unit = tid + 256 * u;
+      const int row = unit >> 2, q = (unit >> 1) & 1, b0 = (unit & 1) * 8;
+      const int gm = m0 + row;
+      if (gm < p.M) {
+        if (AMODE == 0) {
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.a) + (size_t)gm * p.K + k0 + 32 * q + b0;
+          ra[u][0] = *reinterpret_cast<const uint4*>(src);
+          ra[u][1] = *reinterpret_cast<const uint4*>(src + 16);
+        } else {
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.a) + (size_t)gm * p.K + k0 + 32 * q + 2 * b0;
+          ra[u][0] = *reinterpret_cast<const uint4*>(src);
+          ra[u][1] = *reinterpret_cast<const uint4*>(src + 8);
+        }
+      } else {
+        ra[u][0] = make_uint4(0, 0, 0, 0);
+        ra[u][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B_UNITS; ++u) {
+      const int unit = tid + 256 * u;
+      const int col = unit >> 2, q = (unit >> 1) & 1, b0 = (unit & 1) * 8;
+      const int gn = n0 + col;
+      const int kw = p.K >> 5;  // 32-bit sign dwords per row
+      uint32_t dw = 0, mag = (BMODE == BM_ONE) ? 0x3c003c00u : 0u;
+      if (gn < p.N) {
+        dw = reinterpret_cast<const uint32_t*>(p.signs)[(size_t)gn * kw + (k0 >> 5) + q];
+        if (BMODE == BM_GROUP) {
+          const uint32_t s = p.scales[(size_t)gn * (p.K >> 7) + (k0 >> 7)];
+          mag = s | (s << 16);
+        }
+      }
+      rb[u] = make_uint2(dw, mag);
+      if (BMODE == BM_PERK) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(p.kperm + k0 + 32 * q + 2 * b0);
+        rk[u][0] = kp[0];
+        rk[u][1] = kp[1];
+      }
+    }
+  };
+
+  // ---- register -> LDS (convert / unpack) ---------------------------------
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < A_UNITS; ++u) {
+      const int unit = tid + 256 * u;
+      const int row = unit >> 2, q = (unit >> 1) & 1, b0 = (unit & 1) * 8;
+      uint32_t o[8];
+      if (AMODE == 0) {
+        const uint32_t lo[4] = {ra[u][0].x, ra[u][0].y, ra[u][0].z, ra[u][0].w};
+        const uint32_t hi[4] = {ra[u][1].x, ra[u][1].y, ra[u][1].z, ra[u][1].w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t a = (t & 1) ? (lo[t >> 1] & 0xffff0000u) : (lo[t >> 1] << 16);
+          const uint32_t c = (t & 1) ? (hi[t >> 1] & 0xffff0000u) : (hi[t >> 1] << 16);
+          o[t] = (uint32_t)f32_to_f16_bits(__uint_as_float(a)) |
+                 ((uint32_t)f32_to_f16_bits(__uint_as_float(c)) << 16);
+        }
+      } else {
+        o[0] = ra[u][0].x; o[1] = ra[u][0].y; o[2] = ra[u][0].z; o[3] = ra[u][0].w;
+        o[4] = ra[u][1].x; o[5] = ra[u][1].y; o[6] = ra[u][1].z; o[7] = ra[u][1].w;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(&As[buf][row * LDK + 32 * q + 2 * b0]);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+#pragma unroll
+    for (int u = 0; u < B_UNITS; ++u) {
+      const int unit = tid + 256 * u;
+      const int col = unit >> 2, q = (unit >> 1) & 1, b0 = (unit & 1) * 8;
+      const uint32_t dw = rb[u].x;
+      uint32_t o[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int bit = b0 + t;
+        const uint32_t mag = (BMODE == BM_PERK) ? rk[u][t >> 2][t & 3] : rb[u].y;
+        o[t] = ((dw << (15 - bit)) & 0x80008000u) | mag;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][col * LDK + 32 * q + 2 * b0]);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_stage(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      u32x4 af[TM], bfr[TN];
+      const int kofs = 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(&As[cur][(wr * WM + 32 * i + (lane & 31)) * LDK + kofs]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(&Bs[cur][(wc * WN + 32 * j + (lane & 31)) * LDK + kofs]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wc * WN + 32 * j + (lane & 31);
+      if (col >= p.N) continue;
+      const int rbase = m0 + wr * WM + 32 * i + 4 * (lane >> 5);
+      if (EPI == EPI_Y) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + 8 * (r >> 2) + (r & 3);
+          if (row < p.M) store_out(p.out, (size_t)row * p.N + col, acc[i][j][r], p.out_bf16);
+        }
+      } else if (EPI == EPI_HSPLIT) {
+        const float dm = f16_bits_to_f32(p.diag[col]);
+        uint16_t* hp = reinterpret_cast<uint16_t*>(p.out);
+        const int pc = perm_pos(col);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + 8 * (r >> 2) + (r & 3);
+          if (row < p.M) {
+            uint16_t hi, lo;
+            split_f16(acc[i][j][r] * dm, hi, lo);
+            hp[(size_t)(2 * row) * p.N + pc] = hi;
+            hp[(size_t)(2 * row + 1) * p.N + pc] = lo;
+          }
+        }
+      } else {  // EPI_PAIRSUM: rows 2t, 2t+1 are the two pieces of token t
+        const float dg = f16_bits_to_f32(p.diag[col]);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int row = rbase + 8 * (r >> 2) + (r & 3);
+          if (row < p.M) store_out(p.out, (size_t)(row >> 1) * p.N + col, (acc[i][j][r] + acc[i][j][r + 1]) * dg, p.out_bf16);
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int AMODE, int BMODE, int EPI>
+static hipError_t run_tile(const TileArgs& a, hipStream_t st) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_tile<BM, BN, AMODE, BMODE, EPI>), dim3(tiles), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
+                            const uint16_t* scales, void* y, int y_bf16, hipStream_t st) {
+  TileArgs a{};
+  a.a = x; a.M = M; a.N = N; a.K = K; a.signs = signs; a.scales = scales;
+  a.out = y; a.out_bf16 = y_bf16;
+  const long mid = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if (mid >= 256) return run_tile<128, 128, 0, BM_GROUP, EPI_Y>(a, st);
+  return run_tile<64, 64, 0, BM_GROUP, EPI_Y>(a, st);
+}
+
+hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st) {
+  const long mid = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (mid >= 256) return run_tile<128, 128, 0, BM_PERK, EPI_HSPLIT>(a, st);
+  return run_tile<64, 64, 0, BM_PERK, EPI_HSPLIT>(a, st);
+}
+
+hipError_t launch_tile_dbf2(const TileArgs& a, hipStream_t st) {
+  const long mid = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (mid >= 256) return run_tile<128, 128, 1, BM_ONE, EPI_PAIRSUM>(a, st);
+  return run_tile<64, 64, 1, BM_ONE, EPI_PAIRSUM>(a, st);
+}
+
+}  // namespace brq

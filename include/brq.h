@@ -1,0 +1,198 @@
+/*
+ * brq.h -- matrix products against binarized LLM weights on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbrq.so. Every pointer argument named as device memory must be a
+ * device (or device-accessible) pointer; every call enqueues its kernels on
+ * `stream` (a hipStream_t passed as void*, NULL = the null stream) and returns
+ * without synchronising the host. The library keeps no device memory of its
+ * own: buffers and workspaces are owned by the caller. A call that returns a
+ * status other than BRQ_OK has enqueued nothing and written nothing, except
+ * BRQ_E_HIP, which reports a failed launch.
+ *
+ * Formats (the pages these follow are named at each call):
+ *
+ *  SIGN1 plane   -- uint64_t words, 64 signs per word; element k of a row is
+ *                   bit (k % 64) of word (k / 64) of that row (least significant
+ *                   bit first); bit 0 means +1 and bit 1 means -1, the IEEE 754
+ *                   sign-bit convention ("LLM binarization, Episode 01: DBF",
+ *                   sections 1 and 3).
+ *  group-128     -- a SIGN1 plane plus one fp16 scale per run of 128 consecutive
+ *                   weights of a row ("Behaviour-Relearned Quantization", item 02:
+ *                   group-128 signs plus scales; "Banyan: Converting Pretrained
+ *                   Language Models to 1-Bit Weights ...", Abstract: one sign per
+ *                   weight and one shared scale per small group, 1.125 bits per
+ *                   weight). Scale of row n, group g at index n*(cols/128) + g.
+ *                   The dequantised weight is (bit ? -1 : +1) * scale.
+ *  activations   -- bf16 (raw uint16 bits), row-major [rows][cols].
+ *  outputs       -- bf16 or fp32 (brq_dtype), row-major. BRQ_BF16 is the fp32
+ *                   result rounded to nearest, ties to even.
+ *
+ * Numerics: every product multiplies exactly representable operands and
+ * accumulates in fp32. Activations are carried as fp16 inside the products;
+ * bf16 activations must satisfy |x| < 65504 (values below 2^-14 are kept on
+ * fp16's subnormal grid, an absolute change of at most 2^-25). fp32
+ * intermediates (DBF h, MoE SwiGLU output) are carried as an fp16 hi/lo pair
+ * (22 significant bits) under the same range condition.
+ *
+ * Alignment: weight planes, scales and activation rows must be 16-byte
+ * aligned; workspaces 256-byte aligned.
+ *
+ * Errors: each call validates its arguments on the host before touching the
+ * device, and returns a brq_status; brq_last_error() gives a thread-local text
+ * for the last non-OK status of the calling thread. Calls never abort.
+ */
+#ifndef BRQ_H
+#define BRQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BRQ_ABI_VERSION 1
+#define BRQ_GROUP 128
+
+typedef enum {
+  BRQ_OK = 0,
+  BRQ_E_NULL = 1,      /* a required pointer is NULL                                  */
+  BRQ_E_SHAPE = 2,     /* a size is out of range or not the multiple the format needs */
+  BRQ_E_ALIGN = 3,     /* a pointer is not aligned as stated above                    */
+  BRQ_E_DTYPE = 4,     /* unknown output dtype                                        */
+  BRQ_E_WORKSPACE = 5, /* workspace NULL, misaligned or smaller than its size query   */
+  BRQ_E_DEVICE = 6,    /* no current HIP device, or it is not gfx950                  */
+  BRQ_E_HIP = 7        /* a HIP runtime call or a kernel launch failed                */
+} brq_status;
+
+typedef enum { BRQ_BF16 = 0, BRQ_F32 = 1 } brq_dtype;
+
+/* Version of this header's ABI (BRQ_ABI_VERSION). */
+int brq_abi_version(void);
+
+/* Status name, e.g. "BRQ_E_SHAPE". Never NULL. */
+const char* brq_status_str(brq_status s);
+
+/* Text describing the last non-OK status returned on the calling thread
+   ("" if none). Valid until the next brq_* call on the same thread. */
+const char* brq_last_error(void);
+
+/* Number of uint64_t words of a SIGN1 plane of rows x cols (cols % 64 == 0). */
+size_t brq_sign_words(int64_t rows, int64_t cols);
+
+/* Number of fp16 scales of a group-128 matrix of rows x cols (cols % 128 == 0). */
+size_t brq_scale_count(int64_t rows, int64_t cols);
+
+/*
+ * brq_pack -- quantise fp32 weights to the group-128 format, or to a bare SIGN1
+ * plane.
+ *
+ * Follows "Behaviour-Relearned Quantization" (item 02), "Banyan ..." (Abstract)
+ * and "LLM binarization, Episode 01: DBF" (sections 1 and 3). For row n and
+ * group g: bit[n,k] = sign bit of w[n,k]; scale[n,g] = mean of |w[n,k]| over
+ * the 128 k of group g, accumulated in fp64 and rounded once to fp16 (nearest,
+ * ties to even). mean|w| is the least-squares optimum of
+ * ||w - a*sign(w)||^2 over a.
+ *
+ *   w       device, fp32 [rows][cols], row-major, 16-byte aligned
+ *   signs   device, out, brq_sign_words(rows, cols) words
+ *   scales  device, out, brq_scale_count(rows, cols) fp16 (raw bits), or NULL
+ *           to write the SIGN1 plane alone (the DBF factors carry no scale)
+ *   rows >= 1; cols % 128 == 0 when scales != NULL, else cols % 64 == 0.
+ */
+brq_status brq_pack(const float* w, int64_t rows, int64_t cols,
+                    uint64_t* signs, uint16_t* scales, void* stream);
+
+/*
+ * brq_gemm -- y[m][n] = sum_k x[m][k] * Wq[n][k]  (y = x . Wq^T), where Wq is
+ * the dequantised group-128 matrix [N][K]: the activation x binary-weight
+ * product ("Banyan ...", Abstract; "LLM binarization, Episode 01: DBF",
+ * section 1: a binary weight selects x or -x).
+ *
+ *   x       device, bf16 [M][K]
+ *   signs   device, SIGN1 plane of W [N][K]; scales device, fp16 [N][K/128]
+ *   y       device, out, [M][N] of y_dtype
+ *   ws      device workspace of at least brq_gemm_workspace_bytes(M, N, K)
+ *           bytes (may be NULL when that size is 0)
+ *   M >= 1, N >= 1, K >= 128 and K % 128 == 0.
+ */
+size_t brq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                    const uint64_t* signs, const uint16_t* scales,
+                    void* y, brq_dtype y_dtype,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * brq_dbf_gemm -- the Double Binary Factorization chain
+ *   y = D_out . U . D_mid . V . D_in . x   (one output row per row of x)
+ * evaluated in the deployed order x_s = D_in x; h = V x_s; h_s = D_mid h;
+ * y_core = U h_s; y = D_out y_core ("LLM binarization, Episode 01: DBF",
+ * section 1 for the representation, section 4 for the order and the record
+ * din / v / dmid / u / dout). h and h_s are kept in fp32.
+ *
+ *   x      device, bf16 [M][n]
+ *   d_in   device, fp16 [n];  v device, SIGN1 plane of V [r][n]
+ *   d_mid  device, fp16 [r];  u device, SIGN1 plane of U [m][r]
+ *   d_out  device, fp16 [m]
+ *   y      device, out, [M][m] of y_dtype
+ *   ws     device workspace, >= brq_dbf_workspace_bytes(M, m, n, r)
+ *   M >= 1; m >= 1; n, r >= 128 and multiples of 128.
+ */
+size_t brq_dbf_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
+brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int64_t r,
+                        const uint16_t* d_in, const uint64_t* v, const uint16_t* d_mid,
+                        const uint64_t* u, const uint16_t* d_out,
+                        void* y, brq_dtype y_dtype,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * brq_moe_ffn -- routed mixture-of-experts SwiGLU layer on group-128 experts:
+ *   for each token t: ids = the top_k experts by descending fp32 router logit
+ *   (ties to the lower expert index); w = softmax over the top_k selected
+ *   logits; y_t = sum_j w_j * Wd_e (silu(Wg_e x_t) * (Wu_e x_t)), e = ids_j,
+ *   silu(z) = z / (1 + exp(-z)).
+ * Each (token, slot) route carries an expert id and a route weight; gate/up
+ * share the token's hidden vector across its experts, down consumes the
+ * route's own intermediate ("LLM binarization, Episode 01: DBF", section 4).
+ * 256 experts with 8 routed and an f32 router is the layer of the "BTL-4
+ * Compact" news item. The sum over slots is taken in slot order (deterministic).
+ *
+ *   x        device, bf16 [T][H];  logits device, fp32 [T][E]
+ *   gate_s / up_s    device, SIGN1 planes [E][I][H/64]; gate_sc / up_sc fp16 [E][I][H/128]
+ *   down_s           device, SIGN1 plane [E][H][I/64];   down_sc fp16 [E][H][I/128]
+ *   y        device, out, [T][H] of y_dtype
+ *   ids, w   device, out, [T][top_k] int32 / fp32, or NULL
+ *   ws       device workspace, >= brq_moe_workspace_bytes(T, H, I, E, top_k)
+ *   1 <= T <= 256; 1 <= top_k <= min(E, 16); 1 <= E <= 1024;
+ *   H, I multiples of 128 in [128, 65536].
+ */
+size_t brq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
+brq_status brq_moe_ffn(const uint16_t* x, const float* logits,
+                       int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                       const uint64_t* gate_s, const uint16_t* gate_sc,
+                       const uint64_t* up_s, const uint16_t* up_sc,
+                       const uint64_t* down_s, const uint16_t* down_sc,
+                       void* y, brq_dtype y_dtype,
+                       int32_t* ids, float* w,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * brq_kron_rotate -- Kronecker-factored orthogonal activation rotation
+ *   x'_t = (H (x) R) x_t, computed as X'_t = H . X_t . R^T where X_t is row t
+ *   of x reshaped row-major to [n1][n2]
+ * (BWLA commentary: section 3, OKT with Kronecker factors H and R, n1*n2 = n;
+ * section 5, the same orthogonal transform applied to the activations so that
+ * the product with the correspondingly rotated weights is unchanged).
+ * fp32 arithmetic; the output is rounded to bf16 (nearest, ties to even).
+ *
+ *   x   device, bf16 [M][n1*n2];  H device, fp32 [n1][n1];  R device, fp32 [n2][n2]
+ *   y   device, out, bf16 [M][n1*n2]; must not overlap x
+ *   M >= 1; n1 == n2 == 64.
+ */
+brq_status brq_kron_rotate(const uint16_t* x, int64_t M, const float* H, int64_t n1,
+                           const float* R, int64_t n2, uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BRQ_H */

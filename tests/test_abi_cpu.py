@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/brq.h declares, and rejects invalid arguments with the documented
+status before touching a device. No compute call runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import binary_weight_gemm_amd as brq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_WORKSPACE, E_DEVICE, E_HIP = range(8)
+P = ctypes.c_void_p(1 << 20)        # a non-NULL, aligned, never dereferenced address
+PMIS = ctypes.c_void_p((1 << 20) + 2)
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "brq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(brq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return brq.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert len(names) == 13, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(brq.ABI_FUNCTIONS)
+
+
+def test_version_and_status_strings(L):
+    assert L.brq_abi_version() == 1
+    assert L.brq_status_str(E_SHAPE) == b"BRQ_E_SHAPE"
+    assert L.brq_status_str(OK) == b"BRQ_OK"
+    assert L.brq_status_str(99) == b"BRQ_E_UNKNOWN"
+
+
+def test_size_queries(L):
+    assert L.brq_sign_words(4096, 14336) == 4096 * 224
+    assert L.brq_scale_count(4096, 14336) == 4096 * 112
+    assert L.brq_sign_words(3, 65) == 0
+    assert L.brq_scale_count(3, 64) == 0
+    assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 14336 * 2
+    assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 0
+    assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0
+    assert L.brq_dbf_workspace_bytes(1, 4096, 4096, 2048) > 0
+    assert L.brq_moe_workspace_bytes(1, 2048, 512, 256, 8) > 0
+    assert L.brq_moe_workspace_bytes(300, 2048, 512, 256, 8) == 0
+    assert L.brq_moe_workspace_bytes(1, 2048, 512, 256, 17) == 0
+
+
+def _err(L):
+    return L.brq_last_error().decode()
+
+
+def test_pack_validation(L):
+    assert L.brq_pack(None, 4, 128, P, P, None) == E_NULL
+    assert "NULL" in _err(L)
+    assert L.brq_pack(P, 0, 128, P, P, None) == E_SHAPE
+    assert L.brq_pack(P, 4, 100, P, P, None) == E_SHAPE
+    assert L.brq_pack(P, 4, 64, P, P, None) == E_SHAPE       # scales need cols % 128
+    assert L.brq_pack(PMIS, 4, 128, P, P, None) == E_ALIGN
+
+
+def test_gemm_validation(L):
+    g = L.brq_gemm
+    assert g(None, 1, 16, 128, P, P, P, 0, P, 1 << 20, None) == E_NULL
+    assert g(P, 0, 16, 128, P, P, P, 0, P, 1 << 20, None) == E_SHAPE
+    assert g(P, 1, 0, 128, P, P, P, 0, P, 1 << 20, None) == E_SHAPE
+    assert g(P, 1, 16, 192, P, P, P, 0, P, 1 << 20, None) == E_SHAPE
+    assert g(P, 1, 16, 128, P, P, P, 7, P, 1 << 20, None) == E_DTYPE
+    assert g(P, 1, 16, 128, P, PMIS, P, 0, P, 1 << 20, None) == E_ALIGN
+    assert g(P, 1, 16, 128, P, P, P, 0, None, 0, None) == E_WORKSPACE
+    assert g(P, 1, 16, 128, P, P, P, 0, P, 10, None) == E_WORKSPACE
+    assert "workspace" in _err(L)
+
+
+def test_dbf_validation(L):
+    f = L.brq_dbf_gemm
+    args = [P, 1, 4096, 4096, 2048, P, P, P, P, P, P, 0, P, 1 << 30, None]
+    bad = list(args); bad[5] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[3] = 4000
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[4] = 100
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[11] = 5
+    assert f(*bad) == E_DTYPE
+    bad = list(args); bad[13] = 16
+    assert f(*bad) == E_WORKSPACE
+
+
+def test_moe_validation(L):
+    f = L.brq_moe_ffn
+    args = [P, P, 1, 2048, 512, 256, 8, P, P, P, P, P, P, P, 0, None, None, P, 1 << 30, None]
+    bad = list(args); bad[1] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[2] = 0
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[2] = 257
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[6] = 300
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[3] = 2000
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[12] = PMIS
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[18] = 8
+    assert f(*bad) == E_WORKSPACE
+
+
+def test_kron_validation(L):
+    f = L.brq_kron_rotate
+    assert f(None, 4, P, 64, P, 64, P, None) == E_NULL
+    assert f(P, 4, P, 32, P, 128, ctypes.c_void_p(1 << 30), None) == E_SHAPE
+    assert f(P, 4, P, 64, P, 64, P, None) == E_SHAPE         # x and y overlap
+    assert f(PMIS, 4, P, 64, P, 64, ctypes.c_void_p(1 << 30), None) == E_ALIGN
+
+
+def test_device_check_without_gpu(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; valid arguments would reach the device")
+    assert L.brq_pack(P, 4, 128, P, P, None) == E_DEVICE
+    assert L.brq_gemm(P, 1, 16, 128, P, P, P, 0, P, 1 << 20, None) == E_DEVICE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    w = torch.zeros((4, 128), dtype=torch.float32)
+    with pytest.raises(brq.BrqError):
+        brq.pack(w)

@@ -1,0 +1,358 @@
+"""GPU parity: every C-ABI call against the fp64 oracle on the same seeded
+inputs, element by element.
+
+Bars (see the header of include/brq.h for the numerics):
+* sign planes bit-exact; fp16 scales within 1 ulp (counted; expected 0 off);
+* products with fp32 output: max_i|g_i - o_i| / max_i|o_i| <= F32_TOL, small
+  enough that one flipped sign or one dropped group fails;
+* products with bf16 output: every element within 1 bf16 ulp of the oracle
+  rounded to bf16 (or within 1e-5 of the largest output, for outputs so near
+  zero that fp32 accumulation error spans several of their ulps), and l2 relative error <= 2e-3 (bf16 rounding alone reaches
+  2^-8 relative per element, so the 2e-3 bar is applied normwise there);
+* top-k expert ids bit-exact, route weights within 1e-6 relative.
+
+Product parity feeds the oracle's packed bytes to the device, so a scale that
+legitimately differs by one ulp cannot hide a product error; the end-to-end
+cases use device-packed weights instead.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_util import bf16_close, bf16_ulps, check_bf16, check_f32, dev, f16_ulps, f64, host_bits, l2rel, maxrel
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 2e-5
+
+
+def brq():
+    import binary_weight_gemm_amd as b
+    return b
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# S1 pack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,key", [(1, 128, 1), (17, 384, 2), (1024, 1024, 3), (64, 2048, 4)])
+def test_pack_small(rows, cols, key):
+    say("pack", rows, cols)
+    w = datagen.normal_f32((70, key), (rows, cols), 0.02)
+    w[0, :5] = [0.0, -0.0, 1e-30, -1e-30, 0.5]
+    ow, osc = oracle.pack_sign1(w)
+    s, sc = brq().pack(dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(s), ow)
+    ul = f16_ulps(host_bits(sc), osc)
+    assert ul.max() <= 1 and int((ul > 0).sum()) <= max(1, ul.size // 10000)
+
+
+def test_pack_sign1_only_and_c2_full():
+    say("pack sign1-only 2048x4096, pack C2 4096x14336")
+    v = datagen.pm1_f32((3, 0, 2048), (2048, 4096))
+    s, sc = brq().pack(dev(v), scales=False)
+    assert sc is None
+    assert np.array_equal(host_bits(s), oracle.pack_sign1_only(v))
+    w = datagen.C2_weight(0)
+    ow, osc = oracle.pack_sign1(w)
+    s, sc = brq().pack(dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(s), ow)
+    ul = f16_ulps(host_bits(sc), osc)
+    assert ul.max() <= 1
+    assert int((ul > 0).sum()) <= 8, int((ul > 0).sum())
+
+
+def test_pack_round_trip_exact_groups():
+    say("pack round trip")
+    N, K = 8, 512
+    a = np.array([0.5, 0.015625, 3.0, 1e-3, 65504.0, 6.1035156e-05, 0.0123, 7.0], dtype=np.float16)
+    w = (datagen.pm1_f32((96, 0), (N, K)) * np.repeat(a.astype(np.float32)[:, None], K, axis=1)).astype(np.float32)
+    s, sc = brq().pack(dev(w))
+    ow, osc = oracle.pack_sign1(w)
+    assert np.array_equal(host_bits(s), ow)
+    assert np.array_equal(host_bits(sc), osc.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# S2 / S3 products
+# ---------------------------------------------------------------------------
+
+def _gemm_case(M, N, K, key, out=torch.float32):
+    w = datagen.normal_f32((71, key, 0), (N, K), 0.02)
+    x = datagen.bf16_normal((71, key, 1), (M, K))
+    ow, osc = oracle.pack_sign1(w)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(x), ow, osc, N, K)
+    y = brq().gemm(dev(x), dev(ow), dev(osc), N, K, out_dtype=out)
+    torch.cuda.synchronize()
+    return y, o
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (1, 40, 640), (3, 48, 1024), (16, 33, 256), (17, 64, 512),
+                                   (64, 32, 2048), (5, 16, 14336), (1, 1024, 1024)])
+def test_gemm_decode_f32(M, N, K):
+    say("gemm decode f32", M, N, K)
+    y, o = _gemm_case(M, N, K, M * 1000 + N)
+    check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 40, 640), (64, 96, 1024)])
+def test_gemm_decode_bf16(M, N, K):
+    say("gemm decode bf16", M, N, K)
+    y, o = _gemm_case(M, N, K, M * 1000 + N + 7, out=torch.bfloat16)
+    check_bf16(y, o, f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 64, 256), (128, 128, 512), (300, 200, 384), (512, 1024, 1024)])
+def test_gemm_tiled_f32(M, N, K):
+    say("gemm tiled f32", M, N, K)
+    y, o = _gemm_case(M, N, K, M * 1000 + N + 3)
+    check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
+
+
+def test_gemm_tiled_bf16():
+    say("gemm tiled bf16 257x320x768")
+    y, o = _gemm_case(257, 320, 768, 99, out=torch.bfloat16)
+    check_bf16(y, o, "gemm tiled bf16")
+
+
+def test_gemm_c1():
+    say("C1 gemv")
+    w, x = datagen.C1()
+    ow, osc = oracle.pack_sign1(w)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(x), ow, osc, 1024, 1024)
+    for out in (torch.float32, torch.bfloat16):
+        y = brq().gemm(dev(x), dev(ow), dev(osc), 1024, 1024, out_dtype=out)
+        if out == torch.float32:
+            check_f32(f64(y), o, F32_TOL, "C1")
+        else:
+            check_bf16(y, o, "C1")
+
+
+@pytest.fixture(scope="module")
+def c2_packed():
+    out = []
+    for which in (0, 1):
+        w = datagen.C2_weight(which)
+        out.append(oracle.pack_sign1(w))
+    return out
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_gemm_c2_full(c2_packed, which, M):
+    N, K = datagen.C2_SHAPES[which]
+    say("C2 gemm", which, M, N, K)
+    ow, osc = c2_packed[which]
+    x = datagen.C2_x(which, M)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(x), ow, osc, N, K)
+    y = brq().gemm(dev(x), dev(ow), dev(osc), N, K, out_dtype=torch.float32)
+    check_f32(f64(y), o, F32_TOL, f"C2 {which} M={M}")
+    yb = brq().gemm(dev(x), dev(ow), dev(osc), N, K, out_dtype=torch.bfloat16)
+    # the bf16 output is the fp32 result rounded to nearest even
+    assert np.array_equal(host_bits(yb), oracle.bf16_bits(oracle.round_bf16(f64(y))))
+    check_bf16(yb, o, f"C2 {which} M={M} bf16")
+
+
+def test_gemm_deterministic_and_batch_invariant(c2_packed):
+    say("determinism + batch invariance")
+    ow, osc = c2_packed[0]
+    N, K = datagen.C2_SHAPES[0]
+    x = dev(datagen.C2_x(0, 16))
+    S, SC = dev(ow), dev(osc)
+    a = brq().gemm(x, S, SC, N, K, out_dtype=torch.float32)
+    b = brq().gemm(x, S, SC, N, K, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+    for m in (0, 5, 15):
+        r = brq().gemm(x[m:m + 1].contiguous(), S, SC, N, K, out_dtype=torch.float32)
+        assert maxrel(f64(r[0]), f64(a[m])) <= 1e-6
+
+
+def test_gemm_end_to_end_device_packed():
+    say("gemm with device-packed weights 1024x2048")
+    N, K, M = 1024, 2048, 8
+    w = datagen.normal_f32((72, 0), (N, K), 0.02)
+    x = datagen.bf16_normal((72, 1), (M, K))
+    ow, osc = oracle.pack_sign1(w)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(x), ow, osc, N, K)
+    s, sc = brq().pack(dev(w))
+    y = brq().gemm(dev(x), s, sc, N, K, out_dtype=torch.float32)
+    check_f32(f64(y), o, 1e-3, "device-packed")   # scales may differ by one fp16 ulp
+
+
+# ---------------------------------------------------------------------------
+# S4 DBF
+# ---------------------------------------------------------------------------
+
+def _dbf_case(M, m, n, r, key, out=torch.float32):
+    v = datagen.pm1_f32((73, key, 0), (r, n))
+    u = datagen.pm1_f32((73, key, 1), (m, r))
+    d_in = datagen.f16_lognormal((73, key, 2), (n,))
+    d_mid = datagen.f16_lognormal((73, key, 3), (r,))
+    d_out = datagen.f16_lognormal((73, key, 4), (m,))
+    x = datagen.bf16_normal((73, key, 5), (M, n))
+    vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
+    o = oracle.dbf_chain(oracle.bf16_to_f64(x), d_in, vw, d_mid, uw, d_out, m, n, r)
+    y = brq().dbf_gemm(dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r, out_dtype=out)
+    torch.cuda.synchronize()
+    return y, o
+
+
+@pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (1, 48, 256, 384), (3, 200, 512, 256), (32, 64, 640, 512),
+                                     (33, 96, 256, 128), (100, 256, 512, 384)])
+def test_dbf_small(M, m, n, r):
+    say("dbf", M, m, n, r)
+    y, o = _dbf_case(M, m, n, r, M + m + n + r)
+    check_f32(f64(y), o, F32_TOL, f"dbf {M},{m},{n},{r}")
+
+
+@pytest.mark.parametrize("M", [1, 512])
+def test_dbf_c3(M):
+    say("C3 dbf", M)
+    d = datagen.C3(M)
+    vw, uw = oracle.pack_sign1_only(d["v"]), oracle.pack_sign1_only(d["u"])
+    m, n, r = d["m"], d["n"], d["r"]
+    o = oracle.dbf_chain(oracle.bf16_to_f64(d["x"]), d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
+    args = (dev(d["x"]), dev(d["d_in"]), dev(vw), dev(d["d_mid"]), dev(uw), dev(d["d_out"]), m, n, r)
+    y = brq().dbf_gemm(*args, out_dtype=torch.float32)
+    check_f32(f64(y), o, F32_TOL, f"C3 M={M}")
+    yb = brq().dbf_gemm(*args, out_dtype=torch.bfloat16)
+    check_bf16(yb, o, f"C3 M={M} bf16")
+
+
+def test_dbf_device_packed_factors():
+    say("dbf with device-packed SIGN1 factors")
+    m, n, r, M = 128, 256, 128, 2
+    v = datagen.pm1_f32((74, 0), (r, n))
+    u = datagen.pm1_f32((74, 1), (m, r))
+    d_in = datagen.f16_lognormal((74, 2), (n,))
+    d_mid = datagen.f16_lognormal((74, 3), (r,))
+    d_out = datagen.f16_lognormal((74, 4), (m,))
+    x = datagen.bf16_normal((74, 5), (M, n))
+    o = oracle.dbf_chain(oracle.bf16_to_f64(x), d_in, oracle.pack_sign1_only(v), d_mid, oracle.pack_sign1_only(u),
+                         d_out, m, n, r)
+    vs, _ = brq().pack(dev(v), scales=False)
+    us, _ = brq().pack(dev(u), scales=False)
+    y = brq().dbf_gemm(dev(x), dev(d_in), vs, dev(d_mid), us, dev(d_out), m, n, r, out_dtype=torch.float32)
+    check_f32(f64(y), o, F32_TOL, "dbf device-packed")
+
+
+# ---------------------------------------------------------------------------
+# S5 / S6 MoE
+# ---------------------------------------------------------------------------
+
+class _Experts:
+    def __init__(self, cfg: datagen.C4):
+        self.cfg = cfg
+        E, H, I = cfg.E, cfg.H, cfg.I
+        self.gw = np.zeros((E, I, H // 64), np.uint64)
+        self.gs = np.zeros((E, I, H // 128), np.float16)
+        self.uw = np.zeros_like(self.gw)
+        self.us = np.zeros_like(self.gs)
+        self.dw = np.zeros((E, H, I // 64), np.uint64)
+        self.ds = np.zeros((E, H, I // 128), np.float16)
+        for e in range(E):
+            self.gw[e], self.gs[e] = oracle.pack_sign1(cfg.gate(e))
+            self.uw[e], self.us[e] = oracle.pack_sign1(cfg.up(e))
+            self.dw[e], self.ds[e] = oracle.pack_sign1(cfg.down(e))
+        self.d = [dev(a) for a in (self.gw, self.gs, self.uw, self.us, self.dw, self.ds)]
+
+    def __call__(self, e):
+        return self.gw[e], self.gs[e], self.uw[e], self.us[e], self.dw[e], self.ds[e]
+
+
+@pytest.fixture(scope="module")
+def c4_experts():
+    return _Experts(datagen.C4())
+
+
+def _moe_check(ex, T, it=0, out=torch.float32):
+    c = ex.cfg
+    x = c.x(T)
+    lg = c.logits(T, it)
+    o, oids, ow = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, c.H, c.I, c.top_k)
+    y, ids, w = brq().moe_ffn(dev(x), dev(lg), *ex.d, c.E, c.H, c.I, c.top_k, out_dtype=out, return_routing=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids), "top-k ids differ"
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=1e-7)
+    return y, o
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
+def test_moe_c4(c4_experts, T):
+    say("C4 moe", T)
+    y, o = _moe_check(c4_experts, T)
+    check_f32(f64(y), o, F32_TOL, f"moe T={T}")
+
+
+def test_moe_c4_bf16_and_fresh_logits(c4_experts):
+    say("C4 moe bf16, several logit draws")
+    for it in range(3):
+        y, o = _moe_check(c4_experts, 4, it=it + 1, out=torch.bfloat16)
+        check_bf16(y, o, f"moe bf16 it={it}")
+
+
+def test_moe_ties_and_small_shapes():
+    say("moe ties, E=8 H=256 I=128 k=3")
+    cfg = datagen.C4(E=8, H=256, I=128, top_k=3, layer=5)
+    ex = _Experts(cfg)
+    T = 5
+    x = cfg.x(T)
+    lg = np.zeros((T, 8), np.float32)
+    lg[1] = np.round(cfg.logits(1)[0], 0)
+    lg[2, [2, 6, 7]] = 1.5
+    lg[3] = np.arange(8, dtype=np.float32)[::-1]
+    lg[4] = cfg.logits(1, 9)[0]
+    o, oids, ow = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, 3)
+    y, ids, w = brq().moe_ffn(dev(x), dev(lg), *ex.d, 8, cfg.H, cfg.I, 3, out_dtype=torch.float32,
+                              return_routing=True)
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    check_f32(f64(y), o, F32_TOL, "moe ties")
+
+
+# ---------------------------------------------------------------------------
+# S7 Kronecker rotation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 7, 4096])
+def test_kron(M):
+    say("kron", M)
+    d = datagen.C5(M=M)
+    o = oracle.kron_rotate(oracle.bf16_to_f64(d["x"]), d["H"], d["R"])
+    y = brq().kron_rotate(dev(d["x"]), dev(d["H"]), dev(d["R"]))
+    torch.cuda.synchronize()
+    assert bf16_close(host_bits(y), o).all()
+    assert l2rel(f64(y), o) <= 2e-3
+
+
+def test_c5_prefill_sampled_columns():
+    say("C5 rotate + prefill gemm, sampled columns")
+    d = datagen.C5()
+    N, K = d["N"], d["K"]
+    w = datagen.C5_weight(N, K)
+    ow, osc = oracle.pack_sign1(w)
+    xr = brq().kron_rotate(dev(d["x"]), dev(d["H"]), dev(d["R"]))
+    y = brq().gemm(xr, dev(ow), dev(osc), N, K, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cols = np.sort(datagen.rng(75, 0).choice(N, size=96, replace=False))
+    xo = oracle.kron_rotate_bf16(oracle.bf16_to_f64(d["x"]), d["H"], d["R"])
+    o = oracle.bin_gemm_cols(xo, ow, osc, N, K, cols)
+    # end to end: the rotated activations may differ from the oracle's by one
+    # bf16 ulp where fp32 and fp64 straddle a rounding midpoint
+    check_f32(f64(y)[:, cols], o, 1e-4, "C5 e2e")
+    # product parity on the oracle's rotated activations
+    xo_bits = oracle.bf16_bits(xo)
+    y2 = brq().gemm(dev(xo_bits), dev(ow), dev(osc), N, K, out_dtype=torch.float32)
+    yb2 = brq().gemm(dev(xo_bits), dev(ow), dev(osc), N, K, out_dtype=torch.bfloat16)
+    sel = torch.from_numpy(cols).cuda()
+    check_f32(f64(y2)[:, cols], o, F32_TOL, "C5 gemm")
+    check_bf16(yb2[:, sel].contiguous(), o, "C5 gemm bf16")
