@@ -71,7 +71,9 @@ brq_status hip_result(hipError_t e, const char* what) {
 
 bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
 
-size_t gemm_ws(int64_t M, int64_t K) { return M <= 64 ? brq::align256((size_t)M * K * 2) : 0; }
+size_t gemm_ws(int64_t M, int64_t K) {
+  return (M <= 64 && !brq::gemm_dec_in_lds(M, K)) ? brq::align256((size_t)M * K * 2) : 0;
+}
 
 }  // namespace
 
@@ -143,12 +145,8 @@ brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const ui
   if (s != BRQ_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const int yb = y_dtype == BRQ_BF16;
-  if (M <= 64) {
-    uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-    hipError_t e = brq::launch_prep_bf16(x, M, K, xp, st);
-    if (e != hipSuccess) return hip_result(e, "brq_gemm (stage activations)");
-    return hip_result(brq::launch_gemm_dec(xp, (int)M, (int)N, (int)K, signs, scales, y, yb, st), "brq_gemm");
-  }
+  if (M <= 64)
+    return hip_result(brq::launch_gemm_dec(x, (int)M, (int)N, (int)K, signs, scales, y, yb, ws, st), "brq_gemm");
   return hip_result(brq::launch_gemm_tile(x, (int)M, (int)N, (int)K, signs, scales, y, yb, st), "brq_gemm");
 }
 
@@ -183,7 +181,8 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
 }
 
 size_t brq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
-  if (T < 1 || T > 256 || H < 128 || I < 128 || H % 128 || I % 128 || E < 1 || E > 1024 || top_k < 1 ||
+  if (T < 1 || T > 256 || H < 128 || I < 128 || H > 32768 || I > 2048 || H % 128 || I % 128 || E < 1 ||
+      E > 1024 || top_k < 1 ||
       top_k > 16 || top_k > E)
     return 0;
   return brq::moe_ws_bytes(T, H, I, E, top_k);
@@ -199,8 +198,8 @@ brq_status brq_moe_ffn(const uint16_t* x, const float* logits, int64_t T, int64_
   if (E < 1 || E > 1024) return fail(BRQ_E_SHAPE, "brq_moe_ffn: E=%lld must be in [1, 1024]", (long long)E);
   if (top_k < 1 || top_k > 16 || top_k > E)
     return fail(BRQ_E_SHAPE, "brq_moe_ffn: top_k=%lld must be in [1, min(E, 16)]", (long long)top_k);
-  if (H < 128 || I < 128 || H > 65536 || I > 65536 || H % 128 || I % 128)
-    return fail(BRQ_E_SHAPE, "brq_moe_ffn: H=%lld and I=%lld must be multiples of 128 in [128, 65536]",
+  if (H < 128 || I < 128 || H > 32768 || I > 2048 || H % 128 || I % 128)
+    return fail(BRQ_E_SHAPE, "brq_moe_ffn: H=%lld and I=%lld must be multiples of 128, H <= 32768, I <= 2048",
                 (long long)H, (long long)I);
   if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_ffn: unknown y_dtype %d", (int)y_dtype);
   if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(gate_s, 16) || !aligned(up_s, 16) || !aligned(down_s, 16) ||

@@ -16,28 +16,52 @@
 
 namespace brq {
 
-template <int TT>
-__global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ xp, int M, int r, int n,
-                                                   const uint4* __restrict__ v, const u32x4* __restrict__ dinp,
+// Decode path, stage 1: every wave stages its K-slice of x (bf16 -> permuted
+// fp16) and of d_in (permuted) in LDS after issuing its loads; D_in rides on
+// the weight operand (+-d_in[k]).
+template <int TT, int CPW, int MAXR>
+__global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ x, int M, int r, int n,
+                                                   const uint4* __restrict__ v, const uint16_t* __restrict__ d_in,
                                                    const uint16_t* __restrict__ d_mid, uint16_t* __restrict__ hp) {
-  __shared__ f32x4 red[15 * TT * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int col = blockIdx.x * 16 + j;  // row of V = output column of stage 1
   const int G = n >> 7;
-  const uint4* wsig[1] = {col < r ? v + (size_t)col * G : nullptr};
+  const int nchunks = (G + 3) >> 2;
+  const uint4* wsig[1] = {v + (size_t)(col < r ? col : 0) * G};
   const uint16_t* wsc[1] = {nullptr};
-  const u32x4* arow[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int m = 16 * tt + j;
-    arow[tt] = m < M ? reinterpret_cast<const u32x4*>(xp + (size_t)m * n) : nullptr;
-  }
+  const bool rok[1] = {col < r};
+  const int c0 = wave * CPW;
+  // LDS: x slices of all waves (MAXR row slots), then the d_in slices
+  uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+  uint4* dw = smem + (size_t)(blockDim.x / 64) * CPW * MAXR * 64 + (size_t)wave * CPW * 64;
+  BPre<1, CPW> bp;
   f32x4 acc[1][TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  dec_core<BM_PERK, 1, TT>(wsig, wsc, dinp, arow, G, wave, nw, acc);
-  reduce_waves<1, TT>(acc, red);
+  if (c0 < nchunks) {
+    WaveStage<ST_BF16, CPW, MAXR> sx;
+    WaveStage<ST_F16, CPW, 1> sd;
+    sx.load(M, n, c0, [&](int m) { return x + (size_t)m * n; });
+    sd.load(1, n, c0, [&](int) { return d_in; });
+    b_prefetch<BM_PERK, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sx.store(xw);
+    sd.store(dw);
+  }
+  __syncthreads();
+  if (c0 < nchunks) {
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(dw) - (size_t)c0 * 64;
+    auto aop = [&](int tt, int g, int i) -> u32x4 {
+      const int m = min(16 * tt + j, M - 1);
+      return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_PERK, 1, TT, CPW>(bp, kp, G, c0, 1, aop, acc);
+  }
+  __syncthreads();
+  reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
   if (wave != 0 || col >= r) return;
   const float dm = f16_bits_to_f32(d_mid[col]);
   const int pc = perm_pos(col);
@@ -55,28 +79,47 @@ __global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ 
     }
 }
 
-template <int TT>
+// Decode path, stage 2: the two fp16 pieces of every h_s row are staged in LDS
+// (two A rows per token, per-wave slices); U operands are +-1; D_out in the
+// epilogue.
+template <int TT, int CPW, int MAXR>
 __global__ __launch_bounds__(1024) void k_dbf2_dec(const uint16_t* __restrict__ hp, int M, int m, int r,
                                                    const uint4* __restrict__ u, const uint16_t* __restrict__ d_out,
                                                    void* __restrict__ y, int y_bf16) {
-  __shared__ f32x4 red[15 * TT * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int col = blockIdx.x * 16 + j;  // row of U = output column
   const int G = r >> 7;
-  const uint4* wsig[1] = {col < m ? u + (size_t)col * G : nullptr};
+  const int nchunks = (G + 3) >> 2;
+  const int rows = 2 * M;
+  const uint4* wsig[1] = {u + (size_t)(col < m ? col : 0) * G};
   const uint16_t* wsc[1] = {nullptr};
-  const u32x4* arow[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int pr = 16 * tt + j;  // piece row: token pr/2, piece pr%2
-    arow[tt] = pr < 2 * M ? reinterpret_cast<const u32x4*>(hp + (size_t)pr * r) : nullptr;
-  }
+  const bool rok[1] = {col < m};
+  const int c0 = wave * CPW;
+  uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+  BPre<1, CPW> bp;
   f32x4 acc[1][TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  dec_core<BM_ONE, 1, TT>(wsig, wsc, nullptr, arow, G, wave, nw, acc);
-  reduce_waves<1, TT>(acc, red);
+  if (c0 < nchunks) {
+    WaveStage<ST_COPY, CPW, MAXR> sh;
+    sh.load(rows, r, c0, [&](int pr) { return hp + (size_t)pr * r; });
+    b_prefetch<BM_ONE, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sh.store(xw);
+  }
+  __syncthreads();
+  if (c0 < nchunks) {
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    auto aop = [&](int tt, int g, int i) -> u32x4 {
+      const int pr = min(16 * tt + j, rows - 1);  // piece row: token pr/2, piece pr%2
+      return xs[(((g >> 2) - c0) * MAXR + pr) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_ONE, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+  }
+  __syncthreads();
+  reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
   if (wave != 0 || col >= m) return;
   const float dg = f16_bits_to_f32(d_out[col]);
 #pragma unroll
@@ -88,44 +131,64 @@ __global__ __launch_bounds__(1024) void k_dbf2_dec(const uint16_t* __restrict__ 
     }
 }
 
+// Decode path: per-wave staging of the x slice plus d_in (stage 1) and of the
+// 2M h_s piece rows (stage 2) within the LDS budget, M <= 8.
+static bool dbf_split(int64_t rows, int64_t K, DecSplit& sp) {
+  const int64_t chunks = (K / 128 + 3) / 4;
+  if (chunks > 64) return false;
+  sp = dec_split((int)(K / 128), 4);
+  if ((int64_t)sp.waves * sp.cpw < chunks) sp = dec_split((int)(K / 128), 8);
+  if ((int64_t)sp.waves * sp.cpw < chunks) return false;
+  return (int64_t)sp.waves * sp.cpw * rows * 1024 <= kDecLdsBytes;
+}
+
+static int dbf_maxr(int64_t M) { return M <= 1 ? 1 : M <= 4 ? 4 : 8; }
+
+static bool dbf_decode_path(int64_t M, int64_t n, int64_t r) {
+  DecSplit a, b;
+  return M <= 8 && dbf_split(dbf_maxr(M) + 1, n, a) && dbf_split(2 * dbf_maxr(M), r, b);
+}
+
 size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
   (void)m;
-  return align256((size_t)M * n * 2) + align256((size_t)n * 2) + align256((size_t)2 * M * r * 2);
+  const size_t hp = align256((size_t)2 * M * r * 2);
+  if (dbf_decode_path(M, n, r)) return hp;
+  return hp + align256((size_t)n * 2);
+}
+
+template <int MAXR1, int MAXR2>
+static hipError_t dbf_decode(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
+                             const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
+                             uint16_t* hp, hipStream_t st) {
+  DecSplit s1, s2;
+  dbf_split(MAXR1 + 1, n, s1);
+  dbf_split(MAXR2, r, s2);
+  const size_t l1 = (size_t)s1.waves * s1.cpw * (MAXR1 + 1) * 1024, r1 = (size_t)(s1.waves - 1) * 64 * 16;
+  const size_t l2 = (size_t)s2.waves * s2.cpw * MAXR2 * 1024, r2 = (size_t)(s2.waves - 1) * 64 * 16;
+  const uint4* v4 = reinterpret_cast<const uint4*>(v);
+  const uint4* u4 = reinterpret_cast<const uint4*>(u);
+  BRQ_CPW_SWITCH(s1.cpw, hipLaunchKernelGGL((k_dbf1_dec<1, CPW, MAXR1>), dim3((r + 15) / 16), dim3(64 * s1.waves),
+                                            l1 > r1 ? l1 : r1, st, x, M, r, n, v4, d_in, d_mid, hp));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BRQ_CPW_SWITCH(s2.cpw, hipLaunchKernelGGL((k_dbf2_dec<1, CPW, MAXR2>), dim3((m + 15) / 16), dim3(64 * s2.waves),
+                                            l2 > r2 ? l2 : r2, st, hp, M, m, r, u4, d_out, y, y_bf16));
+  return hipGetLastError();
 }
 
 hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in,
                       const uint64_t* v, const uint16_t* d_mid, const uint64_t* u,
                       const uint16_t* d_out, void* y, int y_bf16, void* ws, hipStream_t st) {
   char* base = reinterpret_cast<char*>(ws);
-  uint16_t* xp = reinterpret_cast<uint16_t*>(base);
-  uint16_t* dinp = reinterpret_cast<uint16_t*>(base + align256((size_t)M * n * 2));
-  uint16_t* hp = reinterpret_cast<uint16_t*>(base + align256((size_t)M * n * 2) + align256((size_t)n * 2));
+  uint16_t* hp = reinterpret_cast<uint16_t*>(base);
+  if (dbf_decode_path(M, n, r)) {
+    if (M == 1) return dbf_decode<1, 2>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hp, st);
+    if (M <= 4) return dbf_decode<4, 8>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hp, st);
+    return dbf_decode<8, 16>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hp, st);
+  }
+  uint16_t* dinp = reinterpret_cast<uint16_t*>(base + align256((size_t)2 * M * r * 2));
   hipError_t e = launch_prep_f16(d_in, n, dinp, st);
   if (e != hipSuccess) return e;
-  if (2 * M <= 64) {
-    e = launch_prep_bf16(x, M, n, xp, st);
-    if (e != hipSuccess) return e;
-    const int TT1 = (M + 15) / 16;
-    const dim3 g1((r + 15) / 16), b1(64 * dec_waves(n / 128));
-    const uint4* v4 = reinterpret_cast<const uint4*>(v);
-    const u32x4* dp = reinterpret_cast<const u32x4*>(dinp);
-    if (TT1 == 1)
-      hipLaunchKernelGGL(k_dbf1_dec<1>, g1, b1, 0, st, xp, M, r, n, v4, dp, d_mid, hp);
-    else
-      hipLaunchKernelGGL(k_dbf1_dec<2>, g1, b1, 0, st, xp, M, r, n, v4, dp, d_mid, hp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int TT2 = (2 * M + 15) / 16;
-    const dim3 g2((m + 15) / 16), b2(64 * dec_waves(r / 128));
-    const uint4* u4 = reinterpret_cast<const uint4*>(u);
-    switch (TT2) {
-      case 1: hipLaunchKernelGGL(k_dbf2_dec<1>, g2, b2, 0, st, hp, M, m, r, u4, d_out, y, y_bf16); break;
-      case 2: hipLaunchKernelGGL(k_dbf2_dec<2>, g2, b2, 0, st, hp, M, m, r, u4, d_out, y, y_bf16); break;
-      case 3: hipLaunchKernelGGL(k_dbf2_dec<3>, g2, b2, 0, st, hp, M, m, r, u4, d_out, y, y_bf16); break;
-      default: hipLaunchKernelGGL(k_dbf2_dec<4>, g2, b2, 0, st, hp, M, m, r, u4, d_out, y, y_bf16); break;
-    }
-    return hipGetLastError();
-  }
   TileArgs a1{};
   a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kperm = dinp; a1.diag = d_mid; a1.out = hp;
   e = launch_tile_dbf1(a1, st);

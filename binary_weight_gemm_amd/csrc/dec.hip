@@ -57,30 +57,62 @@ hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream
   return hipGetLastError();
 }
 
-template <int TT>
-__global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ xp, int M, int N, int K,
+// ALDS: every wave stages its own K-slice of x (bf16 -> permuted fp16) in LDS
+// after issuing its loads (one launch, no workspace); MAXR is the row bound
+// of that path. Otherwise `xa` is the permuted fp16 staging written by k_prep
+// and A operands are read from global memory.
+template <int TT, int CPW, bool ALDS, int MAXR>
+__global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ xa, int M, int N, int K,
                                                    const uint4* __restrict__ signs,
                                                    const uint16_t* __restrict__ scales, void* __restrict__ y,
                                                    int y_bf16) {
-  __shared__ f32x4 red[15 * TT * 64];
+  extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int j = lane & 15;
-  const int n0 = blockIdx.x * 16;
-  const int n = n0 + j;
+  const int n = blockIdx.x * 16 + j;
   const int G = K >> 7;
-  const uint4* wsig[1] = {n < N ? signs + (size_t)n * G : nullptr};
-  const uint16_t* wsc[1] = {n < N ? scales + (size_t)n * G : nullptr};
-  const u32x4* arow[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int m = 16 * tt + j;
-    arow[tt] = m < M ? reinterpret_cast<const u32x4*>(xp + (size_t)m * K) : nullptr;
-  }
+  const int nchunks = (G + 3) >> 2;
+  const int nr = n < N ? n : 0;  // clamped row; masked by rok
+  const uint4* wsig[1] = {signs + (size_t)nr * G};
+  const uint16_t* wsc[1] = {scales + (size_t)nr * G};
+  const bool rok[1] = {n < N};
   f32x4 acc[1][TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  dec_core<BM_GROUP, 1, TT>(wsig, wsc, nullptr, arow, G, wave, nw, acc);
-  reduce_waves<1, TT>(acc, red);
+  BPre<1, CPW> bp;
+  if (ALDS) {
+    // one round: wave w owns chunks w*CPW .. w*CPW+CPW-1
+    const int c0 = wave * CPW;
+    uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+    if (c0 < nchunks) {
+      WaveStage<ST_BF16, CPW, MAXR> ws;
+      ws.load(M, K, c0, [&](int m) { return xa + (size_t)m * K; });
+      b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
+      __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+      ws.store(xw);
+    }
+    __syncthreads();
+    if (c0 < nchunks) {
+      const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+      auto aop = [&](int tt, int g, int i) -> u32x4 {
+        const int m = min(16 * tt + j, M - 1);
+        return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
+      };
+      b_compute<BM_GROUP, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+    }
+    __syncthreads();  // the reduction below reuses the staging area
+  } else {
+    for (int base = 0; base < nchunks; base += nw * CPW) {
+      const int c0 = base + wave * CPW;
+      b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
+      auto aop = [&](int tt, int g, int i) -> u32x4 {
+        const int m = min(16 * tt + j, M - 1);
+        return reinterpret_cast<const u32x4*>(xa + (size_t)m * K)[g * 16 + i];
+      };
+      b_compute<BM_GROUP, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+    }
+  }
+  reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
   if (wave != 0 || n >= N) return;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
@@ -91,18 +123,58 @@ __global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ 
     }
 }
 
-hipError_t launch_gemm_dec(const uint16_t* xp, int M, int N, int K, const uint64_t* signs,
-                           const uint16_t* scales, void* y, int y_bf16, hipStream_t st) {
-  const int G = K / 128;
-  const int waves = dec_waves(G);
-  const dim3 grid((N + 15) / 16), block(64 * waves);
+// staged row slots for M activation rows
+static int dec_maxr(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+// LDS path: one round of at most 8 waves x 8 chunks covers K, and the
+// per-wave slices of all row slots (waves * cpw * maxr KiB) fit the staging
+// budget.
+static bool dec_lds_split(int64_t M, int64_t K, DecSplit& sp) {
+  const int64_t chunks = (K / 128 + 3) / 4;
+  if (M > 8 || chunks > 64) return false;
+  sp = dec_split((int)(K / 128), 4);
+  if ((int64_t)sp.waves * sp.cpw < chunks) sp = dec_split((int)(K / 128), 8);
+  if ((int64_t)sp.waves * sp.cpw < chunks) return false;
+  return (int64_t)sp.waves * sp.cpw * dec_maxr(M) * 1024 <= kDecLdsBytes;
+}
+
+bool gemm_dec_in_lds(int64_t M, int64_t K) {
+  DecSplit sp;
+  return dec_lds_split(M, K, sp);
+}
+
+template <int TT, bool ALDS, int MAXR>
+static void gemm_dec_tt(const uint16_t* xa, int M, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
+                        int y_bf16, hipStream_t st) {
+  DecSplit sp2 = dec_split(K / 128, 16);
+  if (ALDS) dec_lds_split(M, K, sp2);
+  size_t lds = (size_t)(sp2.waves - 1) * TT * 64 * 16;
+  const size_t stage = (size_t)sp2.waves * sp2.cpw * MAXR * 1024;
+  if (ALDS && stage > lds) lds = stage;
+  const dim3 grid((N + 15) / 16), block(64 * sp2.waves);
+  BRQ_CPW_SWITCH(sp2.cpw, hipLaunchKernelGGL((k_gemm_dec<TT, CPW, ALDS, MAXR>), grid, block, lds, st, xa, M, N, K,
+                                             s4, scales, y, y_bf16));
+}
+
+hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+                           void* y, int y_bf16, void* ws, hipStream_t st) {
   const uint4* s4 = reinterpret_cast<const uint4*>(signs);
   const int TT = (M + 15) / 16;
+  if (gemm_dec_in_lds(M, K)) {
+    if (M == 1) gemm_dec_tt<1, true, 1>(x, M, N, K, s4, scales, y, y_bf16, st);
+    else if (M <= 2) gemm_dec_tt<1, true, 2>(x, M, N, K, s4, scales, y, y_bf16, st);
+    else if (M <= 4) gemm_dec_tt<1, true, 4>(x, M, N, K, s4, scales, y, y_bf16, st);
+    else gemm_dec_tt<1, true, 8>(x, M, N, K, s4, scales, y, y_bf16, st);
+    return hipGetLastError();
+  }
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
+  hipError_t e = launch_prep_bf16(x, M, K, xp, st);
+  if (e != hipSuccess) return e;
   switch (TT) {
-    case 1: hipLaunchKernelGGL(k_gemm_dec<1>, grid, block, 0, st, xp, M, N, K, s4, scales, y, y_bf16); break;
-    case 2: hipLaunchKernelGGL(k_gemm_dec<2>, grid, block, 0, st, xp, M, N, K, s4, scales, y, y_bf16); break;
-    case 3: hipLaunchKernelGGL(k_gemm_dec<3>, grid, block, 0, st, xp, M, N, K, s4, scales, y, y_bf16); break;
-    default: hipLaunchKernelGGL(k_gemm_dec<4>, grid, block, 0, st, xp, M, N, K, s4, scales, y, y_bf16); break;
+    case 1: gemm_dec_tt<1, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+    case 2: gemm_dec_tt<2, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+    case 3: gemm_dec_tt<3, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+    default: gemm_dec_tt<4, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
   }
   return hipGetLastError();
 }

@@ -20,9 +20,13 @@ hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream
 
 // ---- group-128 product ----------------------------------------------------
 // Few activation rows (M <= 64): split-K inside a workgroup, 16 output columns
-// per workgroup. xp: permuted fp16 activations [M][K].
-hipError_t launch_gemm_dec(const uint16_t* xp, int M, int N, int K, const uint64_t* signs,
-                           const uint16_t* scales, void* y, int y_bf16, hipStream_t st);
+// per workgroup. x: bf16 [M][K]. When M*K*2 <= kDecLdsBytes the activations
+// are staged in LDS by the product kernel itself (one launch, no workspace);
+// otherwise a staging kernel writes them to `ws` (M*K*2 bytes) first.
+constexpr int64_t kDecLdsBytes = 64 * 1024;
+bool gemm_dec_in_lds(int64_t M, int64_t K);
+hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
+                           const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 // Many activation rows: LDS-tiled matrix-core kernel, bf16 activations read directly.
 hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                             const uint16_t* scales, void* y, int y_bf16, hipStream_t st);

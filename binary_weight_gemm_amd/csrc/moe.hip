@@ -25,10 +25,10 @@
 namespace brq {
 
 constexpr int MOE_MAX_E = 1024;
-constexpr int MOE_MAX_R = 4096;  // 256 tokens x 16 slots
+constexpr int MOE_MAX_T = 256;
+constexpr int MOE_MAX_R = MOE_MAX_T * 16;
 
 struct MoeWs {
-  uint16_t* xp;      // [T][H] permuted fp16
   int* ids;          // [T][k]
   float* wts;        // [T][k]
   int* off;          // [E+1]
@@ -45,7 +45,6 @@ static MoeWs moe_carve(void* ws, int64_t T, int64_t H, int64_t I, int64_t E, int
   char* p = reinterpret_cast<char*>(ws);
   const int64_t R = T * k;
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
-  w.xp = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
   w.ids = reinterpret_cast<int*>(take((size_t)R * 4));
   w.wts = reinterpret_cast<float*>(take((size_t)R * 4));
   w.off = reinterpret_cast<int*>(take((size_t)(E + 1) * 4));
@@ -60,49 +59,59 @@ static MoeWs moe_carve(void* ws, int64_t T, int64_t H, int64_t I, int64_t E, int
 
 size_t moe_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t R = T * k;
-  return align256((size_t)T * H * 2) + 2 * align256((size_t)R * 4) + align256((size_t)(E + 1) * 4) +
-         align256((size_t)E * 4) + align256(4) + 2 * align256((size_t)R * 4) +
-         align256((size_t)2 * R * I * 2) + align256((size_t)R * H * 4);
+  return 2 * align256((size_t)R * 4) + align256((size_t)(E + 1) * 4) + align256((size_t)E * 4) + align256(4) +
+         2 * align256((size_t)R * 4) + align256((size_t)2 * R * I * 2) + align256((size_t)R * H * 4);
 }
 
-__global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ logits, int T, int E, int k,
-                                                   const uint16_t* __restrict__ x, int64_t xruns, MoeWs ws,
-                                                   int32_t* __restrict__ ids_user, float* __restrict__ w_user) {
-  if (blockIdx.x > 0) {
-    // ---- stage x in the permuted fp16 operand order (one run of 32 per thread)
-    const int64_t t = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
-    if (t >= xruns) return;
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(x + t * 32);
-    uint32_t o[16];
+// exclusive prefix sum over the block (blockDim.x <= 1024); returns the total
+__device__ int block_exclusive_scan(int v, int* s_part, int& excl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const uint32_t lo = (b & 1) ? (s[b >> 1] >> 16) : (s[b >> 1] & 0xffffu);
-      const uint32_t hi = (b & 1) ? (s[8 + (b >> 1)] >> 16) : (s[8 + (b >> 1)] & 0xffffu);
-      o[b] = (uint32_t)f32_to_f16_bits(bf16_to_f32(lo)) | ((uint32_t)f32_to_f16_bits(bf16_to_f32(hi)) << 16);
-    }
-    uint4* d = reinterpret_cast<uint4*>(ws.xp + t * 32);
-    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    d[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    d[3] = make_uint4(o[12], o[13], o[14], o[15]);
-    return;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
   }
+  if (lane == 63) s_part[wave] = inc;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int p = s_part[w];
+    if (w < wave) before += p;
+    total += p;
+  }
+  excl = before + inc - v;
+  __syncthreads();
+  return total;
+}
+
+// One workgroup of 1024 threads. Top-k: one wave per token. Routes of one
+// expert are ordered by token (slots of one token name distinct experts): the
+// rank of route (t, j) inside its expert is the number of earlier tokens in the
+// expert's token bitmap.
+__global__ __launch_bounds__(1024) void k_moe_route(const float* __restrict__ logits, int T, int E, int k, MoeWs ws,
+                                                    int32_t* __restrict__ ids_user, float* __restrict__ w_user) {
   __shared__ int s_ids[MOE_MAX_R];
   __shared__ int s_cnt[MOE_MAX_E];
-  __shared__ int s_off[MOE_MAX_E + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = T * k;
+  __shared__ int s_off[MOE_MAX_E];
+  __shared__ unsigned long long s_map[MOE_MAX_E * (MOE_MAX_T / 64)];
+  __shared__ int s_part[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int words = (T + 63) >> 6;
+  for (int e = tid; e < E; e += blockDim.x) {
+    s_cnt[e] = 0;
+    for (int q = 0; q < words; ++q) s_map[e * words + q] = 0ull;
+  }
+  __syncthreads();
   const int per_lane = (E + 63) / 64;
-
-  // ---- top-k per token: one wave per token ---------------------------------
-  for (int t = wave; t < T; t += 4) {
+  for (int t = wave; t < T; t += nw) {
     float v[MOE_MAX_E / 64];
-    uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < MOE_MAX_E / 64; ++i) {
       const int e = lane + 64 * i;
       v[i] = (i < per_lane && e < E) ? logits[(size_t)t * E + e] : 0.f;
     }
+    uint32_t taken = 0;
     float sel0 = 0.f, mysel = 0.f;
     int myid = 0;
     for (int j = 0; j < k; ++j) {
@@ -137,70 +146,93 @@ __global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ log
       s_ids[t * k + lane] = myid;
       if (ids_user) ids_user[t * k + lane] = myid;
       if (w_user) w_user[t * k + lane] = w;
+      atomicAdd(&s_cnt[myid], 1);
+      atomicOr(&s_map[myid * words + (t >> 6)], 1ull << (t & 63));
     }
   }
-  for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
   __syncthreads();
-  for (int r = tid; r < R; r += 256) atomicAdd(&s_cnt[s_ids[r]], 1);
-  __syncthreads();
+  // offsets (exclusive scan of counts) and the ascending list of active experts
+  int cnt = 0, off = 0, aidx = 0;
+  if (tid < E) cnt = s_cnt[tid];
+  const int R = block_exclusive_scan(cnt, s_part, off);
+  const int na = block_exclusive_scan(cnt > 0 ? 1 : 0, s_part, aidx);
+  if (tid < E) {
+    s_off[tid] = off;
+    ws.off[tid] = off;
+    if (cnt > 0) ws.act[aidx] = tid;
+  }
   if (tid == 0) {
-    int acc = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = acc;
-      ws.off[e] = acc;
-      if (s_cnt[e] > 0) ws.act[na++] = e;
-      acc += s_cnt[e];
-    }
-    s_off[E] = acc;
-    ws.off[E] = acc;
+    ws.off[E] = R;
     *ws.nact = na;
   }
   __syncthreads();
-  // expert-major route list, routes of one expert in (token, slot) order
-  for (int e = tid; e < E; e += 256) {
-    if (s_cnt[e] == 0) continue;
-    int c = s_off[e];
-    for (int r = 0; r < R; ++r)
-      if (s_ids[r] == e) {
-        ws.route_tok[c] = r / k;
-        ws.route_pos[r] = c;
-        ++c;
-      }
+  for (int r = tid; r < T * k; r += blockDim.x) {
+    const int e = s_ids[r], t = r / k;
+    int rank = 0;
+    for (int q = 0; q < (t >> 6); ++q) rank += __popcll(s_map[e * words + q]);
+    rank += __popcll(s_map[e * words + (t >> 6)] & ((1ull << (t & 63)) - 1ull));
+    const int pos = s_off[e] + rank;
+    ws.route_tok[pos] = t;
+    ws.route_pos[r] = pos;
   }
 }
 
-__global__ __launch_bounds__(1024) void k_moe_gateup(int H, int I, const uint4* __restrict__ gs,
-                                                     const uint16_t* __restrict__ gsc, const uint4* __restrict__ us,
-                                                     const uint16_t* __restrict__ usc, MoeWs ws) {
-  __shared__ f32x4 red[15 * 2 * 64];
+// gate/up: one workgroup per (16 intermediate columns, active expert). The
+// expert's sign words are loaded once; its tokens are staged, a tile of up to
+// tile_rows at a time, each wave staging its own K-slice (bf16 -> permuted
+// fp16).
+template <int CPW, int MAXR>
+__global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__ x, int H, int I,
+                                                    const uint4* __restrict__ gs, const uint16_t* __restrict__ gsc,
+                                                    const uint4* __restrict__ us, const uint16_t* __restrict__ usc,
+                                                    MoeWs ws) {
+  extern __shared__ uint4 smem[];
   if ((int)blockIdx.y >= *ws.nact) return;
   const int e = ws.act[blockIdx.y];
   const int r0 = ws.off[e], cnt = ws.off[e + 1] - r0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int n = blockIdx.x * 16 + j;
-  const int G = H >> 7;
-  const size_t row = (size_t)e * I + n;
-  const uint4* wsig[2] = {n < I ? gs + row * G : nullptr, n < I ? us + row * G : nullptr};
-  const uint16_t* wsc[2] = {n < I ? gsc + row * G : nullptr, n < I ? usc + row * G : nullptr};
+  const int G = H >> 7, nchunks = (G + 3) >> 2;
+  const int c0 = wave * CPW;
+  const size_t row = (size_t)e * I + (n < I ? n : 0);
+  const uint4* wsig[2] = {gs + row * G, us + row * G};
+  const uint16_t* wsc[2] = {gsc + row * G, usc + row * G};
+  const bool rok[2] = {n < I, n < I};
+  BPre<2, CPW> bp;
+  if (c0 < nchunks) b_prefetch<BM_GROUP, 2, CPW>(wsig, wsc, rok, G, c0, 1, bp);
   const int pc = perm_pos(n);
-  for (int tb = 0; tb < cnt; tb += 16) {
-    const u32x4* arow[1] = {tb + j < cnt ? reinterpret_cast<const u32x4*>(ws.xp + (size_t)ws.route_tok[r0 + tb + j] * H)
-                                         : nullptr};
+  for (int tb = 0; tb < cnt; tb += MAXR) {
+    const int rows = (cnt - tb) < MAXR ? (cnt - tb) : MAXR;
+    uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+    if (c0 < nchunks) {
+      WaveStage<ST_BF16, CPW, MAXR> sx;
+      sx.load(rows, H, c0, [&](int rr) { return x + (size_t)ws.route_tok[r0 + tb + rr] * H; });
+      sx.store(xw);
+    }
+    __syncthreads();
     f32x4 acc[2][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}, {f32x4{0.f, 0.f, 0.f, 0.f}}};
-    dec_core<BM_GROUP, 2, 1>(wsig, wsc, nullptr, arow, G, wave, nw, acc);
-    reduce_waves<2, 1>(acc, red);
+    if (c0 < nchunks) {
+      const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+      auto aop = [&](int, int g, int i) -> u32x4 {
+        const int m = min(j, rows - 1);
+        return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
+      };
+      b_compute<BM_GROUP, 2, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+    }
+    __syncthreads();
+    reduce_waves<2, 1>(acc, reinterpret_cast<f32x4*>(smem));
     if (wave == 0 && n < I) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int p = tb + 4 * (lane >> 4) + i;
-        if (p < cnt) {
+        const int p = 4 * (lane >> 4) + i;
+        if (p < rows) {
           const float g = acc[0][0][i], u = acc[1][0][i];
           const float a = g / (1.0f + expf(-g)) * u;
           uint16_t hi, lo;
           split_f16(a, hi, lo);
-          ws.ap[(size_t)(2 * (r0 + p)) * I + pc] = hi;
-          ws.ap[(size_t)(2 * (r0 + p) + 1) * I + pc] = lo;
+          ws.ap[(size_t)(2 * (r0 + tb + p)) * I + pc] = hi;
+          ws.ap[(size_t)(2 * (r0 + tb + p) + 1) * I + pc] = lo;
         }
       }
     }
@@ -208,31 +240,53 @@ __global__ __launch_bounds__(1024) void k_moe_gateup(int H, int I, const uint4* 
   }
 }
 
-__global__ __launch_bounds__(1024) void k_moe_down(int H, int I, const uint4* __restrict__ ds,
-                                                   const uint16_t* __restrict__ dsc, MoeWs ws) {
-  __shared__ f32x4 red[15 * 64];
+// down: one workgroup per (16 hidden columns, active expert); the routes'
+// fp16 hi/lo intermediates are staged per wave, 8 routes (16 piece rows) a
+// tile.
+template <int CPW>
+__global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __restrict__ ds,
+                                                  const uint16_t* __restrict__ dsc, MoeWs ws) {
+  extern __shared__ uint4 smem[];
   if ((int)blockIdx.y >= *ws.nact) return;
   const int e = ws.act[blockIdx.y];
   const int r0 = ws.off[e], cnt = ws.off[e + 1] - r0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int n = blockIdx.x * 16 + j;
-  const int G = I >> 7;
-  const size_t row = (size_t)e * H + n;
-  const uint4* wsig[1] = {n < H ? ds + row * G : nullptr};
-  const uint16_t* wsc[1] = {n < H ? dsc + row * G : nullptr};
+  const int G = I >> 7, nchunks = (G + 3) >> 2;
+  const int c0 = wave * CPW;
+  const size_t row = (size_t)e * H + (n < H ? n : 0);
+  const uint4* wsig[1] = {ds + row * G};
+  const uint16_t* wsc[1] = {dsc + row * G};
+  const bool rok[1] = {n < H};
+  BPre<1, CPW> bp;
+  if (c0 < nchunks) b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
   for (int tb = 0; tb < cnt; tb += 8) {
-    const int p = tb + (j >> 1);
-    const u32x4* arow[1] = {p < cnt ? reinterpret_cast<const u32x4*>(ws.ap + (size_t)(2 * (r0 + p) + (j & 1)) * I)
-                                    : nullptr};
+    const int routes = (cnt - tb) < 8 ? (cnt - tb) : 8;
+    const int rows = 2 * routes;
+    uint4* xw = smem + (size_t)wave * CPW * 16 * 64;
+    if (c0 < nchunks) {
+      WaveStage<ST_COPY, CPW, 16> sa;
+      sa.load(rows, I, c0, [&](int pr) { return ws.ap + (size_t)(2 * (r0 + tb) + pr) * I; });
+      sa.store(xw);
+    }
+    __syncthreads();
     f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
-    dec_core<BM_GROUP, 1, 1>(wsig, wsc, nullptr, arow, G, wave, nw, acc);
-    reduce_waves<1, 1>(acc, red);
+    if (c0 < nchunks) {
+      const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+      auto aop = [&](int, int g, int i) -> u32x4 {
+        const int pr = min(j, rows - 1);
+        return xs[(((g >> 2) - c0) * 16 + pr) * 64 + (g & 3) * 16 + i];
+      };
+      b_compute<BM_GROUP, 1, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+    }
+    __syncthreads();
+    reduce_waves<1, 1>(acc, reinterpret_cast<f32x4*>(smem));
     if (wave == 0 && n < H) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int q = tb + 2 * (lane >> 4) + h;
-        if (q < cnt) ws.o[(size_t)(r0 + q) * H + n] = acc[0][0][2 * h] + acc[0][0][2 * h + 1];
+        const int q = 2 * (lane >> 4) + h;
+        if (q < routes) ws.o[(size_t)(r0 + tb + q) * H + n] = acc[0][0][2 * h] + acc[0][0][2 * h + 1];
       }
     }
     __syncthreads();
@@ -249,24 +303,44 @@ __global__ __launch_bounds__(256) void k_moe_combine(int T, int H, int k, MoeWs 
   store_out(y, (size_t)idx, acc, y_bf16);
 }
 
+// token rows per gate/up tile: staged row slots per chunk, so that
+// waves * cpw * slots KiB fit the staging budget
+static int moe_tile_rows(const DecSplit& sp) {
+  const int64_t chunks = (int64_t)sp.waves * sp.cpw;
+  return chunks <= 4 ? 16 : chunks <= 16 ? 4 : 1;
+}
+
 hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int I, int E, int top_k,
                       const uint64_t* gate_s, const uint16_t* gate_sc, const uint64_t* up_s,
                       const uint16_t* up_sc, const uint64_t* down_s, const uint16_t* down_sc, void* y,
                       int y_bf16, int32_t* ids, float* w, void* ws_ptr, hipStream_t st) {
   MoeWs ws = moe_carve(ws_ptr, T, H, I, E, top_k);
-  const int64_t xruns = (int64_t)T * H / 32;
   const int maxact = (T * top_k < E) ? T * top_k : E;
-  hipLaunchKernelGGL(k_moe_route, dim3((unsigned)(1 + (xruns + 255) / 256)), dim3(256), 0, st, logits, T, E, top_k,
-                     x, xruns, ws, ids, w);
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, logits, T, E, top_k, ws, ids, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_gateup, dim3((I + 15) / 16, maxact), dim3(64 * dec_waves(H / 128)), 0, st, H, I,
-                     reinterpret_cast<const uint4*>(gate_s), gate_sc, reinterpret_cast<const uint4*>(up_s), up_sc,
-                     ws);
+  const DecSplit sg = dec_split(H / 128, 8), sd = dec_split(I / 128, 8);
+  const int tr = moe_tile_rows(sg);
+  size_t lg = (size_t)sg.waves * sg.cpw * tr * 1024, rg = (size_t)(sg.waves - 1) * 2 * 64 * 16;
+  size_t ld = (size_t)sd.waves * sd.cpw * 16 * 1024, rd = (size_t)(sd.waves - 1) * 64 * 16;
+#define BRQ_GATEUP(TR)                                                                                       \
+  BRQ_CPW_SWITCH(sg.cpw, hipLaunchKernelGGL((k_moe_gateup<CPW, TR>), dim3((I + 15) / 16, maxact),                \
+                                            dim3(64 * sg.waves), lg > rg ? lg : rg, st, x, H, I,                \
+                                            reinterpret_cast<const uint4*>(gate_s), gate_sc,                    \
+                                            reinterpret_cast<const uint4*>(up_s), up_sc, ws))
+  if (tr == 16) {
+    BRQ_GATEUP(16);
+  } else if (tr == 4) {
+    BRQ_GATEUP(4);
+  } else {
+    BRQ_GATEUP(1);
+  }
+#undef BRQ_GATEUP
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_down, dim3((H + 15) / 16, maxact), dim3(64 * dec_waves(I / 128)), 0, st, H, I,
-                     reinterpret_cast<const uint4*>(down_s), down_sc, ws);
+  BRQ_CPW_SWITCH(sd.cpw, hipLaunchKernelGGL((k_moe_down<CPW>), dim3((H + 15) / 16, maxact), dim3(64 * sd.waves),
+                                            ld > rd ? ld : rd, st, H, I, reinterpret_cast<const uint4*>(down_s),
+                                            down_sc, ws));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * H + 255) / 256)), dim3(256), 0, st, T, H, top_k,

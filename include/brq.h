@@ -164,7 +164,7 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
  *   ids, w   device, out, [T][top_k] int32 / fp32, or NULL
  *   ws       device workspace, >= brq_moe_workspace_bytes(T, H, I, E, top_k)
  *   1 <= T <= 256; 1 <= top_k <= min(E, 16); 1 <= E <= 1024;
- *   H, I multiples of 128 in [128, 65536].
+ *   H, I multiples of 128 with H <= 32768 and I <= 2048.
  */
 size_t brq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
 brq_status brq_moe_ffn(const uint16_t* x, const float* logits,

@@ -47,7 +47,8 @@ def test_size_queries(L):
     assert L.brq_scale_count(4096, 14336) == 4096 * 112
     assert L.brq_sign_words(3, 65) == 0
     assert L.brq_scale_count(3, 64) == 0
-    assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 14336 * 2
+    assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 0          # staged in LDS
+    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 64 * 14336 * 2
     assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 0
     assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0
     assert L.brq_dbf_workspace_bytes(1, 4096, 4096, 2048) > 0
@@ -77,8 +78,8 @@ def test_gemm_validation(L):
     assert g(P, 1, 16, 192, P, P, P, 0, P, 1 << 20, None) == E_SHAPE
     assert g(P, 1, 16, 128, P, P, P, 7, P, 1 << 20, None) == E_DTYPE
     assert g(P, 1, 16, 128, P, PMIS, P, 0, P, 1 << 20, None) == E_ALIGN
-    assert g(P, 1, 16, 128, P, P, P, 0, None, 0, None) == E_WORKSPACE
-    assert g(P, 1, 16, 128, P, P, P, 0, P, 10, None) == E_WORKSPACE
+    assert g(P, 64, 16, 14336, P, P, P, 0, None, 0, None) == E_WORKSPACE
+    assert g(P, 64, 16, 14336, P, P, P, 0, P, 10, None) == E_WORKSPACE
     assert "workspace" in _err(L)
 
 

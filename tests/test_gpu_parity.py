@@ -356,3 +356,60 @@ def test_c5_prefill_sampled_columns():
     sel = torch.from_numpy(cols).cuda()
     check_f32(f64(y2)[:, cols], o, F32_TOL, "C5 gemm")
     check_bf16(yb2[:, sel].contiguous(), o, "C5 gemm bf16")
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: the calls enqueue only kernels, so they can be captured
+# and replayed; every replay must equal the eager result
+# ---------------------------------------------------------------------------
+
+def test_graph_capture_replay():
+    say("graph capture of gemm (decode + tiled), dbf, moe")
+    b = brq()
+    N, K = 1024, 2048
+    w = datagen.normal_f32((76, 0), (N, K), 0.02)
+    ow, osc = oracle.pack_sign1(w)
+    S, SC = dev(ow), dev(osc)
+    x1 = dev(datagen.bf16_normal((76, 1), (1, K)))
+    x2 = dev(datagen.bf16_normal((76, 2), (96, K)))
+    d = datagen.C3(1, m=256, n=512, r=256)
+    vw, uw = oracle.pack_sign1_only(d["v"]), oracle.pack_sign1_only(d["u"])
+    dargs = (dev(d["x"]), dev(d["d_in"]), dev(vw), dev(d["d_mid"]), dev(uw), dev(d["d_out"]), 256, 512, 256)
+    cfg = datagen.C4(E=16, H=256, I=128, top_k=4, layer=76)
+    packs = [[oracle.pack_sign1(f(e)) for f in (cfg.gate, cfg.up, cfg.down)] for e in range(cfg.E)]
+    mw = [dev(np.stack([pk[p][i] for pk in packs])) for p in range(3) for i in range(2)]
+    xm, lg = dev(cfg.x(2)), dev(cfg.logits(2))
+    y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((96, N), dtype=torch.float32, device="cuda")
+    yd = torch.empty((1, 256), dtype=torch.float32, device="cuda")
+    ym = torch.empty((2, 256), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(b.dbf_workspace_bytes(1, 256, 512, 256), dtype=torch.uint8, device="cuda")
+    wsm = torch.empty(b.moe_workspace_bytes(2, 256, 128, 16, 4), dtype=torch.uint8, device="cuda")
+
+    def work():
+        b.gemm(x1, S, SC, N, K, out_dtype=torch.float32, y=y1)
+        b.gemm(x2, S, SC, N, K, out_dtype=torch.float32, y=y2)
+        b.dbf_gemm(*dargs, out_dtype=torch.float32, y=yd, ws=wsd)
+        b.moe_ffn(xm, lg, *mw, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32, y=ym, ws=wsm)
+
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y1, y2, yd, ym)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(3):
+        for t in (y1, y2, yd, ym):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, r in zip((y1, y2, yd, ym), ref):
+            assert torch.equal(a, r), f"replay {rep} differs"
+        work()  # eager work between replays
+        torch.cuda.synchronize()
