@@ -72,7 +72,7 @@ brq_status hip_result(hipError_t e, const char* what) {
 bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
 
 size_t gemm_ws(int64_t M, int64_t K) {
-  return (M <= 64 && !brq::gemm_dec_in_lds(M, K)) ? brq::align256((size_t)M * K * 2) : 0;
+  return (M <= 64 && brq::gemm_dec_in_lds(M, K)) ? 0 : brq::align256((size_t)M * K * 2);
 }
 
 }  // namespace
@@ -147,7 +147,7 @@ brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const ui
   const int yb = y_dtype == BRQ_BF16;
   if (M <= 64)
     return hip_result(brq::launch_gemm_dec(x, (int)M, (int)N, (int)K, signs, scales, y, yb, ws, st), "brq_gemm");
-  return hip_result(brq::launch_gemm_tile(x, (int)M, (int)N, (int)K, signs, scales, y, yb, st), "brq_gemm");
+  return hip_result(brq::launch_gemm_pf(x, (int)M, (int)N, (int)K, signs, scales, y, yb, ws, st), "brq_gemm");
 }
 
 size_t brq_dbf_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {

@@ -85,12 +85,11 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN): gfx950's
+// hardware conversion.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
 }
 
 // fp32 value as an fp16 hi/lo pair: hi = fp16(v), lo = fp16(v - hi).

@@ -30,6 +30,10 @@ hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_
 // Many activation rows: LDS-tiled matrix-core kernel, bf16 activations read directly.
 hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                             const uint16_t* scales, void* y, int y_bf16, hipStream_t st);
+// Many activation rows (prefill): x staged to `ws` (M*K*2 bytes) as permuted
+// fp16, then the 256 x 256 direct-to-LDS matrix-core kernel.
+hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
+                          const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 
 // ---- DBF chain -------------------------------------------------------------
 // stage 1: hp[2M][r] (fp16 hi/lo pairs, permuted) = D_mid (V (D_in x))

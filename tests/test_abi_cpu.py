@@ -49,7 +49,7 @@ def test_size_queries(L):
     assert L.brq_scale_count(3, 64) == 0
     assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 0          # staged in LDS
     assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 64 * 14336 * 2
-    assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 0
+    assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 4096 * 4096 * 2   # staged activations
     assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0
     assert L.brq_dbf_workspace_bytes(1, 4096, 4096, 2048) > 0
     assert L.brq_moe_workspace_bytes(1, 2048, 512, 256, 8) > 0
