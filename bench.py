@@ -20,6 +20,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cp
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -50,6 +51,46 @@ def dev_np(a):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(a).cuda()
+
+
+def kernel_source_hash(files):
+    """sha256 over the named kernel sources (csrc/), to tie counter readings to the code they came from."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "binary_weight_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+# HBM traffic of the headline kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (profiles/decode_m1_traffic.txt, a JSON record). It is reported only while the kernel
+# sources still hash to the value recorded with the counters.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_m1_traffic.txt")
+DECODE_SOURCES = ("common.h", "dec_core.h", "dec.hip", "abi.hip")
+
+
+def recorded_traffic():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash(DECODE_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(torch, mib=512, reps=5):
+    """Plain device-to-device copies of a known size: the reference reading that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return dict(copy_bytes=n, reps=reps)
 
 
 def ring_copies(per_copy_bytes):
@@ -305,6 +346,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 512 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
@@ -315,6 +358,9 @@ def main():
     import binary_weight_gemm_amd as brq
     brq.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(torch)))
+        return
 
     log("[bench] headline C2 decode M=1")
     head = run_c2(brq, torch, 1, args.steps, args.warmup)
@@ -349,7 +395,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": "decode binary GEMV: W 4096x14336 and 14336x4096 group-128 sign + fp16 scale, "
@@ -359,7 +405,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
             "kernel": "k_gemm_dec (brq_gemm, M=1): one launch per matrix; HIP-graph replay of the timed steps, "
                       "HIP events around each replay, time / launches",
             "launch_us": round(head["launch_ms"] * 1e3, 3),
