@@ -57,11 +57,9 @@ hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream
   return hipGetLastError();
 }
 
-// ALDS: every wave stages its own K-slice of x (bf16 -> permuted fp16) in LDS
-// after issuing its loads (one launch, no workspace); MAXR is the row bound
-// of that path. Otherwise `xa` is the permuted fp16 staging written by k_prep
-// and A operands are read from global memory.
-template <int TT, int CPW, bool ALDS, int MAXR>
+// Few-row product with activations from the permuted copy written by k_prep
+// (8 < M <= 64, or when the activation slices do not fit the LDS budget).
+template <int TT, int CPW>
 __global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ xa, int M, int N, int K,
                                                    const uint4* __restrict__ signs,
                                                    const uint16_t* __restrict__ scales, void* __restrict__ y,
@@ -80,37 +78,14 @@ __global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ 
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   BPre<1, CPW> bp;
-  if (ALDS) {
-    // one round: wave w owns chunks w*CPW .. w*CPW+CPW-1
-    const int c0 = wave * CPW;
-    uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
-    if (c0 < nchunks) {
-      WaveStage<ST_BF16, CPW, MAXR> ws;
-      ws.load(M, K, c0, [&](int m) { return xa + (size_t)m * K; });
-      b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
-      __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
-      ws.store(xw);
-    }
-    __syncthreads();
-    if (c0 < nchunks) {
-      const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
-      auto aop = [&](int tt, int g, int i) -> u32x4 {
-        const int m = min(16 * tt + j, M - 1);
-        return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
-      };
-      b_compute<BM_GROUP, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
-    }
-    __syncthreads();  // the reduction below reuses the staging area
-  } else {
-    for (int base = 0; base < nchunks; base += nw * CPW) {
-      const int c0 = base + wave * CPW;
-      b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
-      auto aop = [&](int tt, int g, int i) -> u32x4 {
-        const int m = min(16 * tt + j, M - 1);
-        return reinterpret_cast<const u32x4*>(xa + (size_t)m * K)[g * 16 + i];
-      };
-      b_compute<BM_GROUP, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
-    }
+  for (int base = 0; base < nchunks; base += nw * CPW) {
+    const int c0 = base + wave * CPW;
+    b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
+    auto aop = [&](int tt, int g, int i) -> u32x4 {
+      const int m = min(16 * tt + j, M - 1);
+      return reinterpret_cast<const u32x4*>(xa + (size_t)m * K)[g * 16 + i];
+    };
+    b_compute<BM_GROUP, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
   }
   reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
   if (wave != 0 || n >= N) return;
@@ -123,18 +98,95 @@ __global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ 
     }
 }
 
+// One-launch product for M <= 8: wave w owns chunks w*CPW .. w*CPW+CPW-1 of
+// the reduction. It issues the loads of its activation slice (all MAXR row
+// slots), of its sign words and of its scales before any wait, converts the
+// slice into its own LDS region (no workgroup barrier: only this wave reads
+// it) and runs its MFMAs as soon as its own data is in. SC16: the scales of
+// the wave's 8 groups arrive as one 16-byte load per lane (needs CPW == 2 and
+// G % 8 == 0); otherwise one 2-byte load per chunk. Only the lanes that hold
+// rows m < M take part in the cross-wave sum (LDS, fixed wave order).
+template <int CPW, int MAXR, bool SC16>
+__global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restrict__ x, int M, int N, int K,
+                                                       const uint4* __restrict__ signs,
+                                                       const uint16_t* __restrict__ scales, void* __restrict__ y,
+                                                       int y_bf16) {
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int n = blockIdx.x * 16 + j;
+  const int G = K >> 7;
+  const int nchunks = (G + 3) >> 2;
+  const bool rok = n < N;
+  const int nr = rok ? n : 0;  // clamped row; masked by bp.ok
+  const uint4* wsig = signs + (size_t)nr * G;
+  const uint16_t* wsc = scales + (size_t)nr * G;
+  const int c0 = wave * CPW;
+  uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+  f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)nw * CPW * MAXR * 64);
+  f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+  if (c0 < nchunks) {  // uniform across the wave
+    WaveStage<ST_BF16, CPW, MAXR> ws;
+    ws.load(M, K, c0, [&](int m) { return x + (size_t)m * K; });
+    BPre<1, CPW> bp;
+    uint4 sq = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int g = 4 * (c0 + c) + kb;
+      const bool ok = rok && g < G;
+      const int gi = ok ? g : 0;
+      bp.ok[0][c] = ok;
+      bp.d[0][c] = wsig[gi];
+      if (!SC16) bp.s[0][c] = wsc[gi];
+    }
+    if (SC16) sq = *reinterpret_cast<const uint4*>(wsc + 4 * c0);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    ws.store(xw);
+    if (SC16) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        // halfword 4c + kb of the 8 scales
+        const uint32_t wv = (kb & 2) ? ((c == 0) ? sq.y : sq.w) : ((c == 0) ? sq.x : sq.z);
+        bp.s[0][c] = (kb & 1) ? (wv >> 16) : (wv & 0xffffu);
+      }
+    }
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    auto aop = [&](int tt, int g, int i) -> u32x4 {
+      const int m = min(j, M - 1);
+      return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_GROUP, 1, 1, CPW, true>(bp, nullptr, G, c0, 1, aop, acc);
+  }
+  // lane (kb, j) holds rows 4*kb .. 4*kb+3 of column j
+  const bool holds = 4 * kb < M;
+  if (wave > 0 && holds) red[(wave - 1) * 64 + lane] = acc[0][0];
+  __syncthreads();
+  if (wave != 0 || !holds || !rok) return;
+#pragma unroll
+  for (int w = 1; w < 16; ++w)
+    if (w < nw) acc[0][0] += red[(w - 1) * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * kb + i;
+    if (m < M) store_out(y, (size_t)m * N + n, acc[0][0][i], y_bf16);
+  }
+}
+
 // staged row slots for M activation rows
 static int dec_maxr(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
-// LDS path: one round of at most 8 waves x 8 chunks covers K, and the
-// per-wave slices of all row slots (waves * cpw * maxr KiB) fit the staging
-// budget.
+// Split of the one-launch path: chunks of 512 over at most 16 waves, two
+// chunks per wave when there are at least four (one chunk each below), more
+// only when 16 waves of two do not cover K. The staged slices
+// (waves * cpw * maxr KiB) must fit the LDS budget.
 static bool dec_lds_split(int64_t M, int64_t K, DecSplit& sp) {
+  if (M > 8) return false;
   const int64_t chunks = (K / 128 + 3) / 4;
-  if (M > 8 || chunks > 64) return false;
-  sp = dec_split((int)(K / 128), 4);
-  if ((int64_t)sp.waves * sp.cpw < chunks) sp = dec_split((int)(K / 128), 8);
-  if ((int64_t)sp.waves * sp.cpw < chunks) return false;
+  int64_t cpw = chunks >= 4 ? 2 : 1;
+  if ((chunks + cpw - 1) / cpw > 16) cpw = (chunks + 15) / 16;
+  if (cpw > 8) return false;
+  sp.cpw = (int)cpw;
+  sp.waves = (int)((chunks + cpw - 1) / cpw);
   return (int64_t)sp.waves * sp.cpw * dec_maxr(M) * 1024 <= kDecLdsBytes;
 }
 
@@ -143,38 +195,48 @@ bool gemm_dec_in_lds(int64_t M, int64_t K) {
   return dec_lds_split(M, K, sp);
 }
 
-template <int TT, bool ALDS, int MAXR>
-static void gemm_dec_tt(const uint16_t* xa, int M, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
-                        int y_bf16, hipStream_t st) {
-  DecSplit sp2 = dec_split(K / 128, 16);
-  if (ALDS) dec_lds_split(M, K, sp2);
-  size_t lds = (size_t)(sp2.waves - 1) * TT * 64 * 16;
-  const size_t stage = (size_t)sp2.waves * sp2.cpw * MAXR * 1024;
-  if (ALDS && stage > lds) lds = stage;
-  const dim3 grid((N + 15) / 16), block(64 * sp2.waves);
-  BRQ_CPW_SWITCH(sp2.cpw, hipLaunchKernelGGL((k_gemm_dec<TT, CPW, ALDS, MAXR>), grid, block, lds, st, xa, M, N, K,
-                                             s4, scales, y, y_bf16));
+template <int MAXR>
+static void gemm_dec_lds(const uint16_t* x, int M, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
+                         int y_bf16, hipStream_t st) {
+  DecSplit sp;
+  dec_lds_split(M, K, sp);
+  const size_t lds = (size_t)sp.waves * sp.cpw * MAXR * 1024 + (size_t)(sp.waves - 1) * 64 * 16;
+  const dim3 grid((N + 15) / 16), block(64 * sp.waves);
+  if (sp.cpw == 2 && (K / 128) % 8 == 0)
+    hipLaunchKernelGGL((k_gemm_dec_lds<2, MAXR, true>), grid, block, lds, st, x, M, N, K, s4, scales, y, y_bf16);
+  else
+    BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_lds<CPW, MAXR, false>), grid, block, lds, st, x, M, N,
+                                              K, s4, scales, y, y_bf16));
+}
+
+template <int TT>
+static void gemm_dec_prep(const uint16_t* xa, int M, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
+                          int y_bf16, hipStream_t st) {
+  const DecSplit sp = dec_split(K / 128, 16);
+  const size_t lds = (size_t)(sp.waves - 1) * TT * 64 * 16;
+  const dim3 grid((N + 15) / 16), block(64 * sp.waves);
+  BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec<TT, CPW>), grid, block, lds, st, xa, M, N, K, s4, scales,
+                                            y, y_bf16));
 }
 
 hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                            void* y, int y_bf16, void* ws, hipStream_t st) {
   const uint4* s4 = reinterpret_cast<const uint4*>(signs);
-  const int TT = (M + 15) / 16;
   if (gemm_dec_in_lds(M, K)) {
-    if (M == 1) gemm_dec_tt<1, true, 1>(x, M, N, K, s4, scales, y, y_bf16, st);
-    else if (M <= 2) gemm_dec_tt<1, true, 2>(x, M, N, K, s4, scales, y, y_bf16, st);
-    else if (M <= 4) gemm_dec_tt<1, true, 4>(x, M, N, K, s4, scales, y, y_bf16, st);
-    else gemm_dec_tt<1, true, 8>(x, M, N, K, s4, scales, y, y_bf16, st);
+    if (M == 1) gemm_dec_lds<1>(x, M, N, K, s4, scales, y, y_bf16, st);
+    else if (M <= 2) gemm_dec_lds<2>(x, M, N, K, s4, scales, y, y_bf16, st);
+    else if (M <= 4) gemm_dec_lds<4>(x, M, N, K, s4, scales, y, y_bf16, st);
+    else gemm_dec_lds<8>(x, M, N, K, s4, scales, y, y_bf16, st);
     return hipGetLastError();
   }
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
   hipError_t e = launch_prep_bf16(x, M, K, xp, st);
   if (e != hipSuccess) return e;
-  switch (TT) {
-    case 1: gemm_dec_tt<1, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-    case 2: gemm_dec_tt<2, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-    case 3: gemm_dec_tt<3, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-    default: gemm_dec_tt<4, false, 1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+  switch ((M + 15) / 16) {
+    case 1: gemm_dec_prep<1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+    case 2: gemm_dec_prep<2>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+    case 3: gemm_dec_prep<3>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
+    default: gemm_dec_prep<4>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
   }
   return hipGetLastError();
 }

@@ -69,7 +69,10 @@ __device__ __forceinline__ void b_prefetch(const uint4* const (&wsig)[NB], const
 // G-1, so it must read valid, finite data for any row (rows past the end are
 // never stored, and a zero weight operand cancels a clamped group).
 // Two accumulators per tile alternate to halve the MFMA dependency chain.
-template <int BMODE, int NB, int TT, int CPW, class AOP>
+// ALL: run every one of the CPW chunks (chunks past G contribute zero through
+// the validity masks) so that the body has no branch; a branch here lets the
+// compiler sink the prefetched loads into it, behind the first wait.
+template <int BMODE, int NB, int TT, int CPW, bool ALL = false, class AOP>
 __device__ __forceinline__ void b_compute(const BPre<NB, CPW>& bp, const u32x4* __restrict__ kp, int G, int c0,
                                           int cstep, AOP&& aop, f32x4 (&acc)[NB][TT]) {
   const int kb = (threadIdx.x & 63) >> 4;
@@ -81,7 +84,7 @@ __device__ __forceinline__ void b_compute(const BPre<NB, CPW>& bp, const u32x4* 
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int chunk = c0 + c * cstep;
-    if (4 * chunk >= G) break;  // uniform across the wave
+    if (!ALL && 4 * chunk >= G) break;  // uniform across the wave
     const int g = 4 * chunk + kb;
     const bool ok = g < G;
     const int ga = ok ? g : G - 1;

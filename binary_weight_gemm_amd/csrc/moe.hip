@@ -85,6 +85,84 @@ __device__ int block_exclusive_scan(int v, int* s_part, int& excl) {
   return total;
 }
 
+// ---- wave-level top-k -------------------------------------------------------
+// A routing candidate is a 64-bit key: the fp32 logit mapped to an unsigned
+// integer of the same order in the high word, the complement of the expert
+// index in the low word. The largest key is the largest logit and, among equal
+// logits, the lower expert index. -0 is folded to +0 first so that the two
+// zeros tie as they do in a plain fp32 comparison. Key 0 marks "no candidate".
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  v = (v == 0.f) ? 0.f : v;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(~(uint32_t)e);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)(~(uint32_t)key); }
+
+// DPP move of a 64-bit value (lanes without a source, or outside ROWMASK, read 0)
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Largest key of the wave, returned to every lane: quad swaps, half-row and row
+// mirrors, then the row broadcasts carry the maximum to lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = max64(v, dpp64<0xB1, 0xf>(v));   // quad_perm [1,0,3,2]
+  v = max64(v, dpp64<0x4E, 0xf>(v));   // quad_perm [2,3,0,1]
+  v = max64(v, dpp64<0x141, 0xf>(v));  // row_half_mirror
+  v = max64(v, dpp64<0x140, 0xf>(v));  // row_mirror
+  v = max64(v, dpp64<0x142, 0xa>(v));  // row_bcast15 into rows 1 and 3
+  v = max64(v, dpp64<0x143, 0xc>(v));  // row_bcast31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum over lanes 0..15 (row 0), returned to every lane.
+__device__ __forceinline__ float row0_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+}
+
+// Top-k routing of one token by one wave: the k largest keys in descending
+// order (k <= 16), then the softmax over the selected logits. Lane j < k
+// returns slot j's expert and weight.
+template <int PER>
+__device__ __forceinline__ void wave_route(const float* __restrict__ lg, int E, int k, int& id, float& wt) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? route_key(lg[e], e) : 0ull;
+  }
+  float sel = 0.f, top = 0.f;
+  id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) m = max64(m, key[i]);
+    const uint64_t w = wave_max_key(m);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[i] = (key[i] == w) ? 0ull : key[i];
+    if (j == 0) top = key_logit(w);
+    if (lane == j) { sel = key_logit(w); id = key_expert(w); }
+  }
+  const float ex = lane < k ? expf(sel - top) : 0.f;
+  wt = ex / row0_sum(ex);
+}
+
 // One workgroup of 1024 threads. Top-k: one wave per token. Routes of one
 // expert are ordered by token (slots of one token name distinct experts): the
 // rank of route (t, j) inside its expert is the number of earlier tokens in the
@@ -103,44 +181,12 @@ __global__ __launch_bounds__(1024) void k_moe_route(const float* __restrict__ lo
     for (int q = 0; q < words; ++q) s_map[e * words + q] = 0ull;
   }
   __syncthreads();
-  const int per_lane = (E + 63) / 64;
   for (int t = wave; t < T; t += nw) {
-    float v[MOE_MAX_E / 64];
-#pragma unroll
-    for (int i = 0; i < MOE_MAX_E / 64; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = (i < per_lane && e < E) ? logits[(size_t)t * E + e] : 0.f;
-    }
-    uint32_t taken = 0;
-    float sel0 = 0.f, mysel = 0.f;
-    int myid = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < MOE_MAX_E / 64; ++i) {
-        const int e = lane + 64 * i;
-        if (i < per_lane && e < E && !((taken >> i) & 1u)) {
-          if (be == 0x7fffffff || v[i] > bv || (v[i] == bv && e < be)) { bv = v[i]; be = e; }
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
-        if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (j == 0) sel0 = bv;  // the largest selected logit
-      if (j == lane) { mysel = bv; myid = be; }
-    }
-    // softmax over the k selected logits (lane j holds slot j)
-    const float ex = lane < k ? expf(mysel - sel0) : 0.f;
-    float esum = ex;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) esum += __shfl_xor(esum, o, 64);
+    int myid;
+    float w;
+    if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, myid, w);
+    else wave_route<16>(logits + (size_t)t * E, E, k, myid, w);
     if (lane < k) {
-      const float w = ex / esum;
       ws.ids[t * k + lane] = myid;
       ws.wts[t * k + lane] = w;
       s_ids[t * k + lane] = myid;
@@ -303,6 +349,184 @@ __global__ __launch_bounds__(256) void k_moe_combine(int T, int H, int k, MoeWs 
   store_out(y, (size_t)idx, acc, y_bf16);
 }
 
+// ---- decode path (few tokens): two launches --------------------------------
+//  A: every workgroup routes all T tokens itself (one wave per token), finds
+//     the a-th active expert (ascending ids) and its routes, and runs gate/up +
+//     SwiGLU for them; the result of route r = t*k + j is stored at piece rows
+//     2r, 2r+1 (token-major). Workgroup (0, 0) also publishes ids and weights.
+//  B: one workgroup per (16 hidden columns, token), one wave per slot: wave j
+//     multiplies expert ids[t][j]'s down rows by route (t, j)'s intermediate;
+//     wave 0 adds w_tj * out_j over the slots in slot order.
+constexpr int MOE_SMALL_T = 8;
+
+template <int CPW, int MAXR>
+__global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict__ x, const float* __restrict__ logits,
+                                                     int T, int E, int k, int H, int I,
+                                                     const uint4* __restrict__ gs, const uint16_t* __restrict__ gsc,
+                                                     const uint4* __restrict__ us, const uint16_t* __restrict__ usc,
+                                                     MoeWs ws, int32_t* __restrict__ ids_user,
+                                                     float* __restrict__ w_user) {
+  extern __shared__ uint4 smem[];
+  __shared__ int s_ids[MOE_SMALL_T * 16];
+  __shared__ float s_w[MOE_SMALL_T * 16];
+  __shared__ uint32_t s_bits[MOE_MAX_E / 32];
+  __shared__ int s_tok[MOE_SMALL_T], s_slot[MOE_SMALL_T];
+  __shared__ int s_e, s_cnt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  for (int i = tid; i < MOE_MAX_E / 32; i += blockDim.x) s_bits[i] = 0u;
+  for (int t = wave; t < T; t += nw) {
+    int id;
+    float w;
+    if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, id, w);
+    else wave_route<16>(logits + (size_t)t * E, E, k, id, w);
+    if (lane < k) {
+      s_ids[t * k + lane] = id;
+      s_w[t * k + lane] = w;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < T * k; r += blockDim.x) atomicOr(&s_bits[s_ids[r] >> 5], 1u << (s_ids[r] & 31));
+  __syncthreads();
+  if (tid == 0) {
+    // the blockIdx.y-th set bit, and the routes (ascending token) of that expert
+    int want = blockIdx.y, e = -1;
+    for (int q = 0; q < (E + 31) / 32 && e < 0; ++q) {
+      uint32_t b = s_bits[q];
+      const int c = __popc(b);
+      if (want < c) {
+        for (int i = 0; i < want; ++i) b &= b - 1u;
+        e = 32 * q + __ffs(b) - 1;
+      } else {
+        want -= c;
+      }
+    }
+    int cnt = 0;
+    if (e >= 0)
+      for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j)
+          if (s_ids[t * k + j] == e) { s_tok[cnt] = t; s_slot[cnt] = j; ++cnt; }
+    s_e = e;
+    s_cnt = cnt;
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int r = tid; r < T * k; r += blockDim.x) {
+      ws.ids[r] = s_ids[r];
+      ws.wts[r] = s_w[r];
+      if (ids_user) ids_user[r] = s_ids[r];
+      if (w_user) w_user[r] = s_w[r];
+    }
+  }
+  __syncthreads();
+  const int e = s_e, cnt = s_cnt;
+  if (e < 0) return;
+  const int j = lane & 15, kb = lane >> 4;
+  const int n = blockIdx.x * 16 + j;
+  const int G = H >> 7, nchunks = (G + 3) >> 2;
+  const int c0 = wave * CPW;
+  const bool rok = n < I;
+  const size_t row = (size_t)e * I + (rok ? n : 0);
+  const uint4* wsig[2] = {gs + row * G, us + row * G};
+  const uint16_t* wsc[2] = {gsc + row * G, usc + row * G};
+  const bool rk[2] = {rok, rok};
+  uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+  f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)nw * CPW * MAXR * 64);
+  f32x4 acc[2][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}, {f32x4{0.f, 0.f, 0.f, 0.f}}};
+  if (c0 < nchunks) {
+    WaveStage<ST_BF16, CPW, MAXR> sx;
+    sx.load(cnt, H, c0, [&](int q) { return x + (size_t)s_tok[q] * H; });
+    BPre<2, CPW> bp;
+    b_prefetch<BM_GROUP, 2, CPW>(wsig, wsc, rk, G, c0, 1, bp);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sx.store(xw);
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int m = min(j, cnt - 1);
+      return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_GROUP, 2, 1, CPW, true>(bp, nullptr, G, c0, 1, aop, acc);
+  }
+  const bool holds = 4 * kb < cnt;
+  if (wave > 0 && holds) {
+    red[(2 * (wave - 1)) * 64 + lane] = acc[0][0];
+    red[(2 * (wave - 1) + 1) * 64 + lane] = acc[1][0];
+  }
+  __syncthreads();
+  if (wave != 0 || !holds || !rok) return;
+  for (int w = 1; w < nw; ++w) {
+    acc[0][0] += red[(2 * (w - 1)) * 64 + lane];
+    acc[1][0] += red[(2 * (w - 1) + 1) * 64 + lane];
+  }
+  const int pc = perm_pos(n);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * kb + i;
+    if (q < cnt) {
+      const float g = acc[0][0][i], u = acc[1][0][i];
+      const float a = g / (1.0f + expf(-g)) * u;
+      uint16_t hi, lo;
+      split_f16(a, hi, lo);
+      const size_t r = (size_t)s_tok[q] * k + s_slot[q];
+      ws.ap[(2 * r) * I + pc] = hi;
+      ws.ap[(2 * r + 1) * I + pc] = lo;
+    }
+  }
+}
+
+template <int CPW>
+__global__ __launch_bounds__(1024) void k_moe_b_token(int H, int I, int k, const uint4* __restrict__ ds,
+                                                      const uint16_t* __restrict__ dsc, MoeWs ws,
+                                                      void* __restrict__ y, int y_bf16) {
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, slot = threadIdx.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int t = blockIdx.y;
+  const int n = blockIdx.x * 16 + j;
+  const int r = t * k + slot;
+  const int e = ws.ids[r];
+  const int G = I >> 7;
+  const bool rok = n < H;
+  const size_t row = (size_t)e * H + (rok ? n : 0);
+  const uint4* wsig[1] = {ds + row * G};
+  const uint16_t* wsc[1] = {dsc + row * G};
+  const bool rk[1] = {rok};
+  uint4* xw = smem + (size_t)slot * CPW * 2 * 64;
+  float* part = reinterpret_cast<float*>(smem + (size_t)k * CPW * 2 * 64);  // [k][16]
+  f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+  {
+    WaveStage<ST_COPY, CPW, 2> sa;
+    sa.load(2, I, 0, [&](int p) { return ws.ap + (size_t)(2 * r + p) * I; });
+    BPre<1, CPW> bp;
+    b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rk, G, 0, 1, bp);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sa.store(xw);
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int p = min(j, 1);
+      return xs[((g >> 2) * 2 + p) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_GROUP, 1, 1, CPW, true>(bp, nullptr, G, 0, 1, aop, acc);
+  }
+  // lanes 0..15 hold piece rows 0 and 1 of column j
+  if (kb == 0) part[slot * 16 + j] = acc[0][0][0] + acc[0][0][1];
+  __syncthreads();
+  if (slot != 0 || kb != 0 || !rok) return;
+  float sum = 0.f;
+  for (int q = 0; q < k; ++q) sum = fmaf(ws.wts[t * k + q], part[q * 16 + j], sum);
+  store_out(y, (size_t)t * H + n, sum, y_bf16);
+}
+
+// The decode path applies when the per-wave staging of both launches fits.
+static bool moe_small_path(int T, int H, int I, int k, DecSplit& sa, int& maxr, int& cpwb) {
+  if (T > MOE_SMALL_T) return false;
+  maxr = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  sa = dec_split(H / 128, 8);
+  const int chunks_b = (I / 128 + 3) / 4;
+  cpwb = chunks_b;
+  if (chunks_b > 4) return false;
+  if ((int64_t)sa.waves * sa.cpw * maxr * 1024 + (int64_t)(sa.waves - 1) * 2 * 64 * 16 > kDecLdsBytes) return false;
+  return (int64_t)k * cpwb * 2 * 1024 + (int64_t)k * 16 * 4 <= kDecLdsBytes;
+}
+
 // token rows per gate/up tile: staged row slots per chunk, so that
 // waves * cpw * slots KiB fit the staging budget
 static int moe_tile_rows(const DecSplit& sp) {
@@ -316,6 +540,33 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
                       int y_bf16, int32_t* ids, float* w, void* ws_ptr, hipStream_t st) {
   MoeWs ws = moe_carve(ws_ptr, T, H, I, E, top_k);
   const int maxact = (T * top_k < E) ? T * top_k : E;
+  {
+    DecSplit sa;
+    int maxr, cpwb;
+    if (moe_small_path(T, H, I, top_k, sa, maxr, cpwb)) {
+      const size_t la = (size_t)sa.waves * sa.cpw * maxr * 1024 + (size_t)(sa.waves - 1) * 2 * 64 * 16;
+      const dim3 ga((I + 15) / 16, maxact), ba(64 * sa.waves);
+      const uint4* g4 = reinterpret_cast<const uint4*>(gate_s);
+      const uint4* u4 = reinterpret_cast<const uint4*>(up_s);
+#define BRQ_A(MR)                                                                                            \
+  BRQ_CPW_SWITCH(sa.cpw, hipLaunchKernelGGL((k_moe_a_small<CPW, MR>), ga, ba, la, st, x, logits, T, E, top_k, H, \
+                                            I, g4, gate_sc, u4, up_sc, ws, ids, w))
+      if (maxr == 1) { BRQ_A(1); } else if (maxr == 2) { BRQ_A(2); } else if (maxr == 4) { BRQ_A(4); } else { BRQ_A(8); }
+#undef BRQ_A
+      hipError_t e1 = hipGetLastError();
+      if (e1 != hipSuccess) return e1;
+      const size_t lb = (size_t)top_k * cpwb * 2 * 1024 + (size_t)top_k * 16 * 4;
+      const dim3 gb((H + 15) / 16, T), bb(64 * top_k);
+      const uint4* d4 = reinterpret_cast<const uint4*>(down_s);
+      switch (cpwb) {
+        case 1: hipLaunchKernelGGL((k_moe_b_token<1>), gb, bb, lb, st, H, I, top_k, d4, down_sc, ws, y, y_bf16); break;
+        case 2: hipLaunchKernelGGL((k_moe_b_token<2>), gb, bb, lb, st, H, I, top_k, d4, down_sc, ws, y, y_bf16); break;
+        case 3: hipLaunchKernelGGL((k_moe_b_token<3>), gb, bb, lb, st, H, I, top_k, d4, down_sc, ws, y, y_bf16); break;
+        default: hipLaunchKernelGGL((k_moe_b_token<4>), gb, bb, lb, st, H, I, top_k, d4, down_sc, ws, y, y_bf16); break;
+      }
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, logits, T, E, top_k, ws, ids, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
