@@ -19,6 +19,8 @@
 //  3. down: one workgroup per (16 hidden columns, active expert); writes the
 //     route's fp32 output.
 //  4. combine: y_t = sum over slots j, in slot order, of w_tj * out(t, j).
+#include <type_traits>
+
 #include "dec_core.h"
 #include "kernels.h"
 
@@ -163,38 +165,46 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ lg, int E, 
   wt = ex / row0_sum(ex);
 }
 
-// One workgroup of 1024 threads. Top-k: one wave per token. Routes of one
-// expert are ordered by token (slots of one token name distinct experts): the
-// rank of route (t, j) inside its expert is the number of earlier tokens in the
-// expert's token bitmap.
-__global__ __launch_bounds__(1024) void k_moe_route(const float* __restrict__ logits, int T, int E, int k, MoeWs ws,
-                                                    int32_t* __restrict__ ids_user, float* __restrict__ w_user) {
+// Top-k of every token, one wave per token, four tokens per workgroup.
+__global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logits, int T, int E, int k, MoeWs ws,
+                                                  int32_t* __restrict__ ids_user, float* __restrict__ w_user) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int id;
+  float w;
+  if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, id, w);
+  else wave_route<16>(logits + (size_t)t * E, E, k, id, w);
+  if (lane < k) {
+    ws.ids[t * k + lane] = id;
+    ws.wts[t * k + lane] = w;
+    if (ids_user) ids_user[t * k + lane] = id;
+    if (w_user) w_user[t * k + lane] = w;
+  }
+}
+
+// One workgroup of 1024 threads builds the expert-major lists from the ids.
+// Routes of one expert are ordered by token (slots of one token name distinct
+// experts): the rank of route (t, j) inside its expert is the number of earlier
+// tokens in the expert's token bitmap.
+__global__ __launch_bounds__(1024) void k_moe_route(int T, int E, int k, MoeWs ws) {
   __shared__ int s_ids[MOE_MAX_R];
   __shared__ int s_cnt[MOE_MAX_E];
   __shared__ int s_off[MOE_MAX_E];
   __shared__ unsigned long long s_map[MOE_MAX_E * (MOE_MAX_T / 64)];
   __shared__ int s_part[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x;
   const int words = (T + 63) >> 6;
   for (int e = tid; e < E; e += blockDim.x) {
     s_cnt[e] = 0;
     for (int q = 0; q < words; ++q) s_map[e * words + q] = 0ull;
   }
   __syncthreads();
-  for (int t = wave; t < T; t += nw) {
-    int myid;
-    float w;
-    if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, myid, w);
-    else wave_route<16>(logits + (size_t)t * E, E, k, myid, w);
-    if (lane < k) {
-      ws.ids[t * k + lane] = myid;
-      ws.wts[t * k + lane] = w;
-      s_ids[t * k + lane] = myid;
-      if (ids_user) ids_user[t * k + lane] = myid;
-      if (w_user) w_user[t * k + lane] = w;
-      atomicAdd(&s_cnt[myid], 1);
-      atomicOr(&s_map[myid * words + (t >> 6)], 1ull << (t & 63));
-    }
+  for (int r = tid; r < T * k; r += blockDim.x) {
+    const int id = ws.ids[r], t = r / k;
+    s_ids[r] = id;
+    atomicAdd(&s_cnt[id], 1);
+    atomicOr(&s_map[id * words + (t >> 6)], 1ull << (t & 63));
   }
   __syncthreads();
   // offsets (exclusive scan of counts) and the ascending list of active experts
@@ -250,22 +260,28 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
   const int pc = perm_pos(n);
   for (int tb = 0; tb < cnt; tb += MAXR) {
     const int rows = (cnt - tb) < MAXR ? (cnt - tb) : MAXR;
-    uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
-    if (c0 < nchunks) {
-      WaveStage<ST_BF16, CPW, MAXR> sx;
-      sx.load(rows, H, c0, [&](int rr) { return x + (size_t)ws.route_tok[r0 + tb + rr] * H; });
-      sx.store(xw);
-    }
-    __syncthreads();
     f32x4 acc[2][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}, {f32x4{0.f, 0.f, 0.f, 0.f}}};
-    if (c0 < nchunks) {
-      const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
-      auto aop = [&](int, int g, int i) -> u32x4 {
-        const int m = min(j, rows - 1);
-        return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
-      };
-      b_compute<BM_GROUP, 2, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
-    }
+    // stage and multiply `rows` tokens with SR staged row slots (SR >= rows)
+    auto tile = [&](auto sr) {
+      constexpr int SR = decltype(sr)::value;
+      uint4* xw = smem + (size_t)wave * CPW * SR * 64;
+      if (c0 < nchunks) {
+        WaveStage<ST_BF16, CPW, SR> sx;
+        sx.load(rows, H, c0, [&](int rr) { return x + (size_t)ws.route_tok[r0 + tb + rr] * H; });
+        sx.store(xw);
+      }
+      __syncthreads();
+      if (c0 < nchunks) {
+        const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+        auto aop = [&](int, int g, int i) -> u32x4 {
+          const int m = min(j, rows - 1);
+          return xs[(((g >> 2) - c0) * SR + m) * 64 + (g & 3) * 16 + i];
+        };
+        b_compute<BM_GROUP, 2, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+      }
+    };
+    if (MAXR > 4 && rows <= 4) tile(std::integral_constant<int, 4>{});
+    else tile(std::integral_constant<int, MAXR>{});
     __syncthreads();
     reduce_waves<2, 1>(acc, reinterpret_cast<f32x4*>(smem));
     if (wave == 0 && n < I) {
@@ -310,22 +326,29 @@ __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __r
   for (int tb = 0; tb < cnt; tb += 8) {
     const int routes = (cnt - tb) < 8 ? (cnt - tb) : 8;
     const int rows = 2 * routes;
-    uint4* xw = smem + (size_t)wave * CPW * 16 * 64;
-    if (c0 < nchunks) {
-      WaveStage<ST_COPY, CPW, 16> sa;
-      sa.load(rows, I, c0, [&](int pr) { return ws.ap + (size_t)(2 * (r0 + tb) + pr) * I; });
-      sa.store(xw);
-    }
-    __syncthreads();
     f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
-    if (c0 < nchunks) {
-      const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
-      auto aop = [&](int, int g, int i) -> u32x4 {
-        const int pr = min(j, rows - 1);
-        return xs[(((g >> 2) - c0) * 16 + pr) * 64 + (g & 3) * 16 + i];
-      };
-      b_compute<BM_GROUP, 1, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
-    }
+    // stage and multiply the `rows` piece rows with SR staged slots (SR >= rows)
+    auto tile = [&](auto sr) {
+      constexpr int SR = decltype(sr)::value;
+      uint4* xw = smem + (size_t)wave * CPW * SR * 64;
+      if (c0 < nchunks) {
+        WaveStage<ST_COPY, CPW, SR> sa;
+        sa.load(rows, I, c0, [&](int pr) { return ws.ap + (size_t)(2 * (r0 + tb) + pr) * I; });
+        sa.store(xw);
+      }
+      __syncthreads();
+      if (c0 < nchunks) {
+        const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+        auto aop = [&](int, int g, int i) -> u32x4 {
+          const int pr = min(j, rows - 1);
+          return xs[(((g >> 2) - c0) * SR + pr) * 64 + (g & 3) * 16 + i];
+        };
+        b_compute<BM_GROUP, 1, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+      }
+    };
+    if (rows <= 4) tile(std::integral_constant<int, 4>{});
+    else if (rows <= 8) tile(std::integral_constant<int, 8>{});
+    else tile(std::integral_constant<int, 16>{});
     __syncthreads();
     reduce_waves<1, 1>(acc, reinterpret_cast<f32x4*>(smem));
     if (wave == 0 && n < H) {
@@ -357,7 +380,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(int T, int H, int k, MoeWs 
 //  B: one workgroup per (16 hidden columns, token), one wave per slot: wave j
 //     multiplies expert ids[t][j]'s down rows by route (t, j)'s intermediate;
 //     wave 0 adds w_tj * out_j over the slots in slot order.
-constexpr int MOE_SMALL_T = 8;
+constexpr int MOE_SMALL_T = 4;
 
 template <int CPW, int MAXR>
 __global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict__ x, const float* __restrict__ logits,
@@ -567,7 +590,8 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, logits, T, E, top_k, ws, ids, w);
+  hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, T, E, top_k, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const DecSplit sg = dec_split(H / 128, 8), sd = dec_split(I / 128, 8);
