@@ -7,15 +7,23 @@
 // kernel moves activation tiles global -> LDS with direct loads
 // (global_load_lds_dwordx4), never through registers.
 //
-// Block tile 256 x 256 x 64, four waves in 2 x 2, each wave 128 x 128 of
-// v_mfma_f32_32x32x16_f16 tiles (16 accumulators of 16 fp32). LDS per stage:
-// A 256 rows x 128 B, B 256 columns x 128 B, two stages (128 KiB). Rows of
-// both tiles hold eight 16-byte chunks stored at slot (chunk ^ ((row/2)%8)),
-// so the 32-row fragment reads of a wave spread over all banks.
-// Per k-step of 64: the direct loads of step k+1 and the sign words of step
-// k+1 are issued first; the 64 MFMAs of step k run; the sign words of step k+1
-// are unpacked (one shift + one and-or per pair) into the other B stage; one
-// barrier.
+// Block tile 256 x 256, k-step 128 (one scale group), four waves in 2 x 2,
+// each wave 128 x 128 of v_mfma_f32_32x32x16_f16 tiles (16 accumulators of
+// 16 fp32). Only the activations go through LDS: 256 rows x 256 B per stage,
+// two stages (128 KiB); a row holds sixteen 16-byte chunks, chunk c at slot
+// c ^ (row % 16), so that the 16 lanes of one LDS pass hit 16 different slots.
+// The weight operand never touches LDS: every lane loads, for each of its four
+// 32-column tiles, the four sign words of its column for the k-step (16 bytes)
+// and the group scale, and builds the MFMA operands in registers (one shift
+// and one and-or per pair of weights).
+//
+// Schedule of one k-step (8 sub-steps of 16 k, 16 MFMAs each): while the
+// MFMAs of sub-step s run, the activation fragments of sub-step s+1 are read
+// from LDS and its weight operands are built. In the middle of sub-step 7 every
+// wave waits for its own direct loads of the next stage and meets the others
+// at one barrier; right after it the direct loads and sign/scale loads two
+// k-steps ahead are issued (one full k-step before they are needed), and the
+// first fragments of the next k-step are read.
 //
 // Layout facts of the 32x32x16 MFMA: A lane l supplies row l%32 and 8
 // consecutive k of block l/32; B lane l supplies column l%32 and the same k
@@ -27,24 +35,21 @@ namespace brq {
 
 namespace {
 
-constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 64;
-constexpr int PF_ROWB = PF_BK * 2;               // bytes per LDS row
-constexpr int PF_TILE = PF_BM * PF_ROWB;         // bytes per A (or B) stage
-
-__device__ __forceinline__ int pf_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 128;
+constexpr int PF_ROWB = PF_BK * 2;        // bytes per LDS row
+constexpr int PF_TILE = PF_BM * PF_ROWB;  // bytes per activation stage
 
 }  // namespace
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf(const uint16_t* __restrict__ xp, int M, int N, int K,
-                                            const uint32_t* __restrict__ signs, const uint16_t* __restrict__ scales,
-                                            void* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* As = lds;                   // [2][PF_TILE]
-  uint8_t* Bs = lds + 2 * PF_TILE;     // [2][PF_TILE]
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf(
+    const uint16_t* __restrict__ xp, int M, int N, int K, const uint32_t* __restrict__ signs,
+    const uint16_t* __restrict__ scales, void* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // [2][PF_TILE]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
 
   // tile id -> (tm, tn): consecutive ids of one XCD (id % 8) cover a
   // contiguous range of tiles, so an XCD streams few activation row-blocks
@@ -53,53 +58,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int bid = blockIdx.x;
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   const int m0 = (bid / tiles_n) * PF_BM, n0 = (bid % tiles_n) * PF_BN;
-  const int nk = K / PF_BK;
-  const int G = K >> 7, KW = K >> 5;  // groups, 32-bit sign words per row
+  const int nk = K / PF_BK;  // k-steps = scale groups
+  const int KW = K >> 5;     // 32-bit sign words per weight row
 
-  // ---- A: this wave's 8 direct-load instructions cover rows 64*wave .. +63
-  // lane L of instruction i: row 64*wave + 8*i + L/8, LDS slot L%8 which holds
-  // chunk (L%8) ^ swz(row)
-  const uint16_t* a_src[8];
+  // ---- activations: this wave's 16 direct loads cover rows 64*wave .. +63;
+  // lane L of load i: row 64*wave + 4*i + L/16, LDS slot L%16, which holds
+  // chunk (L%16) ^ (row%16). Offsets are in bytes from the tile's first row
+  // (rows past M repeat row M-1).
+  uint32_t a_off[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rl = 64 * wave + 8 * i + (lane >> 3);
-    const int gm = m0 + rl < M ? m0 + rl : M - 1;
-    const int chunk = (lane & 7) ^ ((rl >> 1) & 7);
-    a_src[i] = xp + (size_t)gm * K + chunk * 8;
+  for (int i = 0; i < 16; ++i) {
+    const int rl = 64 * wave + 4 * i + (lane >> 4);
+    const int gl = m0 + rl < M ? rl : M - 1 - m0;
+    const int chunk = (lane & 15) ^ (rl & 15);
+    a_off[i] = (uint32_t)gl * (uint32_t)(K * 2) + (uint32_t)(chunk * 16);
   }
-  auto issue_a = [&](int kt, int buf) {
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(xp) + (size_t)m0 * K * 2;
+  // direct loads i0 .. i0+3 of k-step kt into `stage`
+  auto issue_a4 = [&](int kt, int stage, int i0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(a_src[i] + kt * PF_BK, As + buf * PF_TILE + (64 * wave + 8 * i) * PF_ROWB,
-                                       16, 0, 0);
+    for (int i = i0; i < i0 + 4; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xb + a_off[i] + (size_t)kt * PF_ROWB),
+                                       lds + stage * PF_TILE + (64 * wave + 4 * i) * PF_ROWB, 16, 0, 0);
   };
 
-  // ---- B: thread t unpacks column n0 + t (one 64-bit sign word per k-step)
-  const int bn = n0 + tid;
-  const bool bok = bn < N;
-  const int bnr = bok ? bn : N - 1;
-  const uint32_t* b_sig = signs + (size_t)bnr * KW;
-  const uint16_t* b_sc = scales + (size_t)bnr * G;
-  uint2 bw;
-  uint32_t bs;
-  auto load_b = [&](int kt) {
-    bw = *reinterpret_cast<const uint2*>(b_sig + 2 * kt);
-    bs = b_sc[kt >> 1];
-  };
-  auto store_b = [&](int buf) {
-    const uint32_t S = bok ? (bs | (bs << 16)) : 0u;
-    uint8_t* row = Bs + buf * PF_TILE + tid * PF_ROWB;
+  // ---- weights: column tile j of this wave is columns n0 + wc*128 + 32j ..,
+  // lane column fr; the lane's k block (fh) selects pairs 4*fh .. 4*fh+3 of
+  // each half-run, so its sign words are pre-shifted right by 4*fh.
+  const uint32_t* b_sig[4];
+  const uint16_t* b_sc[4];
+  bool b_ok[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t dw = (c < 4) ? bw.x : bw.y;
-      u32x4 o;
+  for (int j = 0; j < 4; ++j) {
+    const int c = n0 + wc * 128 + 32 * j + fr;
+    b_ok[j] = c < N;
+    const int cc = c < N ? c : N - 1;
+    b_sig[j] = signs + (size_t)cc * KW;
+    b_sc[j] = scales + (size_t)cc * nk;
+  }
+  uint4 wn[4];       // sign words of the next k-step (in flight)
+  uint32_t sn[4];    // its scales
+  auto load_b = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wn[j] = *reinterpret_cast<const uint4*>(b_sig[j] + 4 * kt);
+      sn[j] = b_sc[j][kt];
+    }
+  };
+  uint32_t wsh[4][4];  // pre-shifted sign words of the current k-step
+  uint32_t S[4];       // magnitude pair (scale | scale << 16), 0 past N
+  const int bshift = 4 * fh;
+  auto take_b = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wsh[j][0] = wn[j].x >> bshift;
+      wsh[j][1] = wn[j].y >> bshift;
+      wsh[j][2] = wn[j].z >> bshift;
+      wsh[j][3] = wn[j].w >> bshift;
+      S[j] = b_ok[j] ? (sn[j] | (sn[j] << 16)) : 0u;
+    }
+  };
+  // weight operand of tile j, sub-step ks: pairs b = 8*(ks%2) + t of run ks/2
+  u32x4 bo[2][4];
+  auto build_b = [&](int ks, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = wsh[j][ks >> 1];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int bit = 4 * (c & 3) + t;
-        o[t] = ((dw << (15 - bit)) & 0x80008000u) | S;
+        const int b = 8 * (ks & 1) + t;
+        bo[buf][j][t] = ((w << (15 - b)) & 0x80008000u) | S[j];
       }
-      *reinterpret_cast<u32x4*>(row + pf_slot(tid, c) * 16) = o;
     }
+  };
+
+  // ---- activation fragments: row wr*128 + 32i + fr, chunk 2*ks + fh at slot
+  // (2*ks + fh) ^ (row % 16) = (2*ks) ^ (fh ^ fr % 16)
+  const int a_row = (wr * 128 + fr) * PF_ROWB;
+  const int a_x = (fh ^ (fr & 15)) * 16;
+  u32x4 af[2][4];
+  auto read_a = [&](int stage, int ks, int buf) {
+    const uint8_t* p = lds + stage * PF_TILE + a_row + ((32 * ks) ^ a_x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[buf][i] = *reinterpret_cast<const u32x4*>(p + i * 32 * PF_ROWB);
   };
 
   f32x16 acc[4][4];
@@ -110,62 +151,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment read offsets (bytes inside a stage); the k chunk of sub-step ks
-  // is 2*ks + l/32
-  const int fr = lane & 31, fh = lane >> 5;
-  int a_off[4], b_off[4];
+  auto mfmas = [&](int buf, int i0, int i1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_off[i] = (wr * 128 + 32 * i + fr) * PF_ROWB;
-    b_off[i] = (wc * 128 + 32 * i + fr) * PF_ROWB;
-  }
-  const int swz = (fr >> 1) & 7;  // rows of a fragment start at multiples of 32
-
-  // fragments of sub-step ks live in af[ks&1], bfr[ks&1]; the reads of sub-step
-  // ks+1 are issued before the 16 MFMAs of sub-step ks
-  u32x4 af[2][4], bfr[2][4];
-  auto read_frags = [&](const uint8_t* Ac, const uint8_t* Bc, int ks, int set) {
-    const int slot = ((2 * ks + fh) ^ swz) * 16;
+    for (int i = i0; i < i1; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[set][i] = *reinterpret_cast<const u32x4*>(Ac + a_off[i] + slot);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[set][j] = *reinterpret_cast<const u32x4*>(Bc + b_off[j] + slot);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[buf][i], bo[buf][j], acc[i][j]);
   };
 
-  // prologue: stage 0 complete
-  issue_a(0, 0);
+  // One k-step per iteration; stage cur holds k-step kt. During sub-steps
+  // 0..3 the direct loads of k-step kt+1 go into the other stage (free since
+  // the last barrier), 4 per sub-step, and the sign/scale words of kt+1 are
+  // requested in sub-step 0. Each sub-step region below is ordered by
+  // scheduling-group barriers so that the LDS reads, the operand build and the
+  // loads sit between the MFMAs instead of in front of them.
+  issue_a4(0, 0, 0);
+  issue_a4(0, 0, 4);
+  issue_a4(0, 0, 8);
+  issue_a4(0, 0, 12);
   load_b(0);
   __builtin_amdgcn_s_waitcnt(0);
-  store_b(0);
+  take_b();
   __syncthreads();
+  read_a(0, 0, 0);
+  build_b(0, 0);
 
-  // One k-step per iteration. Stage `cur` holds step kt. The direct loads and
-  // the sign words of step kt+1 are issued first (pinned there by a scheduling
-  // barrier), the 64 MFMAs of step kt run, then the sign words are unpacked
-  // into stage cur^1. The body has no branches: the loads of the last step
-  // repeat step nk-1 into the idle stage.
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    const int k1 = kt + 1 < nk ? kt + 1 : kt;
-    const uint8_t* Ac = As + cur * PF_TILE;
-    const uint8_t* Bc = Bs + cur * PF_TILE;
-    issue_a(k1, cur ^ 1);
-    load_b(k1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(Ac, Bc, 0, 0);
+    const int nx = kt + 1 < nk ? kt + 1 : kt;  // past the end: repeat the last step (unused)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) read_frags(Ac, Bc, ks + 1, (ks + 1) & 1);
+    for (int ks = 0; ks < 7; ++ks) {
+      const int b = ks & 1;
+      read_a(cur, ks + 1, b ^ 1);
+      build_b(ks + 1, b ^ 1);
+      if (ks < 4) issue_a4(nx, cur ^ 1, 4 * ks);
+      if (ks == 0) load_b(nx);
+      mfmas(b, 0, 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[ks & 1][i], bfr[ks & 1][j], acc[i][j]);
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+        if (m < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        if (ks < 4 && m < 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
+        if (ks == 0 && m >= 4 && m < 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // sign/scale load
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);      // three VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);  // the sign words are consumed only after the MFMAs
-    store_b(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // direct loads of step kt+1 landed
-    __syncthreads();
+    // sub-step 7: half of its MFMAs, then the k-step boundary
+    mfmas(1, 0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);  // own direct loads of the next stage and its weights landed
+    __syncthreads();                // every wave's loads landed and every wave is done with stage cur
+    take_b();
+    read_a(cur ^ 1, 0, 0);
+    build_b(0, 0);
+    mfmas(1, 2, 4);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
 
   // ---- epilogue: lane writes column fr of each 32 x 32 tile, rows in runs of 4
   const bool full = (m0 + PF_BM <= M) && (n0 + PF_BN <= N);
@@ -200,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-size_t pf_lds_bytes() { return 4 * (size_t)PF_TILE; }
+size_t pf_lds_bytes() { return 2 * (size_t)PF_TILE; }
 
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                           void* y, int y_bf16, void* ws, hipStream_t st) {
