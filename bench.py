@@ -93,6 +93,20 @@ def copy_calibration(torch, mib=512, reps=5):
     return dict(copy_bytes=n, reps=reps)
 
 
+def warm_gpu(torch, seconds=0.5):
+    """Run dense matrix products for about `seconds` so that clocks and power
+    reach their steady state before anything is timed (the first few hundred
+    microseconds of work after an idle period run at lower clocks)."""
+    a = torch.randn((8192, 8192), device="cuda", dtype=torch.float16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            a = torch.matmul(a, a).mul_(1e-4)
+        torch.cuda.synchronize()
+    del a
+
+
 def ring_copies(per_copy_bytes):
     return max(2, int(np.ceil(2 * MALL_BYTES / per_copy_bytes)))
 
@@ -128,6 +142,7 @@ def graph_time(torch, fn, n_items, replays=5):
     """Capture fn() (which enqueues n_items kernel launches) in a HIP graph,
     replay it `replays` times and return ms per replay (median), GPU time only:
     no host submission gaps between the captured launches."""
+    warm_gpu(torch, 0.3)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -275,6 +290,7 @@ def run_prefill(brq, torch, iters=10):
     for _ in range(2):
         brq.kron_rotate(x, H, R, y=xr)
         brq.gemm(xr, s, sc, N, K, y=y)
+    warm_gpu(torch)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     rot_ms = gemm_ms = 0.0
