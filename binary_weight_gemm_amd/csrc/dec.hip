@@ -172,6 +172,178 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
   }
 }
 
+// ---- M = 1 on the fp8 x fp4 matrix cores ----------------------------------
+// A weight operand of +-1 needs only its sign, and fp4 (e2m1) has no infinity
+// or NaN: OR-ing 0b0111 onto a nibble whose top bit is a sign bit gives +-6.0.
+// So one shift-or turns a 32-bit sign word into 8 fp4 operands (dword t of a
+// lane's 32-k block holds, in nibble q, the sign of k = 4q + t). The
+// activation row is split per wave into two fp8 (e4m3) pieces, hi = RNE(x*2^-a)
+// and lo = RNE((x*2^-a - hi)*16), with 2^a chosen from the slice maximum so
+// |x*2^-a| < 256; both are exact for every element within 2^13 of the slice
+// maximum (a bf16 value has 8 significant bits, each piece carries 4), and
+// rows 0/1 of v_mfma_scale_f32_16x16x128_f8f6f4 take them with block
+// exponents a and a-4. One MFMA covers one scale group of 16 columns; the
+// group scale and the 1/6 are applied in fp32 afterwards.
+//
+// Layout facts of that MFMA (fp8 A, fp4 B): A lane l supplies row l%16 with
+// bytes 0..15 = k 16*(l/16).. and bytes 16..31 = k 64+16*(l/16)..; B lane l
+// supplies column l%16 with nibble p = k 32*(l/16)+p; the A block exponent of
+// (row r, k block b) comes from lane r + 16b; D as for the 16x16 f16 MFMA.
+// A lane loads group 4c+kb of its column; four permlane swaps transpose the
+// 4 x 4 (group, word) block of the four lanes of a column so that MFMA i gets
+// word kb of group 4c+i.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// (group, word) transpose across the four 16-lane rows: on entry register w
+// of row g holds word w of group g; on exit register i of row b holds word b
+// of group i.
+__device__ __forceinline__ void transpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3) {
+  auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r0 = c[0];
+  r1 = c[1];
+  r2 = d[0];
+  r3 = d[1];
+}
+
+template <int CPW, int NT>
+__global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict__ x, int N, int K,
+                                                      const uint4* __restrict__ signs,
+                                                      const uint16_t* __restrict__ scales, void* __restrict__ y,
+                                                      int y_bf16) {
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int G = K >> 7;
+  const int nchunks = (G + 3) >> 2;
+  const int c0 = wave * CPW;
+  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * CPW * 1024;  // [chunk][group][piece][128]
+  float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * CPW * 1024);
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+  if (c0 < nchunks) {  // uniform across the wave
+    // ---- loads: activations (8 per lane per chunk), sign words, 4 scales per chunk
+    uint4 xv[CPW];
+    uint4 sg[NT][CPW];
+    uint2 sc[NT][CPW];
+    bool cok[NT];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int k0 = (c0 + c) * 512 + 8 * lane;
+      xv[c] = *reinterpret_cast<const uint4*>(x + (k0 < K ? k0 : 0));
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = (blockIdx.x * NT + t) * 16 + j;
+      cok[t] = n < N;
+      const size_t row = (size_t)(n < N ? n : 0) * G;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int g = 4 * (c0 + c) + kb, gs = 4 * (c0 + c);
+        sg[t][c] = signs[row + (g < G ? g : 0)];
+        sc[t][c] = *reinterpret_cast<const uint2*>(scales + row + (gs < G ? gs : 0));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    // ---- block exponents from the slice maximum
+    uint32_t mx = 0;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint32_t w4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) mx = max(mx, max(w4[h] & 0x7fffu, (w4[h] >> 16) & 0x7fffu));
+    }
+    mx = wave_max_u32(mx);
+    int sh = (int)(mx >> 7) - 7;  // E8M0 exponent of the hi piece: 2^(e_max - 7)
+    sh = sh < 5 ? 5 : (sh > 253 ? 253 : sh);
+    const float mh = __uint_as_float((uint32_t)(254 - sh) << 23);  // 2^(127 - sh)
+    // ---- pieces in the operand order: lane L's 8 values are k = 8L .. 8L+7 of
+    // the chunk (group L/16, word (L%16)/4); value e lands at in-word position
+    // 8*(e%4) + 2*(L%4) + e/4
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint32_t w4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (e & 1) ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16);
+        v[e] = __uint_as_float(h) * mh;
+      }
+      uint8_t* base = xw + c * 1024 + (lane >> 4) * 256 + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int hi2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[t], v[t + 4], 0, false);
+        const float r0 = (v[t] - __builtin_amdgcn_cvt_f32_fp8(hi2, 0)) * 16.f;
+        const float r1 = (v[t + 4] - __builtin_amdgcn_cvt_f32_fp8(hi2, 1)) * 16.f;
+        const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+        *reinterpret_cast<uint16_t*>(base + 8 * t) = (uint16_t)hi2;
+        *reinterpret_cast<uint16_t*>(base + 128 + 8 * t) = (uint16_t)lo2;
+      }
+    }
+    // A block exponent of this lane's row: row 0 = hi, row 1 = lo, other rows
+    // (copies of the lo piece, unused) take the lo exponent as well
+    const int sa = (j == 0) ? sh : sh - 4;
+    const int prow = j == 0 ? 0 : 1;
+    // ---- products
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint8_t* ab = xw + c * 1024 + prow * 128 + 16 * kb;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint32_t w0 = sg[t][c].x, w1 = sg[t][c].y, w2 = sg[t][c].z, w3 = sg[t][c].w;
+        transpose4(w0, w1, w2, w3);
+        const uint32_t wi[4] = {w0, w1, w2, w3};
+        const uint32_t s4[4] = {sc[t][c].x & 0xffffu, sc[t][c].x >> 16, sc[t][c].y & 0xffffu, sc[t][c].y >> 16};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(ab + i * 256);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ab + i * 256 + 64);
+          i32x8 A, B;
+          A[0] = a0[0]; A[1] = a0[1]; A[2] = a0[2]; A[3] = a0[3];
+          A[4] = a1[0]; A[5] = a1[1]; A[6] = a1[2]; A[7] = a1[3];
+          B[0] = (int)((wi[i] << 3) | 0x77777777u);
+          B[1] = (int)((wi[i] << 2) | 0x77777777u);
+          B[2] = (int)((wi[i] << 1) | 0x77777777u);
+          B[3] = (int)(wi[i] | 0x77777777u);
+          B[4] = 0; B[5] = 0; B[6] = 0; B[7] = 0;
+          const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
+                                                                           sa, 0, 127);
+          const bool ok = cok[t] && (4 * (c0 + c) + i < G);
+          const float s = ok ? f16_bits_to_f32(s4[i]) : 0.f;
+          acc[t] = fmaf(s, d[0] + d[1], acc[t]);
+        }
+      }
+    }
+  }
+  // lanes 0..15 hold the partial sums of columns j of the NT tiles
+  if (wave > 0 && kb == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[((wave - 1) * NT + t) * 16 + j] = acc[t];
+  }
+  __syncthreads();
+  if (wave != 0 || kb != 0) return;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float v = acc[t];
+    for (int w = 1; w < nw; ++w) v += red[((w - 1) * NT + t) * 16 + j];
+    const int n = (blockIdx.x * NT + t) * 16 + j;
+    if (n < N) store_out(y, (size_t)n, v / 6.0f, y_bf16);
+  }
+}
+
 // staged row slots for M activation rows
 static int dec_maxr(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
@@ -219,9 +391,34 @@ static void gemm_dec_prep(const uint16_t* xa, int M, int N, int K, const uint4* 
                                             y, y_bf16));
 }
 
+// The fp8 x fp4 path takes M = 1 when the scale groups come in whole chunks
+// of four (K % 512 == 0); it splits K like the one-launch fp16 path. Two
+// column tiles per workgroup when that still leaves well over one workgroup
+// per compute unit (the activation pieces are then shared by both tiles).
+static void gemm_dec_f4(const uint16_t* x, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
+                        int y_bf16, hipStream_t st) {
+  DecSplit sp;
+  dec_lds_split(1, K, sp);
+  const int tiles = (N + 15) / 16;
+  const int nt = tiles >= 768 ? 2 : 1;
+  const size_t lds = (size_t)sp.waves * sp.cpw * 1024 + (size_t)(sp.waves - 1) * nt * 16 * 4;
+  const dim3 grid((tiles + nt - 1) / nt), block(64 * sp.waves);
+  if (nt == 2) {
+    BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 2>), grid, block, lds, st, x, N, K, s4, scales, y,
+                                              y_bf16));
+  } else {
+    BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 1>), grid, block, lds, st, x, N, K, s4, scales, y,
+                                              y_bf16));
+  }
+}
+
 hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                            void* y, int y_bf16, void* ws, hipStream_t st) {
   const uint4* s4 = reinterpret_cast<const uint4*>(signs);
+  if (M == 1 && K % 512 == 0 && gemm_dec_in_lds(M, K)) {
+    gemm_dec_f4(x, N, K, s4, scales, y, y_bf16, st);
+    return hipGetLastError();
+  }
   if (gemm_dec_in_lds(M, K)) {
     if (M == 1) gemm_dec_lds<1>(x, M, N, K, s4, scales, y, y_bf16, st);
     else if (M <= 2) gemm_dec_lds<2>(x, M, N, K, s4, scales, y, y_bf16, st);
