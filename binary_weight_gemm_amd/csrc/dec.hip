@@ -177,13 +177,15 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 // or NaN: OR-ing 0b0111 onto a nibble whose top bit is a sign bit gives +-6.0.
 // So one shift-or turns a 32-bit sign word into 8 fp4 operands (dword t of a
 // lane's 32-k block holds, in nibble q, the sign of k = 4q + t). The
-// activation row is split per wave into two fp8 (e4m3) pieces, hi = RNE(x*2^-a)
-// and lo = RNE((x*2^-a - hi)*16), with 2^a chosen from the slice maximum so
-// |x*2^-a| < 256; both are exact for every element within 2^13 of the slice
-// maximum (a bf16 value has 8 significant bits, each piece carries 4), and
-// rows 0/1 of v_mfma_scale_f32_16x16x128_f8f6f4 take them with block
-// exponents a and a-4. One MFMA covers one scale group of 16 columns; the
-// group scale and the 1/6 are applied in fp32 afterwards.
+// activation row is split per wave into three fp8 (e4m3) pieces, p0 =
+// RNE(v), p1 = RNE((v - p0)*16), p2 = RNE(((v - p0)*16 - p1)*16) with
+// v = x*2^-a and 2^a chosen from the slice maximum so |v| < 256. A bf16 value
+// has 8 significant bits and each piece carries 4, so the pieces add up to x
+// exactly for every element within 2^17 of the slice maximum; smaller ones are
+// off by at most 2^-25 of the maximum. Rows 0/1/2 of
+// v_mfma_scale_f32_16x16x128_f8f6f4 take them with block exponents a, a-4 and
+// a-8. One MFMA covers one scale group of 16 columns; the group scale and the
+// 1/6 are applied in fp32 afterwards.
 //
 // Layout facts of that MFMA (fp8 A, fp4 B): A lane l supplies row l%16 with
 // bytes 0..15 = k 16*(l/16).. and bytes 16..31 = k 64+16*(l/16)..; B lane l
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 // 4 x 4 (group, word) block of the four lanes of a column so that MFMA i gets
 // word kb of group 4c+i.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int F4_CHUNK = 4 * 3 * 128;  // LDS bytes of one chunk: 4 groups x 3 pieces x 128
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
@@ -229,8 +232,8 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
   const int G = K >> 7;
   const int nchunks = (G + 3) >> 2;
   const int c0 = wave * CPW;
-  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * CPW * 1024;  // [chunk][group][piece][128]
-  float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * CPW * 1024);
+  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * CPW * F4_CHUNK;  // [chunk][group][piece][128]
+  float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * CPW * F4_CHUNK);
   float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.f;
@@ -267,8 +270,8 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
       for (int h = 0; h < 4; ++h) mx = max(mx, max(w4[h] & 0x7fffu, (w4[h] >> 16) & 0x7fffu));
     }
     mx = wave_max_u32(mx);
-    int sh = (int)(mx >> 7) - 7;  // E8M0 exponent of the hi piece: 2^(e_max - 7)
-    sh = sh < 5 ? 5 : (sh > 253 ? 253 : sh);
+    int sh = (int)(mx >> 7) - 7;  // E8M0 exponent of piece 0: 2^(e_max - 7)
+    sh = sh < 9 ? 9 : (sh > 253 ? 253 : sh);
     const float mh = __uint_as_float((uint32_t)(254 - sh) << 23);  // 2^(127 - sh)
     // ---- pieces in the operand order: lane L's 8 values are k = 8L .. 8L+7 of
     // the chunk (group L/16, word (L%16)/4); value e lands at in-word position
@@ -282,25 +285,29 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
         const uint32_t h = (e & 1) ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16);
         v[e] = __uint_as_float(h) * mh;
       }
-      uint8_t* base = xw + c * 1024 + (lane >> 4) * 256 + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
+      uint8_t* base = xw + c * F4_CHUNK + (lane >> 4) * 384 + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int hi2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[t], v[t + 4], 0, false);
-        const float r0 = (v[t] - __builtin_amdgcn_cvt_f32_fp8(hi2, 0)) * 16.f;
-        const float r1 = (v[t + 4] - __builtin_amdgcn_cvt_f32_fp8(hi2, 1)) * 16.f;
-        const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-        *reinterpret_cast<uint16_t*>(base + 8 * t) = (uint16_t)hi2;
-        *reinterpret_cast<uint16_t*>(base + 128 + 8 * t) = (uint16_t)lo2;
+        float a0 = v[t], a1 = v[t + 4];
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc) {
+          const int q2 = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+          *reinterpret_cast<uint16_t*>(base + 128 * pc + 8 * t) = (uint16_t)q2;
+          if (pc < 2) {
+            a0 = (a0 - __builtin_amdgcn_cvt_f32_fp8(q2, 0)) * 16.f;
+            a1 = (a1 - __builtin_amdgcn_cvt_f32_fp8(q2, 1)) * 16.f;
+          }
+        }
       }
     }
-    // A block exponent of this lane's row: row 0 = hi, row 1 = lo, other rows
-    // (copies of the lo piece, unused) take the lo exponent as well
-    const int sa = (j == 0) ? sh : sh - 4;
-    const int prow = j == 0 ? 0 : 1;
+    // A row j holds piece min(j, 2) (rows past 2 repeat piece 2 and are not
+    // used) with block exponent sh - 4 * piece
+    const int prow = j < 2 ? j : 2;
+    const int sa = sh - 4 * prow;
     // ---- products
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const uint8_t* ab = xw + c * 1024 + prow * 128 + 16 * kb;
+      const uint8_t* ab = xw + c * F4_CHUNK + prow * 128 + 16 * kb;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t w0 = sg[t][c].x, w1 = sg[t][c].y, w2 = sg[t][c].z, w3 = sg[t][c].w;
@@ -309,8 +316,8 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
         const uint32_t s4[4] = {sc[t][c].x & 0xffffu, sc[t][c].x >> 16, sc[t][c].y & 0xffffu, sc[t][c].y >> 16};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(ab + i * 256);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ab + i * 256 + 64);
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(ab + i * 384);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ab + i * 384 + 64);
           i32x8 A, B;
           A[0] = a0[0]; A[1] = a0[1]; A[2] = a0[2]; A[3] = a0[3];
           A[4] = a1[0]; A[5] = a1[1]; A[6] = a1[2]; A[7] = a1[3];
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
                                                                            sa, 0, 127);
           const bool ok = cok[t] && (4 * (c0 + c) + i < G);
           const float s = ok ? f16_bits_to_f32(s4[i]) : 0.f;
-          acc[t] = fmaf(s, d[0] + d[1], acc[t]);
+          acc[t] = fmaf(s, (d[0] + d[1]) + d[2], acc[t]);
         }
       }
     }
@@ -401,7 +408,7 @@ static void gemm_dec_f4(const uint16_t* x, int N, int K, const uint4* s4, const 
   dec_lds_split(1, K, sp);
   const int tiles = (N + 15) / 16;
   const int nt = tiles >= 768 ? 2 : 1;
-  const size_t lds = (size_t)sp.waves * sp.cpw * 1024 + (size_t)(sp.waves - 1) * nt * 16 * 4;
+  const size_t lds = (size_t)sp.waves * sp.cpw * F4_CHUNK + (size_t)(sp.waves - 1) * nt * 16 * 4;
   const dim3 grid((tiles + nt - 1) / nt), block(64 * sp.waves);
   if (nt == 2) {
     BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 2>), grid, block, lds, st, x, N, K, s4, scales, y,
