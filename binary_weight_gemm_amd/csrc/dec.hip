@@ -249,18 +249,21 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
       const int k0 = (c0 + c) * 512 + 8 * lane;
       xv[c] = *reinterpret_cast<const uint4*>(x + (k0 < K ? k0 : 0));
     }
+    size_t row[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int n = (blockIdx.x * NT + t) * 16 + j;
       cok[t] = n < N;
-      const size_t row = (size_t)(n < N ? n : 0) * G;
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        const int g = 4 * (c0 + c) + kb, gs = 4 * (c0 + c);
-        sg[t][c] = signs[row + (g < G ? g : 0)];
-        sc[t][c] = *reinterpret_cast<const uint2*>(scales + row + (gs < G ? gs : 0));
-      }
+      row[t] = (size_t)(n < N ? n : 0) * G;
     }
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int g = 4 * (c0 + c) + kb, gs = 4 * (c0 + c);
+        sg[t][c] = signs[row[t] + (g < G ? g : 0)];
+        sc[t][c] = *reinterpret_cast<const uint2*>(scales + row[t] + (gs < G ? gs : 0));
+      }
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
     // ---- block exponents from the slice maximum
     uint32_t mx = 0;
@@ -401,8 +404,12 @@ static void gemm_dec_prep(const uint16_t* xa, int M, int N, int K, const uint4* 
 // per compute unit (the activation pieces are then shared by both tiles).
 static void gemm_dec_f4(const uint16_t* x, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
                         int y_bf16, hipStream_t st) {
+  // one chunk per wave up to 16 waves (the less a wave computes after its
+  // last sign word lands, the shorter the tail), two beyond
+  const int chunks = K / 512;
   DecSplit sp;
-  dec_lds_split(1, K, sp);
+  sp.cpw = chunks <= 16 ? 1 : (chunks + 15) / 16;
+  sp.waves = (chunks + sp.cpw - 1) / sp.cpw;
   const int tiles = (N + 15) / 16;
   const int nt = tiles >= 768 ? 2 : 1;
   const size_t lds = (size_t)sp.waves * sp.cpw * F4_CHUNK + (size_t)(sp.waves - 1) * nt * 16 * 4;
