@@ -66,7 +66,7 @@ def kernel_source_hash(files):
 # (profiles/decode_m1_traffic.txt, a JSON record). It is reported only while the kernel
 # sources still hash to the value recorded with the counters.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_m1_traffic.txt")
-DECODE_SOURCES = ("common.h", "dec_core.h", "dec.hip", "abi.hip")
+DECODE_SOURCES = ("common.h", "dec_core.h", "dec.hip", "abi.hip", "kernels.h")
 
 
 def recorded_traffic():
@@ -411,7 +411,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "fp8xfp4",
         "data": "synthetic",
         "config": {
             "workload": "decode binary GEMV: W 4096x14336 and 14336x4096 group-128 sign + fp16 scale, "
