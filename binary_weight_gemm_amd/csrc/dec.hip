@@ -354,6 +354,10 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
 // staged row slots for M activation rows
 static int dec_maxr(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
+// staging budget of the one-launch path: up to 128 KiB of LDS (beyond 64 KiB
+// the kernel needs the per-function opt-in below)
+constexpr int64_t kDecLdsBig = 128 * 1024;
+
 // Split of the one-launch path: chunks of 512 over at most 16 waves, two
 // chunks per wave when there are at least four (one chunk each below), more
 // only when 16 waves of two do not cover K. The staged slices
@@ -366,7 +370,7 @@ static bool dec_lds_split(int64_t M, int64_t K, DecSplit& sp) {
   if (cpw > 8) return false;
   sp.cpw = (int)cpw;
   sp.waves = (int)((chunks + cpw - 1) / cpw);
-  return (int64_t)sp.waves * sp.cpw * dec_maxr(M) * 1024 <= kDecLdsBytes;
+  return (int64_t)sp.waves * sp.cpw * dec_maxr(M) * 1024 <= kDecLdsBig;
 }
 
 bool gemm_dec_in_lds(int64_t M, int64_t K) {
@@ -381,11 +385,17 @@ static void gemm_dec_lds(const uint16_t* x, int M, int N, int K, const uint4* s4
   dec_lds_split(M, K, sp);
   const size_t lds = (size_t)sp.waves * sp.cpw * MAXR * 1024 + (size_t)(sp.waves - 1) * 64 * 16;
   const dim3 grid((N + 15) / 16), block(64 * sp.waves);
-  if (sp.cpw == 2 && (K / 128) % 8 == 0)
+  auto opt_in = [&](const void* fn) {
+    if (lds > 64 * 1024) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  };
+  if (sp.cpw == 2 && (K / 128) % 8 == 0) {
+    opt_in(reinterpret_cast<const void*>(&k_gemm_dec_lds<2, MAXR, true>));
     hipLaunchKernelGGL((k_gemm_dec_lds<2, MAXR, true>), grid, block, lds, st, x, M, N, K, s4, scales, y, y_bf16);
-  else
-    BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_lds<CPW, MAXR, false>), grid, block, lds, st, x, M, N,
-                                              K, s4, scales, y, y_bf16));
+  } else {
+    BRQ_CPW_SWITCH(sp.cpw, opt_in(reinterpret_cast<const void*>(&k_gemm_dec_lds<CPW, MAXR, false>));
+                   hipLaunchKernelGGL((k_gemm_dec_lds<CPW, MAXR, false>), grid, block, lds, st, x, M, N, K, s4,
+                                      scales, y, y_bf16));
+  }
 }
 
 template <int TT>
