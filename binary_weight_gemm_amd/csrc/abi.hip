@@ -71,8 +71,9 @@ brq_status hip_result(hipError_t e, const char* what) {
 
 bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
 
-size_t gemm_ws(int64_t M, int64_t K) {
-  return (M <= 64 && brq::gemm_dec_in_lds(M, K)) ? 0 : brq::align256((size_t)M * K * 2);
+size_t gemm_ws(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64) return brq::gemm_dec_in_lds(M, K) ? 0 : brq::mid_ws_bytes(M, N, K);
+  return brq::align256((size_t)M * K * 2);
 }
 
 }  // namespace
@@ -123,9 +124,8 @@ brq_status brq_pack(const float* w, int64_t rows, int64_t cols, uint64_t* signs,
 }
 
 size_t brq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)N;
-  if (M < 1 || K < 128 || K % 128) return 0;
-  return gemm_ws(M, K);
+  if (M < 1 || N < 1 || K < 128 || K % 128) return 0;
+  return gemm_ws(M, N, K);
 }
 
 brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint64_t* signs,
@@ -138,7 +138,7 @@ brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const ui
   if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm: unknown y_dtype %d", (int)y_dtype);
   if (!aligned(x, 16) || !aligned(signs, 16) || !aligned(scales, 16) || !aligned(y, 16))
     return fail(BRQ_E_ALIGN, "brq_gemm: x, signs, scales and y must be 16-byte aligned");
-  const size_t need = gemm_ws(M, K);
+  const size_t need = gemm_ws(M, N, K);
   if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
     return fail(BRQ_E_WORKSPACE, "brq_gemm: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
   brq_status s = check_device();

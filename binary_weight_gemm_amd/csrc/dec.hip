@@ -57,47 +57,6 @@ hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream
   return hipGetLastError();
 }
 
-// Few-row product with activations from the permuted copy written by k_prep
-// (8 < M <= 64, or when the activation slices do not fit the LDS budget).
-template <int TT, int CPW>
-__global__ __launch_bounds__(1024) void k_gemm_dec(const uint16_t* __restrict__ xa, int M, int N, int K,
-                                                   const uint4* __restrict__ signs,
-                                                   const uint16_t* __restrict__ scales, void* __restrict__ y,
-                                                   int y_bf16) {
-  extern __shared__ uint4 smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int j = lane & 15;
-  const int n = blockIdx.x * 16 + j;
-  const int G = K >> 7;
-  const int nchunks = (G + 3) >> 2;
-  const int nr = n < N ? n : 0;  // clamped row; masked by rok
-  const uint4* wsig[1] = {signs + (size_t)nr * G};
-  const uint16_t* wsc[1] = {scales + (size_t)nr * G};
-  const bool rok[1] = {n < N};
-  f32x4 acc[1][TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  BPre<1, CPW> bp;
-  for (int base = 0; base < nchunks; base += nw * CPW) {
-    const int c0 = base + wave * CPW;
-    b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
-    auto aop = [&](int tt, int g, int i) -> u32x4 {
-      const int m = min(16 * tt + j, M - 1);
-      return reinterpret_cast<const u32x4*>(xa + (size_t)m * K)[g * 16 + i];
-    };
-    b_compute<BM_GROUP, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
-  }
-  reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
-  if (wave != 0 || n >= N) return;
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * tt + 4 * (lane >> 4) + i;
-      if (m < M) store_out(y, (size_t)m * N + n, acc[0][tt][i], y_bf16);
-    }
-}
-
 // One-launch product for M <= 8: wave w owns chunks w*CPW .. w*CPW+CPW-1 of
 // the reduction. It issues the loads of its activation slice (all MAXR row
 // slots), of its sign words and of its scales before any wait, converts the
@@ -398,16 +357,6 @@ static void gemm_dec_lds(const uint16_t* x, int M, int N, int K, const uint4* s4
   }
 }
 
-template <int TT>
-static void gemm_dec_prep(const uint16_t* xa, int M, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
-                          int y_bf16, hipStream_t st) {
-  const DecSplit sp = dec_split(K / 128, 16);
-  const size_t lds = (size_t)(sp.waves - 1) * TT * 64 * 16;
-  const dim3 grid((N + 15) / 16), block(64 * sp.waves);
-  BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec<TT, CPW>), grid, block, lds, st, xa, M, N, K, s4, scales,
-                                            y, y_bf16));
-}
-
 // The fp8 x fp4 path takes M = 1 when the scale groups come in whole chunks
 // of four (K % 512 == 0); it splits K like the one-launch fp16 path. Two
 // column tiles per workgroup when that still leaves well over one workgroup
@@ -447,16 +396,7 @@ hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_
     else gemm_dec_lds<8>(x, M, N, K, s4, scales, y, y_bf16, st);
     return hipGetLastError();
   }
-  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-  hipError_t e = launch_prep_bf16(x, M, K, xp, st);
-  if (e != hipSuccess) return e;
-  switch ((M + 15) / 16) {
-    case 1: gemm_dec_prep<1>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-    case 2: gemm_dec_prep<2>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-    case 3: gemm_dec_prep<3>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-    default: gemm_dec_prep<4>(xp, M, N, K, s4, scales, y, y_bf16, st); break;
-  }
-  return hipGetLastError();
+  return launch_gemm_mid(x, M, N, K, signs, scales, y, y_bf16, ws, st);
 }
 
 }  // namespace brq

@@ -103,7 +103,8 @@ def _gemm_case(M, N, K, key, out=torch.float32):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (1, 40, 640), (3, 48, 1024), (16, 33, 256), (17, 64, 512),
-                                   (64, 32, 2048), (5, 16, 14336), (1, 1024, 1024)])
+                                   (64, 32, 2048), (5, 16, 14336), (1, 1024, 1024), (9, 16, 128),
+                                   (33, 130, 4480), (40, 2000, 3200), (20, 32768, 512), (64, 4100, 1280)])
 def test_gemm_decode_f32(M, N, K):
     say("gemm decode f32", M, N, K)
     y, o = _gemm_case(M, N, K, M * 1000 + N)
