@@ -27,9 +27,9 @@ constexpr int64_t kDecLdsBytes = 64 * 1024;
 bool gemm_dec_in_lds(int64_t M, int64_t K);
 hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
-// Rows not taken by the one-launch path (M <= 64): staging launch + split-K
-// matrix-core product over 128-column tiles (+ a slice-sum launch when K is
-// split); `ws` holds mid_ws_bytes(M, N, K).
+// Rows not taken by the one-launch path (M <= 64): split-K matrix-core product
+// over 128-column tiles (+ a slice-sum launch when K is split); `ws` holds
+// mid_ws_bytes(M, N, K) bytes (0: no workspace).
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);

@@ -2,18 +2,18 @@
 // vector and the prefill tiles, "LLM binarization, Episode 01: DBF", section 4:
 // each matrix is now applied to a handful of vectors).
 //
-// A staging launch writes x as fp16 in the permuted operand order. The product splits the work into
-// 128-column tiles x K-slices: a workgroup (4 waves, 32 columns each) streams
-// its slice in k-steps of 128 (one scale group) through a ring of LDS stages
-// filled by direct loads -- all M rows of x (16*TT rows), the 16-byte sign
-// records and the scales of its 128 columns -- so the loads of a k-step are in
-// flight STAGES-1 k-steps ahead. Every wave multiplies all rows (TT tiles of
-// 16) by its two 16-column groups with v_mfma_f32_16x16x32_f16 on +-scale
-// fp16 weight operands: one activation operand serves two MFMAs and one weight
-// operand serves TT.
+// The work is split into 128-column tiles x K-slices of at most 8 k-steps
+// (one 128-byte line of every sign row). A workgroup (4 waves, 32 columns
+// each) first issues direct loads of all sign records of its slice into LDS
+// and reads its scales; the activations stream through registers: each wave
+// loads its share of the bf16 rows PREF k-steps ahead, converts them to fp16
+// in the permuted operand order and writes them to one of two LDS stages. Every
+// wave multiplies all rows (TT tiles of 16) by its two 16-column groups with
+// v_mfma_f32_16x16x32_f16 on +-scale fp16 weight operands: one activation
+// operand serves two MFMAs and one weight operand serves TT.
 //
 // With several K-slices each workgroup writes its fp32 partial tile to the
-// workspace and a third launch adds the slices in slice order (deterministic).
+// workspace and a second launch adds the slices in slice order (deterministic).
 // (Meeting inside the product launch instead -- last-arriving workgroup adds
 // the tile -- needs a device-scope release per workgroup, which writes back
 // the whole L2 of its chiplet and cost far more than the extra launch.)
@@ -24,93 +24,141 @@ namespace brq {
 
 namespace {
 
-constexpr int MID_NB = 2;              // 16-column groups per wave
-constexpr int MID_BN = 64 * MID_NB;    // columns per workgroup
-constexpr int MID_SIG = MID_BN * 16;   // sign bytes per stage
-constexpr int MID_SC = 4 * 256;        // scale dwords per stage: 64 lanes x 4 B per wave
+constexpr int MID_NB = 2;            // 16-column groups per wave
+constexpr int MID_BN = 64 * MID_NB;  // columns per workgroup
+constexpr int MID_KPS = 8;           // most k-steps per slice: 8 x 16 B = one 128-byte line of a sign row
 
-// ring depth: more stages in flight where a stage is small
-__host__ __device__ constexpr int mid_stages(int tt) { return tt == 1 ? 8 : tt == 2 ? 6 : 4; }
-__host__ __device__ constexpr int mid_stage_bytes(int tt) { return 16 * tt * 256 + MID_SIG + MID_SC; }
+// k-steps of activations in flight in registers
+__host__ __device__ constexpr int mid_pref(int tt) { return tt <= 2 ? 4 : 2; }
+// dynamic LDS: the slice's sign records, its scale pairs, two activation stages
+__host__ __device__ constexpr int mid_lds_bytes(int tt) {
+  return MID_BN * MID_KPS * 16 + MID_BN * MID_KPS * 4 + 2 * 16 * tt * 256;
+}
 
 struct MidPlan {
   int tiles, slices, kps;  // column tiles, K-slices, k-steps per slice
 };
 
-// About two workgroups per compute unit for the rows that stream weights
-// (TT <= 2), one for the rows that are matrix-core bound (fewer partial tiles).
-MidPlan mid_plan(int64_t M, int64_t N, int64_t K) {
+// Slices of 8 k-steps (each column's sign records of a slice are one 128-byte
+// line), halved while the grid has fewer than 256 workgroups.
+MidPlan mid_plan(int64_t N, int64_t K) {
   MidPlan p;
   const int nk = (int)(K / 128);
-  const int target = M <= 32 ? 512 : 256;
   p.tiles = (int)((N + MID_BN - 1) / MID_BN);
-  int s = (target + p.tiles - 1) / p.tiles;
-  if (s > nk) s = nk;
-  if (s < 1) s = 1;
-  p.kps = (nk + s - 1) / s;
-  p.slices = (nk + p.kps - 1) / p.kps;  // no empty slice
+  int kps = MID_KPS;
+  while (kps > 1 && (int64_t)p.tiles * ((nk + kps - 1) / kps) < 256) kps /= 2;
+  p.kps = kps;
+  p.slices = (nk + kps - 1) / kps;
   return p;
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// fp16 pair (lo, hi) from two bf16 values, round to nearest even
+__device__ __forceinline__ uint32_t bf16x2_to_f16_pair(uint32_t lo_bits, uint32_t hi_bits) {
+  const h2 v = {(_Float16)__uint_as_float(lo_bits), (_Float16)__uint_as_float(hi_bits)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 }  // namespace
 
 template <int TT>
-__global__ __launch_bounds__(256) void k_mid(const uint16_t* __restrict__ xp, int M, int N, int K,
+__global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, int K,
                                              const uint32_t* __restrict__ signs, const uint16_t* __restrict__ scales,
                                              void* __restrict__ y, int y_bf16, float* __restrict__ part, int kps,
                                              int S) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int ROWS = 16 * TT, SB = mid_stage_bytes(TT), STAGES = mid_stages(TT);
+  constexpr int PREF = mid_pref(TT), SB = 16 * TT * 256;
   constexpr int NB = MID_NB, BN = MID_BN;
-  constexpr int OPS = TT + NB + 1;  // direct loads per wave per k-step
+  uint8_t* const l_sig = lds;                                                 // [2*kps blocks][1 KiB]
+  uint32_t* const l_sc = reinterpret_cast<uint32_t*>(lds + BN * MID_KPS * 16);  // [kps][BN] scale pairs
+  uint8_t* const l_a = lds + BN * MID_KPS * 20;                               // [2][16*TT rows][256 B]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, kb = lane >> 4;
   const int tile = blockIdx.x, sl = blockIdx.y;
   const int nk = K >> 7;
   const int kt0 = sl * kps, kt1 = kt0 + kps < nk ? kt0 + kps : nk, nks = kt1 - kt0;
   const int n0 = tile * BN;
-  const int cw = n0 + 16 * NB * wave;  // first column of this wave
-  const int KW = K >> 5;               // 32-bit sign words per weight row
+  const int KW = K >> 5;  // 32-bit sign words per weight row
 
-  // ---- direct loads of one k-step into a stage
-  // activations: wave w loads rows 4*TT*w + 4i + L/16 (i < TT), 16-byte chunk
-  // L%16 of the k-step to LDS slot (L%16) ^ (row%16); rows past M repeat M-1
-  // (their products are never stored).
-  const uint8_t* xb = reinterpret_cast<const uint8_t*>(xp);
-  const uint8_t* ap[TT];
+  // ---- the slice's sign records, one direct load per 64 x 16 B: block i
+  // holds columns C*i .. C*i+C-1 (C = 64/kps) for all kps steps, lane L ->
+  // column C*i + L % C, step L / C, at byte 16*L of the block. A column's
+  // records of the slice are contiguous in memory (one line when kps = 8).
+  // Columns past N repeat N-1 and steps past K repeat the last (never used).
+  {
+    const int C = 64 / kps;
+    const int c = lane % C, q = lane / C;
+    const int kt = kt0 + q < nk ? kt0 + q : nk - 1;
+    for (int i = wave; i < 2 * kps; i += 4) {
+      const int n = n0 + C * i + c < N ? n0 + C * i + c : N - 1;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(signs + (size_t)n * KW + 4 * kt), l_sig + i * 1024,
+                                       16, 0, 0);
+    }
+  }
+
+  // ---- the slice's scales: thread e -> (column e % BN, step e / BN)
+  uint32_t scv[MID_KPS * BN / 256];
+#pragma unroll
+  for (int i = 0; i < MID_KPS * BN / 256; ++i) {
+    const int e = tid + 256 * i, c = e % BN, q = e / BN;
+    const int n = n0 + c < N ? n0 + c : N - 1;
+    const int kt = kt0 + q < nk ? kt0 + q : nk - 1;
+    scv[i] = q < kps ? scales[(size_t)n * nk + kt] : 0u;
+  }
+
+  // ---- activations: lane (rr = L/16, c = L%16) of wave w stages rows
+  // r = 4*TT*w + 4i + rr (i < TT; rows past M repeat M-1, never stored),
+  // permuted 16-byte chunk c of each k-step: run c/4, pairs b = 4(c%4) + u,
+  // i.e. bf16 elements 4(c%4)+u (low halves) and 16+4(c%4)+u (high halves)
+  // of the run -- two 8-byte loads. The chunk goes to LDS slot c ^ (r%16).
+  const int rr = lane >> 4, cc = lane & 15;
+  const uint8_t* xr[TT];
+  uint32_t a_dst[TT];
 #pragma unroll
   for (int i = 0; i < TT; ++i) {
-    const int r = 4 * TT * wave + 4 * i + (lane >> 4);
+    const int r = 4 * TT * wave + 4 * i + rr;
     const int rg = r < M ? r : M - 1;
-    const int chunk = (lane & 15) ^ (r & 15);
-    ap[i] = xb + (size_t)rg * K * 2 + chunk * 16;
+    xr[i] = reinterpret_cast<const uint8_t*>(x) + (size_t)rg * K * 2 + (cc >> 2) * 64 + (cc & 3) * 8;
+    a_dst[i] = (uint32_t)(r * 256 + ((cc ^ (r & 15)) * 16));
   }
-  // signs of group g: lane L loads word L%4 of column cw + 16g + L/4; columns
-  // past N repeat N-1 (never stored)
-  const uint32_t* sig[NB];
+  uint2 ra[PREF][TT][2];
+  // (x is not __restrict__: the prefetch loads must stay ahead of the
+  // barriers, which are memory clobbers)
+  auto load_step = [&](uint2 (&dst)[TT][2], int q) {
+    const size_t off = (size_t)(kt0 + (q < nks ? q : nks - 1)) * 256;
 #pragma unroll
-  for (int g = 0; g < NB; ++g) {
-    const int c = cw + 16 * g + (lane >> 2);
-    sig[g] = signs + (size_t)(c < N ? c : N - 1) * KW + (lane & 3);
-  }
-  // scales: lane L loads the aligned dword holding the scale of column
-  // cw + L % (16*NB) (lanes past 16*NB repeat); the reader picks the half
-  const int scc = cw + (lane & (16 * NB - 1));
-  const size_t sc_idx = (size_t)(scc < N ? scc : N - 1) * nk;
-  const uint32_t* scw = reinterpret_cast<const uint32_t*>(scales);
-  auto issue = [&](int kt, int st) {
-    uint8_t* base = lds + st * SB;
-#pragma unroll
-    for (int i = 0; i < TT; ++i)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ap[i] + (size_t)kt * 256),
-                                       base + (4 * TT * wave + 4 * i) * 256, 16, 0, 0);
-#pragma unroll
-    for (int g = 0; g < NB; ++g)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(sig[g] + 4 * kt),
-                                       base + ROWS * 256 + (NB * wave + g) * 256, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(scw + ((sc_idx + kt) >> 1)),
-                                     base + ROWS * 256 + MID_SIG + wave * 256, 4, 0, 0);
+    for (int i = 0; i < TT; ++i) {
+      dst[i][0] = *reinterpret_cast<const uint2*>(xr[i] + off);
+      dst[i][1] = *reinterpret_cast<const uint2*>(xr[i] + off + 32);
+    }
   };
+  auto stage_step = [&](const uint2 (&src)[TT][2], int st) {
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      const uint2 lo = src[i][0], hi = src[i][1];
+      u32x4 o;
+      o[0] = bf16x2_to_f16_pair(lo.x << 16, hi.x << 16);
+      o[1] = bf16x2_to_f16_pair(lo.x & 0xffff0000u, hi.x & 0xffff0000u);
+      o[2] = bf16x2_to_f16_pair(lo.y << 16, hi.y << 16);
+      o[3] = bf16x2_to_f16_pair(lo.y & 0xffff0000u, hi.y & 0xffff0000u);
+      *reinterpret_cast<u32x4*>(l_a + st * SB + a_dst[i]) = o;
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < PREF; ++d) load_step(ra[d], d);
+
+#pragma unroll
+  for (int i = 0; i < MID_KPS * BN / 256; ++i) {
+    const int e = tid + 256 * i;
+    l_sc[e] = scv[i] | (scv[i] << 16);
+  }
+  stage_step(ra[0], 0);
+  load_step(ra[0], PREF);
+  // every older load of this wave -- its sign records included -- landed
+  // (only the activation loads of steps 1 .. PREF may be in flight), then
+  // every wave's stage-0 writes and sign records are in
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * TT * PREF) : "memory");
 
   f32x4 acc[TT][NB];
 #pragma unroll
@@ -118,64 +166,68 @@ __global__ __launch_bounds__(256) void k_mid(const uint16_t* __restrict__ xp, in
 #pragma unroll
     for (int g = 0; g < NB; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int bsh = 4 * kb;  // the lane's k block takes pairs 4*kb .. 4*kb+3 of each half-run
-  // the reader's scale halves: column cw + 16g + j at step kt sits in the high
-  // half when its element index is odd
-  int sc_odd[NB];
-#pragma unroll
-  for (int g = 0; g < NB; ++g) {
-    const int c = cw + 16 * g + j;
-    sc_odd[g] = (int)(((size_t)(c < N ? c : N - 1) * nk) & 1);
-  }
-
-  // prologue: the first STAGES-1 k-steps in flight (steps past the slice
-  // repeat its last step and are never used)
-#pragma unroll
-  for (int q = 0; q < STAGES - 1; ++q) issue(kt0 + (q < nks ? q : nks - 1), q);
-
-  for (int q = 0; q < nks; ++q) {
-    const int st = q % STAGES;
-    // this wave's loads of step q landed (the STAGES-2 younger steps may still
-    // be in flight), then every wave's loads landed and every wave is done
-    // with the stage the next issue overwrites. A plain s_barrier: the
-    // workgroup fence of __syncthreads would make the compiler drain every
-    // direct load in flight, the prefetches included.
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((STAGES - 2) * OPS) : "memory");
-    {
-      const int qn = q + STAGES - 1;
-      issue(kt0 + (qn < nks ? qn : nks - 1), qn % STAGES);
-    }
-    const uint8_t* base = lds + st * SB;
-    u32x4 w4[NB];
-    uint32_t S[NB];
-    const int kodd = (kt0 + q) & 1;
+  // where this lane's columns sit in the sign blocks
+  int sg_off[NB];
+  {
+    const int C = 64 / kps;
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
-      w4[g] = *reinterpret_cast<const u32x4*>(base + ROWS * 256 + (NB * wave + g) * 256 + j * 16);
-      const uint32_t d = *reinterpret_cast<const uint32_t*>(base + ROWS * 256 + MID_SIG + wave * 256 + (16 * g + j) * 4);
-      // element sc_idx + kt sits in the high half iff its index is odd
-      const uint32_t h = (sc_odd[g] ^ kodd) ? (d >> 16) : (d & 0xffffu);
-      S[g] = h | (h << 16);
+      const int cl = 16 * (NB * wave + g) + j;
+      sg_off[g] = (cl / C) * 1024 + (cl % C) * 16;
+    }
+  }
+  const int sg_step = (64 / kps) * 16;
+
+  // one k-step: stage step q+1 into the other LDS stage (every wave finished
+  // reading it before the last barrier) and refill its registers with step
+  // q+1+PREF (both unconditional: past the slice they repeat its last step,
+  // unused), then multiply step q. d = q % PREF picks the registers.
+  auto step = [&](const int q, const int d) {
+    stage_step(ra[(d + 1) % PREF], (q + 1) & 1);
+    load_step(ra[(d + 1) % PREF], q + 1 + PREF);
+    const uint8_t* base = l_a + (q & 1) * SB;
+    u32x4 a[4][TT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < TT; ++t)  // chunk 4s+kb of row 16t+j
+        a[s][t] = *reinterpret_cast<const u32x4*>(base + (16 * t + j) * 256 + (((4 * s + kb) ^ j) * 16));
+    u32x4 w4[NB];
+    uint32_t Sc[NB];
+#pragma unroll
+    for (int g = 0; g < NB; ++g) {
+      w4[g] = *reinterpret_cast<const u32x4*>(l_sig + sg_off[g] + q * sg_step);
+      Sc[g] = l_sc[q * BN + 16 * (NB * wave + g) + j];
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int slot = ((4 * s + kb) ^ j) * 16;  // chunk 4s+kb of row 16t+j
-      u32x4 a[TT];
-#pragma unroll
-      for (int t = 0; t < TT; ++t) a[t] = *reinterpret_cast<const u32x4*>(base + (16 * t + j) * 256 + slot);
 #pragma unroll
       for (int g = 0; g < NB; ++g) {
         const uint32_t w = w4[g][s] >> bsh;
         u32x4 b;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) b[u] = ((w << (15 - u)) & 0x80008000u) | S[g];
+        for (int u = 0; u < 4; ++u) b[u] = ((w << (15 - u)) & 0x80008000u) | Sc[g];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) acc[t][g] = mfma16(a[t], b, acc[t][g]);
+        for (int t = 0; t < TT; ++t) acc[t][g] = mfma16(a[s][t], b, acc[t][g]);
       }
     }
+    // the next stage's writes are in and every wave is done with this one
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // whole rounds of PREF steps with no branch inside, so that the compiler's
+  // wait before each staging counts the PREF-1 younger steps in flight
+  int q = 0;
+  for (; q + PREF <= nks; q += PREF) {
+#pragma unroll
+    for (int d = 0; d < PREF; ++d) step(q + d, d);
   }
+#pragma unroll
+  for (int d = 0; d < PREF - 1; ++d)
+    if (q + d < nks) step(q + d, d);
   __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
 
   // lane (kb, j) holds rows 16t + 4kb + i of column cw + 16g + j
+  const int cw = n0 + 16 * NB * wave;
   if (S == 1) {
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
@@ -233,22 +285,20 @@ __global__ __launch_bounds__(256) void k_mid_sum(const float* __restrict__ part,
 }
 
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const MidPlan p = mid_plan(M, N, K);
-  size_t b = align256((size_t)M * K * 2);
-  if (p.slices > 1) b += align256((size_t)p.tiles * p.slices * M * MID_BN * 4);
-  return b;
+  const MidPlan p = mid_plan(N, K);
+  return p.slices > 1 ? align256((size_t)p.tiles * p.slices * M * MID_BN * 4) : 0;
 }
 
 template <int TT>
-static hipError_t mid_launch(const uint16_t* xp, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+static hipError_t mid_launch(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                              void* y, int y_bf16, float* part, const MidPlan& p, hipStream_t st) {
-  const int lds = mid_stages(TT) * mid_stage_bytes(TT);
+  const int lds = mid_lds_bytes(TT);
   if (lds > 64 * 1024) {  // per-function opt-in beyond 64 KiB of dynamic LDS
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid<TT>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_mid<TT>, dim3(p.tiles, p.slices), dim3(256), lds, st, xp, M, N, K,
+  hipLaunchKernelGGL(k_mid<TT>, dim3(p.tiles, p.slices), dim3(256), lds, st, x, M, N, K,
                      reinterpret_cast<const uint32_t*>(signs), scales, y, y_bf16, part, p.kps, p.slices);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.slices == 1) return e;
@@ -260,17 +310,13 @@ static hipError_t mid_launch(const uint16_t* xp, int M, int N, int K, const uint
 
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                            void* y, int y_bf16, void* ws, hipStream_t st) {
-  const MidPlan p = mid_plan(M, N, K);
-  char* base = reinterpret_cast<char*>(ws);
-  uint16_t* xp = reinterpret_cast<uint16_t*>(base);
-  float* part = reinterpret_cast<float*>(base + align256((size_t)M * K * 2));
-  const hipError_t e = launch_prep_bf16(x, M, K, xp, st);
-  if (e != hipSuccess) return e;
+  const MidPlan p = mid_plan(N, K);
+  float* part = reinterpret_cast<float*>(ws);
   switch ((M + 15) / 16) {
-    case 1: return mid_launch<1>(xp, M, N, K, signs, scales, y, y_bf16, part, p, st);
-    case 2: return mid_launch<2>(xp, M, N, K, signs, scales, y, y_bf16, part, p, st);
-    case 3: return mid_launch<3>(xp, M, N, K, signs, scales, y, y_bf16, part, p, st);
-    default: return mid_launch<4>(xp, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 1: return mid_launch<1>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 2: return mid_launch<2>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 3: return mid_launch<3>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    default: return mid_launch<4>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
   }
 }
 

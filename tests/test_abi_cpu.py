@@ -48,10 +48,10 @@ def test_size_queries(L):
     assert L.brq_sign_words(3, 65) == 0
     assert L.brq_scale_count(3, 64) == 0
     assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 0          # staged in LDS
-    # staged fp16 activations + fp32 partial tiles: 8 K-slices x 32 tiles of 128 columns
-    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 64 * 14336 * 2 + 8 * 32 * 64 * 128 * 4
-    # one K-slice (K = 512 over 256 tiles): no partials
-    assert L.brq_gemm_workspace_bytes(64, 32768, 512) == 64 * 512 * 2
+    # fp32 partial tiles: 14 K-slices of 8 k-steps x 32 tiles of 128 columns
+    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 14 * 32 * 64 * 128 * 4
+    # one K-slice (K = 512 over 256 tiles of 128 columns): no workspace
+    assert L.brq_gemm_workspace_bytes(64, 32768, 512) == 0
     assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 4096 * 4096 * 2   # staged activations
     assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0
     assert L.brq_dbf_workspace_bytes(1, 4096, 4096, 2048) > 0
