@@ -13,10 +13,10 @@
 //     index), softmax over the k selected logits, per-expert counts and
 //     offsets, the list of active experts and the expert-major route list;
 //     the other workgroups stage x in the permuted fp16 operand order.
-//  2. gate/up: one workgroup per (16 intermediate columns, active expert);
+//  2. gate/up: one workgroup per (64 intermediate columns, active expert);
 //     both products share every activation operand; SwiGLU in fp32; the
 //     result is stored as an fp16 hi/lo pair per route, permuted.
-//  3. down: one workgroup per (16 hidden columns, active expert); writes the
+//  3. down: one workgroup per (128 hidden columns, active expert); writes the
 //     route's fp32 output.
 //  4. combine: y_t = sum over slots j, in slot order, of w_tj * out(t, j).
 #include <type_traits>
@@ -34,8 +34,7 @@ struct MoeWs {
   int* ids;          // [T][k]
   float* wts;        // [T][k]
   int* off;          // [E+1]
-  int* act;          // [E]
-  int* nact;         // [1]
+  int4* blk;         // [E] (expert, first route, routes, 0) of the a-th active expert; zeros after the last
   int* route_tok;    // [R] token of each expert-major route position
   int* route_pos;    // [T][k] expert-major position of route (t, j)
   uint16_t* ap;      // [2R][I] permuted fp16 hi/lo of the SwiGLU output
@@ -50,8 +49,7 @@ static MoeWs moe_carve(void* ws, int64_t T, int64_t H, int64_t I, int64_t E, int
   w.ids = reinterpret_cast<int*>(take((size_t)R * 4));
   w.wts = reinterpret_cast<float*>(take((size_t)R * 4));
   w.off = reinterpret_cast<int*>(take((size_t)(E + 1) * 4));
-  w.act = reinterpret_cast<int*>(take((size_t)E * 4));
-  w.nact = reinterpret_cast<int*>(take(4));
+  w.blk = reinterpret_cast<int4*>(take((size_t)E * 16));
   w.route_tok = reinterpret_cast<int*>(take((size_t)R * 4));
   w.route_pos = reinterpret_cast<int*>(take((size_t)R * 4));
   w.ap = reinterpret_cast<uint16_t*>(take((size_t)2 * R * I * 2));
@@ -61,7 +59,7 @@ static MoeWs moe_carve(void* ws, int64_t T, int64_t H, int64_t I, int64_t E, int
 
 size_t moe_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t R = T * k;
-  return 2 * align256((size_t)R * 4) + align256((size_t)(E + 1) * 4) + align256((size_t)E * 4) + align256(4) +
+  return 2 * align256((size_t)R * 4) + align256((size_t)(E + 1) * 4) + align256((size_t)E * 16) +
          2 * align256((size_t)R * 4) + align256((size_t)2 * R * I * 2) + align256((size_t)R * H * 4);
 }
 
@@ -215,12 +213,12 @@ __global__ __launch_bounds__(1024) void k_moe_route(int T, int E, int k, MoeWs w
   if (tid < E) {
     s_off[tid] = off;
     ws.off[tid] = off;
-    if (cnt > 0) ws.act[aidx] = tid;
+    // one 16-byte record per active expert, so that a gate/up or down
+    // workgroup learns its expert, routes and count in one load
+    if (cnt > 0) ws.blk[aidx] = make_int4(tid, off, cnt, 0);
+    if (tid >= na) ws.blk[tid] = make_int4(0, 0, 0, 0);
   }
-  if (tid == 0) {
-    ws.off[E] = R;
-    *ws.nact = na;
-  }
+  if (tid == 0) ws.off[E] = R;
   __syncthreads();
   for (int r = tid; r < T * k; r += blockDim.x) {
     const int e = s_ids[r], t = r / k;
@@ -233,34 +231,79 @@ __global__ __launch_bounds__(1024) void k_moe_route(int T, int E, int k, MoeWs w
   }
 }
 
-// gate/up: one workgroup per (16 intermediate columns, active expert). The
-// expert's sign words are loaded once; its tokens are staged, a tile of up to
-// tile_rows at a time, each wave staging its own K-slice (bf16 -> permuted
-// fp16).
-template <int CPW, int MAXR>
+// The sign and scale words look invariant across the token tiles of a
+// workgroup; an empty asm that "rewrites" them per tile keeps the compiler
+// from hoisting every block's weight operands out of the tile loop (CB x 16 x
+// 4 registers) and from waiting for the words before the first tile's
+// activation loads are issued.
+template <int NB, int CPW>
+__device__ __forceinline__ void pin_signs(BPre<NB, CPW>& bp) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      asm volatile("" : "+v"(bp.d[nb][c].x), "+v"(bp.d[nb][c].y), "+v"(bp.d[nb][c].z), "+v"(bp.d[nb][c].w),
+                   "+v"(bp.s[nb][c]));
+}
+
+// reduce_waves over CB column blocks of NB accumulators each (wave order)
+template <int CB, int NB>
+__device__ __forceinline__ void reduce_waves_cb(f32x4 (&acc)[CB][NB][1], f32x4* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (nw == 1) return;
+  if (wave > 0) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[(((wave - 1) * CB + cb) * NB + nb) * 64 + lane] = acc[cb][nb][0];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < nw; ++w)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[cb][nb][0] += red[(((w - 1) * CB + cb) * NB + nb) * 64 + lane];
+  }
+}
+
+// gate/up: one workgroup per (CB blocks of 16 intermediate columns, active
+// expert). The sign words of all CB blocks are loaded first; the expert's
+// tokens are staged once per tile of up to tile_rows tokens (each wave its own
+// K-slice, bf16 -> permuted fp16) and multiplied by every block, so a
+// workgroup keeps CB blocks' loads in flight and pays one staging per tile.
+template <int CPW, int MAXR, int CB>
 __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__ x, int H, int I,
                                                     const uint4* __restrict__ gs, const uint16_t* __restrict__ gsc,
                                                     const uint4* __restrict__ us, const uint16_t* __restrict__ usc,
                                                     MoeWs ws) {
   extern __shared__ uint4 smem[];
-  if ((int)blockIdx.y >= *ws.nact) return;
-  const int e = ws.act[blockIdx.y];
-  const int r0 = ws.off[e], cnt = ws.off[e + 1] - r0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int4 bk = ws.blk[blockIdx.y];
+  const int e = bk.x, r0 = bk.y, cnt = bk.z;
+  if (cnt == 0) return;  // past the last active expert
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int j = lane & 15;
-  const int n = blockIdx.x * 16 + j;
   const int G = H >> 7, nchunks = (G + 3) >> 2;
   const int c0 = wave * CPW;
-  const size_t row = (size_t)e * I + (n < I ? n : 0);
-  const uint4* wsig[2] = {gs + row * G, us + row * G};
-  const uint16_t* wsc[2] = {gsc + row * G, usc + row * G};
-  const bool rok[2] = {n < I, n < I};
-  BPre<2, CPW> bp;
-  if (c0 < nchunks) b_prefetch<BM_GROUP, 2, CPW>(wsig, wsc, rok, G, c0, 1, bp);
-  const int pc = perm_pos(n);
-  for (int tb = 0; tb < cnt; tb += MAXR) {
+  BPre<2, CPW> bp[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int n = (blockIdx.x * CB + cb) * 16 + j;
+    const size_t row = (size_t)e * I + (n < I ? n : 0);
+    const uint4* wsig[2] = {gs + row * G, us + row * G};
+    const uint16_t* wsc[2] = {gsc + row * G, usc + row * G};
+    const bool rok[2] = {n < I, n < I};
+    // unconditional (indices clamped): a conditional prefetch makes the
+    // compiler wait for each block's words before issuing the next block's
+    b_prefetch<BM_GROUP, 2, CPW>(wsig, wsc, rok, G, c0, 1, bp[cb]);
+  }
+  // one tile of up to MAXR tokens; the first is peeled off the loop so that
+  // its activation loads issue while the sign words are still in flight
+  auto run_tile = [&](const int tb) {
     const int rows = (cnt - tb) < MAXR ? (cnt - tb) : MAXR;
-    f32x4 acc[2][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}, {f32x4{0.f, 0.f, 0.f, 0.f}}};
+    f32x4 acc[CB][2][1];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb][0][0] = acc[cb][1][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     // stage and multiply `rows` tokens with SR staged row slots (SR >= rows)
     auto tile = [&](auto sr) {
       constexpr int SR = decltype(sr)::value;
@@ -277,56 +320,75 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
           const int m = min(j, rows - 1);
           return xs[(((g >> 2) - c0) * SR + m) * 64 + (g & 3) * 16 + i];
         };
-        b_compute<BM_GROUP, 2, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          pin_signs(bp[cb]);
+          b_compute<BM_GROUP, 2, 1, CPW>(bp[cb], nullptr, G, c0, 1, aop, acc[cb]);
+        }
       }
     };
     if (MAXR > 4 && rows <= 4) tile(std::integral_constant<int, 4>{});
     else tile(std::integral_constant<int, MAXR>{});
     __syncthreads();
-    reduce_waves<2, 1>(acc, reinterpret_cast<f32x4*>(smem));
-    if (wave == 0 && n < I) {
+    reduce_waves_cb<CB, 2>(acc, reinterpret_cast<f32x4*>(smem));
+    if (wave == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = 4 * (lane >> 4) + i;
-        if (p < rows) {
-          const float g = acc[0][0][i], u = acc[1][0][i];
-          const float a = g / (1.0f + expf(-g)) * u;
-          uint16_t hi, lo;
-          split_f16(a, hi, lo);
-          ws.ap[(size_t)(2 * (r0 + tb + p)) * I + pc] = hi;
-          ws.ap[(size_t)(2 * (r0 + tb + p) + 1) * I + pc] = lo;
+      for (int cb = 0; cb < CB; ++cb) {
+        const int n = (blockIdx.x * CB + cb) * 16 + j;
+        if (n >= I) continue;
+        const int pc = perm_pos(n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = 4 * (lane >> 4) + i;
+          if (p < rows) {
+            const float g = acc[cb][0][0][i], u = acc[cb][1][0][i];
+            const float a = g / (1.0f + expf(-g)) * u;
+            uint16_t hi, lo;
+            split_f16(a, hi, lo);
+            ws.ap[(size_t)(2 * (r0 + tb + p)) * I + pc] = hi;
+            ws.ap[(size_t)(2 * (r0 + tb + p) + 1) * I + pc] = lo;
+          }
         }
       }
     }
     __syncthreads();
-  }
+  };
+  run_tile(0);  // an active expert has at least one route
+  for (int tb = MAXR; tb < cnt; tb += MAXR) run_tile(tb);
+  (void)nw;
 }
 
-// down: one workgroup per (16 hidden columns, active expert); the routes'
-// fp16 hi/lo intermediates are staged per wave, 8 routes (16 piece rows) a
-// tile.
-template <int CPW>
+// down: one workgroup per (CB blocks of 16 hidden columns, active expert); the
+// routes' fp16 hi/lo intermediates are staged per wave, 8 routes (16 piece
+// rows) a tile, and multiplied by every block.
+template <int CPW, int CB, int RT>
 __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __restrict__ ds,
                                                   const uint16_t* __restrict__ dsc, MoeWs ws) {
   extern __shared__ uint4 smem[];
-  if ((int)blockIdx.y >= *ws.nact) return;
-  const int e = ws.act[blockIdx.y];
-  const int r0 = ws.off[e], cnt = ws.off[e + 1] - r0;
+  const int4 bk = ws.blk[blockIdx.y];
+  const int e = bk.x, r0 = bk.y, cnt = bk.z;
+  if (cnt == 0) return;  // past the last active expert
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
-  const int n = blockIdx.x * 16 + j;
   const int G = I >> 7, nchunks = (G + 3) >> 2;
   const int c0 = wave * CPW;
-  const size_t row = (size_t)e * H + (n < H ? n : 0);
-  const uint4* wsig[1] = {ds + row * G};
-  const uint16_t* wsc[1] = {dsc + row * G};
-  const bool rok[1] = {n < H};
-  BPre<1, CPW> bp;
-  if (c0 < nchunks) b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
-  for (int tb = 0; tb < cnt; tb += 8) {
-    const int routes = (cnt - tb) < 8 ? (cnt - tb) : 8;
+  BPre<1, CPW> bp[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int n = (blockIdx.x * CB + cb) * 16 + j;
+    const size_t row = (size_t)e * H + (n < H ? n : 0);
+    const uint4* wsig[1] = {ds + row * G};
+    const uint16_t* wsc[1] = {dsc + row * G};
+    const bool rok[1] = {n < H};
+    b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp[cb]);  // unconditional, as in gate/up
+  }
+  // one tile of up to RT routes; the first is peeled off the loop (as in gate/up)
+  auto run_tile = [&](const int tb) {
+    const int routes = (cnt - tb) < RT ? (cnt - tb) : RT;
     const int rows = 2 * routes;
-    f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+    f32x4 acc[CB][1][1];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb][0][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     // stage and multiply the `rows` piece rows with SR staged slots (SR >= rows)
     auto tile = [&](auto sr) {
       constexpr int SR = decltype(sr)::value;
@@ -343,23 +405,34 @@ __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __r
           const int pr = min(j, rows - 1);
           return xs[(((g >> 2) - c0) * SR + pr) * 64 + (g & 3) * 16 + i];
         };
-        b_compute<BM_GROUP, 1, 1, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          pin_signs(bp[cb]);
+          b_compute<BM_GROUP, 1, 1, CPW>(bp[cb], nullptr, G, c0, 1, aop, acc[cb]);
+        }
       }
     };
     if (rows <= 4) tile(std::integral_constant<int, 4>{});
-    else if (rows <= 8) tile(std::integral_constant<int, 8>{});
+    else if (RT <= 4 || rows <= 8) tile(std::integral_constant<int, 8>{});
     else tile(std::integral_constant<int, 16>{});
     __syncthreads();
-    reduce_waves<1, 1>(acc, reinterpret_cast<f32x4*>(smem));
-    if (wave == 0 && n < H) {
+    reduce_waves_cb<CB, 1>(acc, reinterpret_cast<f32x4*>(smem));
+    if (wave == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = 2 * (lane >> 4) + h;
-        if (q < routes) ws.o[(size_t)(r0 + tb + q) * H + n] = acc[0][0][2 * h] + acc[0][0][2 * h + 1];
+      for (int cb = 0; cb < CB; ++cb) {
+        const int n = (blockIdx.x * CB + cb) * 16 + j;
+        if (n >= H) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int q = 2 * (lane >> 4) + h;
+          if (q < routes) ws.o[(size_t)(r0 + tb + q) * H + n] = acc[cb][0][0][2 * h] + acc[cb][0][0][2 * h + 1];
+        }
       }
     }
     __syncthreads();
-  }
+  };
+  run_tile(0);
+  for (int tb = RT; tb < cnt; tb += RT) run_tile(tb);
 }
 
 __global__ __launch_bounds__(256) void k_moe_combine(int T, int H, int k, MoeWs ws, void* __restrict__ y,
@@ -381,6 +454,10 @@ __global__ __launch_bounds__(256) void k_moe_combine(int T, int H, int k, MoeWs 
 //     multiplies expert ids[t][j]'s down rows by route (t, j)'s intermediate;
 //     wave 0 adds w_tj * out_j over the slots in slot order.
 constexpr int MOE_SMALL_T = 4;
+// 16-column blocks per gate/up (down) workgroup: fewer where each wave holds
+// more chunks of sign words, so that the prefetched words stay in registers
+constexpr int moe_cb_gu(int cpw) { return cpw == 1 ? 4 : cpw == 2 ? 2 : 1; }
+constexpr int moe_cb_dn(int cpw) { return cpw == 1 ? 4 : cpw == 2 ? 2 : 1; }
 
 template <int CPW, int MAXR>
 __global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict__ x, const float* __restrict__ logits,
@@ -551,10 +628,13 @@ static bool moe_small_path(int T, int H, int I, int k, DecSplit& sa, int& maxr, 
 }
 
 // token rows per gate/up tile: staged row slots per chunk, so that
-// waves * cpw * slots KiB fit the staging budget
-static int moe_tile_rows(const DecSplit& sp) {
+// waves * cpw * slots KiB fit the staging budget; 4 when an expert expects at
+// most 3 routes (T*k/E), which quarters the staging LDS and lets more
+// workgroups share a compute unit
+static int moe_tile_rows(const DecSplit& sp, int T, int E, int k) {
   const int64_t chunks = (int64_t)sp.waves * sp.cpw;
-  return chunks <= 4 ? 16 : chunks <= 16 ? 4 : 1;
+  const int r = chunks <= 4 ? 16 : chunks <= 16 ? 4 : 1;
+  return (r > 4 && (int64_t)T * k <= 3 * (int64_t)E) ? 4 : r;
 }
 
 hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int I, int E, int top_k,
@@ -595,11 +675,15 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const DecSplit sg = dec_split(H / 128, 8), sd = dec_split(I / 128, 8);
-  const int tr = moe_tile_rows(sg);
-  size_t lg = (size_t)sg.waves * sg.cpw * tr * 1024, rg = (size_t)(sg.waves - 1) * 2 * 64 * 16;
-  size_t ld = (size_t)sd.waves * sd.cpw * 16 * 1024, rd = (size_t)(sd.waves - 1) * 64 * 16;
+  const int tr = moe_tile_rows(sg, T, E, top_k);
+  const int rt = 8;  // routes per down tile (4 is built too: more registers, less LDS)
+  const int cbg = moe_cb_gu(sg.cpw), cbd = moe_cb_dn(sd.cpw);
+  size_t lg = (size_t)sg.waves * sg.cpw * tr * 1024, rg = (size_t)(sg.waves - 1) * 2 * cbg * 64 * 16;
+  size_t ld = (size_t)sd.waves * sd.cpw * 2 * rt * 1024, rd = (size_t)(sd.waves - 1) * cbd * 64 * 16;
+  const unsigned gx = (unsigned)((I + 16 * cbg - 1) / (16 * cbg));
+  const unsigned dx = (unsigned)((H + 16 * cbd - 1) / (16 * cbd));
 #define BRQ_GATEUP(TR)                                                                                       \
-  BRQ_CPW_SWITCH(sg.cpw, hipLaunchKernelGGL((k_moe_gateup<CPW, TR>), dim3((I + 15) / 16, maxact),                \
+  BRQ_CPW_SWITCH(sg.cpw, hipLaunchKernelGGL((k_moe_gateup<CPW, TR, moe_cb_gu(CPW)>), dim3(gx, maxact),           \
                                             dim3(64 * sg.waves), lg > rg ? lg : rg, st, x, H, I,                \
                                             reinterpret_cast<const uint4*>(gate_s), gate_sc,                    \
                                             reinterpret_cast<const uint4*>(up_s), up_sc, ws))
@@ -613,9 +697,16 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
 #undef BRQ_GATEUP
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  BRQ_CPW_SWITCH(sd.cpw, hipLaunchKernelGGL((k_moe_down<CPW>), dim3((H + 15) / 16, maxact), dim3(64 * sd.waves),
-                                            ld > rd ? ld : rd, st, H, I, reinterpret_cast<const uint4*>(down_s),
-                                            down_sc, ws));
+#define BRQ_DOWN(RT)                                                                                         \
+  BRQ_CPW_SWITCH(sd.cpw, hipLaunchKernelGGL((k_moe_down<CPW, moe_cb_dn(CPW), RT>), dim3(dx, maxact),              \
+                                            dim3(64 * sd.waves), ld > rd ? ld : rd, st, H, I,                   \
+                                            reinterpret_cast<const uint4*>(down_s), down_sc, ws))
+  if (rt == 4) {
+    BRQ_DOWN(4);
+  } else {
+    BRQ_DOWN(8);
+  }
+#undef BRQ_DOWN
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * H + 255) / 256)), dim3(256), 0, st, T, H, top_k,
