@@ -8,17 +8,18 @@
 // empty experts skipped). 256 experts with 8 routed and an f32 router follow
 // the "BTL-4 Compact" news item.
 //
-// Launches, all on the caller's stream, no host read-back:
-//  1. route: top-k per token (descending fp32 logit, ties to the lower expert
-//     index), softmax over the k selected logits, per-expert counts and
-//     offsets, the list of active experts and the expert-major route list;
-//     the other workgroups stage x in the permuted fp16 operand order.
-//  2. gate/up: one workgroup per (64 intermediate columns, active expert);
-//     both products share every activation operand; SwiGLU in fp32; the
-//     result is stored as an fp16 hi/lo pair per route, permuted.
-//  3. down: one workgroup per (128 hidden columns, active expert); writes the
-//     route's fp32 output.
-//  4. combine: y_t = sum over slots j, in slot order, of w_tj * out(t, j).
+// Launches, all on the caller's stream, no host read-back (T > 4; the
+// decode path for T <= 4 is described further down):
+//  1. top-k per token (descending fp32 logit, ties to the lower expert index)
+//     and the softmax over the k selected logits, one wave per token.
+//  2. route: per-expert counts and offsets, one record per active expert and
+//     the expert-major route list (one workgroup).
+//  3. gate/up: one workgroup per (4 blocks of 16 intermediate columns, active
+//     expert); both products share every activation operand; SwiGLU in fp32;
+//     the result is stored as an fp16 hi/lo pair per route, permuted.
+//  4. down: one workgroup per (4 blocks of 16 hidden columns, active expert);
+//     writes the route's fp32 output.
+//  5. combine: y_t = sum over slots j, in slot order, of w_tj * out(t, j).
 #include <type_traits>
 
 #include "dec_core.h"

@@ -35,17 +35,21 @@ namespace brq {
 
 namespace {
 
-constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 128;
+constexpr int PF_BM = 256, PF_BK = 128;
 constexpr int PF_ROWB = PF_BK * 2;        // bytes per LDS row
 constexpr int PF_TILE = PF_BM * PF_ROWB;  // bytes per activation stage
 
 }  // namespace
 
-template <bool OUT_BF16>
+// BN = 256 (NJ = 4 column tiles of 32 per wave) or 128 (NJ = 2, used for the
+// columns of a last partial round of 256-wide tiles, see launch_gemm_pf). The
+// launch covers column tiles starting at column n_base, tiles_n of them.
+template <bool OUT_BF16, int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf(
     const uint16_t* __restrict__ xp, int M, int N, int K, const uint32_t* __restrict__ signs,
-    const uint16_t* __restrict__ scales, void* __restrict__ y) {
+    const uint16_t* __restrict__ scales, void* __restrict__ y, int n_base, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // [2][PF_TILE]
+  constexpr int NJ = BN / 64;  // 32-column tiles per wave
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -53,11 +57,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // tile id -> (tm, tn): consecutive ids of one XCD (id % 8) cover a
   // contiguous range of tiles, so an XCD streams few activation row-blocks
-  const int tiles_m = (M + PF_BM - 1) / PF_BM, tiles_n = (N + PF_BN - 1) / PF_BN;
+  const int tiles_m = (M + PF_BM - 1) / PF_BM;
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  const int m0 = (bid / tiles_n) * PF_BM, n0 = (bid % tiles_n) * PF_BN;
+  const int m0 = (bid / tiles_n) * PF_BM, n0 = n_base + (bid % tiles_n) * BN;
   const int nk = K / PF_BK;  // k-steps = scale groups
   const int KW = K >> 5;     // 32-bit sign words per weight row
 
@@ -82,35 +86,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                        lds + stage * PF_TILE + (64 * wave + 4 * i) * PF_ROWB, 16, 0, 0);
   };
 
-  // ---- weights: column tile j of this wave is columns n0 + wc*128 + 32j ..,
+  // ---- weights: column tile j of this wave is columns n0 + wc*BN/2 + 32j ..,
   // lane column fr; the lane's k block (fh) selects pairs 4*fh .. 4*fh+3 of
   // each half-run, so its sign words are pre-shifted right by 4*fh.
-  const uint32_t* b_sig[4];
-  const uint16_t* b_sc[4];
-  bool b_ok[4];
+  const uint32_t* b_sig[NJ];
+  const uint16_t* b_sc[NJ];
+  bool b_ok[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = n0 + wc * 128 + 32 * j + fr;
+  for (int j = 0; j < NJ; ++j) {
+    const int c = n0 + wc * (BN / 2) + 32 * j + fr;
     b_ok[j] = c < N;
     const int cc = c < N ? c : N - 1;
     b_sig[j] = signs + (size_t)cc * KW;
     b_sc[j] = scales + (size_t)cc * nk;
   }
-  uint4 wn[4];       // sign words of the next k-step (in flight)
-  uint32_t sn[4];    // its scales
+  uint4 wn[NJ];       // sign words of the next k-step (in flight)
+  uint32_t sn[NJ];    // its scales
   auto load_b = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       wn[j] = *reinterpret_cast<const uint4*>(b_sig[j] + 4 * kt);
       sn[j] = b_sc[j][kt];
     }
   };
-  uint32_t wsh[4][4];  // pre-shifted sign words of the current k-step
-  uint32_t S[4];       // magnitude pair (scale | scale << 16), 0 past N
+  uint32_t wsh[NJ][4];  // pre-shifted sign words of the current k-step
+  uint32_t S[NJ];       // magnitude pair (scale | scale << 16), 0 past N
   const int bshift = 4 * fh;
   auto take_b = [&]() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       wsh[j][0] = wn[j].x >> bshift;
       wsh[j][1] = wn[j].y >> bshift;
       wsh[j][2] = wn[j].z >> bshift;
@@ -119,10 +123,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
   // weight operand of tile j, sub-step ks: pairs b = 8*(ks%2) + t of run ks/2
-  u32x4 bo[2][4];
+  u32x4 bo[2][NJ];
   auto build_b = [&](int ks, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const uint32_t w = wsh[j][ks >> 1];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -143,11 +147,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < 4; ++i) af[buf][i] = *reinterpret_cast<const u32x4*>(p + i * 32 * PF_ROWB);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = i0; i < i1; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[buf][i], bo[buf][j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(af[buf][i], bo[buf][j], acc[i][j]);
   };
 
   // One k-step per iteration; stage cur holds k-step kt. During sub-steps
@@ -187,11 +191,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (ks == 0) load_b(nx);
       mfmas(b, 0, 4);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
+      for (int m = 0; m < 4 * NJ; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
         if (m < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         if (ks < 4 && m < 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
-        if (ks == 0 && m >= 4 && m < 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // sign/scale load
+        if (ks == 0 && m >= 4 && m < 4 + 2 * NJ) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // sign/scale load
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);      // three VALU
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     build_b(0, 0);
     mfmas(1, 2, 4);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 2 * NJ; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (m < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
 
   // ---- epilogue: lane writes column fr of each 32 x 32 tile, rows in runs of 4
-  const bool full = (m0 + PF_BM <= M) && (n0 + PF_BN <= N);
+  const bool full = (m0 + PF_BM <= M) && (n0 + BN <= N);
   auto put = [&](size_t idx, float v) {
     if (OUT_BF16)
       reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16_bits(v);
@@ -227,8 +231,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const size_t base = (size_t)(m0 + wr * 128 + 32 * i + 4 * fh) * N + (n0 + wc * 128 + 32 * j + fr);
+      for (int j = 0; j < NJ; ++j) {
+        const size_t base = (size_t)(m0 + wr * 128 + 32 * i + 4 * fh) * N + (n0 + wc * (BN / 2) + 32 * j + fr);
 #pragma unroll
         for (int r = 0; r < 16; ++r) put(base + (size_t)(8 * (r >> 2) + (r & 3)) * N, acc[i][j][r]);
       }
@@ -236,8 +240,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wc * 128 + 32 * j + fr;
+      for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + wc * (BN / 2) + 32 * j + fr;
         const int rbase = m0 + wr * 128 + 32 * i + 4 * fh;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -250,24 +254,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 size_t pf_lds_bytes() { return 2 * (size_t)PF_TILE; }
 
+template <bool OUT_BF16, int BN>
+static hipError_t pf_launch(const uint16_t* xp, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+                            void* y, int n_base, int tiles_n, hipStream_t st) {
+  // 128 KiB of dynamic LDS needs the per-function opt-in (set on every call:
+  // the attribute is per device and cheap to repeat)
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf<OUT_BF16, BN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)pf_lds_bytes());
+  if (e != hipSuccess) return e;
+  const int tiles = ((M + PF_BM - 1) / PF_BM) * tiles_n;
+  hipLaunchKernelGGL((k_pf<OUT_BF16, BN>), dim3(tiles), dim3(256), pf_lds_bytes(), st, xp, M, N, K,
+                     reinterpret_cast<const uint32_t*>(signs), scales, y, n_base, tiles_n);
+  return hipGetLastError();
+}
+
+// Tile plan. One 256x256 tile per compute unit at a time (128 KiB of LDS), so
+// the tiles run in rounds of `cus`. When the last round is at most half full,
+// its columns are given to 256x128 tiles instead: a full round of half-size
+// tiles, so the launch takes rounds + 1/2 tile-times instead of rounds + 1
+// (C5, 4096 x 14336: 768 tiles of 256 wide, then 256 tiles of 128 wide over
+// the last 2048 columns).
+void pf_plan(int M, int N, int cus, int& big_n, int& small_n) {
+  const int tiles_m = (M + PF_BM - 1) / PF_BM, tiles_n = (N + 255) / 256;
+  const int64_t total = (int64_t)tiles_m * tiles_n;
+  const int64_t rest = total % cus;
+  big_n = tiles_n;
+  small_n = 0;
+  if (total < cus || rest == 0 || 2 * rest > cus) return;
+  const int cols = (int)((rest + tiles_m - 1) / tiles_m);  // 256-wide column tiles in the last round
+  big_n = tiles_n - cols;
+  small_n = (N - big_n * 256 + 127) / 128;
+  if ((int64_t)tiles_m * small_n > cus) {  // the 128-wide tiles would not fit one round
+    big_n = tiles_n;
+    small_n = 0;
+  }
+}
+
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                           void* y, int y_bf16, void* ws, hipStream_t st) {
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
   hipError_t e = launch_prep_bf16(x, M, K, xp, st);
   if (e != hipSuccess) return e;
-  // 128 KiB of dynamic LDS needs the per-function opt-in (set on every call:
-  // the attribute is per device and cheap to repeat)
-  const void* fn = y_bf16 ? reinterpret_cast<const void*>(&k_pf<true>) : reinterpret_cast<const void*>(&k_pf<false>);
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pf_lds_bytes());
-  if (e != hipSuccess) return e;
-  const int tiles = ((M + PF_BM - 1) / PF_BM) * ((N + PF_BN - 1) / PF_BN);
-  if (y_bf16)
-    hipLaunchKernelGGL(k_pf<true>, dim3(tiles), dim3(256), pf_lds_bytes(), st, xp, M, N, K,
-                       reinterpret_cast<const uint32_t*>(signs), scales, y);
-  else
-    hipLaunchKernelGGL(k_pf<false>, dim3(tiles), dim3(256), pf_lds_bytes(), st, xp, M, N, K,
-                       reinterpret_cast<const uint32_t*>(signs), scales, y);
-  return hipGetLastError();
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (cus < 1) cus = 256;
+  int big_n, small_n;
+  pf_plan(M, N, cus, big_n, small_n);
+  if (big_n > 0) {
+    e = y_bf16 ? pf_launch<true, 256>(xp, M, N, K, signs, scales, y, 0, big_n, st)
+               : pf_launch<false, 256>(xp, M, N, K, signs, scales, y, 0, big_n, st);
+    if (e != hipSuccess) return e;
+  }
+  if (small_n > 0)
+    e = y_bf16 ? pf_launch<true, 128>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, st)
+               : pf_launch<false, 128>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, st);
+  return e;
 }
 
 }  // namespace brq

@@ -158,6 +158,17 @@ def test_gemm_tiled_f32(M, N, K):
     check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
 
 
+# More 256-wide tiles than compute units with a last round at most half full:
+# the last round's columns go to 128-wide tiles (a second launch). 256 x 65892:
+# 256 tiles of 256 columns, then 3 of 128 (the last ragged); 300 x 33280: two
+# row blocks (the second ragged), 128 + 4 column tiles.
+@pytest.mark.parametrize("M,N,K", [(256, 65892, 128), (300, 33280, 256)])
+def test_gemm_tiled_split_tail(M, N, K):
+    say("gemm tiled split tail", M, N, K)
+    y, o = _gemm_case(M, N, K, M * 7 + 1)
+    check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
+
+
 def test_gemm_tiled_bf16():
     say("gemm tiled bf16 257x320x768")
     y, o = _gemm_case(257, 320, 768, 99, out=torch.bfloat16)
