@@ -8,7 +8,7 @@ import numpy as np
 __all__ = [
     "GROUP", "bf16_to_f64", "f16_to_f64", "round_bf16", "bf16_bits",
     "sign_bits", "pack_words", "unpack_signs", "group_mean_abs", "pack_sign1", "pack_sign1_only",
-    "dequantize", "bin_gemm", "bin_gemm_cols", "bin_gemm_loops",
+    "dequantize", "bin_gemm", "bin_gemm_cols", "bin_gemm_loops", "bin_gemm_lr", "bin_gemm_lr_dense",
     "dbf_chain", "dbf_dense", "dbf_bpe", "dbf_bits",
     "route_topk", "silu", "moe_ffn", "moe_ffn_loops",
     "kron_rotate", "kron_rotate_bf16",
@@ -22,6 +22,7 @@ PINS = {
     "pack_sign1": "closed form + brute-force scale search + brute-force sign search + round trip + Gaussian error law",
     "pack_sign1_only": "bit convention + round trip",
     "bin_gemm": "one-hot / all-plus / all-minus closed forms + definitional loops + linearity",
+    "bin_gemm_lr": "dense materialisation of Wq + U.V + zero-factor reduction + one-hot rank-1 closed form",
     "dbf_chain": "dense reconstruction + Sylvester-Hadamard identity",
     "dbf_bpe": "worked example of the DBF post, section 1.1",
     "route_topk": "brute-force ordering + softmax invariants",
@@ -179,6 +180,32 @@ def bin_gemm_loops(x, words, scales, N: int, K: int) -> np.ndarray:
                 parts.append(sc[n, g] * math.fsum(terms))
             y[m, n] = math.fsum(parts)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Binary product plus a low-rank correction ("BWLA" commentary, section 4:
+# the residual that the binarised weights leave is approximated by a truncated
+# SVD, a rank-r matrix added to the binarised weights as a correction term)
+# ---------------------------------------------------------------------------
+
+def bin_gemm_lr(x, words, scales, v, u, N: int, K: int, r: int) -> np.ndarray:
+    """y = x . (W_q + U V)^T = x . W_q^T + (x . V^T) . U^T in fp64, with the
+    correction in factored form: V is r x K, U is N x r, both fp16 arrays
+    (like the group scales). The factored order is how the correction is applied at inference
+    (r dot products per row, then r products per output)."""
+    x = np.asarray(x, dtype=np.float64)
+    V = f16_to_f64(v).reshape(r, K)
+    U = f16_to_f64(u).reshape(N, r)
+    t = x @ V.T
+    return bin_gemm(x, words, scales, N, K) + t @ U.T
+
+
+def bin_gemm_lr_dense(x, words, scales, v, u, N: int, K: int, r: int) -> np.ndarray:
+    """The same product through the materialised corrected matrix W_q + U V
+    (N x K, fp64): the definition the factored form must equal."""
+    x = np.asarray(x, dtype=np.float64)
+    W = dequantize(words, scales, N, K) + f16_to_f64(u).reshape(N, r) @ f16_to_f64(v).reshape(r, K)
+    return x @ W.T
 
 
 # ---------------------------------------------------------------------------

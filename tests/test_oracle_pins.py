@@ -215,6 +215,54 @@ def test_gemm_linear_and_row_independent():
 
 
 # ---------------------------------------------------------------------------
+# binary product + low-rank correction (BWLA commentary, section 4)
+# ---------------------------------------------------------------------------
+
+def _f16(a):
+    return np.asarray(a, dtype=np.float16)
+
+
+def test_lowrank_zero_factors_reduce_to_bin_gemm():
+    M, N, K, r = 3, 24, 256, 5
+    w, words, scales = _packed((95, 0), N, K)
+    x = oracle.bf16_to_f64(datagen.bf16_normal((95, 1), (M, K)))
+    z = oracle.bin_gemm_lr(x, words, scales, _f16(np.zeros((r, K))), _f16(np.zeros((N, r))), N, K, r)
+    assert np.array_equal(z, oracle.bin_gemm(x, words, scales, N, K))
+
+
+def test_lowrank_one_hot_factors_closed_form():
+    # V rows one-hot at k = j_i and U columns u_i: the correction is
+    # sum_i x[:, j_i] (outer) u_i -- swapping the roles of U and V, or
+    # transposing either, breaks it
+    M, N, K = 4, 40, 384
+    w, words, scales = _packed((95, 2), N, K)
+    x = oracle.bf16_to_f64(datagen.bf16_normal((95, 3), (M, K)))
+    js = [5, 200, 383]
+    V = np.zeros((len(js), K))
+    for i, jj in enumerate(js):
+        V[i, jj] = 1.0
+    U = np.asarray(datagen.normal_f32((95, 4), (N, len(js)), 0.5), dtype=np.float16).astype(np.float64)
+    y = oracle.bin_gemm_lr(x, words, scales, _f16(V), _f16(U), N, K, len(js))
+    corr = sum(np.outer(x[:, jj], U[:, i]) for i, jj in enumerate(js))
+    assert np.allclose(y - oracle.bin_gemm(x, words, scales, N, K), corr, rtol=1e-12, atol=1e-14)
+
+
+def test_lowrank_factored_equals_materialised_matrix():
+    M, N, K, r = 5, 48, 512, 20
+    w, words, scales = _packed((95, 5), N, K)
+    x = oracle.bf16_to_f64(datagen.bf16_normal((95, 6), (M, K)))
+    v = _f16(datagen.normal_f32((95, 7), (r, K), 0.05))
+    u = _f16(datagen.normal_f32((95, 8), (N, r), 0.05))
+    y = oracle.bin_gemm_lr(x, words, scales, v, u, N, K, r)
+    # materialised from scratch: signs by the bit convention, scales per group
+    bits = np.array([[(int(words[n, k // 64]) >> (k % 64)) & 1 for k in range(K)] for n in range(N)])
+    Wq = np.where(bits == 1, -1.0, 1.0) * np.repeat(scales.astype(np.float64), 128, axis=1)
+    W = Wq + u.astype(np.float64).reshape(N, r) @ v.astype(np.float64).reshape(r, K)
+    assert np.allclose(y, x @ W.T, rtol=1e-12, atol=1e-13)
+    assert np.allclose(oracle.bin_gemm_lr_dense(x, words, scales, v, u, N, K, r), x @ W.T, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # S4 DBF
 # ---------------------------------------------------------------------------
 
