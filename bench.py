@@ -10,7 +10,8 @@ Infinity Cache, so every call streams its weights from HBM.
 Also reported (extra): the same product at M = 4, 16, 64; the routed MoE layer
 (256 experts, top-8, hidden 2048, intermediate 512) at T = 1 and 64 decode
 tokens; the DBF chain (4096x4096, r = 2048) at M = 1 and 512; the prefill
-product at M = 4096 (4096 -> 14336) with the Kronecker rotation before it.
+product at M = 4096 (4096 -> 14336) with the Kronecker rotation before it, and
+the same product with a rank-20 weight correction fused into its epilogue.
 
 The CPU baseline is the fp64 numpy oracle on the host cores, timed on a bounded
 sample of the headline workload.
@@ -305,13 +306,42 @@ def run_prefill(brq, torch, iters=10):
         gemm_ms += ev[1].elapsed_time(ev[2])
     rot_ms /= iters
     gemm_ms /= iters
+    # the same product with a rank-20 weight correction fused into its epilogue
+    # (rank 0.005 of the dimension); factors are synthetic normal fp16
+    r = 20
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20)
+    v = (torch.randn((r, K), device="cuda", generator=g) * 0.02).to(torch.float16)
+    u = (torch.randn((N, r), device="cuda", generator=g) * 0.02).to(torch.float16)
+    ws_lr = torch.empty(brq.gemm_lr_workspace_bytes(x.shape[0], N, K, r), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        brq.gemm_lr(xr, s, sc, v, u, N, K, r, y=y, ws=ws_lr)
+    torch.cuda.synchronize()
+
+    # both products graph-replayed (the corrected one is five launches, two of
+    # them short: eager timing would measure the host's launch gaps)
+    ws_pf = torch.empty(brq.gemm_workspace_bytes(x.shape[0], N, K), dtype=torch.uint8, device="cuda")
+
+    def plain():
+        for _ in range(iters):
+            brq.gemm(xr, s, sc, N, K, y=y, ws=ws_pf)
+
+    def corrected():
+        for _ in range(iters):
+            brq.gemm_lr(xr, s, sc, v, u, N, K, r, y=y, ws=ws_lr)
+
+    gemm_graph_ms = graph_time(torch, plain, 3 * iters) / iters
+    lr_ms = graph_time(torch, corrected, 5 * iters) / iters
     M = x.shape[0]
     flops = 2.0 * M * N * K
+    flops_lr = flops + 2.0 * M * r * (K + N)
     res = dict(M=M, N=N, K=K, gemm_us=gemm_ms * 1e3, gemm_tflops=flops / (gemm_ms * 1e-3) / 1e12,
                gemm_frac_of_f16_peak=flops / (gemm_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+               gemm_graph_us=gemm_graph_ms * 1e3,
+               gemm_lr20_us=lr_ms * 1e3, gemm_lr20_tflops=flops_lr / (lr_ms * 1e-3) / 1e12,
                rotate_us=rot_ms * 1e3, rotate_gbs=(2 * M * K * 2) / (rot_ms * 1e-3) / 1e9,
                tokens_per_s=M / ((rot_ms + gemm_ms) * 1e-3))
-    del s, sc, x, xr, y
+    del s, sc, x, xr, y, v, u, ws_lr, ws_pf
     torch.cuda.empty_cache()
     return res
 

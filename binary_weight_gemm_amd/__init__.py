@@ -23,8 +23,9 @@ import os
 import torch
 
 __all__ = [
-    "BrqError", "lib", "library_path", "pack", "gemm", "dbf_gemm", "moe_ffn", "kron_rotate",
-    "gemm_workspace_bytes", "dbf_workspace_bytes", "moe_workspace_bytes", "sign_words", "scale_count",
+    "BrqError", "lib", "library_path", "pack", "gemm", "gemm_lr", "dbf_gemm", "moe_ffn", "kron_rotate",
+    "gemm_workspace_bytes", "gemm_lr_workspace_bytes", "dbf_workspace_bytes", "moe_workspace_bytes",
+    "sign_words", "scale_count",
     "BRQ_BF16", "BRQ_F32", "ABI_FUNCTIONS",
 ]
 
@@ -49,6 +50,8 @@ ABI_FUNCTIONS = {
     "brq_pack": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "brq_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "brq_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "brq_gemm_lr_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "brq_gemm_lr": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _sz, _vp]),
     "brq_dbf_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "brq_dbf_gemm": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
     "brq_moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
@@ -172,6 +175,31 @@ def gemm(x: torch.Tensor, signs: torch.Tensor, scales: torch.Tensor, N: int, K: 
     _check(lib().brq_gemm(_dev(x, "x", torch.bfloat16), M, N, K, _dev(signs, "signs", torch.int64),
                           _dev(scales, "scales", torch.float16), _dev(y, "y", out_dtype), code,
                           _dev(ws, "ws") if ws is not None else None, wsb, _stream()), "brq_gemm")
+    return y
+
+
+def gemm_lr_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return lib().brq_gemm_lr_workspace_bytes(M, N, K, r)
+
+
+def gemm_lr(x: torch.Tensor, signs: torch.Tensor, scales: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
+            N: int, K: int, r: int, out_dtype=torch.bfloat16, y=None, ws=None) -> torch.Tensor:
+    """brq_gemm_lr: y[M, N] = x . (Wq + U V)^T with V fp16 [r, K] and U fp16 [N, r]."""
+    M = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise BrqError(f"x must be [M, {K}]")
+    if signs.numel() != N * K // 64 or scales.numel() != N * K // 128:
+        raise BrqError("signs/scales do not match N x K")
+    if v.numel() != r * K or u.numel() != N * r:
+        raise BrqError("v must be r x K and u N x r")
+    code = _out_code(out_dtype)
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ws, wsb = _ws(gemm_lr_workspace_bytes(M, N, K, r), x.device, ws)
+    _check(lib().brq_gemm_lr(_dev(x, "x", torch.bfloat16), M, N, K, _dev(signs, "signs", torch.int64),
+                             _dev(scales, "scales", torch.float16), _dev(v, "v", torch.float16),
+                             _dev(u, "u", torch.float16), r, _dev(y, "y", out_dtype), code, _dev(ws, "ws"), wsb,
+                             _stream()), "brq_gemm_lr")
     return y
 
 

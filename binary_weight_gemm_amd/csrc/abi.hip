@@ -72,7 +72,7 @@ brq_status hip_result(hipError_t e, const char* what) {
 bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K) {
-  if (M <= 64) return brq::gemm_dec_in_lds(M, K) ? 0 : brq::mid_ws_bytes(M, N, K);
+  if (M <= 64) return brq::gemm_dec_ws_bytes(M, N, K);
   return brq::align256((size_t)M * K * 2);
 }
 
@@ -148,6 +148,36 @@ brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const ui
   if (M <= 64)
     return hip_result(brq::launch_gemm_dec(x, (int)M, (int)N, (int)K, signs, scales, y, yb, ws, st), "brq_gemm");
   return hip_result(brq::launch_gemm_pf(x, (int)M, (int)N, (int)K, signs, scales, y, yb, ws, st), "brq_gemm");
+}
+
+size_t brq_gemm_lr_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 1 || N < 1 || K < 128 || K % 128 || r < 1 || r > 64) return 0;
+  return brq::lr_ws_bytes(M, N, K);
+}
+
+brq_status brq_gemm_lr(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint64_t* signs,
+                       const uint16_t* scales, const uint16_t* v, const uint16_t* u, int64_t r, void* y,
+                       brq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !signs || !scales || !v || !u || !y)
+    return fail(BRQ_E_NULL, "brq_gemm_lr: x, signs, scales, v, u and y must not be NULL");
+  if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim)
+    return fail(BRQ_E_SHAPE, "brq_gemm_lr: M=%lld N=%lld out of range", (long long)M, (long long)N);
+  if (K < 128 || K > kMaxDim || K % 128)
+    return fail(BRQ_E_SHAPE, "brq_gemm_lr: K=%lld must be a positive multiple of 128", (long long)K);
+  if (r < 1 || r > 64) return fail(BRQ_E_SHAPE, "brq_gemm_lr: rank r=%lld must be in 1..64", (long long)r);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm_lr: unknown y_dtype %d", (int)y_dtype);
+  if (!aligned(x, 16) || !aligned(signs, 16) || !aligned(scales, 16) || !aligned(y, 16) || !aligned(v, 2) ||
+      !aligned(u, 2))
+    return fail(BRQ_E_ALIGN, "brq_gemm_lr: x, signs, scales and y must be 16-byte aligned, v and u 2-byte");
+  const size_t need = brq::lr_ws_bytes(M, N, K);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(BRQ_E_WORKSPACE, "brq_gemm_lr: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  return hip_result(brq::launch_gemm_lr(x, (int)M, (int)N, (int)K, signs, scales, v, u, (int)r, y,
+                                        y_dtype == BRQ_BF16, ws, (hipStream_t)stream),
+                    "brq_gemm_lr");
 }
 
 size_t brq_dbf_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {

@@ -31,6 +31,10 @@ hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_
 // over 128-column tiles (+ a slice-sum launch when K is split); `ws` holds
 // mid_ws_bytes(M, N, K) bytes (0: no workspace).
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K);
+// workspace of launch_gemm_dec (M <= 64)
+inline size_t gemm_dec_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return gemm_dec_in_lds(M, K) ? 0 : mid_ws_bytes(M, N, K);
+}
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 // Many activation rows: LDS-tiled matrix-core kernel, bf16 activations read directly.
@@ -40,6 +44,16 @@ hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64
 // fp16, then the 256 x 256 direct-to-LDS matrix-core kernel.
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                           const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
+// The same with one extra k-step per tile that adds a rank-r correction:
+// lr_t [M][128] fp16 (x V^T as hi | lo), lr_u [N][64] fp16 (U padded).
+hipError_t launch_gemm_pf_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
+                             const uint16_t* scales, const uint16_t* lr_t, const uint16_t* lr_u, void* y,
+                             int y_bf16, void* ws, hipStream_t st);
+// y = x . (Wq + U V)^T, r <= 64; `ws` holds lr_ws_bytes(M, N, K) bytes.
+size_t lr_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
+                          const uint16_t* scales, const uint16_t* v, const uint16_t* u, int r, void* y,
+                          int y_bf16, void* ws, hipStream_t st);
 
 // ---- DBF chain -------------------------------------------------------------
 // stage 1: hp[2M][r] (fp16 hi/lo pairs, permuted) = D_mid (V (D_in x))

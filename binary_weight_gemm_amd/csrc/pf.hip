@@ -44,10 +44,16 @@ constexpr int PF_TILE = PF_BM * PF_ROWB;  // bytes per activation stage
 // BN = 256 (NJ = 4 column tiles of 32 per wave) or 128 (NJ = 2, used for the
 // columns of a last partial round of 256-wide tiles, see launch_gemm_pf). The
 // launch covers column tiles starting at column n_base, tiles_n of them.
-template <bool OUT_BF16, int BN>
+// LR: one more k-step after the last adds a rank-r weight correction,
+// (x V^T) U^T: its activation operand is lr_t [M][128] fp16 (x V^T as hi
+// parts in k 0..63 and lo parts in k 64..127, natural order), staged like an
+// activation k-step, and its weight operand is lr_u [N][64] fp16 (U padded
+// with zeros), factor index k % 64, loaded straight into registers.
+template <bool OUT_BF16, int BN, bool LR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf(
     const uint16_t* __restrict__ xp, int M, int N, int K, const uint32_t* __restrict__ signs,
-    const uint16_t* __restrict__ scales, void* __restrict__ y, int n_base, int tiles_n) {
+    const uint16_t* __restrict__ scales, void* __restrict__ y, int n_base, int tiles_n,
+    const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_u) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // [2][PF_TILE]
   constexpr int NJ = BN / 64;  // 32-column tiles per wave
 
@@ -219,6 +225,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
 
+  if constexpr (LR) {
+    __syncthreads();  // every wave is done with the stages
+    // the tile's rows of x V^T into stage 0, laid out like an activation k-step
+    const uint8_t* tb = reinterpret_cast<const uint8_t*>(lr_t) + (size_t)m0 * PF_ROWB;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = 64 * wave + 4 * i + (lane >> 4);
+      const int gl = m0 + rl < M ? rl : M - 1 - m0;
+      const int chunk = (lane & 15) ^ (rl & 15);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tb + (size_t)gl * PF_ROWB + chunk * 16),
+                                       lds + (64 * wave + 4 * i) * PF_ROWB, 16, 0, 0);
+    }
+    // weight operand of tile j, sub-step ks: U[col][16*(ks%4) + 8*fh .. +7]
+    u32x4 bu[NJ][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = n0 + wc * (BN / 2) + 32 * j + fr;
+      const uint16_t* ur = lr_u + (size_t)(c < N ? c : N - 1) * 64 + 8 * fh;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bu[j][q] = *reinterpret_cast<const u32x4*>(ur + 16 * q);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      read_a(0, ks, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(af[0][i], bu[j][ks & 3], acc[i][j]);
+    }
+  }
+
   // ---- epilogue: lane writes column fr of each 32 x 32 tile, rows in runs of 4
   const bool full = (m0 + PF_BM <= M) && (n0 + BN <= N);
   auto put = [&](size_t idx, float v) {
@@ -254,17 +293,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 size_t pf_lds_bytes() { return 2 * (size_t)PF_TILE; }
 
-template <bool OUT_BF16, int BN>
+template <bool OUT_BF16, int BN, bool LR>
 static hipError_t pf_launch(const uint16_t* xp, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
-                            void* y, int n_base, int tiles_n, hipStream_t st) {
+                            void* y, int n_base, int tiles_n, const uint16_t* lr_t, const uint16_t* lr_u,
+                            hipStream_t st) {
   // 128 KiB of dynamic LDS needs the per-function opt-in (set on every call:
   // the attribute is per device and cheap to repeat)
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf<OUT_BF16, BN>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf<OUT_BF16, BN, LR>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)pf_lds_bytes());
   if (e != hipSuccess) return e;
   const int tiles = ((M + PF_BM - 1) / PF_BM) * tiles_n;
-  hipLaunchKernelGGL((k_pf<OUT_BF16, BN>), dim3(tiles), dim3(256), pf_lds_bytes(), st, xp, M, N, K,
-                     reinterpret_cast<const uint32_t*>(signs), scales, y, n_base, tiles_n);
+  hipLaunchKernelGGL((k_pf<OUT_BF16, BN, LR>), dim3(tiles), dim3(256), pf_lds_bytes(), st, xp, M, N, K,
+                     reinterpret_cast<const uint32_t*>(signs), scales, y, n_base, tiles_n, lr_t, lr_u);
   return hipGetLastError();
 }
 
@@ -290,25 +330,42 @@ void pf_plan(int M, int N, int cus, int& big_n, int& small_n) {
   }
 }
 
-hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
-                          void* y, int y_bf16, void* ws, hipStream_t st) {
-  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-  hipError_t e = launch_prep_bf16(x, M, K, xp, st);
-  if (e != hipSuccess) return e;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (cus < 1) cus = 256;
+template <bool LR>
+static hipError_t pf_run(const uint16_t* xp, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+                         void* y, int y_bf16, const uint16_t* lr_t, const uint16_t* lr_u, hipStream_t st) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;  // MI355X
   int big_n, small_n;
   pf_plan(M, N, cus, big_n, small_n);
+  hipError_t e = hipSuccess;
   if (big_n > 0) {
-    e = y_bf16 ? pf_launch<true, 256>(xp, M, N, K, signs, scales, y, 0, big_n, st)
-               : pf_launch<false, 256>(xp, M, N, K, signs, scales, y, 0, big_n, st);
+    e = y_bf16 ? pf_launch<true, 256, LR>(xp, M, N, K, signs, scales, y, 0, big_n, lr_t, lr_u, st)
+               : pf_launch<false, 256, LR>(xp, M, N, K, signs, scales, y, 0, big_n, lr_t, lr_u, st);
     if (e != hipSuccess) return e;
   }
   if (small_n > 0)
-    e = y_bf16 ? pf_launch<true, 128>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, st)
-               : pf_launch<false, 128>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, st);
+    e = y_bf16 ? pf_launch<true, 128, LR>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, lr_t, lr_u, st)
+               : pf_launch<false, 128, LR>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, lr_t, lr_u, st);
   return e;
+}
+
+hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+                          void* y, int y_bf16, void* ws, hipStream_t st) {
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
+  const hipError_t e = launch_prep_bf16(x, M, K, xp, st);
+  if (e != hipSuccess) return e;
+  return pf_run<false>(xp, M, N, K, signs, scales, y, y_bf16, nullptr, nullptr, st);
+}
+
+hipError_t launch_gemm_pf_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+                             const uint16_t* lr_t, const uint16_t* lr_u, void* y, int y_bf16, void* ws,
+                             hipStream_t st) {
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
+  const hipError_t e = launch_prep_bf16(x, M, K, xp, st);
+  if (e != hipSuccess) return e;
+  return pf_run<true>(xp, M, N, K, signs, scales, y, y_bf16, lr_t, lr_u, st);
 }
 
 }  // namespace brq

@@ -123,6 +123,30 @@ brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * brq_gemm_lr -- y = x . (Wq + U V)^T = x . Wq^T + (x . V^T) . U^T: the
+ * binary product plus a rank-r correction of the weights (BWLA commentary,
+ * section 4: the residual left by binarisation is approximated by a
+ * truncated SVD and added to the binarised weights; rank about 0.5% of the
+ * dimension, ~20 for 4096).
+ *
+ *   x, signs, scales, y   as for brq_gemm
+ *   v       device, fp16 [r][K] (row i: the i-th right factor)
+ *   u       device, fp16 [N][r]
+ *   ws      device workspace of at least brq_gemm_lr_workspace_bytes(M, N, K, r)
+ *   1 <= r <= 64; M, N, K as for brq_gemm. x . V^T must stay inside the fp16
+ *   range (it is carried as an fp16 hi/lo pair on the many-row path).
+ * For M > 64 the correction runs on the matrix cores inside the product's
+ * epilogue (one extra k-step per tile); for M <= 64 it is added to the fp32
+ * product before the output is written. One rounding to y_dtype either way.
+ */
+size_t brq_gemm_lr_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+brq_status brq_gemm_lr(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                       const uint64_t* signs, const uint16_t* scales,
+                       const uint16_t* v, const uint16_t* u, int64_t r,
+                       void* y, brq_dtype y_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
  * brq_dbf_gemm -- the Double Binary Factorization chain
  *   y = D_out . U . D_mid . V . D_in . x   (one output row per row of x)
  * evaluated in the deployed order x_s = D_in x; h = V x_s; h_s = D_mid h;

@@ -8,7 +8,7 @@ import numpy as np
 __all__ = [
     "GROUP", "bf16_to_f64", "f16_to_f64", "round_bf16", "bf16_bits",
     "sign_bits", "pack_words", "unpack_signs", "group_mean_abs", "pack_sign1", "pack_sign1_only",
-    "dequantize", "bin_gemm", "bin_gemm_cols", "bin_gemm_loops", "bin_gemm_lr", "bin_gemm_lr_dense",
+    "dequantize", "bin_gemm", "bin_gemm_cols", "bin_gemm_loops", "bin_gemm_lr", "bin_gemm_lr_cols", "bin_gemm_lr_dense",
     "dbf_chain", "dbf_dense", "dbf_bpe", "dbf_bits",
     "route_topk", "silu", "moe_ffn", "moe_ffn_loops",
     "kron_rotate", "kron_rotate_bf16",
@@ -198,6 +198,14 @@ def bin_gemm_lr(x, words, scales, v, u, N: int, K: int, r: int) -> np.ndarray:
     U = f16_to_f64(u).reshape(N, r)
     t = x @ V.T
     return bin_gemm(x, words, scales, N, K) + t @ U.T
+
+
+def bin_gemm_lr_cols(x, words, scales, v, u, N: int, K: int, r: int, cols) -> np.ndarray:
+    """Only the output columns ``cols`` of bin_gemm_lr (for sampled checks at full size)."""
+    cols = np.asarray(cols)
+    x = np.asarray(x, dtype=np.float64)
+    t = x @ f16_to_f64(v).reshape(r, K).T
+    return bin_gemm_cols(x, words, scales, N, K, cols) + t @ f16_to_f64(u).reshape(N, r)[cols].T
 
 
 def bin_gemm_lr_dense(x, words, scales, v, u, N: int, K: int, r: int) -> np.ndarray:

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(brq.ABI_FUNCTIONS)
@@ -84,6 +84,29 @@ def test_gemm_validation(L):
     assert g(P, 64, 16, 14336, P, P, P, 0, None, 0, None) == E_WORKSPACE
     assert g(P, 64, 16, 14336, P, P, P, 0, P, 10, None) == E_WORKSPACE
     assert "workspace" in _err(L)
+
+
+def test_gemm_lr_validation(L):
+    g = L.brq_gemm_lr
+    ok = (P, 4, 16, 256, P, P, P, P, 20, P, 0, P, 1 << 22, None)
+    assert g(None, *ok[1:]) == E_NULL
+    assert g(*ok[:6], None, *ok[7:]) == E_NULL                        # v
+    assert g(*ok[:8], 0, *ok[9:]) == E_SHAPE                           # rank 0
+    assert g(*ok[:8], 65, *ok[9:]) == E_SHAPE                          # rank past 64
+    assert "rank" in _err(L)
+    assert g(*ok[:3], 200, *ok[4:]) == E_SHAPE                         # K % 128
+    assert g(*ok[:10], 5, *ok[11:]) == E_DTYPE
+    assert g(PMIS, *ok[1:]) == E_ALIGN
+    assert g(*ok[:11], None, 0, None) == E_WORKSPACE
+    assert L.brq_gemm_lr_workspace_bytes(4, 16, 256, 0) == 0
+    assert L.brq_gemm_lr_workspace_bytes(4, 16, 256, 65) == 0
+    # decode rows: padded V (64 x K fp16) + x V^T (fp32 [M][64]) + fp32 product + the product's own workspace
+    M, N, K = 4, 4096, 14336
+    assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == (64 * K * 2 + 1024 + M * N * 4
+                                                          + L.brq_gemm_workspace_bytes(M, N, K))
+    # many rows: padded V + padded U (N x 64 fp16) + x V^T hi/lo (M x 128 fp16) + staged activations
+    M, N, K = 4096, 14336, 4096
+    assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == 64 * K * 2 + N * 128 + M * 256 + M * K * 2
 
 
 def test_dbf_validation(L):

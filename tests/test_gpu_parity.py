@@ -169,6 +169,58 @@ def test_gemm_tiled_split_tail(M, N, K):
     check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
 
 
+# ---------------------------------------------------------------------------
+# binary product + rank-r correction: decode rows (correction added to the fp32
+# product) and many rows (fused k-step in the prefill epilogue, incl. the
+# split-tail launch)
+# ---------------------------------------------------------------------------
+
+def _lr_case(M, N, K, r, key, out=torch.float32):
+    w = datagen.normal_f32((77, key, 0), (N, K), 0.02)
+    x = datagen.bf16_normal((77, key, 1), (M, K))
+    v = np.asarray(datagen.normal_f32((77, key, 2), (r, K), 0.05), dtype=np.float16)
+    u = np.asarray(datagen.normal_f32((77, key, 3), (N, r), 0.05), dtype=np.float16)
+    ow, osc = oracle.pack_sign1(w)
+    o = oracle.bin_gemm_lr(oracle.bf16_to_f64(x), ow, osc, v, u, N, K, r)
+    y = brq().gemm_lr(dev(x), dev(ow), dev(osc), dev(v), dev(u), N, K, r, out_dtype=out)
+    torch.cuda.synchronize()
+    return y, o
+
+
+@pytest.mark.parametrize("M,N,K,r", [(1, 40, 640, 1), (1, 1000, 1536, 20), (4, 130, 1024, 20), (17, 200, 2048, 33),
+                                     (64, 96, 1024, 64), (65, 64, 256, 20), (300, 200, 384, 7),
+                                     (512, 1024, 1024, 64), (256, 65892, 128, 20)])
+def test_gemm_lr(M, N, K, r):
+    say("gemm lr", M, N, K, r)
+    y, o = _lr_case(M, N, K, r, M * 31 + r)
+    # M = 1 with K % 512 == 0 takes the single-row fp8 x fp4 product
+    tol = F4_TOL if (M == 1 and K % 512 == 0) else F32_TOL
+    check_f32(f64(y), o, tol, f"gemm lr {M}x{N}x{K} r={r}")
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_gemm_lr_bf16(M):
+    say("gemm lr bf16", M)
+    y, o = _lr_case(M, 384, 1024, 20, 900 + M, out=torch.bfloat16)
+    check_bf16(y, o, f"gemm lr bf16 M={M}")
+
+
+def test_gemm_lr_c5_sampled_columns():
+    say("gemm lr at the C5 shape, rank 20, sampled columns")
+    d = datagen.C5()
+    N, K, r = d["N"], d["K"], 20
+    w = datagen.C5_weight(N, K)
+    ow, osc = oracle.pack_sign1(w)
+    v = np.asarray(datagen.normal_f32((78, 0), (r, K), 0.02), dtype=np.float16)
+    u = np.asarray(datagen.normal_f32((78, 1), (N, r), 0.02), dtype=np.float16)
+    x = datagen.bf16_normal((78, 2), (4096, K))
+    y = brq().gemm_lr(dev(x), dev(ow), dev(osc), dev(v), dev(u), N, K, r, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cols = np.sort(datagen.rng(79, 0).choice(N, size=64, replace=False))
+    o = oracle.bin_gemm_lr_cols(oracle.bf16_to_f64(x), ow, osc, v, u, N, K, r, cols)
+    check_f32(f64(y)[:, cols], o, F32_TOL, "C5 gemm lr")
+
+
 def test_gemm_tiled_bf16():
     say("gemm tiled bf16 257x320x768")
     y, o = _gemm_case(257, 320, 768, 99, out=torch.bfloat16)

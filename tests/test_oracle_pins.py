@@ -260,6 +260,8 @@ def test_lowrank_factored_equals_materialised_matrix():
     W = Wq + u.astype(np.float64).reshape(N, r) @ v.astype(np.float64).reshape(r, K)
     assert np.allclose(y, x @ W.T, rtol=1e-12, atol=1e-13)
     assert np.allclose(oracle.bin_gemm_lr_dense(x, words, scales, v, u, N, K, r), x @ W.T, rtol=1e-12, atol=1e-13)
+    cols = np.array([47, 0, 13])
+    assert np.allclose(oracle.bin_gemm_lr_cols(x, words, scales, v, u, N, K, r, cols), y[:, cols], rtol=1e-14)
 
 
 # ---------------------------------------------------------------------------
