@@ -141,6 +141,33 @@ class C4:
         return router_logits((4, 1, T, it), T, self.E)
 
 
+class C4D:
+    """Routed MoE layer whose experts are DBF chains (the deployed workload of
+    the DBF post: gate/up 512x2048 and down 2048x512 per expert, r = 1024).
+    Per (expert, projection): V r x n and U m x r uniform +-1, d_in and d_out
+    fp16 log-normal(0, 0.5), d_mid fp16 log-normal(0, 0.5) * 2^-12 so that the
+    reconstructed matrix has the spread of a trained projection (about 0.017)
+    and every intermediate stays well inside fp16. Drawn lazily per expert."""
+
+    def __init__(self, E: int = 256, H: int = 2048, I: int = 512, r: int = 1024, top_k: int = 8, layer: int = 0):
+        self.E, self.H, self.I, self.r, self.top_k, self.layer = E, H, I, r, top_k, layer
+
+    def proj(self, e: int, p: int):
+        """p = 0 gate, 1 up (m = I, n = H), 2 down (m = H, n = I)."""
+        m, n = (self.I, self.H) if p < 2 else (self.H, self.I)
+        key = (6, self.layer, e, p)
+        d_mid = (np.exp(rng(*key, 3).standard_normal(size=(self.r,)) * 0.5) * 2.0 ** -12).astype(np.float16)
+        return dict(v=pm1_f32(key + (0,), (self.r, n)), u=pm1_f32(key + (1,), (m, self.r)),
+                    d_in=f16_lognormal(key + (2,), (n,)), d_mid=d_mid, d_out=f16_lognormal(key + (4,), (m,)),
+                    m=m, n=n)
+
+    def x(self, T):
+        return bf16_normal((6, 100, T), (T, self.H))
+
+    def logits(self, T, it: int = 0):
+        return router_logits((6, 101, T, it), T, self.E)
+
+
 def C5(M: int = 4096, K: int = 4096, N: int = 14336, n1: int = 64, n2: int = 64):
     """Prefill with a Kronecker rotation: x bf16 [M, K] ~N(0,1); H (n1 x n1) and
     R (n2 x n2) Haar orthogonal, handed to both sides as fp32; W fp32 [N, K]

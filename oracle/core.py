@@ -10,7 +10,7 @@ __all__ = [
     "sign_bits", "pack_words", "unpack_signs", "group_mean_abs", "pack_sign1", "pack_sign1_only",
     "dequantize", "bin_gemm", "bin_gemm_cols", "bin_gemm_loops", "bin_gemm_lr", "bin_gemm_lr_cols", "bin_gemm_lr_dense",
     "dbf_chain", "dbf_dense", "dbf_bpe", "dbf_bits",
-    "route_topk", "silu", "moe_ffn", "moe_ffn_loops",
+    "route_topk", "silu", "moe_ffn", "moe_ffn_loops", "moe_dbf_ffn", "moe_dbf_dense",
     "kron_rotate", "kron_rotate_bf16",
     "packed_bytes", "bits_per_weight",
 ]
@@ -27,6 +27,7 @@ PINS = {
     "dbf_bpe": "worked example of the DBF post, section 1.1",
     "route_topk": "brute-force ordering + softmax invariants",
     "moe_ffn": "identical-experts reduction + single-route dense FFN + loops",
+    "moe_dbf_ffn": "dense reconstruction of every chain + identical-experts reduction + single route",
     "kron_rotate": "numpy.kron identity + orthogonality invariants",
 }
 
@@ -318,6 +319,48 @@ def moe_ffn_loops(x, logits, expert, H: int, I: int, k: int):
             outs.append(wts[t, j] * bin_gemm_loops(a[None, :], dw, ds, H, I)[0])
         for h in range(H):
             y[t, h] = math.fsum(o[h] for o in outs)
+    return y, ids, wts
+
+
+def moe_dbf_ffn(x, logits, expert, H: int, I: int, r: int, k: int, tokens=None):
+    """The routed SwiGLU layer with DBF experts (the DBF post's deployed model:
+    every routed gate, up and down projection is a D_in V D_mid U D_out chain,
+    section 4, evaluated in the deployed order by dbf_chain):
+    y_t = sum_j w_tj * down_e(silu(gate_e(x_t)) * up_e(x_t)), e = id_tj.
+
+    ``expert(e)`` returns three records (gate, up, down), each a tuple
+    (d_in, v_words, d_mid, u_words, d_out); gate and up map H -> I, down
+    I -> H. ``tokens`` restricts the evaluation to those rows (sampled checks).
+    Returns (y fp64 [T, H] (zero rows outside ``tokens``), ids, weights)."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    ids, wts = route_topk(logits, k)
+    y = np.zeros((T, H))
+    cache = {}
+    for t in (range(T) if tokens is None else tokens):
+        for j in range(k):
+            e = int(ids[t, j])
+            if e not in cache:
+                cache[e] = expert(e)
+            g, u, d = cache[e]
+            xt = x[t:t + 1]
+            a = silu(dbf_chain(xt, *g, I, H, r)) * dbf_chain(xt, *u, I, H, r)
+            y[t] += wts[t, j] * dbf_chain(a, *d, H, I, r)[0]
+    return y, ids, wts
+
+
+def moe_dbf_dense(x, logits, expert, H: int, I: int, r: int, k: int):
+    """The same layer through the dense reconstructions D_out U D_mid V D_in of
+    every chain (dbf_dense) and a plain dense SwiGLU."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    ids, wts = route_topk(logits, k)
+    y = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            g, u, d = expert(int(ids[t, j]))
+            Wg, Wu, Wd = dbf_dense(*g, I, H, r), dbf_dense(*u, I, H, r), dbf_dense(*d, H, I, r)
+            y[t] += wts[t, j] * (Wd @ (silu(Wg @ x[t]) * (Wu @ x[t])))
     return y, ids, wts
 
 

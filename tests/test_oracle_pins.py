@@ -401,6 +401,50 @@ def test_moe_matches_definitional_loops():
 # S7 Kronecker rotation
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# MoE with DBF experts (the DBF post's deployed layer)
+# ---------------------------------------------------------------------------
+
+def _dbf_experts(cfg):
+    def rec(e, p):
+        d = cfg.proj(e, p)
+        return (d["d_in"], oracle.pack_sign1_only(d["v"]), d["d_mid"], oracle.pack_sign1_only(d["u"]), d["d_out"])
+
+    return lambda e: (rec(e, 0), rec(e, 1), rec(e, 2))
+
+
+def test_moe_dbf_equals_dense_reconstruction_and_sampling():
+    cfg = datagen.C4D(E=6, H=256, I=128, r=128, top_k=2)
+    x = oracle.bf16_to_f64(cfg.x(3))
+    lg = cfg.logits(3)
+    ex = _dbf_experts(cfg)
+    y, ids, w = oracle.moe_dbf_ffn(x, lg, ex, cfg.H, cfg.I, cfg.r, cfg.top_k)
+    yd, ids2, w2 = oracle.moe_dbf_dense(x, lg, ex, cfg.H, cfg.I, cfg.r, cfg.top_k)
+    assert np.array_equal(ids, ids2)
+    assert np.allclose(y, yd, rtol=1e-11, atol=1e-13 * np.abs(yd).max())
+    ys, _, _ = oracle.moe_dbf_ffn(x, lg, ex, cfg.H, cfg.I, cfg.r, cfg.top_k, tokens=[2, 0])
+    assert np.array_equal(ys[[0, 2]], y[[0, 2]]) and not ys[1].any()
+
+
+def test_moe_dbf_identical_experts_and_single_route_from_raw_matrices():
+    cfg = datagen.C4D(E=5, H=256, I=128, r=128, top_k=3)
+    x = oracle.bf16_to_f64(cfg.x(4))
+    lg = cfg.logits(4)
+    one = _dbf_experts(cfg)(0)
+    y, _, _ = oracle.moe_dbf_ffn(x, lg, lambda e: one, cfg.H, cfg.I, cfg.r, cfg.top_k)
+    # expert 0 built from the raw +-1 arrays and fp16 diagonals (no unpacking)
+    raw = [cfg.proj(0, p) for p in range(3)]
+
+    def chain(d, v):
+        h = d["v"].astype(np.float64) @ (d["d_in"].astype(np.float64) * v)
+        return d["d_out"].astype(np.float64) * (d["u"].astype(np.float64) @ (d["d_mid"].astype(np.float64) * h))
+
+    for t in range(4):
+        g, u = chain(raw[0], x[t]), chain(raw[1], x[t])
+        expect = chain(raw[2], g / (1.0 + np.exp(-g)) * u)
+        assert np.allclose(y[t], expect, rtol=1e-11, atol=1e-13 * np.abs(expect).max())
+
+
 def test_kron_rotate_is_kronecker_product():
     n1, n2, M = 8, 16, 5
     H = datagen.haar_orthogonal((89, 0), n1)
