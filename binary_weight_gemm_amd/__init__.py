@@ -23,7 +23,8 @@ import os
 import torch
 
 __all__ = [
-    "BrqError", "lib", "library_path", "pack", "gemm", "gemm_lr", "dbf_gemm", "moe_ffn", "kron_rotate",
+    "BrqError", "lib", "library_path", "pack", "gemm", "gemm_lr", "dbf_gemm", "moe_ffn", "moe_dbf_ffn",
+    "kron_rotate", "DbfFactors", "moe_dbf_workspace_bytes",
     "gemm_workspace_bytes", "gemm_lr_workspace_bytes", "dbf_workspace_bytes", "moe_workspace_bytes",
     "sign_words", "scale_count",
     "BRQ_BF16", "BRQ_F32", "ABI_FUNCTIONS",
@@ -57,8 +58,16 @@ ABI_FUNCTIONS = {
     "brq_moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "brq_moe_ffn": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int,
                            _vp, _vp, _vp, _sz, _vp]),
+    "brq_moe_dbf_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "brq_moe_dbf_ffn": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _vp, _vp,
+                               _vp, _sz, _vp]),
     "brq_kron_rotate": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
 }
+
+
+class DbfFactors(ctypes.Structure):
+    """brq_dbf_factors: device pointers of one DBF chain record (all experts)."""
+    _fields_ = [("d_in", _vp), ("v", _vp), ("d_mid", _vp), ("u", _vp), ("d_out", _vp)]
 
 
 class BrqError(RuntimeError):
@@ -252,6 +261,51 @@ def moe_ffn(x, logits, gate_s, gate_sc, up_s, up_sc, down_s, down_sc, E: int, H:
                              _dev(ids, "ids", torch.int32) if ids is not None else None,
                              _dev(wts, "w", torch.float32) if wts is not None else None,
                              _dev(ws, "ws"), wsb, _stream()), "brq_moe_ffn")
+    if return_routing:
+        return y, ids, wts
+    return y
+
+
+def moe_dbf_workspace_bytes(T: int, H: int, I: int, E: int, top_k: int, r: int) -> int:
+    return lib().brq_moe_dbf_workspace_bytes(T, H, I, E, top_k, r)
+
+
+def moe_dbf_ffn(x, logits, gate, up, down, E: int, H: int, I: int, r: int, top_k: int,
+                out_dtype=torch.bfloat16, y=None, ws=None, return_routing: bool = False):
+    """brq_moe_dbf_ffn: the routed SwiGLU layer with DBF experts. gate, up, down
+    are (d_in, v, d_mid, u, d_out) tensor tuples for all experts: d_in fp16
+    [E, n], v int64 [E, r, n/64], d_mid fp16 [E, r], u int64 [E, m, r/64],
+    d_out fp16 [E, m], with (m, n) = (I, H) for gate/up and (H, I) for down."""
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != H or logits.shape != (T, E):
+        raise BrqError("x must be [T, H] and logits [T, E]")
+
+    def rec(t, m, n, name):
+        d_in, v, d_mid, u, d_out = t
+        if (d_in.numel() != E * n or v.numel() != E * r * n // 64 or d_mid.numel() != E * r
+                or u.numel() != E * m * r // 64 or d_out.numel() != E * m):
+            raise BrqError(f"{name} record does not match E={E}, m={m}, n={n}, r={r}")
+        return DbfFactors(_dev(d_in, f"{name}.d_in", torch.float16), _dev(v, f"{name}.v", torch.int64),
+                          _dev(d_mid, f"{name}.d_mid", torch.float16), _dev(u, f"{name}.u", torch.int64),
+                          _dev(d_out, f"{name}.d_out", torch.float16))
+
+    g, u_, d = rec(gate, I, H, "gate"), rec(up, I, H, "up"), rec(down, H, I, "down")
+    code = _out_code(out_dtype)
+    if y is None:
+        y = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    ids = wts = None
+    if return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+        wts = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    ws, wsb = _ws(moe_dbf_workspace_bytes(T, H, I, E, top_k, r), x.device, ws)
+    if ws is None:
+        raise BrqError("invalid DBF MoE shape")
+    _check(lib().brq_moe_dbf_ffn(_dev(x, "x", torch.bfloat16), _dev(logits, "logits", torch.float32), T, H, I, E,
+                                 top_k, r, ctypes.byref(g), ctypes.byref(u_), ctypes.byref(d),
+                                 _dev(y, "y", out_dtype), code,
+                                 _dev(ids, "ids", torch.int32) if ids is not None else None,
+                                 _dev(wts, "w", torch.float32) if wts is not None else None,
+                                 _dev(ws, "ws"), wsb, _stream()), "brq_moe_dbf_ffn")
     if return_routing:
         return y, ids, wts
     return y

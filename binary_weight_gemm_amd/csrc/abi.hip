@@ -247,6 +247,50 @@ brq_status brq_moe_ffn(const uint16_t* x, const float* logits, int64_t T, int64_
                     "brq_moe_ffn");
 }
 
+size_t brq_moe_dbf_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t r) {
+  if (T < 1 || T > 256 || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || top_k > E) return 0;
+  if (H < 128 || I < 128 || r < 128 || H % 128 || I % 128 || r % 128 || H > 4096 || I > 2048 || r > 2048) return 0;
+  return brq::moe_dbf_ws_bytes(T, H, I, E, top_k, r);
+}
+
+brq_status brq_moe_dbf_ffn(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I, int64_t E,
+                           int64_t top_k, int64_t r, const brq_dbf_factors* gate, const brq_dbf_factors* up,
+                           const brq_dbf_factors* down, void* y, brq_dtype y_dtype, int32_t* ids, float* w, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!x || !logits || !gate || !up || !down || !y)
+    return fail(BRQ_E_NULL, "brq_moe_dbf_ffn: x, logits, the three records and y must not be NULL");
+  const brq_dbf_factors* recs[3] = {gate, up, down};
+  for (const brq_dbf_factors* f : recs)
+    if (!f->d_in || !f->v || !f->d_mid || !f->u || !f->d_out)
+      return fail(BRQ_E_NULL, "brq_moe_dbf_ffn: every tensor of the gate, up and down records must be set");
+  if (T < 1 || T > 256) return fail(BRQ_E_SHAPE, "brq_moe_dbf_ffn: T=%lld must be in [1, 256]", (long long)T);
+  if (E < 1 || E > 1024) return fail(BRQ_E_SHAPE, "brq_moe_dbf_ffn: E=%lld must be in [1, 1024]", (long long)E);
+  if (top_k < 1 || top_k > 16 || top_k > E)
+    return fail(BRQ_E_SHAPE, "brq_moe_dbf_ffn: top_k=%lld must be in [1, min(E, 16)]", (long long)top_k);
+  if (H < 128 || I < 128 || r < 128 || H % 128 || I % 128 || r % 128 || H > 4096 || I > 2048 || r > 2048)
+    return fail(BRQ_E_SHAPE,
+                "brq_moe_dbf_ffn: H=%lld, I=%lld, r=%lld must be multiples of 128 with H <= 4096, I <= 2048, "
+                "r <= 2048",
+                (long long)H, (long long)I, (long long)r);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_dbf_ffn: unknown y_dtype %d", (int)y_dtype);
+  bool al = aligned(x, 16) && aligned(logits, 4) && aligned(y, 16) && (!ids || aligned(ids, 4)) && (!w || aligned(w, 4));
+  for (const brq_dbf_factors* f : recs)
+    al = al && aligned(f->v, 16) && aligned(f->u, 16) && aligned(f->d_in, 16) && aligned(f->d_mid, 2) &&
+         aligned(f->d_out, 2);
+  if (!al)
+    return fail(BRQ_E_ALIGN, "brq_moe_dbf_ffn: x, y, sign planes and d_in must be 16-byte aligned, diagonals 2-byte");
+  const size_t need = brq::moe_dbf_ws_bytes(T, H, I, E, top_k, r);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(BRQ_E_WORKSPACE, "brq_moe_dbf_ffn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  auto rec = [](const brq_dbf_factors* f) { return brq::DbfFactors{f->d_in, f->v, f->d_mid, f->u, f->d_out}; };
+  return hip_result(brq::launch_moe_dbf(x, logits, (int)T, (int)H, (int)I, (int)E, (int)top_k, (int)r, rec(gate),
+                                        rec(up), rec(down), y, y_dtype == BRQ_BF16, ids, w, ws, (hipStream_t)stream),
+                    "brq_moe_dbf_ffn");
+}
+
 brq_status brq_kron_rotate(const uint16_t* x, int64_t M, const float* H, int64_t n1, const float* R, int64_t n2,
                            uint16_t* y, void* stream) {
   if (!x || !H || !R || !y) return fail(BRQ_E_NULL, "brq_kron_rotate: x, H, R and y must not be NULL");

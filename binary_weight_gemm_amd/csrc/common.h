@@ -100,6 +100,18 @@ __device__ __forceinline__ void split_f16(float v, uint16_t& hi, uint16_t& lo) {
   lo = __builtin_bit_cast(uint16_t, (_Float16)r);
 }
 
+// Largest value of the wave, returned to every lane (uniform): quad swaps,
+// half-row and row mirrors, then the row broadcasts carry it to lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ void store_out(void* y, size_t idx, float v, int out_bf16) {
   if (out_bf16)
     reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16_bits(v);

@@ -157,16 +157,6 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int F4_CHUNK = 4 * 2 * 128;  // LDS bytes of one chunk: 4 groups x 2 pieces x 128
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // (group, word) transpose across the four 16-lane rows: on entry register w
 // of row g holds word w of group g; on exit register i of row b holds word b
 // of group i.

@@ -195,6 +195,79 @@ struct WaveStage {
   }
 };
 
+// Per-wave staging of fp32 rows (intermediate vectors of a chain) as scaled
+// fp16 pieces. Row m of the wave's slice becomes LDS rows 2m (hi) and 2m+1
+// (lo) of u = v * 2^s[m]: hi = fp16(u), lo = fp16(u - hi). s[m] (uniform over
+// the wave) puts the largest magnitude of the slice in [2^14, 2^15), so every
+// value down to 2^-18 of that maximum keeps about 22 significant bits and the
+// pieces never overflow, whatever the row's magnitude (an unscaled fp16 pair
+// keeps fewer bits for every |v| < 2^-3, where lo is subnormal). A product of
+// the two rows, added and scaled by 2^-s[m] (exact), is the product of the
+// fp32 row to that precision. Slot (chunk c, piece row p) is xs + (c*2*MAXR +
+// p)*64 (uint4 units) in the permuted order; loads are clamped as in
+// WaveStage, so clamped chunks only enter the maximum with values of the row.
+template <int CPW, int MAXR>
+struct WaveStageF32 {
+  f32x4 a[CPW][MAXR], b[CPW][MAXR];  // ext vectors: HIP float4 copies defeat SROA
+  int us[2];  // -s of the rows 2kb and 2kb+1 (lane l = 16kb + j), the MFMA
+              // output rows 4kb .. 4kb+3 of this lane being their pieces
+
+  template <class ROWPTR>
+  __device__ __forceinline__ void load(int rows, int K, int c0, ROWPTR&& rowptr) {
+    const int lane = threadIdx.x & 63;
+    const int run = lane >> 2, b0 = (lane & 3) * 4;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int m = 0; m < MAXR; ++m) {
+        const int kr = (c0 + c) * 512 + 32 * run;
+        const int kc = kr < K ? kr : 0;
+        const float* src = rowptr(m < rows ? m : rows - 1) + kc;
+        a[c][m] = *reinterpret_cast<const f32x4*>(src + b0);
+        b[c][m] = *reinterpret_cast<const f32x4*>(src + 16 + b0);
+      }
+  }
+
+  __device__ __forceinline__ void store(uint4* xs) {
+    const int lane = threadIdx.x & 63;
+    const int run = lane >> 2, kb = lane >> 4;
+    us[0] = us[1] = 0;
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        #pragma unroll
+        for (int t = 0; t < 4; ++t)
+          mx = max(mx, max(__float_as_uint(a[c][m][t]) & 0x7fffffffu, __float_as_uint(b[c][m][t]) & 0x7fffffffu));
+      }
+      mx = wave_max_u32(mx);
+      const int sm = 14 - ((int)(mx >> 23) - 127);  // 0 -> s = 141, harmless: every value is 0
+      // selected from scalars, not from an indexed array (which would go to scratch)
+      us[0] = (2 * kb == m) ? -sm : us[0];
+      us[1] = (2 * kb + 1 == m) ? -sm : us[1];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        uint32_t oh[4], ol[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint16_t ha, la, hb, lb;
+          split_f16(__builtin_amdgcn_ldexpf(a[c][m][t], sm), ha, la);
+          split_f16(__builtin_amdgcn_ldexpf(b[c][m][t], sm), hb, lb);
+          oh[t] = (uint32_t)ha | ((uint32_t)hb << 16);
+          ol[t] = (uint32_t)la | ((uint32_t)lb << 16);
+        }
+        uint4* d = xs + (size_t)(c * 2 * MAXR + 2 * m) * 64 + run * 4 + (lane & 3);
+        d[0] = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+        d[64] = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+      }
+    }
+  }
+
+  // exponent that scales this lane's MFMA output row 4kb + i back
+  __device__ __forceinline__ int unscale(int i) const { return us[i >> 1]; }
+};
+
 // Stage `rows` activation rows of K values in LDS as permuted fp16, row r at
 // xs + r * (K/8) (uint4 units). MODE as below. rowptr(r) returns the global
 // start of source row r.

@@ -65,6 +65,18 @@ size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
 
 // ---- routed MoE ------------------------------------------------------------
 size_t moe_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);
+// The layer with DBF experts (one record of five tensors per projection).
+struct DbfFactors {
+  const uint16_t* d_in;
+  const uint64_t* v;
+  const uint16_t* d_mid;
+  const uint64_t* u;
+  const uint16_t* d_out;
+};
+size_t moe_dbf_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t r);
+hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, int I, int E, int top_k, int r,
+                          const DbfFactors& gate, const DbfFactors& up, const DbfFactors& down, void* y,
+                          int y_bf16, int32_t* ids, float* w, void* ws, hipStream_t st);
 hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int I, int E,
                       int top_k, const uint64_t* gate_s, const uint16_t* gate_sc,
                       const uint64_t* up_s, const uint16_t* up_sc, const uint64_t* down_s,

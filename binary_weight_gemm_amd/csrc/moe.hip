@@ -715,4 +715,242 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
   return hipGetLastError();
 }
 
+// ===========================================================================
+// MoE layer with DBF experts: every routed gate, up and down projection is a
+// chain y = D_out U D_mid V D_in x ("LLM binarization, Episode 01: DBF",
+// section 4). After top-k and route (as above) four grouped launches run the
+// chains, one workgroup per (CB blocks of 16 output columns, active expert),
+// waves splitting the reduction axis:
+//  stage 0: gate and up V factors on the expert's token rows (the hidden
+//           vector shared by the token's experts), D_in folded into the weight
+//           operand (+-d_in[k]), D_mid in the epilogue -> h_s (fp32 rows)
+//  stage 1: gate and up U factors on the route's own h_s rows (+-1 operands),
+//           D_out, SwiGLU -> the intermediate a (fp32 rows)
+//  stage 2: down V factor on a (+-d_in), D_mid -> h_s (reusing stage 0's buffer)
+//  stage 3: down U factor on h_s (+-1), D_out -> the route's fp32 output
+// and the combine launch sums the slots in slot order. Stages 1-3 read their
+// fp32 input rows as scaled fp16 hi/lo pieces (WaveStageF32): two MFMA rows
+// per route, added and scaled back per wave before the waves' partials meet.
+// ===========================================================================
+
+struct DbfStageArgs {
+  const uint4* sig[2];     // sign rows of the stage's matrices (all experts)
+  const uint16_t* din[2];  // D_in of the matrices (V stages)
+  const uint16_t* dg[2];   // epilogue diagonal: D_mid (V stages) or D_out (U stages)
+  const float* in[2];      // fp32 input rows (stages 1-3): [R][K]
+  float* out;              // fp32 output rows (stages 0 and 2): [R][N] per matrix
+};
+
+template <int STAGE, int CPW, int SR, int CB>
+__global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x, int H, int I, int r, int R,
+                                                 DbfStageArgs a, MoeWs ws) {
+  constexpr int NMAT = STAGE < 2 ? 2 : 1;
+  constexpr bool PERK = STAGE == 0 || STAGE == 2;  // D_in rides on the weight operand
+  constexpr bool PIECES = STAGE != 0;              // inputs are fp32 rows, staged as two piece rows per route
+  constexpr int NIN = STAGE == 1 ? 2 : 1;          // separate input rows per matrix (stage 1)
+  constexpr int RT = PIECES ? SR / 2 : SR;         // routes per tile
+  constexpr int BMODE = PERK ? BM_PERK : BM_ONE;
+  extern __shared__ uint4 smem[];
+  const int4 bk = ws.blk[blockIdx.y];
+  const int e = bk.x, r0 = bk.y, cnt = bk.z;
+  if (cnt == 0) return;  // past the last active expert
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15;
+  const int K = STAGE == 0 ? H : STAGE == 2 ? I : r;  // reduction axis
+  const int N = STAGE == 1 ? I : STAGE == 3 ? H : r;  // outputs (rows of the stage's matrices)
+  const int G = K >> 7, nchunks = (G + 3) >> 2;
+  const int c0 = wave * CPW;
+  // LDS: D_in slices of every wave first (kept across tiles), then the input
+  // rows of every wave (overwritten per tile), the wave partials alias them
+  uint4* dw = smem + (size_t)wave * NMAT * CPW * 64;
+  uint4* stage_base = smem + (PERK ? (size_t)nw * NMAT * CPW * 64 : 0);
+  uint4* xw = stage_base + (size_t)wave * NIN * CPW * SR * 64;
+
+  // every block's sign words (and D_in) in flight before any wait
+  BPre<1, CPW> bp[NMAT][CB];
+#pragma unroll
+  for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = (blockIdx.x * CB + cb) * 16 + j;
+      const uint4* wsig[1] = {a.sig[q] + ((size_t)e * N + (col < N ? col : 0)) * G};
+      const uint16_t* wsc[1] = {nullptr};
+      const bool rok[1] = {col < N};
+      b_prefetch<BMODE, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp[q][cb]);
+    }
+  if constexpr (PERK) {
+    if (c0 < nchunks) {
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q) {
+        WaveStage<ST_F16, CPW, 1> sd;
+        sd.load(1, K, c0, [&](int) { return a.din[q] + (size_t)e * K; });
+        sd.store(dw + q * CPW * 64);
+      }
+    }
+  }
+
+  // one tile of up to RT routes; the first is peeled off the loop so that its
+  // input loads issue while the sign words are still in flight
+  auto run_tile = [&](const int tb) {
+    const int routes = (cnt - tb) < RT ? (cnt - tb) : RT;
+    const int rows = PIECES ? 2 * routes : routes;
+    f32x4 acc[CB][NMAT][1];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q) acc[cb][q][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    WaveStageF32<CPW, RT> sf0, sf1;  // the two inputs of stage 1 (gate, up); sf0 elsewhere
+    if (c0 < nchunks) {
+      if constexpr (PIECES) {
+        sf0.load(routes, K, c0, [&](int m) { return a.in[0] + (size_t)(r0 + tb + m) * K; });
+        if constexpr (NIN == 2) sf1.load(routes, K, c0, [&](int m) { return a.in[1] + (size_t)(r0 + tb + m) * K; });
+        sf0.store(xw);
+        if constexpr (NIN == 2) sf1.store(xw + CPW * SR * 64);
+      } else {
+        WaveStage<ST_BF16, CPW, SR> sx;
+        sx.load(rows, K, c0, [&](int rr) { return x + (size_t)ws.route_tok[r0 + tb + rr] * H; });
+        sx.store(xw);
+      }
+    }
+    __syncthreads();
+    if (c0 < nchunks) {
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q) {
+        const u32x4* xs = reinterpret_cast<const u32x4*>(xw + (NIN == 2 ? q : 0) * CPW * SR * 64);
+        auto aop = [&](int, int g, int i) -> u32x4 {
+          const int m = min(j, rows - 1);
+          return xs[(((g >> 2) - c0) * SR + m) * 64 + (g & 3) * 16 + i];
+        };
+        const u32x4* kp = PERK ? reinterpret_cast<const u32x4*>(dw + q * CPW * 64) - (size_t)c0 * 64 : nullptr;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          pin_signs(bp[q][cb]);
+          f32x4 t[1][1] = {{acc[cb][q][0]}};
+          b_compute<BMODE, 1, 1, CPW>(bp[q][cb], kp, G, c0, 1, aop, t);
+          acc[cb][q][0] = t[0][0];
+        }
+        if constexpr (PIECES) {
+          // back from the wave's scaled pieces (exact powers of two)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int us = (NIN == 2 && q == 1) ? sf1.unscale(i) : sf0.unscale(i);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[cb][q][0][i] = __builtin_amdgcn_ldexpf(acc[cb][q][0][i], us);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    reduce_waves_cb<CB, NMAT>(acc, reinterpret_cast<f32x4*>(stage_base));
+    if (wave == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int col = (blockIdx.x * CB + cb) * 16 + j;
+        if (col >= N) continue;
+        if constexpr (STAGE == 0) {
+          // rows are routes: lane (kb, j) holds routes 4kb + i of column col
+#pragma unroll
+          for (int q = 0; q < NMAT; ++q) {
+            const float dm = f16_bits_to_f32(a.dg[q][(size_t)e * N + col]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int p = 4 * (lane >> 4) + i;
+              if (p < routes) a.out[(size_t)q * R * r + (size_t)(r0 + tb + p) * r + col] = acc[cb][q][0][i] * dm;
+            }
+          }
+        } else {
+          // rows are pieces: route 2kb + h is rows 4kb + 2h (hi) and + 1 (lo)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int p = 2 * (lane >> 4) + h;
+            if (p >= routes) continue;
+            const size_t route = (size_t)(r0 + tb + p);
+            const float v0 = (acc[cb][0][0][2 * h] + acc[cb][0][0][2 * h + 1]) *
+                             f16_bits_to_f32(a.dg[0][(size_t)e * N + col]);
+            if constexpr (STAGE == 1) {
+              const float u = (acc[cb][NMAT - 1][0][2 * h] + acc[cb][NMAT - 1][0][2 * h + 1]) *
+                              f16_bits_to_f32(a.dg[1][(size_t)e * N + col]);
+              reinterpret_cast<float*>(ws.ap)[route * I + col] = v0 / (1.0f + expf(-v0)) * u;
+            } else if constexpr (STAGE == 2) {
+              a.out[route * r + col] = v0;
+            } else {
+              ws.o[route * H + col] = v0;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  };
+  run_tile(0);  // an active expert has at least one route
+  for (int tb = RT; tb < cnt; tb += RT) run_tile(tb);
+}
+
+size_t moe_dbf_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t r) {
+  return moe_ws_bytes(T, H, I, E, k) + align256((size_t)2 * T * k * r * 4);  // h_s: fp32 [2][T*k][r]
+}
+
+template <int STAGE, int SR>
+static hipError_t moe_dbf_stage(const uint16_t* x, int H, int I, int r, int R, int maxact, const DbfStageArgs& a,
+                                const MoeWs& ws, hipStream_t st) {
+  const int K = STAGE == 0 ? H : STAGE == 2 ? I : r;
+  const int N = STAGE == 1 ? I : STAGE == 3 ? H : r;
+  constexpr int NMAT = STAGE < 2 ? 2 : 1;
+  constexpr int NIN = STAGE == 1 ? 2 : 1;
+  constexpr bool PERK = STAGE == 0 || STAGE == 2;
+  const DecSplit sp = dec_split(K / 128, 8);
+  const size_t din = PERK ? (size_t)sp.waves * NMAT * sp.cpw * 1024 : 0;
+  const size_t stg = (size_t)sp.waves * NIN * sp.cpw * SR * 1024;
+  BRQ_CPW_SWITCH(sp.cpw, {
+    constexpr int CB = moe_cb_gu(CPW);
+    const size_t red = (size_t)(sp.waves - 1) * CB * NMAT * 1024;
+    const size_t lds = din + (stg > red ? stg : red);
+    const dim3 grid((unsigned)((N + 16 * CB - 1) / (16 * CB)), (unsigned)maxact);
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_moe_dbf<STAGE, CPW, SR, CB>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_moe_dbf<STAGE, CPW, SR, CB>), grid, dim3(64 * sp.waves), lds, st, x, H, I, r, R, a, ws);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, int I, int E, int top_k, int r,
+                          const DbfFactors& gate, const DbfFactors& up, const DbfFactors& down, void* y, int y_bf16,
+                          int32_t* ids, float* w, void* ws_ptr, hipStream_t st) {
+  MoeWs ws = moe_carve(ws_ptr, T, H, I, E, top_k);
+  float* hbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(ws_ptr) + moe_ws_bytes(T, H, I, E, top_k));
+  const int R = T * top_k;
+  const int maxact = R < E ? R : E;
+  hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, T, E, top_k, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  auto u4 = [](const uint64_t* p) { return reinterpret_cast<const uint4*>(p); };
+  // token tiles of 4 when experts expect at most 3 routes, as in the group-128 layer
+  const bool small = (int64_t)R <= 3 * (int64_t)E;
+  DbfStageArgs a0{{u4(gate.v), u4(up.v)}, {gate.d_in, up.d_in}, {gate.d_mid, up.d_mid}, {nullptr, nullptr}, hbuf};
+  DbfStageArgs a1{{u4(gate.u), u4(up.u)}, {nullptr, nullptr}, {gate.d_out, up.d_out},
+                  {hbuf, hbuf + (size_t)R * r}, nullptr};
+  DbfStageArgs a2{{u4(down.v), nullptr}, {down.d_in, nullptr}, {down.d_mid, nullptr},
+                  {reinterpret_cast<const float*>(ws.ap), nullptr}, hbuf};
+  DbfStageArgs a3{{u4(down.u), nullptr}, {nullptr, nullptr}, {down.d_out, nullptr}, {hbuf, nullptr}, nullptr};
+  if (small) {
+    err = moe_dbf_stage<0, 4>(x, H, I, r, R, maxact, a0, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<1, 8>(x, H, I, r, R, maxact, a1, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<2, 8>(x, H, I, r, R, maxact, a2, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<3, 8>(x, H, I, r, R, maxact, a3, ws, st);
+  } else {
+    err = moe_dbf_stage<0, 16>(x, H, I, r, R, maxact, a0, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<1, 16>(x, H, I, r, R, maxact, a1, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<2, 16>(x, H, I, r, R, maxact, a2, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<3, 16>(x, H, I, r, R, maxact, a3, ws, st);
+  }
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * H + 255) / 256)), dim3(256), 0, st, T, H, top_k,
+                     ws, y, y_bf16);
+  return hipGetLastError();
+}
+
 }  // namespace brq

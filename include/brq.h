@@ -201,6 +201,48 @@ brq_status brq_moe_ffn(const uint16_t* x, const float* logits,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One DBF chain record (the five tensors of a routed expert projection,
+ * "LLM binarization, Episode 01: DBF", section 4): for E experts of an m x n
+ * projection with inner dimension r,
+ *   d_in  fp16 [E][n];  v  SIGN1 [E][r][n/64];  d_mid fp16 [E][r];
+ *   u     SIGN1 [E][m][r/64];  d_out fp16 [E][m].
+ */
+typedef struct {
+  const uint16_t* d_in;
+  const uint64_t* v;
+  const uint16_t* d_mid;
+  const uint64_t* u;
+  const uint16_t* d_out;
+} brq_dbf_factors;
+
+/*
+ * brq_moe_dbf_ffn -- the routed SwiGLU layer of brq_moe_ffn with every routed
+ * gate, up and down projection a DBF chain y = D_out U D_mid V D_in x, each
+ * evaluated in the deployed order (DBF post, section 4: the deployed model
+ * converts its routed experts to DBDBD with r = 1024 on 512 x 2048 gate/up and
+ * 2048 x 512 down). Routing as in brq_moe_ffn. gate/up first factors consume
+ * the token's hidden vector shared by its experts; second factors and the down
+ * chain consume the route's own intermediates (section 4's two input
+ * topologies). Intermediates are carried as fp16 hi/lo pairs.
+ *
+ *   x, logits, T, E, top_k, y, ids, w   as for brq_moe_ffn
+ *   gate, up   host pointers to records of H -> I chains (m = I, n = H)
+ *   down       host pointer to a record of an I -> H chain (m = H, n = I)
+ *   ws       device workspace, >= brq_moe_dbf_workspace_bytes(T, H, I, E, top_k, r)
+ *   H, I, r multiples of 128 with H <= 4096, I <= 2048, r <= 2048; T, E, top_k
+ *   as for brq_moe_ffn. x, y, the sign planes and d_in 16-byte aligned, d_mid
+ *   and d_out 2-byte aligned.
+ */
+size_t brq_moe_dbf_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t r);
+brq_status brq_moe_dbf_ffn(const uint16_t* x, const float* logits,
+                           int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t r,
+                           const brq_dbf_factors* gate, const brq_dbf_factors* up,
+                           const brq_dbf_factors* down,
+                           void* y, brq_dtype y_dtype,
+                           int32_t* ids, float* w,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * brq_kron_rotate -- Kronecker-factored orthogonal activation rotation
  *   x'_t = (H (x) R) x_t, computed as X'_t = H . X_t . R^T where X_t is row t
  *   of x reshaped row-major to [n1][n2]

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(brq.ABI_FUNCTIONS)
@@ -107,6 +107,36 @@ def test_gemm_lr_validation(L):
     # many rows: padded V + padded U (N x 64 fp16) + x V^T hi/lo (M x 128 fp16) + staged activations
     M, N, K = 4096, 14336, 4096
     assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == 64 * K * 2 + N * 128 + M * 256 + M * K * 2
+
+
+def test_moe_dbf_validation(L):
+    f = L.brq_moe_dbf_ffn
+    rec = brq.DbfFactors(P, P, P, P, P)
+    bad = brq.DbfFactors(P, None, P, P, P)
+    mis = brq.DbfFactors(P, PMIS, P, P, P)
+    R = ctypes.byref
+    ok = [P, P, 4, 2048, 512, 256, 8, 1024, R(rec), R(rec), R(rec), P, 0, None, None, P, 1 << 30, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == E_NULL
+    assert call(a9=R(bad)) == E_NULL                     # a missing tensor in the up record
+    assert "record" in _err(L)
+    assert call(a2=0) == E_SHAPE                          # T
+    assert call(a7=100) == E_SHAPE                        # r % 128
+    assert call(a3=8192) == E_SHAPE                       # H past 4096
+    assert call(a7=4096) == E_SHAPE                       # r past 2048
+    assert call(a6=300) == E_SHAPE                        # top_k past min(E, 16)
+    assert call(a12=9) == E_DTYPE
+    assert call(a10=R(mis)) == E_ALIGN
+    assert call(a15=None) == E_WORKSPACE
+    assert L.brq_moe_dbf_workspace_bytes(4, 2048, 512, 256, 8, 1024) == (
+        L.brq_moe_workspace_bytes(4, 2048, 512, 256, 8) + 2 * 2 * 4 * 8 * 1024 * 2)
+    assert L.brq_moe_dbf_workspace_bytes(4, 2048, 512, 256, 8, 100) == 0
 
 
 def test_dbf_validation(L):

@@ -408,6 +408,92 @@ def test_moe_c4_bf16_and_fresh_logits(c4_experts):
         check_bf16(y, o, f"moe bf16 it={it}")
 
 
+# ---------------------------------------------------------------------------
+# MoE with DBF experts (the DBF post's deployed layer): every projection a
+# D_in V D_mid U D_out chain
+# ---------------------------------------------------------------------------
+
+def _dbf_moe_dev(cfg, experts):
+    """Device records [E, ...] per projection: the configuration's factors for
+    `experts`, zeros for the others (never selected by the logits used)."""
+    E, H, I, r = cfg.E, cfg.H, cfg.I, cfg.r
+    recs = []
+    for p, (m, n) in enumerate(((I, H), (I, H), (H, I))):
+        d_in = np.zeros((E, n), np.float16)
+        v = np.zeros((E, r, n // 64), np.uint64)
+        d_mid = np.zeros((E, r), np.float16)
+        u = np.zeros((E, m, r // 64), np.uint64)
+        d_out = np.zeros((E, m), np.float16)
+        for e in experts:
+            d = cfg.proj(e, p)
+            d_in[e], d_mid[e], d_out[e] = d["d_in"], d["d_mid"], d["d_out"]
+            v[e] = oracle.pack_sign1_only(d["v"]).reshape(r, n // 64)
+            u[e] = oracle.pack_sign1_only(d["u"]).reshape(m, r // 64)
+        recs.append(tuple(dev(a) for a in (d_in, v, d_mid, u, d_out)))
+    return recs
+
+
+def _dbf_moe_oracle_experts(cfg):
+    def rec(e, p):
+        d = cfg.proj(e, p)
+        return (d["d_in"], oracle.pack_sign1_only(d["v"]), d["d_mid"], oracle.pack_sign1_only(d["u"]), d["d_out"])
+
+    cache = {}
+
+    def ex(e):
+        if e not in cache:
+            cache[e] = (rec(e, 0), rec(e, 1), rec(e, 2))
+        return cache[e]
+
+    return ex
+
+
+def _dbf_moe_case(cfg, T, out=torch.float32, it=0):
+    x = cfg.x(T)
+    lg = cfg.logits(T, it)
+    ids_o, _ = oracle.route_topk(lg, cfg.top_k)
+    recs = _dbf_moe_dev(cfg, sorted(set(int(e) for e in ids_o.ravel())))
+    o, oids, ow = oracle.moe_dbf_ffn(oracle.bf16_to_f64(x), lg, _dbf_moe_oracle_experts(cfg), cfg.H, cfg.I, cfg.r,
+                                     cfg.top_k)
+    y, ids, w = brq().moe_dbf_ffn(dev(x), dev(lg), *recs, cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k, out_dtype=out,
+                                  return_routing=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids), "top-k ids differ"
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=1e-7)
+    return y, o
+
+
+# small experts: T = 1 and 5 take 4-token tiles, T = 64 (16 routes per expert)
+# 16-token tiles and several tiles per expert; odd sizes with ragged blocks
+@pytest.mark.parametrize("T,E,H,I,r,k", [(1, 16, 256, 128, 128, 4), (5, 16, 256, 128, 128, 4),
+                                         (64, 16, 256, 128, 128, 4), (7, 8, 384, 256, 256, 3)])
+def test_moe_dbf_small(T, E, H, I, r, k):
+    say("moe dbf", T, E, H, I, r, k)
+    cfg = datagen.C4D(E=E, H=H, I=I, r=r, top_k=k, layer=1)
+    y, o = _dbf_moe_case(cfg, T)
+    check_f32(f64(y), o, F32_TOL, f"moe dbf T={T}")
+
+
+def test_moe_dbf_deployed_shape():
+    # the deployed layer (256 experts, top-8, gate/up 512x2048, down 2048x512,
+    # r = 1024) at T = 4: every selected expert built, fp32 and bf16 outputs
+    say("moe dbf deployed shape T=4")
+    cfg = datagen.C4D()
+    T = 4
+    x, lg = cfg.x(T), cfg.logits(T)
+    ids_o, _ = oracle.route_topk(lg, cfg.top_k)
+    recs = _dbf_moe_dev(cfg, sorted(set(int(e) for e in ids_o.ravel())))
+    o, _, _ = oracle.moe_dbf_ffn(oracle.bf16_to_f64(x), lg, _dbf_moe_oracle_experts(cfg), cfg.H, cfg.I, cfg.r,
+                                 cfg.top_k)
+    for out in (torch.float32, torch.bfloat16):
+        y = brq().moe_dbf_ffn(dev(x), dev(lg), *recs, cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k, out_dtype=out)
+        torch.cuda.synchronize()
+        if out == torch.float32:
+            check_f32(f64(y), o, F32_TOL, "moe dbf deployed")
+        else:
+            check_bf16(y, o, "moe dbf deployed bf16")
+
+
 def test_moe_ties_and_small_shapes():
     say("moe ties, E=8 H=256 I=128 k=3")
     cfg = datagen.C4(E=8, H=256, I=128, top_k=3, layer=5)
