@@ -6,10 +6,12 @@
 //
 // Stage 1 folds D_in into the weight operand: V[j][k] * d_in[k] is the exact
 // fp16 value +-d_in[k], so the first product reads x unscaled. Its epilogue
-// applies D_mid in fp32 and stores h_s as an fp16 hi/lo pair (22 significant
-// bits) in the permuted operand order. Stage 2 multiplies U (+-1 operands) by
-// both pieces (two activation rows per token), adds the pieces and applies
-// D_out in fp32.
+// applies D_mid in fp32 and stores h_s as fp32 rows. Stage 2 multiplies U
+// (+-1 operands) by h_s split into two fp16 pieces of h_s * 2^s (hi, lo: two
+// activation rows per token), adds the pieces, undoes the power of two and
+// applies D_out in fp32. The scale 2^s puts the largest |h_s| of the staged
+// slice (decode: per wave; tiled: per row, set by k_dbf_split) near 2^14, so
+// the pieces keep about 22 significant bits whatever the magnitude of D_mid.
 #include "dec_core.h"
 #include "kernels.h"
 #include "tile.h"
@@ -22,7 +24,7 @@ namespace brq {
 template <int TT, int CPW, int MAXR>
 __global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ x, int M, int r, int n,
                                                    const uint4* __restrict__ v, const uint16_t* __restrict__ d_in,
-                                                   const uint16_t* __restrict__ d_mid, uint16_t* __restrict__ hp) {
+                                                   const uint16_t* __restrict__ d_mid, float* __restrict__ hs) {
   extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
@@ -64,28 +66,23 @@ __global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ 
   reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
   if (wave != 0 || col >= r) return;
   const float dm = f16_bits_to_f32(d_mid[col]);
-  const int pc = perm_pos(col);
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * tt + 4 * (lane >> 4) + i;
-      if (m < M) {
-        uint16_t hi, lo;
-        split_f16(acc[0][tt][i] * dm, hi, lo);
-        hp[(size_t)(2 * m) * r + pc] = hi;
-        hp[(size_t)(2 * m + 1) * r + pc] = lo;
-      }
+      if (m < M) hs[(size_t)m * r + col] = acc[0][tt][i] * dm;
     }
 }
 
-// Decode path, stage 2: the two fp16 pieces of every h_s row are staged in LDS
-// (two A rows per token, per-wave slices); U operands are +-1; D_out in the
-// epilogue.
+// Decode path, stage 2: every h_s row is staged in LDS as two scaled fp16
+// pieces (two A rows per token, per-wave slices, WaveStageF32); U operands are
+// +-1; each wave scales its partials back; D_out in the epilogue.
 template <int TT, int CPW, int MAXR>
-__global__ __launch_bounds__(1024) void k_dbf2_dec(const uint16_t* __restrict__ hp, int M, int m, int r,
+__global__ __launch_bounds__(1024) void k_dbf2_dec(const float* __restrict__ hs, int M, int m, int r,
                                                    const uint4* __restrict__ u, const uint16_t* __restrict__ d_out,
                                                    void* __restrict__ y, int y_bf16) {
+  static_assert(TT == 1, "one tile of piece rows (up to 8 tokens)");
   extern __shared__ uint4 smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15;
@@ -102,9 +99,9 @@ __global__ __launch_bounds__(1024) void k_dbf2_dec(const uint16_t* __restrict__ 
   f32x4 acc[1][TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  WaveStageF32<CPW, MAXR / 2> sh;
   if (c0 < nchunks) {
-    WaveStage<ST_COPY, CPW, MAXR> sh;
-    sh.load(rows, r, c0, [&](int pr) { return hp + (size_t)pr * r; });
+    sh.load(M, r, c0, [&](int t) { return hs + (size_t)t * r; });
     b_prefetch<BM_ONE, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp);
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
     sh.store(xw);
@@ -117,6 +114,8 @@ __global__ __launch_bounds__(1024) void k_dbf2_dec(const uint16_t* __restrict__ 
       return xs[(((g >> 2) - c0) * MAXR + pr) * 64 + (g & 3) * 16 + i];
     };
     b_compute<BM_ONE, 1, TT, CPW>(bp, nullptr, G, c0, 1, aop, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], sh.unscale(i));
   }
   __syncthreads();
   reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));
@@ -149,17 +148,60 @@ static bool dbf_decode_path(int64_t M, int64_t n, int64_t r) {
   return M <= 8 && dbf_split(dbf_maxr(M) + 1, n, a) && dbf_split(2 * dbf_maxr(M), r, b);
 }
 
+// Tiled path, between the stages: one workgroup per h_s row finds the row's
+// largest magnitude, writes the row as fp16 pieces of h_s * 2^s (rows 2t and
+// 2t+1, permuted operand order) with the largest near 2^14, and records -s.
+__global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs, int r, uint16_t* __restrict__ hp,
+                                                   int* __restrict__ rexp) {
+  __shared__ uint32_t s_max[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* row = hs + (size_t)t * r;
+  const int quads = r >> 3;  // 8 values (4 permuted pairs) per quad
+  uint32_t mx = 0;
+  for (int q = tid; q < quads; q += 256) {
+    const int k = 32 * (q >> 2) + 4 * (q & 3);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k), b = *reinterpret_cast<const f32x4*>(row + k + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mx = max(mx, max(__float_as_uint(a[i]) & 0x7fffffffu, __float_as_uint(b[i]) & 0x7fffffffu));
+  }
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+  __syncthreads();
+  mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const int s = 14 - ((int)(mx >> 23) - 127);  // 0 -> s = 141, harmless: every value is 0
+  if (tid == 0) rexp[t] = -s;
+  for (int q = tid; q < quads; q += 256) {
+    const int k = 32 * (q >> 2) + 4 * (q & 3);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k), b = *reinterpret_cast<const f32x4*>(row + k + 16);
+    uint32_t oh[4], ol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t ha, la, hb, lb;
+      split_f16(__builtin_amdgcn_ldexpf(a[i], s), ha, la);
+      split_f16(__builtin_amdgcn_ldexpf(b[i], s), hb, lb);
+      oh[i] = (uint32_t)ha | ((uint32_t)hb << 16);
+      ol[i] = (uint32_t)la | ((uint32_t)lb << 16);
+    }
+    // pairs (k+i, k+16+i) are words 4(q&3)+i of run q>>2: 8 fp16 from 8*q
+    *reinterpret_cast<uint4*>(hp + (size_t)(2 * t) * r + 8 * q) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+    *reinterpret_cast<uint4*>(hp + (size_t)(2 * t + 1) * r + 8 * q) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  }
+}
+
+// workspace: h_s fp32 [M][r]; tiled path also the pieces [2M][r], the row
+// exponents [M] and the permuted d_in [n]
 size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
   (void)m;
-  const size_t hp = align256((size_t)2 * M * r * 2);
-  if (dbf_decode_path(M, n, r)) return hp;
-  return hp + align256((size_t)n * 2);
+  const size_t hs = align256((size_t)M * r * 4);
+  if (dbf_decode_path(M, n, r)) return hs;
+  return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4) + align256((size_t)n * 2);
 }
 
 template <int MAXR1, int MAXR2>
 static hipError_t dbf_decode(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
                              const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
-                             uint16_t* hp, hipStream_t st) {
+                             float* hs, hipStream_t st) {
   DecSplit s1, s2;
   dbf_split(MAXR1 + 1, n, s1);
   dbf_split(MAXR2, r, s2);
@@ -168,11 +210,11 @@ static hipError_t dbf_decode(const uint16_t* x, int M, int m, int n, int r, cons
   const uint4* v4 = reinterpret_cast<const uint4*>(v);
   const uint4* u4 = reinterpret_cast<const uint4*>(u);
   BRQ_CPW_SWITCH(s1.cpw, hipLaunchKernelGGL((k_dbf1_dec<1, CPW, MAXR1>), dim3((r + 15) / 16), dim3(64 * s1.waves),
-                                            l1 > r1 ? l1 : r1, st, x, M, r, n, v4, d_in, d_mid, hp));
+                                            l1 > r1 ? l1 : r1, st, x, M, r, n, v4, d_in, d_mid, hs));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   BRQ_CPW_SWITCH(s2.cpw, hipLaunchKernelGGL((k_dbf2_dec<1, CPW, MAXR2>), dim3((m + 15) / 16), dim3(64 * s2.waves),
-                                            l2 > r2 ? l2 : r2, st, hp, M, m, r, u4, d_out, y, y_bf16));
+                                            l2 > r2 ? l2 : r2, st, hs, M, m, r, u4, d_out, y, y_bf16));
   return hipGetLastError();
 }
 
@@ -180,21 +222,30 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
                       const uint64_t* v, const uint16_t* d_mid, const uint64_t* u,
                       const uint16_t* d_out, void* y, int y_bf16, void* ws, hipStream_t st) {
   char* base = reinterpret_cast<char*>(ws);
-  uint16_t* hp = reinterpret_cast<uint16_t*>(base);
+  float* hs = reinterpret_cast<float*>(base);
   if (dbf_decode_path(M, n, r)) {
-    if (M == 1) return dbf_decode<1, 2>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hp, st);
-    if (M <= 4) return dbf_decode<4, 8>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hp, st);
-    return dbf_decode<8, 16>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hp, st);
+    if (M == 1) return dbf_decode<1, 2>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hs, st);
+    if (M <= 4) return dbf_decode<4, 8>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hs, st);
+    return dbf_decode<8, 16>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hs, st);
   }
-  uint16_t* dinp = reinterpret_cast<uint16_t*>(base + align256((size_t)2 * M * r * 2));
+  base += align256((size_t)M * r * 4);
+  uint16_t* hp = reinterpret_cast<uint16_t*>(base);
+  base += align256((size_t)2 * M * r * 2);
+  int* rexp = reinterpret_cast<int*>(base);
+  base += align256((size_t)M * 4);
+  uint16_t* dinp = reinterpret_cast<uint16_t*>(base);
   hipError_t e = launch_prep_f16(d_in, n, dinp, st);
   if (e != hipSuccess) return e;
   TileArgs a1{};
-  a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kperm = dinp; a1.diag = d_mid; a1.out = hp;
+  a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kperm = dinp; a1.diag = d_mid; a1.out = hs;
   e = launch_tile_dbf1(a1, st);
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dbf_split, dim3(M), dim3(256), 0, st, hs, r, hp, rexp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   TileArgs a2{};
-  a2.a = hp; a2.M = 2 * M; a2.N = m; a2.K = r; a2.signs = u; a2.diag = d_out; a2.out = y; a2.out_bf16 = y_bf16;
+  a2.a = hp; a2.M = 2 * M; a2.N = m; a2.K = r; a2.signs = u; a2.diag = d_out; a2.rexp = rexp;
+  a2.out = y; a2.out_bf16 = y_bf16;
   return launch_tile_dbf2(a2, st);
 }
 

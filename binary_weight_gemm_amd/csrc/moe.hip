@@ -16,8 +16,9 @@
 //     the expert-major route list (one workgroup).
 //  3. gate/up: one workgroup per (4 blocks of 16 intermediate columns, active
 //     expert); both products share every activation operand; SwiGLU in fp32;
-//     the result is stored as an fp16 hi/lo pair per route, permuted.
+//     the result is stored as an fp32 row per route.
 //  4. down: one workgroup per (4 blocks of 16 hidden columns, active expert);
+//     stages the fp32 rows as scaled fp16 hi/lo pieces (WaveStageF32) and
 //     writes the route's fp32 output.
 //  5. combine: y_t = sum over slots j, in slot order, of w_tj * out(t, j).
 #include <type_traits>
@@ -38,7 +39,7 @@ struct MoeWs {
   int4* blk;         // [E] (expert, first route, routes, 0) of the a-th active expert; zeros after the last
   int* route_tok;    // [R] token of each expert-major route position
   int* route_pos;    // [T][k] expert-major position of route (t, j)
-  uint16_t* ap;      // [2R][I] permuted fp16 hi/lo of the SwiGLU output
+  float* ap;         // [R][I] fp32 SwiGLU output (staged by the down launch as scaled pieces)
   float* o;          // [R][H]
 };
 
@@ -53,7 +54,7 @@ static MoeWs moe_carve(void* ws, int64_t T, int64_t H, int64_t I, int64_t E, int
   w.blk = reinterpret_cast<int4*>(take((size_t)E * 16));
   w.route_tok = reinterpret_cast<int*>(take((size_t)R * 4));
   w.route_pos = reinterpret_cast<int*>(take((size_t)R * 4));
-  w.ap = reinterpret_cast<uint16_t*>(take((size_t)2 * R * I * 2));
+  w.ap = reinterpret_cast<float*>(take((size_t)R * I * 4));
   w.o = reinterpret_cast<float*>(take((size_t)R * H * 4));
   return w;
 }
@@ -61,7 +62,7 @@ static MoeWs moe_carve(void* ws, int64_t T, int64_t H, int64_t I, int64_t E, int
 size_t moe_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t R = T * k;
   return 2 * align256((size_t)R * 4) + align256((size_t)(E + 1) * 4) + align256((size_t)E * 16) +
-         2 * align256((size_t)R * 4) + align256((size_t)2 * R * I * 2) + align256((size_t)R * H * 4);
+         2 * align256((size_t)R * 4) + align256((size_t)R * I * 4) + align256((size_t)R * H * 4);
 }
 
 // exclusive prefix sum over the block (blockDim.x <= 1024); returns the total
@@ -337,17 +338,12 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
       for (int cb = 0; cb < CB; ++cb) {
         const int n = (blockIdx.x * CB + cb) * 16 + j;
         if (n >= I) continue;
-        const int pc = perm_pos(n);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = 4 * (lane >> 4) + i;
           if (p < rows) {
             const float g = acc[cb][0][0][i], u = acc[cb][1][0][i];
-            const float a = g / (1.0f + expf(-g)) * u;
-            uint16_t hi, lo;
-            split_f16(a, hi, lo);
-            ws.ap[(size_t)(2 * (r0 + tb + p)) * I + pc] = hi;
-            ws.ap[(size_t)(2 * (r0 + tb + p) + 1) * I + pc] = lo;
+            ws.ap[(size_t)(r0 + tb + p) * I + n] = g / (1.0f + expf(-g)) * u;
           }
         }
       }
@@ -360,8 +356,9 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
 }
 
 // down: one workgroup per (CB blocks of 16 hidden columns, active expert); the
-// routes' fp16 hi/lo intermediates are staged per wave, 8 routes (16 piece
-// rows) a tile, and multiplied by every block.
+// routes' fp32 intermediates are staged per wave as scaled fp16 hi/lo pieces
+// (WaveStageF32), up to 8 routes (16 piece rows) a tile, and multiplied by
+// every block; each wave scales its partials back before the waves meet.
 template <int CPW, int CB, int RT>
 __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __restrict__ ds,
                                                   const uint16_t* __restrict__ dsc, MoeWs ws) {
@@ -394,9 +391,9 @@ __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __r
     auto tile = [&](auto sr) {
       constexpr int SR = decltype(sr)::value;
       uint4* xw = smem + (size_t)wave * CPW * SR * 64;
+      WaveStageF32<CPW, SR / 2> sa;
       if (c0 < nchunks) {
-        WaveStage<ST_COPY, CPW, SR> sa;
-        sa.load(rows, I, c0, [&](int pr) { return ws.ap + (size_t)(2 * (r0 + tb) + pr) * I; });
+        sa.load(routes, I, c0, [&](int m) { return ws.ap + (size_t)(r0 + tb + m) * I; });
         sa.store(xw);
       }
       __syncthreads();
@@ -410,6 +407,12 @@ __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __r
         for (int cb = 0; cb < CB; ++cb) {
           pin_signs(bp[cb]);
           b_compute<BM_GROUP, 1, 1, CPW>(bp[cb], nullptr, G, c0, 1, aop, acc[cb]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int us = sa.unscale(i);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) acc[cb][0][0][i] = __builtin_amdgcn_ldexpf(acc[cb][0][0][i], us);
         }
       }
     };
@@ -557,18 +560,12 @@ __global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict_
     acc[0][0] += red[(2 * (w - 1)) * 64 + lane];
     acc[1][0] += red[(2 * (w - 1) + 1) * 64 + lane];
   }
-  const int pc = perm_pos(n);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = 4 * kb + i;
     if (q < cnt) {
       const float g = acc[0][0][i], u = acc[1][0][i];
-      const float a = g / (1.0f + expf(-g)) * u;
-      uint16_t hi, lo;
-      split_f16(a, hi, lo);
-      const size_t r = (size_t)s_tok[q] * k + s_slot[q];
-      ws.ap[(2 * r) * I + pc] = hi;
-      ws.ap[(2 * r + 1) * I + pc] = lo;
+      ws.ap[((size_t)s_tok[q] * k + s_slot[q]) * I + n] = g / (1.0f + expf(-g)) * u;
     }
   }
 }
@@ -593,9 +590,9 @@ __global__ __launch_bounds__(1024) void k_moe_b_token(int H, int I, int k, const
   uint4* xw = smem + (size_t)slot * CPW * 2 * 64;
   float* part = reinterpret_cast<float*>(smem + (size_t)k * CPW * 2 * 64);  // [k][16]
   f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+  WaveStageF32<CPW, 1> sa;  // the route's fp32 row as two scaled piece rows
   {
-    WaveStage<ST_COPY, CPW, 2> sa;
-    sa.load(2, I, 0, [&](int p) { return ws.ap + (size_t)(2 * r + p) * I; });
+    sa.load(1, I, 0, [&](int) { return ws.ap + (size_t)r * I; });
     BPre<1, CPW> bp;
     b_prefetch<BM_GROUP, 1, CPW>(wsig, wsc, rk, G, 0, 1, bp);
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
@@ -608,7 +605,7 @@ __global__ __launch_bounds__(1024) void k_moe_b_token(int H, int I, int k, const
     b_compute<BM_GROUP, 1, 1, CPW, true>(bp, nullptr, G, 0, 1, aop, acc);
   }
   // lanes 0..15 hold piece rows 0 and 1 of column j
-  if (kb == 0) part[slot * 16 + j] = acc[0][0][0] + acc[0][0][1];
+  if (kb == 0) part[slot * 16 + j] = __builtin_amdgcn_ldexpf(acc[0][0][0] + acc[0][0][1], sa.unscale(0));
   __syncthreads();
   if (slot != 0 || kb != 0 || !rok) return;
   float sum = 0.f;
@@ -870,7 +867,7 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
             if constexpr (STAGE == 1) {
               const float u = (acc[cb][NMAT - 1][0][2 * h] + acc[cb][NMAT - 1][0][2 * h + 1]) *
                               f16_bits_to_f32(a.dg[1][(size_t)e * N + col]);
-              reinterpret_cast<float*>(ws.ap)[route * I + col] = v0 / (1.0f + expf(-v0)) * u;
+              ws.ap[route * I + col] = v0 / (1.0f + expf(-v0)) * u;
             } else if constexpr (STAGE == 2) {
               a.out[route * r + col] = v0;
             } else {
@@ -934,7 +931,7 @@ hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, 
   DbfStageArgs a1{{u4(gate.u), u4(up.u)}, {nullptr, nullptr}, {gate.d_out, up.d_out},
                   {hbuf, hbuf + (size_t)R * r}, nullptr};
   DbfStageArgs a2{{u4(down.v), nullptr}, {down.d_in, nullptr}, {down.d_mid, nullptr},
-                  {reinterpret_cast<const float*>(ws.ap), nullptr}, hbuf};
+                  {ws.ap, nullptr}, hbuf};
   DbfStageArgs a3{{u4(down.u), nullptr}, {nullptr, nullptr}, {down.d_out, nullptr}, {hbuf, nullptr}, nullptr};
   if (small) {
     err = moe_dbf_stage<0, 4>(x, H, I, r, R, maxact, a0, ws, st);

@@ -7,7 +7,7 @@
 
 namespace brq {
 
-enum { EPI_Y = 0, EPI_HSPLIT = 1, EPI_PAIRSUM = 2 };
+enum { EPI_Y = 0, EPI_HS32 = 1, EPI_PAIRSUM = 2 };
 
 struct TileArgs {
   const void* a;            // activations: bf16 [M][K] (AMODE 0) or permuted fp16 [M][K] (AMODE 1)
@@ -15,7 +15,8 @@ struct TileArgs {
   const uint64_t* signs;    // SIGN1 plane [N][K/64]
   const uint16_t* scales;   // group-128 scales [N][K/128] (BM_GROUP)
   const uint16_t* kperm;    // permuted fp16 per-k magnitudes [K] (BM_PERK)
-  const uint16_t* diag;     // fp16 per-column diagonal (EPI_HSPLIT, EPI_PAIRSUM)
+  const uint16_t* diag;     // fp16 per-column diagonal (EPI_HS32, EPI_PAIRSUM)
+  const int* rexp;          // per-token exponent applied to the piece sum (EPI_PAIRSUM)
   void* out;
   int out_bf16;
 };

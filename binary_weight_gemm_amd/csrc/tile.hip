@@ -17,10 +17,10 @@
 // 8 consecutive k of block l/32; B lane l supplies column l%32 and the same k
 // block; D lane l holds, in item r, row 8*(r/4) + 4*(l/32) + r%4 of column l%32.
 //
-// Epilogues: EPI_Y writes y (fp32 or bf16); EPI_HSPLIT multiplies by a per-column
-// fp16 diagonal and writes fp16 hi/lo pairs in the permuted order (the DBF
-// intermediate h_s); EPI_PAIRSUM adds the two piece rows of every token and
-// multiplies by a per-column diagonal (the DBF output).
+// Epilogues: EPI_Y writes y (fp32 or bf16); EPI_HS32 multiplies by a per-column
+// fp16 diagonal and writes fp32 rows (the DBF intermediate h_s); EPI_PAIRSUM
+// adds the two piece rows of every token, applies the token's power of two
+// (2^rexp, exact) and multiplies by a per-column diagonal (the DBF output).
 #include "common.h"
 #include "dec_core.h"
 #include "kernels.h"
@@ -192,26 +192,22 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
           if (row < p.M) store_out(p.out, (size_t)row * p.N + col, acc[i][j][r], p.out_bf16);
         }
-      } else if (EPI == EPI_HSPLIT) {
+      } else if (EPI == EPI_HS32) {
         const float dm = f16_bits_to_f32(p.diag[col]);
-        uint16_t* hp = reinterpret_cast<uint16_t*>(p.out);
-        const int pc = perm_pos(col);
+        float* hs = reinterpret_cast<float*>(p.out);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < p.M) {
-            uint16_t hi, lo;
-            split_f16(acc[i][j][r] * dm, hi, lo);
-            hp[(size_t)(2 * row) * p.N + pc] = hi;
-            hp[(size_t)(2 * row + 1) * p.N + pc] = lo;
-          }
+          if (row < p.M) hs[(size_t)row * p.N + col] = acc[i][j][r] * dm;
         }
       } else {  // EPI_PAIRSUM: rows 2t, 2t+1 are the two pieces of token t
         const float dg = f16_bits_to_f32(p.diag[col]);
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < p.M) store_out(p.out, (size_t)(row >> 1) * p.N + col, (acc[i][j][r] + acc[i][j][r + 1]) * dg, p.out_bf16);
+          if (row < p.M)
+            store_out(p.out, (size_t)(row >> 1) * p.N + col,
+                      __builtin_amdgcn_ldexpf(acc[i][j][r] + acc[i][j][r + 1], p.rexp[row >> 1]) * dg, p.out_bf16);
         }
       }
     }
@@ -236,8 +232,8 @@ hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64
 
 hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st) {
   const long mid = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (mid >= 256) return run_tile<128, 128, 0, BM_PERK, EPI_HSPLIT>(a, st);
-  return run_tile<64, 64, 0, BM_PERK, EPI_HSPLIT>(a, st);
+  if (mid >= 256) return run_tile<128, 128, 0, BM_PERK, EPI_HS32>(a, st);
+  return run_tile<64, 64, 0, BM_PERK, EPI_HS32>(a, st);
 }
 
 hipError_t launch_tile_dbf2(const TileArgs& a, hipStream_t st) {

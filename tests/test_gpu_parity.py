@@ -322,6 +322,29 @@ def test_dbf_small(M, m, n, r):
     check_f32(f64(y), o, F32_TOL, f"dbf {M},{m},{n},{r}")
 
 
+# h_s of small magnitude (d_mid at 2^-12 of its usual spread, so |h_s| ~ 1e-3
+# and below): an unscaled fp16 hi/lo pair keeps few bits there (its lo piece is
+# subnormal below 2^-3); the scaled pieces keep about 22. Decode (M <= 8) and
+# tiled (M = 100) paths.
+@pytest.mark.parametrize("M", [1, 5, 100])
+def test_dbf_small_intermediates(M):
+    say("dbf small h_s", M)
+    m, n, r = 192, 512, 384
+    key = (74, M)
+    v = datagen.pm1_f32(key + (0,), (r, n))
+    u = datagen.pm1_f32(key + (1,), (m, r))
+    d_in = datagen.f16_lognormal(key + (2,), (n,))
+    d_mid = (datagen.f16_lognormal(key + (3,), (r,)).astype(np.float32) * 2.0 ** -12).astype(np.float16)
+    d_out = datagen.f16_lognormal(key + (4,), (m,))
+    x = datagen.bf16_normal(key + (5,), (M, n))
+    vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
+    o = oracle.dbf_chain(oracle.bf16_to_f64(x), d_in, vw, d_mid, uw, d_out, m, n, r)
+    y = brq().dbf_gemm(dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_f32(f64(y), o, F32_TOL, f"dbf small h_s M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 512])
 def test_dbf_c3(M):
     say("C3 dbf", M)
@@ -399,6 +422,23 @@ def test_moe_c4(c4_experts, T):
     say("C4 moe", T)
     y, o = _moe_check(c4_experts, T)
     check_f32(f64(y), o, F32_TOL, f"moe T={T}")
+
+
+# activations at 2^-7 of the usual scale put the SwiGLU output near 1e-4,
+# where an unscaled fp16 hi/lo pair is subnormal; the down launches stage it
+# as scaled pieces. T = 2 takes the token path, T = 24 the grouped one.
+@pytest.mark.parametrize("T", [2, 24])
+def test_moe_small_intermediates(T):
+    say("moe small SwiGLU output", T)
+    cfg = datagen.C4(E=16, H=256, I=256, top_k=4, layer=7)
+    ex = _Experts(cfg)
+    xf = oracle.bf16_to_f64(cfg.x(T)) * 2.0 ** -7
+    x = (xf.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # exact: a power-of-two scale
+    lg = cfg.logits(T)
+    o, _, _ = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, cfg.top_k)
+    y = brq().moe_ffn(dev(x), dev(lg), *ex.d, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_f32(f64(y), o, F32_TOL, f"moe small a T={T}")
 
 
 def test_moe_c4_bf16_and_fresh_logits(c4_experts):
