@@ -9,7 +9,7 @@ Infinity Cache, so every call streams its weights from HBM.
 
 Also reported (extra): the same product at M = 4, 16, 64; the routed MoE layer
 (256 experts, top-8, hidden 2048, intermediate 512) at T = 1 and 64 decode
-tokens; the DBF chain (4096x4096, r = 2048) at M = 1 and 512; the prefill
+tokens, with group-128 experts and with DBF-chain experts (r = 1024); the DBF chain (4096x4096, r = 2048) at M = 1 and 512; the prefill
 product at M = 4096 (4096 -> 14336) with the Kronecker rotation before it, and
 the same product with a rank-20 weight correction fused into its epilogue.
 
@@ -244,6 +244,58 @@ def run_moe(brq, torch, Ts, iters=50):
     return out
 
 
+def run_moe_dbf(brq, torch, Ts, iters=50):
+    """The DBF-expert MoE layer at the deployed shape (256 experts, top-8,
+    gate/up 512x2048, down 2048x512, r = 1024): random sign words and fp16
+    log-normal diagonals on the device (timing does not depend on their
+    values), D_mid at 2^-12 as in the parity inputs."""
+    import datagen
+    cfg = datagen.C4D()
+    E, H, I, r, k = cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+
+    def words(*shape):
+        return torch.randint(-2 ** 62, 2 ** 62, shape, dtype=torch.int64, device="cuda", generator=gen)
+
+    def diag(n, scale=1.0):
+        g = torch.randn((E, n), device="cuda", generator=gen)
+        return (torch.exp(0.5 * g) * scale).to(torch.float16)
+
+    def rec(m, n):
+        return (diag(n), words(E, r, n // 64), diag(r, 2.0 ** -12), words(E, m, r // 64), diag(m))
+
+    base = (rec(I, H), rec(I, H), rec(H, I))
+    exp_bytes = 2 * ((r * H + I * r) // 8 + 2 * (H + r + I)) + (r * I + H * r) // 8 + 2 * (I + r + H)
+    copies = ring_copies(E * exp_bytes)
+    ring = [base] + [tuple(tuple(t.clone() for t in rc) for rc in base) for _ in range(copies - 1)]
+    out = {}
+    for T in Ts:
+        x = dev_np(cfg.x(T))
+        lgs = [dev_np(cfg.logits(T, it)) for it in range(iters)]
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(brq.moe_dbf_workspace_bytes(T, H, I, E, k, r), dtype=torch.uint8, device="cuda")
+        # algorithmic bytes: distinct selected experts' factors + x + logits + y
+        nbytes = 0
+        for it in range(iters):
+            ids = np.argsort(-cfg.logits(T, it), axis=1, kind="stable")[:, :k]
+            nbytes += len(np.unique(ids)) * exp_bytes + T * (H * 2 * 2 + E * 4)
+        for it in range(5):
+            brq.moe_dbf_ffn(x, lgs[it], *ring[it % copies], E, H, I, r, k, y=y, ws=ws)
+        torch.cuda.synchronize()
+
+        def timed():
+            for it in range(iters):
+                brq.moe_dbf_ffn(x, lgs[it], *ring[it % copies], E, H, I, r, k, y=y, ws=ws)
+
+        ms = graph_time(torch, timed, iters) / iters
+        out[f"T={T}"] = dict(us_per_layer=ms * 1e3, gbs=nbytes / iters / (ms * 1e-3) / 1e9,
+                             tokens_per_s=T / (ms * 1e-3), ring_copies=copies)
+    del ring, base
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_dbf(brq, torch, Ms, iters=50):
     import datagen
     out = {}
@@ -420,6 +472,8 @@ def main():
             extra["c2"][f"M={M}"] = {k: r[k] for k in ("ms_per_step", "gbs", "tflops")}
         log("[bench] MoE")
         extra["moe"] = run_moe(brq, torch, (1, 64))
+        log("[bench] MoE with DBF experts")
+        extra["moe_dbf"] = run_moe_dbf(brq, torch, (1, 64))
         log("[bench] DBF")
         extra["dbf"] = run_dbf(brq, torch, (1, 512))
         log("[bench] prefill")

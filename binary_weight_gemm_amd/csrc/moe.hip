@@ -763,18 +763,24 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
   uint4* stage_base = smem + (PERK ? (size_t)nw * NMAT * CPW * 64 : 0);
   uint4* xw = stage_base + (size_t)wave * NIN * CPW * SR * 64;
 
-  // every block's sign words (and D_in) in flight before any wait
-  BPre<1, CPW> bp[NMAT][CB];
+  // every block's sign words (and D_in) in flight before any wait; the CB
+  // blocks of a matrix are one b_compute call, so each activation operand
+  // (and D_in operand) is read from LDS once for all of them
+  BPre<CB, CPW> bp[NMAT];
 #pragma unroll
-  for (int q = 0; q < NMAT; ++q)
+  for (int q = 0; q < NMAT; ++q) {
+    const uint4* wsig[CB];
+    const uint16_t* wsc[CB];
+    bool rok[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int col = (blockIdx.x * CB + cb) * 16 + j;
-      const uint4* wsig[1] = {a.sig[q] + ((size_t)e * N + (col < N ? col : 0)) * G};
-      const uint16_t* wsc[1] = {nullptr};
-      const bool rok[1] = {col < N};
-      b_prefetch<BMODE, 1, CPW>(wsig, wsc, rok, G, c0, 1, bp[q][cb]);
+      wsig[cb] = a.sig[q] + ((size_t)e * N + (col < N ? col : 0)) * G;
+      wsc[cb] = nullptr;
+      rok[cb] = col < N;
     }
+    b_prefetch<BMODE, CB, CPW>(wsig, wsc, rok, G, c0, 1, bp[q]);
+  }
   if constexpr (PERK) {
     if (c0 < nchunks) {
 #pragma unroll
@@ -791,11 +797,11 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
   auto run_tile = [&](const int tb) {
     const int routes = (cnt - tb) < RT ? (cnt - tb) : RT;
     const int rows = PIECES ? 2 * routes : routes;
-    f32x4 acc[CB][NMAT][1];
+    f32x4 acc[NMAT][CB][1];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-      for (int q = 0; q < NMAT; ++q) acc[cb][q][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CB; ++cb) acc[q][cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     WaveStageF32<CPW, RT> sf0, sf1;  // the two inputs of stage 1 (gate, up); sf0 elsewhere
     if (c0 < nchunks) {
       if constexpr (PIECES) {
@@ -819,26 +825,21 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
           return xs[(((g >> 2) - c0) * SR + m) * 64 + (g & 3) * 16 + i];
         };
         const u32x4* kp = PERK ? reinterpret_cast<const u32x4*>(dw + q * CPW * 64) - (size_t)c0 * 64 : nullptr;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          pin_signs(bp[q][cb]);
-          f32x4 t[1][1] = {{acc[cb][q][0]}};
-          b_compute<BMODE, 1, 1, CPW>(bp[q][cb], kp, G, c0, 1, aop, t);
-          acc[cb][q][0] = t[0][0];
-        }
+        pin_signs(bp[q]);
+        b_compute<BMODE, CB, 1, CPW>(bp[q], kp, G, c0, 1, aop, acc[q]);
         if constexpr (PIECES) {
           // back from the wave's scaled pieces (exact powers of two)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int us = (NIN == 2 && q == 1) ? sf1.unscale(i) : sf0.unscale(i);
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) acc[cb][q][0][i] = __builtin_amdgcn_ldexpf(acc[cb][q][0][i], us);
+            for (int cb = 0; cb < CB; ++cb) acc[q][cb][0][i] = __builtin_amdgcn_ldexpf(acc[q][cb][0][i], us);
           }
         }
       }
     }
     __syncthreads();
-    reduce_waves_cb<CB, NMAT>(acc, reinterpret_cast<f32x4*>(stage_base));
+    reduce_waves_cb<NMAT, CB>(acc, reinterpret_cast<f32x4*>(stage_base));
     if (wave == 0) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
@@ -852,7 +853,7 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int p = 4 * (lane >> 4) + i;
-              if (p < routes) a.out[(size_t)q * R * r + (size_t)(r0 + tb + p) * r + col] = acc[cb][q][0][i] * dm;
+              if (p < routes) a.out[(size_t)q * R * r + (size_t)(r0 + tb + p) * r + col] = acc[q][cb][0][i] * dm;
             }
           }
         } else {
@@ -862,10 +863,10 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
             const int p = 2 * (lane >> 4) + h;
             if (p >= routes) continue;
             const size_t route = (size_t)(r0 + tb + p);
-            const float v0 = (acc[cb][0][0][2 * h] + acc[cb][0][0][2 * h + 1]) *
+            const float v0 = (acc[0][cb][0][2 * h] + acc[0][cb][0][2 * h + 1]) *
                              f16_bits_to_f32(a.dg[0][(size_t)e * N + col]);
             if constexpr (STAGE == 1) {
-              const float u = (acc[cb][NMAT - 1][0][2 * h] + acc[cb][NMAT - 1][0][2 * h + 1]) *
+              const float u = (acc[NMAT - 1][cb][0][2 * h] + acc[NMAT - 1][cb][0][2 * h + 1]) *
                               f16_bits_to_f32(a.dg[1][(size_t)e * N + col]);
               ws.ap[route * I + col] = v0 / (1.0f + expf(-v0)) * u;
             } else if constexpr (STAGE == 2) {
@@ -887,30 +888,42 @@ size_t moe_dbf_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, i
   return moe_ws_bytes(T, H, I, E, k) + align256((size_t)2 * T * k * r * 4);  // h_s: fp32 [2][T*k][r]
 }
 
+template <int STAGE, int SR, int CB>
+static hipError_t moe_dbf_stage_cb(const uint16_t* x, int H, int I, int r, int R, int maxact, const DbfStageArgs& a,
+                                   const MoeWs& ws, int waves, hipStream_t st) {
+  const int N = STAGE == 1 ? I : STAGE == 3 ? H : r;
+  constexpr int NMAT = STAGE < 2 ? 2 : 1;
+  constexpr int NIN = STAGE == 1 ? 2 : 1;
+  constexpr bool PERK = STAGE == 0 || STAGE == 2;
+  const size_t din = PERK ? (size_t)waves * NMAT * 1024 : 0;
+  const size_t stg = (size_t)waves * NIN * SR * 1024;
+  const size_t red = (size_t)(waves - 1) * CB * NMAT * 1024;
+  const size_t lds = din + (stg > red ? stg : red);
+  const dim3 grid((unsigned)((N + 16 * CB - 1) / (16 * CB)), (unsigned)maxact);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_moe_dbf<STAGE, 1, SR, CB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_moe_dbf<STAGE, 1, SR, CB>), grid, dim3(64 * waves), lds, st, x, H, I, r, R, a, ws);
+  return hipGetLastError();
+}
+
+// One chunk (512 of the reduction axis) per wave: the accepted shapes have
+// K <= 4096, so at most 8 waves. CB blocks of 16 columns per workgroup: 4
+// when that still gives about four workgroups per compute unit for the
+// experts that can be active, fewer otherwise (decode at T = 1 has 8).
 template <int STAGE, int SR>
 static hipError_t moe_dbf_stage(const uint16_t* x, int H, int I, int r, int R, int maxact, const DbfStageArgs& a,
                                 const MoeWs& ws, hipStream_t st) {
   const int K = STAGE == 0 ? H : STAGE == 2 ? I : r;
   const int N = STAGE == 1 ? I : STAGE == 3 ? H : r;
-  constexpr int NMAT = STAGE < 2 ? 2 : 1;
-  constexpr int NIN = STAGE == 1 ? 2 : 1;
-  constexpr bool PERK = STAGE == 0 || STAGE == 2;
   const DecSplit sp = dec_split(K / 128, 8);
-  const size_t din = PERK ? (size_t)sp.waves * NMAT * sp.cpw * 1024 : 0;
-  const size_t stg = (size_t)sp.waves * NIN * sp.cpw * SR * 1024;
-  BRQ_CPW_SWITCH(sp.cpw, {
-    constexpr int CB = moe_cb_gu(CPW);
-    const size_t red = (size_t)(sp.waves - 1) * CB * NMAT * 1024;
-    const size_t lds = din + (stg > red ? stg : red);
-    const dim3 grid((unsigned)((N + 16 * CB - 1) / (16 * CB)), (unsigned)maxact);
-    if (lds > 64 * 1024) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_moe_dbf<STAGE, CPW, SR, CB>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k_moe_dbf<STAGE, CPW, SR, CB>), grid, dim3(64 * sp.waves), lds, st, x, H, I, r, R, a, ws);
-  });
-  return hipGetLastError();
+  if (sp.cpw != 1) return hipErrorInvalidValue;  // outside the accepted shapes
+  const int64_t blocks = (int64_t)((N + 15) / 16) * maxact;
+  if (blocks >= 4096) return moe_dbf_stage_cb<STAGE, SR, 4>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
+  if (blocks >= 2048) return moe_dbf_stage_cb<STAGE, SR, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
+  return moe_dbf_stage_cb<STAGE, SR, 1>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
 }
 
 hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, int I, int E, int top_k, int r,
