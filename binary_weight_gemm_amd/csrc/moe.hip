@@ -439,14 +439,40 @@ __global__ __launch_bounds__(512) void k_moe_down(int H, int I, const uint4* __r
   for (int tb = RT; tb < cnt; tb += RT) run_tile(tb);
 }
 
+// One thread per 4 consecutive hidden columns of a token: the slots' positions
+// and weights are loaded first (k <= 16, unrolled), then one 16-byte load per
+// slot; y = sum over j in slot order of w_tj * out(t, j), one fma per slot.
 __global__ __launch_bounds__(256) void k_moe_combine(int T, int H, int k, MoeWs ws, void* __restrict__ y,
                                                      int y_bf16) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)T * H) return;
-  const int t = (int)(idx / H), n = (int)(idx % H);
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) acc = fmaf(ws.wts[t * k + j], ws.o[(size_t)ws.route_pos[t * k + j] * H + n], acc);
-  store_out(y, (size_t)idx, acc, y_bf16);
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int h4 = H >> 2;
+  if (q >= (int64_t)T * h4) return;
+  const int t = (int)(q / h4), n = 4 * (int)(q % h4);
+  int pos[16];
+  float wt[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int jj = j < k ? j : 0;  // clamped, unconditional loads
+    pos[j] = ws.route_pos[t * k + jj];
+    wt[j] = ws.wts[t * k + jj];
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= k) break;
+    const f32x4 o = *reinterpret_cast<const f32x4*>(ws.o + (size_t)pos[j] * H + n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt[j], o[i], acc[i]);
+  }
+  const size_t base = (size_t)t * H + n;
+  if (y_bf16) {
+    uint2 b;
+    b.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+    b.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + base) = b;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + base) = acc;
+  }
 }
 
 // ---- decode path (few tokens): two launches --------------------------------
@@ -707,7 +733,7 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
 #undef BRQ_DOWN
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * H + 255) / 256)), dim3(256), 0, st, T, H, top_k,
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * (H / 4) + 255) / 256)), dim3(256), 0, st, T, H, top_k,
                      ws, y, y_bf16);
   return hipGetLastError();
 }
@@ -958,7 +984,7 @@ hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, 
     if (err == hipSuccess) err = moe_dbf_stage<3, 16>(x, H, I, r, R, maxact, a3, ws, st);
   }
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * H + 255) / 256)), dim3(256), 0, st, T, H, top_k,
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)(((int64_t)T * (H / 4) + 255) / 256)), dim3(256), 0, st, T, H, top_k,
                      ws, y, y_bf16);
   return hipGetLastError();
 }

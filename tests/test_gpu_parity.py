@@ -144,6 +144,35 @@ def test_gemm_single_row_wide_range(N, K):
         assert np.array_equal(host_bits(yb), oracle.bf16_bits(oracle.round_bf16(f64(y))))
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 40, 512), (5, 1000, 1536), (8, 2049, 4096), (4, 4096, 14336)])
+def test_gemm_few_rows_wide_range(M, N, K):
+    """2 to 8 activation rows of very different magnitude (1e4, 36 binades
+    inside a row, all zero, 2^-20 with one outlier) in one product on the fp16
+    matrix cores: the rows must not disturb each other, and values below
+    fp16's normal range lose at most 2^-25 each (the activation-range
+    precondition), far below the fp32 bar of each row."""
+    say("gemm few rows, wide range", M, N, K)
+    w = datagen.normal_f32((75, N, K), (N, K), 0.02)
+    ow, osc = oracle.pack_sign1(w)
+    g = datagen.rng(75, N, K, 1)
+    base = g.standard_normal((M, K)).astype(np.float32)
+    kinds = [lambda r: r * np.float32(1e4),
+             lambda r: r * np.exp2(g.integers(-24, 12, size=K)).astype(np.float32),
+             lambda r: np.zeros(K, np.float32),
+             lambda r: r * np.float32(2.0 ** -20)]
+    rows = np.stack([kinds[m % 4](base[m]) if m < 4 else base[m] for m in range(M)])
+    if M > 3:
+        rows[3, K // 3] = 3000.0
+    xb = datagen.bf16_bits_from_f32(rows)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(xb), ow, osc, N, K)
+    y = f64(brq().gemm(dev(xb), dev(ow), dev(osc), N, K, out_dtype=torch.float32))
+    for m in range(M):
+        if m == 2:
+            assert not np.any(y[m] != 0)
+        else:
+            check_f32(y[m], o[m], F32_TOL, f"row {m} of {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 40, 640), (64, 96, 1024)])
 def test_gemm_decode_bf16(M, N, K):
     say("gemm decode bf16", M, N, K)
