@@ -910,6 +910,90 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
   for (int tb = RT; tb < cnt; tb += RT) run_tile(tb);
 }
 
+// ---- DBF experts, few tokens (T <= 4): five launches ----------------------
+//  route: one workgroup, one wave per token: top-k, then one block record per
+//         route in token-major order (route i = t*k + j forms its own block of
+//         one route), ids and weights out;
+//  stages 0-2: k_moe_dbf on those one-route blocks;
+//  stage 3 + combine: one workgroup per (16 hidden columns, token), one wave
+//         per slot: the down U factor on the route's h_s (scaled pieces, the
+//         wave covers the whole rank), D_out; wave 0 then adds w_tj * out_j
+//         in slot order.
+__global__ __launch_bounds__(256) void k_moe_route_tok(const float* __restrict__ logits, int T, int E, int k,
+                                                       MoeWs ws, int32_t* __restrict__ ids_user,
+                                                       float* __restrict__ w_user) {
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+  if (t >= T) return;
+  int id;
+  float w;
+  if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, id, w);
+  else wave_route<16>(logits + (size_t)t * E, E, k, id, w);
+  if (lane < k) {
+    const int r = t * k + lane;
+    ws.ids[r] = id;
+    ws.wts[r] = w;
+    ws.blk[r] = make_int4(id, r, 1, 0);
+    ws.route_tok[r] = t;
+    ws.route_pos[r] = r;
+    if (ids_user) ids_user[r] = id;
+    if (w_user) w_user[r] = w;
+  }
+}
+
+template <int CPW>
+__global__ __launch_bounds__(1024) void k_moe_dbf_down_tok(int H, int r, int k, const uint4* __restrict__ u,
+                                                           const uint16_t* __restrict__ d_out,
+                                                           const float* __restrict__ hs, MoeWs ws,
+                                                           void* __restrict__ y, int y_bf16) {
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, slot = threadIdx.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int t = blockIdx.y;
+  const int n = blockIdx.x * 16 + j;
+  const int route = t * k + slot;
+  const int e = ws.ids[route];
+  const int G = r >> 7;
+  const bool rok = n < H;
+  const size_t row = (size_t)e * H + (rok ? n : 0);
+  const uint4* wsig[1] = {u + row * G};
+  const uint16_t* wsc[1] = {nullptr};
+  const bool rk[1] = {rok};
+  uint4* xw = smem + (size_t)slot * CPW * 2 * 64;
+  float* part = reinterpret_cast<float*>(smem + (size_t)k * CPW * 2 * 64);  // [k][16]
+  f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+  WaveStageF32<CPW, 1> sh;  // the route's h_s row as two scaled piece rows
+  {
+    sh.load(1, r, 0, [&](int) { return hs + (size_t)route * r; });
+    BPre<1, CPW> bp;
+    b_prefetch<BM_ONE, 1, CPW>(wsig, wsc, rk, G, 0, 1, bp);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sh.store(xw);
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int p = min(j, 1);
+      return xs[((g >> 2) * 2 + p) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_ONE, 1, 1, CPW, true>(bp, nullptr, G, 0, 1, aop, acc);
+  }
+  // lanes 0..15 hold piece rows 0 and 1 of column j
+  if (kb == 0)
+    part[slot * 16 + j] =
+        __builtin_amdgcn_ldexpf(acc[0][0][0] + acc[0][0][1], sh.unscale(0)) * f16_bits_to_f32(d_out[row]);
+  __syncthreads();
+  if (slot != 0 || kb != 0 || !rok) return;
+  float sum = 0.f;
+  for (int q = 0; q < k; ++q) sum = fmaf(ws.wts[t * k + q], part[q * 16 + j], sum);
+  store_out(y, (size_t)t * H + n, sum, y_bf16);
+}
+
+// the few-token path applies when the last launch's staging fits and the
+// one-route blocks fit the E block records of the workspace (T*k <= E)
+static bool moe_dbf_tok_path(int T, int E, int r, int k, int& cpw, size_t& lds) {
+  cpw = (r / 128 + 3) / 4;
+  lds = (size_t)k * cpw * 2 * 1024 + (size_t)k * 16 * 4;
+  return T <= MOE_SMALL_T && T * k <= E && cpw <= 4 && lds <= (size_t)kDecLdsBytes;
+}
+
 size_t moe_dbf_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t r) {
   return moe_ws_bytes(T, H, I, E, k) + align256((size_t)2 * T * k * r * 4);  // h_s: fp32 [2][T*k][r]
 }
@@ -958,9 +1042,16 @@ hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, 
   MoeWs ws = moe_carve(ws_ptr, T, H, I, E, top_k);
   float* hbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(ws_ptr) + moe_ws_bytes(T, H, I, E, top_k));
   const int R = T * top_k;
-  const int maxact = R < E ? R : E;
-  hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, T, E, top_k, ws);
+  int cpw3;
+  size_t lds3;
+  const bool tok = moe_dbf_tok_path(T, E, r, top_k, cpw3, lds3);
+  const int maxact = tok ? R : (R < E ? R : E);
+  if (tok) {
+    hipLaunchKernelGGL(k_moe_route_tok, dim3(1), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
+  } else {
+    hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
+    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, T, E, top_k, ws);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   auto u4 = [](const uint64_t* p) { return reinterpret_cast<const uint4*>(p); };
@@ -972,6 +1063,21 @@ hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, 
   DbfStageArgs a2{{u4(down.v), nullptr}, {down.d_in, nullptr}, {down.d_mid, nullptr},
                   {ws.ap, nullptr}, hbuf};
   DbfStageArgs a3{{u4(down.u), nullptr}, {nullptr, nullptr}, {down.d_out, nullptr}, {hbuf, nullptr}, nullptr};
+  if (tok) {
+    err = moe_dbf_stage<0, 4>(x, H, I, r, R, maxact, a0, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<1, 8>(x, H, I, r, R, maxact, a1, ws, st);
+    if (err == hipSuccess) err = moe_dbf_stage<2, 8>(x, H, I, r, R, maxact, a2, ws, st);
+    if (err != hipSuccess) return err;
+    const dim3 g3((H + 15) / 16, T), b3(64 * top_k);
+    const uint4* du = u4(down.u);
+    switch (cpw3) {
+      case 1: hipLaunchKernelGGL((k_moe_dbf_down_tok<1>), g3, b3, lds3, st, H, r, top_k, du, down.d_out, hbuf, ws, y, y_bf16); break;
+      case 2: hipLaunchKernelGGL((k_moe_dbf_down_tok<2>), g3, b3, lds3, st, H, r, top_k, du, down.d_out, hbuf, ws, y, y_bf16); break;
+      case 3: hipLaunchKernelGGL((k_moe_dbf_down_tok<3>), g3, b3, lds3, st, H, r, top_k, du, down.d_out, hbuf, ws, y, y_bf16); break;
+      default: hipLaunchKernelGGL((k_moe_dbf_down_tok<4>), g3, b3, lds3, st, H, r, top_k, du, down.d_out, hbuf, ws, y, y_bf16); break;
+    }
+    return hipGetLastError();
+  }
   if (small) {
     err = moe_dbf_stage<0, 4>(x, H, I, r, R, maxact, a0, ws, st);
     if (err == hipSuccess) err = moe_dbf_stage<1, 8>(x, H, I, r, R, maxact, a1, ws, st);

@@ -532,9 +532,13 @@ def _dbf_moe_case(cfg, T, out=torch.float32, it=0):
     return y, o
 
 
-# small experts: T = 1 and 5 take 4-token tiles, T = 64 (16 routes per expert)
-# 16-token tiles and several tiles per expert; odd sizes with ragged blocks
-@pytest.mark.parametrize("T,E,H,I,r,k", [(1, 16, 256, 128, 128, 4), (5, 16, 256, 128, 128, 4),
+# small experts: T = 1 and 3 take the few-token path (one route per block, the
+# last stage fused with the slot sum; r = 640 gives a ragged last chunk), T = 4
+# with T*k > E and T = 5 the grouped one with 4-token tiles, T = 64 (16 routes
+# per expert) 16-token tiles and several tiles per expert; odd sizes with
+# ragged blocks
+@pytest.mark.parametrize("T,E,H,I,r,k", [(1, 16, 256, 128, 128, 4), (3, 16, 256, 128, 640, 4),
+                                         (4, 8, 256, 128, 128, 3), (5, 16, 256, 128, 128, 4),
                                          (64, 16, 256, 128, 128, 4), (7, 8, 384, 256, 256, 3)])
 def test_moe_dbf_small(T, E, H, I, r, k):
     say("moe dbf", T, E, H, I, r, k)
