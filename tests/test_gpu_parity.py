@@ -567,6 +567,49 @@ def test_moe_dbf_deployed_shape():
             check_bf16(y, o, "moe dbf deployed bf16")
 
 
+def test_moe_dbf_deployed_shape_t64_sampled_tokens():
+    # the deployed layer at T = 64 (the grouped path, every expert built),
+    # checked on 8 sampled tokens (fp32) and on all of them for the routing
+    say("moe dbf deployed shape T=64, sampled tokens")
+    cfg = datagen.C4D()
+    T = 64
+    x, lg = cfg.x(T), cfg.logits(T)
+    ids_o, _ = oracle.route_topk(lg, cfg.top_k)
+    recs = _dbf_moe_dev(cfg, sorted(set(int(e) for e in ids_o.ravel())))
+    toks = [0, 5, 17, 31, 32, 47, 58, 63]
+    o, oids, ow = oracle.moe_dbf_ffn(oracle.bf16_to_f64(x), lg, _dbf_moe_oracle_experts(cfg), cfg.H, cfg.I, cfg.r,
+                                     cfg.top_k, tokens=toks)
+    y, ids, w = brq().moe_dbf_ffn(dev(x), dev(lg), *recs, cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k,
+                                  out_dtype=torch.float32, return_routing=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    check_f32(f64(y)[toks], o[toks], F32_TOL, "moe dbf deployed T=64")
+
+
+# the ABI limits of the routed layers: T = 256 tokens, E = 1024 experts,
+# top-16, with small projections (H = I = r = 128) so that every expert fits
+def test_moe_limits():
+    say("moe limits T=256 E=1024 k=16")
+    cfg = datagen.C4(E=1024, H=128, I=128, top_k=16, layer=9)
+    ex = _Experts(cfg)
+    T = 256
+    x, lg = cfg.x(T), cfg.logits(T)
+    o, oids, ow = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, cfg.top_k)
+    y, ids, w = brq().moe_ffn(dev(x), dev(lg), *ex.d, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32,
+                              return_routing=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=1e-7)
+    check_f32(f64(y), o, F32_TOL, "moe limits")
+
+
+def test_moe_dbf_limits():
+    say("moe dbf limits T=256 E=1024 k=16")
+    cfg = datagen.C4D(E=1024, H=128, I=128, r=128, top_k=16, layer=9)
+    y, o = _dbf_moe_case(cfg, 256)
+    check_f32(f64(y), o, F32_TOL, "moe dbf limits")
+
+
 def test_moe_ties_and_small_shapes():
     say("moe ties, E=8 H=256 I=128 k=3")
     cfg = datagen.C4(E=8, H=256, I=128, top_k=3, layer=5)
