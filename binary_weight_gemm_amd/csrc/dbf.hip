@@ -148,19 +148,31 @@ static bool dbf_decode_path(int64_t M, int64_t n, int64_t r) {
   return M <= 8 && dbf_split(dbf_maxr(M) + 1, n, a) && dbf_split(2 * dbf_maxr(M), r, b);
 }
 
-// Tiled path, between the stages: one workgroup per h_s row finds the row's
-// largest magnitude, writes the row as fp16 pieces of h_s * 2^s (rows 2t and
-// 2t+1, permuted operand order) with the largest near 2^14, and records -s.
-__global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs, int r, uint16_t* __restrict__ hp,
-                                                   int* __restrict__ rexp) {
+// Tiled path, between the stages: one workgroup per h_s row adds the row's
+// S K-slice partials (slice order), finds the row's largest magnitude, writes
+// the row as fp16 pieces of h_s * 2^s (rows 2t and 2t+1, permuted operand
+// order) with the largest near 2^14, and records -s.
+__global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs, int M, int r, int S,
+                                                   uint16_t* __restrict__ hp, int* __restrict__ rexp) {
   __shared__ uint32_t s_max[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const float* row = hs + (size_t)t * r;
+  const size_t slice = (size_t)M * r;
   const int quads = r >> 3;  // 8 values (4 permuted pairs) per quad
+  // values k .. k+3 and k+16 .. k+19 of the row, partials added in slice order
+  auto get = [&](int k, f32x4& a, f32x4& b) {
+    a = *reinterpret_cast<const f32x4*>(row + k);
+    b = *reinterpret_cast<const f32x4*>(row + k + 16);
+    for (int sl = 1; sl < S; ++sl) {
+      a += *reinterpret_cast<const f32x4*>(row + sl * slice + k);
+      b += *reinterpret_cast<const f32x4*>(row + sl * slice + k + 16);
+    }
+  };
   uint32_t mx = 0;
   for (int q = tid; q < quads; q += 256) {
     const int k = 32 * (q >> 2) + 4 * (q & 3);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k), b = *reinterpret_cast<const f32x4*>(row + k + 16);
+    f32x4 a, b;
+    get(k, a, b);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       mx = max(mx, max(__float_as_uint(a[i]) & 0x7fffffffu, __float_as_uint(b[i]) & 0x7fffffffu));
@@ -173,7 +185,8 @@ __global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs,
   if (tid == 0) rexp[t] = -s;
   for (int q = tid; q < quads; q += 256) {
     const int k = 32 * (q >> 2) + 4 * (q & 3);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k), b = *reinterpret_cast<const f32x4*>(row + k + 16);
+    f32x4 a, b;
+    get(k, a, b);
     uint32_t oh[4], ol[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -189,12 +202,13 @@ __global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs,
   }
 }
 
-// workspace: h_s fp32 [M][r]; tiled path also the pieces [2M][r], the row
-// exponents [M] and the permuted d_in [n]
+// workspace: h_s fp32 [M][r]; the tiled path holds one such partial per
+// K-slice of stage 1, then the pieces [2M][r], the row exponents [M] and the
+// permuted d_in [n]
 size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
   (void)m;
-  const size_t hs = align256((size_t)M * r * 4);
-  if (dbf_decode_path(M, n, r)) return hs;
+  if (dbf_decode_path(M, n, r)) return align256((size_t)M * r * 4);
+  const size_t hs = align256((size_t)dbf1_ksplit((int)M, (int)r, (int)n) * M * r * 4);
   return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4) + align256((size_t)n * 2);
 }
 
@@ -228,7 +242,8 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
     if (M <= 4) return dbf_decode<4, 8>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hs, st);
     return dbf_decode<8, 16>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hs, st);
   }
-  base += align256((size_t)M * r * 4);
+  const int ks = dbf1_ksplit(M, r, n);
+  base += align256((size_t)ks * M * r * 4);
   uint16_t* hp = reinterpret_cast<uint16_t*>(base);
   base += align256((size_t)2 * M * r * 2);
   int* rexp = reinterpret_cast<int*>(base);
@@ -238,9 +253,10 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
   if (e != hipSuccess) return e;
   TileArgs a1{};
   a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kperm = dinp; a1.diag = d_mid; a1.out = hs;
+  a1.ksplit = ks;
   e = launch_tile_dbf1(a1, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dbf_split, dim3(M), dim3(256), 0, st, hs, r, hp, rexp);
+  hipLaunchKernelGGL(k_dbf_split, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   TileArgs a2{};

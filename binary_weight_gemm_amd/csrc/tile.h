@@ -19,7 +19,10 @@ struct TileArgs {
   const int* rexp;          // per-token exponent applied to the piece sum (EPI_PAIRSUM)
   void* out;
   int out_bf16;
+  int ksplit = 1;           // K-slices (grid y); EPI_HS32 writes slice s at out + s*M*N
 };
+
+int dbf1_ksplit(int M, int r, int n);
 
 hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st);
 hipError_t launch_tile_dbf2(const TileArgs& a, hipStream_t st);

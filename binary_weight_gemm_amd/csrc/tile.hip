@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   const int tm = bid / tiles_n, tn = bid % tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = p.K / BK;
+  // K-slice blockIdx.y of p.ksplit: k-steps kt0 .. kt0 + nk - 1
+  const int nk = p.K / BK / p.ksplit;
+  const int kt0 = (int)blockIdx.y * nk;
 
   // ---- global -> register staging --------------------------------------
   uint4 ra[A_UNITS][2];
@@ -152,13 +154,13 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  load_stage(0);
+  load_stage(kt0);
   store_stage(0);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
+    if (kt + 1 < nk) load_stage(kt0 + kt + 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       u32x4 af[TM], bfr[TN];
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
         }
       } else if (EPI == EPI_HS32) {
         const float dm = f16_bits_to_f32(p.diag[col]);
-        float* hs = reinterpret_cast<float*>(p.out);
+        float* hs = reinterpret_cast<float*>(p.out) + (size_t)blockIdx.y * p.M * p.N;  // this K-slice's partial
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
@@ -216,8 +218,19 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 template <int BM, int BN, int AMODE, int BMODE, int EPI>
 static hipError_t run_tile(const TileArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_tile<BM, BN, AMODE, BMODE, EPI>), dim3(tiles), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_tile<BM, BN, AMODE, BMODE, EPI>), dim3(tiles, a.ksplit), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// DBF stage 1 tiling: 128 x 128 tiles, the reduction axis split into
+// ksplit slices (a power of two, at most 8, whole 64-wide k-steps) until
+// tiles x slices fills the 256 compute units; each slice writes its own fp32
+// partial h_s and k_dbf_split adds them in slice order
+int dbf1_ksplit(int M, int r, int n) {
+  const long tiles = (long)((M + 127) / 128) * ((r + 127) / 128);
+  int s = 1;
+  while (s < 8 && tiles * s < 256 && (n / 64) % (2 * s) == 0) s *= 2;
+  return s;
 }
 
 hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
@@ -231,9 +244,7 @@ hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64
 }
 
 hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st) {
-  const long mid = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (mid >= 256) return run_tile<128, 128, 0, BM_PERK, EPI_HS32>(a, st);
-  return run_tile<64, 64, 0, BM_PERK, EPI_HS32>(a, st);
+  return run_tile<128, 128, 0, BM_PERK, EPI_HS32>(a, st);
 }
 
 hipError_t launch_tile_dbf2(const TileArgs& a, hipStream_t st) {
