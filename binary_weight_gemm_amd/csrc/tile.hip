@@ -224,12 +224,13 @@ static hipError_t run_tile(const TileArgs& a, hipStream_t st) {
 
 // DBF stage 1 tiling: 128 x 128 tiles, the reduction axis split into
 // ksplit slices (a power of two, at most 8, whole 64-wide k-steps) until
-// tiles x slices fills the 256 compute units; each slice writes its own fp32
-// partial h_s and k_dbf_split adds them in slice order
+// tiles x slices gives two workgroups per compute unit (the second hides the
+// first's loads); each slice writes its own fp32 partial h_s and k_dbf_split
+// adds them in slice order
 int dbf1_ksplit(int M, int r, int n) {
   const long tiles = (long)((M + 127) / 128) * ((r + 127) / 128);
   int s = 1;
-  while (s < 8 && tiles * s < 256 && (n / 64) % (2 * s) == 0) s *= 2;
+  while (s < 8 && tiles * s < 512 && (n / 64) % (2 * s) == 0) s *= 2;
   return s;
 }
 
@@ -247,9 +248,12 @@ hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st) {
   return run_tile<128, 128, 0, BM_PERK, EPI_HS32>(a, st);
 }
 
+// DBF stage 2: 64 x 128 tiles (two or more workgroups per compute unit, so
+// one workgroup's loads hide behind another's products) while they number at
+// least two per compute unit, 64 x 64 below
 hipError_t launch_tile_dbf2(const TileArgs& a, hipStream_t st) {
-  const long mid = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (mid >= 256) return run_tile<128, 128, 1, BM_ONE, EPI_PAIRSUM>(a, st);
+  const long mid = (long)((a.M + 63) / 64) * ((a.N + 127) / 128);
+  if (mid >= 512) return run_tile<64, 128, 1, BM_ONE, EPI_PAIRSUM>(a, st);
   return run_tile<64, 64, 1, BM_ONE, EPI_PAIRSUM>(a, st);
 }
 
