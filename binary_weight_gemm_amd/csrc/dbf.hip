@@ -203,13 +203,12 @@ __global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs,
 }
 
 // workspace: h_s fp32 [M][r]; the tiled path holds one such partial per
-// K-slice of stage 1, then the pieces [2M][r], the row exponents [M] and the
-// permuted d_in [n]
+// K-slice of stage 1, then the pieces [2M][r] and the row exponents [M]
 size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
   (void)m;
   if (dbf_decode_path(M, n, r)) return align256((size_t)M * r * 4);
   const size_t hs = align256((size_t)dbf1_ksplit((int)M, (int)r, (int)n) * M * r * 4);
-  return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4) + align256((size_t)n * 2);
+  return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4);
 }
 
 template <int MAXR1, int MAXR2>
@@ -247,14 +246,10 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
   uint16_t* hp = reinterpret_cast<uint16_t*>(base);
   base += align256((size_t)2 * M * r * 2);
   int* rexp = reinterpret_cast<int*>(base);
-  base += align256((size_t)M * 4);
-  uint16_t* dinp = reinterpret_cast<uint16_t*>(base);
-  hipError_t e = launch_prep_f16(d_in, n, dinp, st);
-  if (e != hipSuccess) return e;
   TileArgs a1{};
-  a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kperm = dinp; a1.diag = d_mid; a1.out = hs;
+  a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kmag = d_in; a1.diag = d_mid; a1.out = hs;
   a1.ksplit = ks;
-  e = launch_tile_dbf1(a1, st);
+  hipError_t e = launch_tile_dbf1(a1, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dbf_split, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
   e = hipGetLastError();

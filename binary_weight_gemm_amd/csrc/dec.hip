@@ -8,9 +8,8 @@
 
 namespace brq {
 
-// One thread per run of 32: load 32 values, write them in the permuted order
-// slot 2b+h <- k = 16h+b, as fp16.
-template <bool FROM_BF16>
+// One thread per run of 32: load 32 bf16 values, write them in the permuted
+// order slot 2b+h <- k = 16h+b, as fp16.
 __global__ __launch_bounds__(256) void k_prep(const uint16_t* __restrict__ src, int64_t runs,
                                               uint16_t* __restrict__ dst) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -28,14 +27,8 @@ __global__ __launch_bounds__(256) void k_prep(const uint16_t* __restrict__ src, 
     // element b lives in word b/2 (half b%2); element 16+b in word 8+b/2
     const uint32_t lo16 = (b & 1) ? (v[b >> 1] >> 16) : (v[b >> 1] & 0xffffu);
     const uint32_t hi16 = (b & 1) ? (v[8 + (b >> 1)] >> 16) : (v[8 + (b >> 1)] & 0xffffu);
-    uint32_t a, c;
-    if (FROM_BF16) {
-      a = f32_to_f16_bits(bf16_to_f32(lo16));
-      c = f32_to_f16_bits(bf16_to_f32(hi16));
-    } else {
-      a = lo16;
-      c = hi16;
-    }
+    const uint32_t a = f32_to_f16_bits(bf16_to_f32(lo16));
+    const uint32_t c = f32_to_f16_bits(bf16_to_f32(hi16));
     o[b] = a | (c << 16);
   }
   uint4* d = reinterpret_cast<uint4*>(dst + t * 32);
@@ -47,15 +40,10 @@ __global__ __launch_bounds__(256) void k_prep(const uint16_t* __restrict__ src, 
 
 hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st) {
   const int64_t runs = rows * (K / 32);
-  hipLaunchKernelGGL(k_prep<true>, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, st, x, runs, xp);
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, st, x, runs, xp);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream_t st) {
-  const int64_t runs = K / 32;
-  hipLaunchKernelGGL(k_prep<false>, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, st, v, runs, vp);
-  return hipGetLastError();
-}
 
 // One-launch product for M <= 8: wave w owns chunks w*CPW .. w*CPW+CPW-1 of
 // the reduction. It issues the loads of its activation slice (all MAXR row

@@ -16,7 +16,6 @@ hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, uint64_t* sig
 // bf16 [rows][K] -> fp16 [rows][K] in the permuted operand order.
 hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st);
 // fp16 vector [K] -> fp16 [K] in the permuted operand order.
-hipError_t launch_prep_f16(const uint16_t* v, int64_t K, uint16_t* vp, hipStream_t st);
 
 // ---- group-128 product ----------------------------------------------------
 // Few activation rows (M <= 64): split-K inside a workgroup, 16 output columns

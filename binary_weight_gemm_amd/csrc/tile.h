@@ -14,7 +14,7 @@ struct TileArgs {
   int M, N, K;              // A rows, output columns, reduction length
   const uint64_t* signs;    // SIGN1 plane [N][K/64]
   const uint16_t* scales;   // group-128 scales [N][K/128] (BM_GROUP)
-  const uint16_t* kperm;    // permuted fp16 per-k magnitudes [K] (BM_PERK)
+  const uint16_t* kmag;     // fp16 per-k magnitudes [K], natural order (BM_PERK)
   const uint16_t* diag;     // fp16 per-column diagonal (EPI_HS32, EPI_PAIRSUM)
   const int* rexp;          // per-token exponent applied to the piece sum (EPI_PAIRSUM)
   void* out;

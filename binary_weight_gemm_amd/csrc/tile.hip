@@ -96,9 +96,10 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
       }
       rb[u] = make_uint2(dw, mag);
       if (BMODE == BM_PERK) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(p.kperm + k0 + 32 * q + 2 * b0);
-        rk[u][0] = kp[0];
-        rk[u][1] = kp[1];
+        // natural-order magnitudes of this unit's pairs (k, k + 16), k = run + b0 .. b0 + 7
+        const uint16_t* kr = p.kmag + k0 + 32 * q + b0;
+        rk[u][0] = *reinterpret_cast<const u32x4*>(kr);
+        rk[u][1] = *reinterpret_cast<const u32x4*>(kr + 16);
       }
     }
   };
@@ -137,7 +138,11 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int bit = b0 + t;
-        const uint32_t mag = (BMODE == BM_PERK) ? rk[u][t >> 2][t & 3] : rb[u].y;
+        uint32_t mag = rb[u].y;
+        if (BMODE == BM_PERK) {
+          const uint32_t lw = rk[u][0][t >> 1], hw = rk[u][1][t >> 1];
+          mag = (t & 1) ? ((lw >> 16) | (hw & 0xffff0000u)) : ((lw & 0xffffu) | (hw << 16));
+        }
         o[t] = ((dw << (15 - bit)) & 0x80008000u) | mag;
       }
       uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][col * LDK + 32 * q + 2 * b0]);
