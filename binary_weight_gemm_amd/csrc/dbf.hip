@@ -152,7 +152,74 @@ static bool dbf_decode_path(int64_t M, int64_t n, int64_t r) {
 // S K-slice partials (slice order), finds the row's largest magnitude, writes
 // the row as fp16 pieces of h_s * 2^s (rows 2t and 2t+1, permuted operand
 // order) with the largest near 2^14, and records -s.
+template <int QPT>
 __global__ __launch_bounds__(256) void k_dbf_split(const float* __restrict__ hs, int M, int r, int S,
+                                                   uint16_t* __restrict__ hp, int* __restrict__ rexp) {
+  __shared__ uint32_t s_max[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* row = hs + (size_t)t * r;
+  const size_t slice = (size_t)M * r;
+  const int quads = r >> 3;  // 8 values (4 permuted pairs) per quad; quads <= 256 * QPT
+  // thread tid holds quads tid + 256 i: values k .. k+3 and k+16 .. k+19 of
+  // the row, the S (<= 8) partials added in slice order; every load is issued
+  // before the sums (slices past S re-read slice 0 and are not added)
+  f32x4 a[QPT], b[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int q = tid + 256 * i;
+    const int k = q < quads ? 32 * (q >> 2) + 4 * (q & 3) : 0;
+    f32x4 pa[8], pb[8];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const size_t off = (sl < S ? sl : 0) * slice + k;
+      pa[sl] = *reinterpret_cast<const f32x4*>(row + off);
+      pb[sl] = *reinterpret_cast<const f32x4*>(row + off + 16);
+    }
+    a[i] = pa[0];
+    b[i] = pb[0];
+#pragma unroll
+    for (int sl = 1; sl < 8; ++sl)
+      if (sl < S) {
+        a[i] += pa[sl];
+        b[i] += pb[sl];
+      }
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i)
+    if (tid + 256 * i < quads) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        mx = max(mx, max(__float_as_uint(a[i][e]) & 0x7fffffffu, __float_as_uint(b[i][e]) & 0x7fffffffu));
+    }
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+  __syncthreads();
+  mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const int s = 14 - ((int)(mx >> 23) - 127);  // 0 -> s = 141, harmless: every value is 0
+  if (tid == 0) rexp[t] = -s;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int q = tid + 256 * i;
+    if (q >= quads) continue;
+    uint32_t oh[4], ol[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint16_t ha, la, hb, lb;
+      split_f16(__builtin_amdgcn_ldexpf(a[i][e], s), ha, la);
+      split_f16(__builtin_amdgcn_ldexpf(b[i][e], s), hb, lb);
+      oh[e] = (uint32_t)ha | ((uint32_t)hb << 16);
+      ol[e] = (uint32_t)la | ((uint32_t)lb << 16);
+    }
+    // pairs (k+e, k+16+e) are words 4(q&3)+e of run q>>2: 8 fp16 from 8*q
+    *reinterpret_cast<uint4*>(hp + (size_t)(2 * t) * r + 8 * q) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+    *reinterpret_cast<uint4*>(hp + (size_t)(2 * t + 1) * r + 8 * q) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  }
+}
+
+// Rows too long to keep in registers (r > 16384): the same in two passes over
+// the row, the partials added again in the second.
+__global__ __launch_bounds__(256) void k_dbf_split_wide(const float* __restrict__ hs, int M, int r, int S,
                                                    uint16_t* __restrict__ hp, int* __restrict__ rexp) {
   __shared__ uint32_t s_max[4];
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -251,7 +318,17 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
   a1.ksplit = ks;
   hipError_t e = launch_tile_dbf1(a1, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dbf_split, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
+  const int qpt = (r / 8 + 255) / 256;  // quads of 8 values per thread
+  if (qpt <= 1)
+    hipLaunchKernelGGL(k_dbf_split<1>, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
+  else if (qpt <= 2)
+    hipLaunchKernelGGL(k_dbf_split<2>, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
+  else if (qpt <= 4)
+    hipLaunchKernelGGL(k_dbf_split<4>, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
+  else if (qpt <= 8)
+    hipLaunchKernelGGL(k_dbf_split<8>, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
+  else
+    hipLaunchKernelGGL(k_dbf_split_wide, dim3(M), dim3(256), 0, st, hs, M, r, ks, hp, rexp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   TileArgs a2{};

@@ -351,6 +351,15 @@ def test_dbf_small(M, m, n, r):
     check_f32(f64(y), o, F32_TOL, f"dbf {M},{m},{n},{r}")
 
 
+# long h_s rows on the tiled path: the row split keeps 1, 2, 4 or 8 quads of
+# values per thread in registers (r up to 16384) and re-reads longer rows
+@pytest.mark.parametrize("r", [4096, 8192, 16384, 16512])
+def test_dbf_tiled_long_rank(r):
+    say("dbf tiled, long rank", r)
+    y, o = _dbf_case(9, 64, 256, r, 9000 + r)
+    check_f32(f64(y), o, F32_TOL, f"dbf 9,64,256,{r}")
+
+
 # h_s of small magnitude (d_mid at 2^-12 of its usual spread, so |h_s| ~ 1e-3
 # and below): an unscaled fp16 hi/lo pair keeps few bits there (its lo piece is
 # subnormal below 2^-3); the scaled pieces keep about 22. Decode (M <= 8) and
