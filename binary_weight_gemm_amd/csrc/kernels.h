@@ -55,8 +55,8 @@ hipError_t launch_gemm_lr(const uint16_t* x, int M, int N, int K, const uint64_t
                           int y_bf16, void* ws, hipStream_t st);
 
 // ---- DBF chain -------------------------------------------------------------
-// stage 1: hp[2M][r] (fp16 hi/lo pairs, permuted) = D_mid (V (D_in x))
-// stage 2: y[M][m] = D_out (U h_s)
+// stage 1: h_s[M][r] (fp32) = D_mid (V (D_in x))
+// stage 2: y[M][m] = D_out (U h_s), h_s taken as scaled fp16 pieces
 hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in,
                       const uint64_t* v, const uint16_t* d_mid, const uint64_t* u,
                       const uint16_t* d_out, void* y, int y_bf16, void* ws, hipStream_t st);

@@ -31,8 +31,11 @@
  * accumulates in fp32. Activations are carried as fp16 inside the products;
  * bf16 activations must satisfy |x| < 65504 (values below 2^-14 are kept on
  * fp16's subnormal grid, an absolute change of at most 2^-25). fp32
- * intermediates (DBF h, MoE SwiGLU output) are carried as an fp16 hi/lo pair
- * (22 significant bits) under the same range condition.
+ * intermediates (DBF h, MoE SwiGLU output) are stored as fp32 and enter the
+ * next product as two fp16 pieces of v * 2^s, s a power of two that puts the
+ * largest magnitude of the staged slice (or row) near 2^14: about 22
+ * significant bits for every value down to 2^-18 of that maximum, whatever
+ * its magnitude.
  *
  * Alignment: weight planes, scales and activation rows must be 16-byte
  * aligned; workspaces 256-byte aligned.
@@ -223,7 +226,8 @@ typedef struct {
  * 2048 x 512 down). Routing as in brq_moe_ffn. gate/up first factors consume
  * the token's hidden vector shared by its experts; second factors and the down
  * chain consume the route's own intermediates (section 4's two input
- * topologies). Intermediates are carried as fp16 hi/lo pairs.
+ * topologies). Intermediates are fp32, taken by the next product as scaled
+ * fp16 pieces (see Numerics above).
  *
  *   x, logits, T, E, top_k, y, ids, w   as for brq_moe_ffn
  *   gate, up   host pointers to records of H -> I chains (m = I, n = H)
