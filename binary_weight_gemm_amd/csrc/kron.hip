@@ -1,121 +1,191 @@
 // Kronecker-factored orthogonal activation rotation x' = (H (x) R) x, computed
 // per token as X' = H X R^T with X the token reshaped row-major to [64][64]
 // (BWLA commentary: section 3, OKT with Kronecker factors; section 5, the same
-// transform applied to the activations). fp32 arithmetic, bf16 output.
+// transform applied to the activations). bf16 output.
 //
-// One workgroup per compute unit (persistent): H^T and R^T are staged in LDS
-// once per workgroup (rows padded to 65 floats so the transposing stores and
-// the column reads spread over all banks); each of its six waves then takes
-// tokens in turn. For a token, the wave stages X^T in its own LDS slot, forms
-// T = X R^T with lane (a, b) computing the 8 x 8 block rows 8a.., columns 8b..,
-// writes T back to its slot and forms Y = H T the same way. No barrier is
-// needed between tokens: a wave only touches its own slot.
+// Both products are 64 x 64 x 64 contractions and run on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16, fp32 accumulate). x is bf16 already; the
+// fp32 factors H and R and the fp32 intermediate T = X R^T enter as three
+// bf16 pieces each (v = p0 + p1 + p2, each piece the round-to-nearest of what
+// is left, 24 significant bits together). T = sum_p X R_p^T (three products)
+// and Y = sum_{p+q<=2} H_p T_q (six products): a product of two pieces is
+// exact in fp32 and the dropped terms are below 2^-24 of the largest, so Y
+// matches fp32 arithmetic to a few units of 2^-24 before its bf16 rounding.
+//
+// One wave per token (the waves of the grid take tokens in turn). The piece
+// fragments of R and H are laid out in LDS once per workgroup in the per-lane
+// operand order (fragment f, lane l at 16 (64 f + l) bytes: conflict-free
+// 16-byte reads). X is read straight from global memory as the A operand
+// (lane l: row 32i + l%32, k = 16s + 8(l/32) .. +7: 16 contiguous bytes).
+// T's accumulator layout (lane l, item r: row 8(r/4) + 4(l/32) + r%4, column
+// l%32) becomes the B operand of the second product (lane l: column l%32, k =
+// 8(l/32) .. +7 of a 16-row step) with one permlane32 swap per pair of items:
+// of the rows 16u .. 16u+15 of a tile, lanes 0-31 hold 0-3 and 8-11 and lanes
+// 32-63 hold 4-7 and 12-15; swapping the upper lanes' first half with the
+// lower lanes' second half leaves rows 0-7 in lanes 0-31 and 8-15 in 32-63.
 #include "common.h"
 #include "kernels.h"
 
 namespace brq {
 
-constexpr int KRON_WAVES = 6;
-constexpr int KRON_LD = 65;  // padded row length of H^T and R^T
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// v = p0 + p1 + p2 (bf16 bits): each piece rounds what the previous left
+// (exact remainders in fp32)
+__device__ __forceinline__ void split3_bf16(float v, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+  p0 = f32_to_bf16_bits(v);
+  const float r0 = v - bf16_to_f32(p0);
+  p1 = f32_to_bf16_bits(r0);
+  const float r1 = r0 - bf16_to_f32(p1);
+  p2 = f32_to_bf16_bits(r1);
+}
+
+constexpr int KRON_WAVES = 4;
+constexpr int KRON_FRAGS = 2 * 2 * 4 * 3;  // (factor R/H, row tile, k-step, piece)
+constexpr size_t KRON_LDS = (size_t)KRON_FRAGS * 64 * 16;
 
 __global__ __launch_bounds__(64 * KRON_WAVES) void k_kron(const uint16_t* __restrict__ x, int M,
                                                          const float* __restrict__ H, const float* __restrict__ R,
                                                          uint16_t* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) float kl[];
-  float* Ht = kl;                       // Ht[c][a] = H[a][c], row length KRON_LD
-  float* Rt = kl + 64 * KRON_LD;        // Rt[d][b] = R[b][d]
+  extern __shared__ __attribute__((aligned(16))) uint4 kf[];  // [KRON_FRAGS][64]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* B = kl + 2 * 64 * KRON_LD + wave * 64 * 64;  // this wave's 64 x 64 slot
-  for (int i = tid; i < 64 * 64; i += blockDim.x) {
-    const int r = i >> 6, c = i & 63;
-    Ht[c * KRON_LD + r] = H[i];
-    Rt[c * KRON_LD + r] = R[i];
+  // fragment (m, tile, s) for lane l: factor m (0 R, 1 H), row 32 tile + l%32,
+  // k = 16 s + 8 (l/32) + e, e = 0..7, as three piece fragments
+  for (int idx = tid; idx < 2 * 2 * 4 * 64; idx += blockDim.x) {
+    const int l = idx & 63, s = (idx >> 6) & 3, tile = (idx >> 8) & 1, m = idx >> 9;
+    const float* src = (m == 0 ? R : H) + (32 * tile + (l & 31)) * 64 + 16 * s + 8 * (l >> 5);
+    uint32_t pc[3][4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t a0, a1, a2, b0, b1, b2;
+      split3_bf16(src[2 * e2], a0, a1, a2);
+      split3_bf16(src[2 * e2 + 1], b0, b1, b2);
+      pc[0][e2] = a0 | (b0 << 16);
+      pc[1][e2] = a1 | (b1 << 16);
+      pc[2][e2] = a2 | (b2 << 16);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      kf[(((m * 2 + tile) * 4 + s) * 3 + p) * 64 + l] = make_uint4(pc[p][0], pc[p][1], pc[p][2], pc[p][3]);
   }
   __syncthreads();
-  const int ab = (lane >> 3) * 8, bb = (lane & 7) * 8;
+  const int h = lane >> 5, c = lane & 31;
   const int nwaves = gridDim.x * KRON_WAVES;
   for (int t = blockIdx.x * KRON_WAVES + wave; t < M; t += nwaves) {
-    // X^T: B[d][a] = x[t][64a + d]; lane reads run a = lane of 64 values
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * 4096 + lane * 64);
-    uint4 v[8];
+    // the fragments are read from LDS for every token: an opaque offset keeps
+    // the compiler from hoisting all 48 of them into registers (192 VGPRs),
+    // which would leave room for one wave per SIMD only
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    const u32x4* fr = reinterpret_cast<const u32x4*>(kf) + lo;
+    auto frag = [&](int m, int tile, int s, int p) { return fr[(((m * 2 + tile) * 4 + s) * 3 + p) * 64]; };
+    const uint16_t* xt = x + (size_t)t * 4096;
+    u32x4 xa[2][4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = src[q];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+      for (int s = 0; s < 4; ++s) xa[i][s] = *reinterpret_cast<const u32x4*>(xt + (32 * i + c) * 64 + 16 * s + 8 * h);
+    // Y = H T, one row tile of T at a time (T rows 32 ti .. are the k-steps
+    // s = 2 ti, 2 ti + 1 of the second product), so that only half of T and
+    // its pieces are live at once
+    f32x16 Y[2][2];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int d = q * 8 + 2 * h;
-        B[d * 64 + lane] = bf16_to_f32(w[h] & 0xffffu);
-        B[(d + 1) * 64 + lane] = bf16_to_f32(w[h] >> 16);
-      }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Y[i][j][r] = 0.f;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      // T rows 32 ti .. 32 ti + 31 = X rows of that tile times R^T
+      f32x16 T[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) T[j][r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int p = 0; p < 3; ++p) T[j] = mfma32_bf16(xa[ti][s], frag(0, j, s, p), T[j]);
+      // those rows as B operand pieces: piece q of column tile j, step 2 ti + u
+      u32x4 tb[3][2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float v[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[j][8 * u + q]),
+                                                             __float_as_uint(T[j][8 * u + 4 + q]), false, false);
+            v[q] = __uint_as_float(sw[0]);
+            v[4 + q] = __uint_as_float(sw[1]);
+          }
+          uint32_t pc[3][4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t a0, a1, a2, b0, b1, b2;
+            split3_bf16(v[2 * e2], a0, a1, a2);
+            split3_bf16(v[2 * e2 + 1], b0, b1, b2);
+            pc[0][e2] = a0 | (b0 << 16);
+            pc[1][e2] = a1 | (b1 << 16);
+            pc[2][e2] = a2 | (b2 << 16);
+          }
+#pragma unroll
+          for (int q = 0; q < 3; ++q) tb[q][j][u] = u32x4{pc[q][0], pc[q][1], pc[q][2], pc[q][3]};
+        }
+      // Y += H_p T_q over the piece pairs p + q <= 2, steps 2 ti and 2 ti + 1
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            const u32x4 a = frag(1, i, 2 * ti + u, p);
+#pragma unroll
+            for (int q = 0; q + p < 3; ++q)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) Y[i][j] = mfma32_bf16(a, tb[q][j][u], Y[i][j]);
+          }
     }
-    float acc[8][8];
+    // bf16 out: lane l holds column 32 j + l%32 of rows 32 i + 8 (r/4) + 4 h +
+    // r%4. Neighbouring lanes trade one item of each pair (r, r+1): the even
+    // lane then writes columns c, c+1 of row r, the odd lane columns c-1, c of
+    // row r+1, four bytes each
+    uint16_t* yt = y + (size_t)t * 4096;
+    const bool odd = c & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-    // T[a][b] = sum_d X[a][d] R[b][d]
-    for (int d = 0; d < 64; ++d) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&B[d * 64 + ab]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&B[d * 64 + ab + 4]);
-      float rb[8];
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rb[j] = Rt[d * KRON_LD + bb + j];
-      const float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xa[i], rb[j], acc[i][j]);
-    }
-    // T row-major: B[c][b] (every lane of this wave has finished reading X^T:
-    // LDS operations of one wave complete in order)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<float4*>(&B[(ab + i) * 64 + bb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-      *reinterpret_cast<float4*>(&B[(ab + i) * 64 + bb + 4]) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-    // Y[a][b] = sum_c H[a][c] T[c][b]
-    for (int c = 0; c < 64; ++c) {
-      float ha[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ha[i] = Ht[c * KRON_LD + ab + i];
-      const float4 t0 = *reinterpret_cast<const float4*>(&B[c * 64 + bb]);
-      const float4 t1 = *reinterpret_cast<const float4*>(&B[c * 64 + bb + 4]);
-      const float tb[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(ha[i], tb[j], acc[i][j]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t o[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        o[h] = (uint32_t)f32_to_bf16_bits(acc[i][2 * h]) | ((uint32_t)f32_to_bf16_bits(acc[i][2 * h + 1]) << 16);
-      *reinterpret_cast<uint4*>(y + (size_t)t * 4096 + (ab + i) * 64 + bb) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+        for (int r = 0; r < 16; r += 2) {
+          const float a = Y[i][j][r], b = Y[i][j][r + 1];
+          const float got = __shfl_xor(odd ? a : b, 1);
+          const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3) + (odd ? 1 : 0);
+          const uint32_t lo = f32_to_bf16_bits(odd ? got : a), hi = f32_to_bf16_bits(odd ? b : got);
+          *reinterpret_cast<uint32_t*>(yt + row * 64 + 32 * j + (c & ~1)) = lo | (hi << 16);
+        }
   }
 }
 
 hipError_t launch_kron(const uint16_t* x, int M, const float* H, const float* R, uint16_t* y, hipStream_t st) {
-  const size_t lds = (size_t)(2 * 64 * KRON_LD + KRON_WAVES * 64 * 64) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_kron),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
+  // three workgroups per compute unit fit the 48 KiB of fragments each
   const int need = (M + KRON_WAVES - 1) / KRON_WAVES;
-  const int grid = need < cus ? need : cus;
-  hipLaunchKernelGGL(k_kron, dim3(grid), dim3(64 * KRON_WAVES), lds, st, x, M, H, R, y);
+  const int grid = need < 3 * cus ? need : 3 * cus;
+  hipLaunchKernelGGL(k_kron, dim3(grid), dim3(64 * KRON_WAVES), KRON_LDS, st, x, M, H, R, y);
   return hipGetLastError();
 }
 
