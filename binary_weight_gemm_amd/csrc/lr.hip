@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_lr_prep(const uint16_t* __restrict__ v,
   u_pad[q] = i < r ? u[(size_t)n * r + i] : (uint16_t)0;
 }
 
-// t = x . V^T for 32 rows (two 16-row tiles) per workgroup on the fp16
+// t = x . V^T for 16 TT rows (TT 16-row tiles) per workgroup on the fp16
 // matrix cores: x converted to fp16 in registers (the same conversion the
 // product's own activation staging applies), V as given (fp16, padded to 64
 // rows). The waves take interleaved 64-k blocks (wave w of eight: blocks w,
@@ -87,11 +87,10 @@ __global__ __launch_bounds__(256) void k_lr_prep(const uint16_t* __restrict__ v,
 // Lane (kb, j): A = row m0+16t+j, k 8kb.. of each 32-k half-block; B = factor
 // 16c+j, same k. Factor tiles c >= NC (past the rank) are written as zeros.
 // HILO: store fp16 hi/lo pairs [M][128] (hi at i, lo at 64+i), else fp32 [M][64].
-template <bool HILO, int NC>
+template <bool HILO, int NC, int TT>
 __global__ __launch_bounds__(512) void k_lr_t(const uint16_t* __restrict__ x, int M, int K,
                                               const uint16_t* __restrict__ vp, uint16_t* __restrict__ t16,
                                               float* __restrict__ t32) {
-  constexpr int TT = 2;                 // row tiles per workgroup
   constexpr int BPR = NC <= 2 ? 4 : 2;  // blocks per round: the round's loads stay in registers
   constexpr int NW = 8;                 // waves: interleaved 64-k blocks
   __shared__ f32x4 red[NW - 1][TT][NC][64];
@@ -212,16 +211,23 @@ hipError_t launch_gemm_lr(const uint16_t* x, int M, int N, int K, const uint64_t
                      w.vb, w.u_pad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 tg((unsigned)((M + 31) / 32));
+  // two row tiles per workgroup once that still gives one workgroup per
+  // compute unit, one below (M = 4096: 256 workgroups of 16 rows)
+  const bool two = (M + 31) / 32 >= 256;
+  const dim3 tg((unsigned)(two ? (M + 31) / 32 : (M + 15) / 16));
   const int nc = (r + 15) / 16;  // factor tiles of 16 that the rank needs
   auto lr_t = [&](auto hilo) {
     constexpr bool H = decltype(hilo)::value;
+#define BRQ_LRT(NC)                                                                                   \
+  if (two) hipLaunchKernelGGL((k_lr_t<H, NC, 2>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32); \
+  else hipLaunchKernelGGL((k_lr_t<H, NC, 1>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32)
     switch (nc) {
-      case 1: hipLaunchKernelGGL((k_lr_t<H, 1>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32); break;
-      case 2: hipLaunchKernelGGL((k_lr_t<H, 2>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32); break;
-      case 3: hipLaunchKernelGGL((k_lr_t<H, 3>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32); break;
-      default: hipLaunchKernelGGL((k_lr_t<H, 4>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32); break;
+      case 1: BRQ_LRT(1); break;
+      case 2: BRQ_LRT(2); break;
+      case 3: BRQ_LRT(3); break;
+      default: BRQ_LRT(4); break;
     }
+#undef BRQ_LRT
     return hipGetLastError();
   };
   if (many) {
