@@ -382,8 +382,13 @@ def run_prefill(brq, torch, iters=10):
         for _ in range(iters):
             brq.gemm_lr(xr, s, sc, v, u, N, K, r, y=y, ws=ws_lr)
 
+    def rotations():
+        for _ in range(iters):
+            brq.kron_rotate(x, H, R, y=xr)
+
     gemm_graph_ms = graph_time(torch, plain, 3 * iters) / iters
     lr_ms = graph_time(torch, corrected, 5 * iters) / iters
+    rot_graph_ms = graph_time(torch, rotations, iters) / iters
     M = x.shape[0]
     flops = 2.0 * M * N * K
     flops_lr = flops + 2.0 * M * r * (K + N)
@@ -392,6 +397,8 @@ def run_prefill(brq, torch, iters=10):
                gemm_graph_us=gemm_graph_ms * 1e3,
                gemm_lr20_us=lr_ms * 1e3, gemm_lr20_tflops=flops_lr / (lr_ms * 1e-3) / 1e12,
                rotate_us=rot_ms * 1e3, rotate_gbs=(2 * M * K * 2) / (rot_ms * 1e-3) / 1e9,
+               rotate_graph_us=rot_graph_ms * 1e3,
+               rotate_graph_tflops_f32=2.0 * 2 * 64 ** 3 * M / (rot_graph_ms * 1e-3) / 1e12,
                tokens_per_s=M / ((rot_ms + gemm_ms) * 1e-3))
     del s, sc, x, xr, y, v, u, ws_lr, ws_pf
     torch.cuda.empty_cache()
