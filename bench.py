@@ -7,7 +7,8 @@ HBM bytes (packed weights + activations in + outputs out) per second. The
 weights rotate through a ring of copies larger than twice the 256 MB
 Infinity Cache, so every call streams its weights from HBM.
 
-Also reported (extra): the same product at M = 4, 16, 64; the routed MoE layer
+Also reported (extra): the same product at M = 4, 16, 64; the packing pass of
+the 14336 x 4096 matrix; the routed MoE layer
 (256 experts, top-8, hidden 2048, intermediate 512) at T = 1 and 64 decode
 tokens, with group-128 experts and with DBF-chain experts (r = 1024); the DBF chain (4096x4096, r = 2048) at M = 1 and 512; the prefill
 product at M = 4096 (4096 -> 14336) with the Kronecker rotation before it, and
@@ -200,6 +201,30 @@ def run_c2(brq, torch, M, steps, warmup):
 # ---------------------------------------------------------------------------
 # extras
 # ---------------------------------------------------------------------------
+
+def run_pack(brq, torch, iters=10):
+    """The packing pass (group-128 sign + fp16 scale) of the larger decode
+    matrix, 14336 x 4096 fp32, graph-timed: algorithmic bytes are the fp32
+    weights read and the packed bytes written."""
+    import datagen
+    N, K = datagen.C2_SHAPES[1]
+    w = torch.from_numpy(datagen.C2_weight(1)).cuda()
+    s = torch.empty((N, K // 64), dtype=torch.int64, device="cuda")
+    sc = torch.empty((N, K // 128), dtype=torch.float16, device="cuda")
+    brq.pack(w, out=(s, sc))
+    torch.cuda.synchronize()
+
+    def timed():
+        for _ in range(iters):
+            brq.pack(w, out=(s, sc))
+
+    ms = graph_time(torch, timed, iters) / iters
+    nbytes = 4 * N * K + packed_bytes(N, K)
+    del w, s, sc
+    torch.cuda.empty_cache()
+    return dict(shape=[N, K], us=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
+                frac_of_hbm=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
 
 def run_moe(brq, torch, Ts, iters=50):
     import datagen
@@ -477,6 +502,8 @@ def main():
             log(f"[bench] C2 M={M}")
             r = run_c2(brq, torch, M, 50, 10)
             extra["c2"][f"M={M}"] = {k: r[k] for k in ("ms_per_step", "gbs", "tflops")}
+        log("[bench] pack")
+        extra["pack"] = run_pack(brq, torch)
         log("[bench] MoE")
         extra["moe"] = run_moe(brq, torch, (1, 64))
         log("[bench] MoE with DBF experts")
