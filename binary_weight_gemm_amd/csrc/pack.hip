@@ -8,9 +8,9 @@
 // rows*cols/128 groups, group G at w + 128*G, its sign words at 2*G and 2*G+1,
 // its scale at G. One wave packs 64 consecutive groups: for each group the 64
 // lanes read 2 x 256 contiguous bytes, two wave ballots of the IEEE sign bits
-// give the two 64-bit words directly (lane l <-> bit l), and a butterfly sum
-// in fp64 gives sum|w|. Lane i keeps group i's results so the stores are
-// coalesced.
+// give the two 64-bit words directly (lane l <-> bit l), and sum|w| is added
+// in fp64 (each lane's two values, then the 64 lane partials in lane order).
+// Lane i keeps group i's results so the stores are coalesced.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,30 +42,46 @@ __device__ uint16_t f64_to_f16_rne(double v) {
   return sign | (uint16_t)q;  // subnormal (q == 1024 encodes the smallest normal)
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 __global__ __launch_bounds__(256) void k_pack_g128(const float* __restrict__ w, int64_t ngroups,
                                                    uint64_t* __restrict__ signs,
                                                    uint16_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
+  // per wave: |w| partials of 16 groups x 64 lanes, summed by the 16 lanes
+  // that keep those groups (a transposed reduction instead of one butterfly
+  // per group)
+  __shared__ double part[4][16][65];  // rows padded: the 16 summing lanes hit different banks
+  const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
   const int64_t wv = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
   for (int64_t t0 = wv * 64; t0 < ngroups; t0 += nw * 64) {
     const int cnt = (int)((ngroups - t0) < 64 ? (ngroups - t0) : 64);
     uint64_t my0 = 0, my1 = 0;
     double mysum = 0.0;
-    for (int i = 0; i < cnt; ++i) {
-      const float* src = w + (t0 + i) * 128;
-      const float a = src[lane];
-      const float c = src[64 + lane];
-      const uint64_t b0 = __ballot(__float_as_uint(a) >> 31);
-      const uint64_t b1 = __ballot(__float_as_uint(c) >> 31);
-      const double s = wave_sum_f64((double)fabsf(a) + (double)fabsf(c));
-      if (lane == i) { my0 = b0; my1 = b1; mysum = s; }
+    // sixteen groups per round: all their loads first (groups past cnt
+    // re-read the last one and are dropped), then the ballots, then the sums
+    for (int i0 = 0; i0 < cnt; i0 += 16) {
+      float a[16], c[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = i0 + q < cnt ? i0 + q : cnt - 1;
+        const float* src = w + (t0 + i) * 128;
+        a[q] = src[lane];
+        c[q] = src[64 + lane];
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint64_t b0 = __ballot(__float_as_uint(a[q]) >> 31);
+        const uint64_t b1 = __ballot(__float_as_uint(c[q]) >> 31);
+        if (lane == i0 + q) { my0 = b0; my1 = b1; }
+        part[wl][q][lane] = (double)fabsf(a[q]) + (double)fabsf(c[q]);
+      }
+      // lane i0 + q adds group i0 + q's 64 partials in lane order (the LDS
+      // operations of one wave complete in order, so no barrier is needed)
+      const int q = lane - i0;
+      if (q >= 0 && q < 16) {
+        double sum = 0.0;
+        for (int j = 0; j < 64; ++j) sum += part[wl][q][j];
+        mysum = sum;
+      }
     }
     if (lane < cnt) {
       signs[2 * (t0 + lane)] = my0;
@@ -83,10 +99,15 @@ __global__ __launch_bounds__(256) void k_pack_sign1(const float* __restrict__ w,
   for (int64_t t0 = wv * 64; t0 < nwords; t0 += nw * 64) {
     const int cnt = (int)((nwords - t0) < 64 ? (nwords - t0) : 64);
     uint64_t my = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const float a = w[(t0 + i) * 64 + lane];
-      const uint64_t b = __ballot(__float_as_uint(a) >> 31);
-      if (lane == i) my = b;
+    for (int i0 = 0; i0 < cnt; i0 += 8) {  // eight words per round, loads first
+      float a[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[q] = w[(t0 + (i0 + q < cnt ? i0 + q : cnt - 1)) * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint64_t b = __ballot(__float_as_uint(a[q]) >> 31);
+        if (lane == i0 + q) my = b;
+      }
     }
     if (lane < cnt) signs[t0 + lane] = my;
   }
