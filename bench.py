@@ -7,7 +7,9 @@ HBM bytes (packed weights + activations in + outputs out) per second. The
 weights rotate through a ring of copies larger than twice the 256 MB
 Infinity Cache, so every call streams its weights from HBM.
 
-Also reported (extra): the same product at M = 4, 16, 64; the packing pass of
+Also reported (extra): device facts and reference rates (a 1 GiB device copy,
+the vendor library's bf16 GEMM); the 1024 x 1024 single GEMV (cache resident);
+the same product at M = 4, 16, 64; the packing pass of
 the 14336 x 4096 matrix; the routed MoE layer
 (256 experts, top-8, hidden 2048, intermediate 512) at T = 1 and 64 decode
 tokens, with group-128 experts and with DBF-chain experts (r = 1024); the DBF chain (4096x4096, r = 2048) at M = 1 and 512; the prefill
@@ -201,6 +203,88 @@ def run_c2(brq, torch, M, steps, warmup):
 # ---------------------------------------------------------------------------
 # extras
 # ---------------------------------------------------------------------------
+
+def device_facts(torch):
+    p = torch.cuda.get_device_properties(0)
+    return dict(name=p.name, arch=getattr(p, "gcnArchName", ""), compute_units=p.multi_processor_count,
+                memory_gib=round(p.total_memory / 2 ** 30, 1))
+
+
+def achievable_peaks(torch, reps=10):
+    """Reference rates on this device (not the product): a 1 GiB device copy
+    (read + write) for HBM, and the vendor library's 8192^3 bf16 GEMM
+    (hipBLASLt through torch.matmul) for the matrix cores; back-to-back calls
+    between two events."""
+    n = 2 ** 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    c = torch.empty_like(a)
+    warm_gpu(torch, 0.3)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    copy_ms = timed(lambda: dst.copy_(src))
+    gemm_ms = timed(lambda: torch.matmul(a, b, out=c))
+    del src, dst, a, b, c
+    torch.cuda.empty_cache()
+    copy_gbs = 2 * n / (copy_ms * 1e-3) / 1e9
+    gemm_tflops = 2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
+    return dict(hbm_copy_gbs=copy_gbs, hbm_copy_frac=copy_gbs / HBM_PEAK_GBS,
+                bf16_gemm_tflops=gemm_tflops, bf16_gemm_frac=gemm_tflops / MFMA_F16_PEAK_TFLOPS)
+
+
+def isolated_call_us(brq, torch, reps=20):
+    """One decode product (M = 1, the 14336 x 4096 matrix) launched on its own
+    between two synchronisations, median of `reps`: launch overhead included."""
+    import datagen
+    N, K = datagen.C2_SHAPES[1]
+    s, sc = brq.pack(torch.from_numpy(datagen.C2_weight(1)).cuda())
+    x = dev_np(datagen.C2_x(1, 1))
+    y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+    brq.gemm(x, s, sc, N, K, y=y)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        brq.gemm(x, s, sc, N, K, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def run_c1(brq, torch, iters=50):
+    """C1, the single GEMV on a 1024 x 1024 matrix: its 151 KB stay in the
+    caches, so this is a latency figure, not an HBM one."""
+    import datagen
+    w, xh = datagen.C1()
+    s, sc = brq.pack(torch.from_numpy(w).cuda())
+    x = dev_np(xh)
+    y = torch.empty((1, 1024), dtype=torch.bfloat16, device="cuda")
+    brq.gemm(x, s, sc, 1024, 1024, y=y)
+    torch.cuda.synchronize()
+
+    def timed():
+        for _ in range(iters):
+            brq.gemm(x, s, sc, 1024, 1024, y=y)
+
+    ms = graph_time(torch, timed, iters) / iters
+    nbytes = packed_bytes(1024, 1024) + 1024 * 2 * 2
+    return dict(us=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9, note="cache-resident, latency-bound")
+
 
 def run_pack(brq, torch, iters=10):
     """The packing pass (group-128 sign + fp16 scale) of the larger decode
@@ -462,9 +546,29 @@ def cpu_baseline(budget_s=12.0):
             break
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
+    # the same on one BLAS thread, a shorter sample
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            n1, t1 = 0, time.perf_counter()
+            while time.perf_counter() - t1 < budget_s / 3:
+                for N, K, words, scales, x in mats:
+                    oracle.bin_gemm(x, words, scales, N, K)
+                n1 += 1
+            one = step_bytes * n1 / (time.perf_counter() - t1) / 1e9
+    except Exception:  # pragma: no cover
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return dict(value=step_bytes * steps / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
                 sample=f"{steps} steps of the headline workload (both C2 matrices at M=1, fp64 numpy "
-                       f"dequantise + matmul) in {el:.1f} s")
+                       f"dequantise + matmul) in {el:.1f} s",
+                one_thread_value=one, cpu_model=model)
 
 
 # ---------------------------------------------------------------------------
@@ -497,6 +601,12 @@ def main():
     log(f"[bench] headline {head}")
     extra = {}
     if not args.no_extra:
+        extra["device"] = device_facts(torch)
+        log("[bench] achievable peaks")
+        extra["achievable"] = achievable_peaks(torch)
+        log("[bench] C1")
+        extra["c1"] = run_c1(brq, torch)
+        extra["isolated_decode_call_us"] = isolated_call_us(brq, torch)
         extra["c2"] = {}
         for M in (4, 16, 64):
             log(f"[bench] C2 M={M}")
