@@ -9,7 +9,7 @@ __all__ = [
     "GROUP", "bf16_to_f64", "f16_to_f64", "round_bf16", "bf16_bits",
     "sign_bits", "pack_words", "unpack_signs", "group_mean_abs", "pack_sign1", "pack_sign1_only",
     "dequantize", "bin_gemm", "bin_gemm_cols", "bin_gemm_loops", "bin_gemm_lr", "bin_gemm_lr_cols", "bin_gemm_lr_dense",
-    "dbf_chain", "dbf_dense", "dbf_bpe", "dbf_bits",
+    "dbf_chain", "dbf_dense", "dbf_bpe", "dbf_bits", "q8_rows", "dbf_chain_q8",
     "route_topk", "silu", "moe_ffn", "moe_ffn_loops", "moe_dbf_ffn", "moe_dbf_dense",
     "kron_rotate", "kron_rotate_bf16",
     "packed_bytes", "bits_per_weight",
@@ -25,6 +25,8 @@ PINS = {
     "bin_gemm_lr": "dense materialisation of Wq + U.V + zero-factor reduction + one-hot rank-1 closed form",
     "dbf_chain": "dense reconstruction + Sylvester-Hadamard identity",
     "dbf_bpe": "worked example of the DBF post, section 1.1",
+    "q8_rows": "rounding bound + minimal exponent + exact codes for representable rows + zero row",
+    "dbf_chain_q8": "Sylvester-Hadamard closed form + odd symmetry + power-of-two equivariance + distance to the unquantised chain",
     "route_topk": "brute-force ordering + softmax invariants",
     "moe_ffn": "identical-experts reduction + single-route dense FFN + loops",
     "moe_dbf_ffn": "dense reconstruction of every chain + identical-experts reduction + single route",
@@ -233,6 +235,53 @@ def dbf_chain(x, d_in, v_words, d_mid, u_words, d_out, m: int, n: int, r: int) -
     h = xs @ V.T
     hs = h * f16_to_f64(d_mid)[None, :]
     yc = hs @ U.T
+    return yc * f16_to_f64(d_out)[None, :]
+
+
+def q8_rows(v) -> tuple:
+    """Sign-magnitude Q8 activations with one exponent per reduction row (DBF
+    post, section 5, item 4: the row is denormalised to a shared exponent and
+    encoded as a sign plane and seven magnitude planes). Reading: the exponent
+    e of a row is the smallest integer with max|v| <= 127 * 2^e and
+    q = round-half-even(v / 2^e), so |q| <= 127; an all-zero row takes e = 0.
+    Returns (q int64 [rows, n], e int64 [rows])."""
+    v = np.asarray(v, dtype=np.float64)
+    v2 = v.reshape(-1, v.shape[-1])
+    e = np.zeros(v2.shape[0], dtype=np.int64)
+    for i, m in enumerate(np.abs(v2).max(axis=1)):
+        if m == 0.0:
+            continue
+        k = int(np.floor(np.log2(m)))  # refined below against the exact bounds
+        k -= 6
+        while m > 127.0 * 2.0 ** k:
+            k += 1
+        while m <= 127.0 * 2.0 ** (k - 1):
+            k -= 1
+        e[i] = k
+    q = np.rint(v2 / np.exp2(e.astype(np.float64))[:, None])
+    return q.astype(np.int64).reshape(v.shape), e
+
+
+def dbf_chain_q8(x, d_in, v_words, d_mid, u_words, d_out, m: int, n: int, r: int) -> np.ndarray:
+    """The DBF chain of dbf_chain with both binary products taken over Q8
+    activations (the prompt-processing formulation of the DBF post, section
+    5, item 4: row-denormalised sign-magnitude activations, an exact integer
+    reduction of signs times magnitudes, then one shared scale):
+    x_s = D_in x -> (q1, e1) = q8_rows(x_s); h = 2^e1 (V q1);
+    h_s = fp32(D_mid h) -> (q2, e2) = q8_rows(h_s); y = D_out 2^e2 (U q2).
+    The quantised codes are integer decisions taken on floating-point values,
+    so they follow the precision the products run in: x_s = d_in x is exact
+    in fp32 and fp64 alike, and h_s is rounded once to fp32 (as the products'
+    epilogue does) before it is quantised."""
+    x = np.asarray(x, dtype=np.float64)
+    V = unpack_signs(v_words, r, n).astype(np.int64)
+    U = unpack_signs(u_words, m, r).astype(np.int64)
+    xs = x * f16_to_f64(d_in)[None, :]
+    q1, e1 = q8_rows(xs)
+    h = (q1 @ V.T).astype(np.float64) * np.exp2(e1.astype(np.float64))[:, None]
+    hs = (np.asarray(d_mid, dtype=np.float16).astype(np.float32)[None, :] * h.astype(np.float32)).astype(np.float64)
+    q2, e2 = q8_rows(hs)
+    yc = (q2 @ U.T).astype(np.float64) * np.exp2(e2.astype(np.float64))[:, None]
     return yc * f16_to_f64(d_out)[None, :]
 
 

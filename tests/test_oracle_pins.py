@@ -309,6 +309,73 @@ def test_dbf_hadamard_identity():
     assert np.allclose(y, expect, rtol=1e-13, atol=1e-14)
 
 
+# ---- Q8 activations (DBF post, section 5, item 4) --------------------------
+
+def test_q8_rows_codes_and_exponents():
+    """Rounding bound, minimal exponent, ties to even, zero row, exact codes
+    of representable rows, over rows spanning many binades."""
+    g = datagen.rng(95, 0)
+    v = g.standard_normal((6, 300)) * np.exp2(g.integers(-30, 30, size=(6, 1)))
+    v[2] = 0.0
+    v[3, :5] = [63.5, -64.5, 2.5, -0.5, 127.0]   # ties at e = 0 (max 127)
+    v[3, 5:] = 0.0
+    q, e = oracle.q8_rows(v)
+    for i in range(v.shape[0]):
+        m = np.abs(v[i]).max()
+        if m == 0:
+            assert e[i] == 0 and not q[i].any()
+            continue
+        s = 2.0 ** e[i]
+        assert m <= 127 * s and m > 127 * s / 2          # smallest exponent with |q| <= 127
+        assert np.abs(q[i]).max() <= 127 and np.abs(q[i]).max() >= 64
+        assert np.all(np.abs(v[i] - q[i] * s) <= s / 2)  # nearest code
+        half = np.abs(v[i] / s - np.trunc(v[i] / s)) == 0.5
+        assert np.all(q[i][half] % 2 == 0)               # ties to even
+    assert list(q[3, :5]) == [64, -64, 2, 0, 127] and e[3] == 0
+    # a row of codes times a power of two is reproduced exactly
+    codes = g.integers(-127, 128, size=(1, 64))
+    codes[0, 0] = 100
+    q2, e2 = oracle.q8_rows(codes * 2.0 ** -9)
+    assert e2[0] == -9 and np.array_equal(q2, codes)
+
+
+def test_dbf_chain_q8_hadamard_closed_form():
+    """V = U = Sylvester Hadamard H_n, unit diagonals, x = 127 e_k: every
+    intermediate is an exact Q8 code, so y = H (127 H e_k) = 127 n e_k."""
+    n = 128
+    Hd = _sylvester(n).astype(np.float32)
+    W = oracle.pack_sign1_only(Hd)
+    one = np.ones(n, dtype=np.float16)
+    x = np.zeros((3, n))
+    for i, k in enumerate((0, 37, 127)):
+        x[i, k] = 127.0 * (-1) ** i
+    y = oracle.dbf_chain_q8(x, one, W, one, W, one, n, n, n)
+    expect = 127.0 * n * x / 127.0
+    assert np.array_equal(y, expect)
+
+
+def test_dbf_chain_q8_symmetries_and_distance():
+    """Odd symmetry (x -> -x), power-of-two equivariance (x -> 2^k x scales y by
+    2^k exactly: the exponents shift, the codes stay), and the distance to
+    the unquantised chain is that of two 8-bit roundings: nonzero, and a few
+    percent in L2 with log-normal diagonals (a wrong exponent or a dropped
+    scale would be off by a factor)."""
+    n, r, m = 256, 128, 192
+    v = datagen.pm1_f32((95, 1, 0), (r, n))
+    u = datagen.pm1_f32((95, 1, 1), (m, r))
+    d_in = datagen.f16_lognormal((95, 1, 2), (n,))
+    d_mid = datagen.f16_lognormal((95, 1, 3), (r,))
+    d_out = datagen.f16_lognormal((95, 1, 4), (m,))
+    vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
+    x = oracle.bf16_to_f64(datagen.bf16_normal((95, 1, 5), (4, n)))
+    y = oracle.dbf_chain_q8(x, d_in, vw, d_mid, uw, d_out, m, n, r)
+    assert np.array_equal(oracle.dbf_chain_q8(-x, d_in, vw, d_mid, uw, d_out, m, n, r), -y)
+    assert np.array_equal(oracle.dbf_chain_q8(x * 2.0 ** 5, d_in, vw, d_mid, uw, d_out, m, n, r), y * 2.0 ** 5)
+    ref = oracle.dbf_chain(x, d_in, vw, d_mid, uw, d_out, m, n, r)
+    rel = np.linalg.norm(y - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert np.all(rel < 5e-2) and np.all(rel > 1e-3)
+
+
 def test_dbf_bit_budget_worked_example():
     g = _gold("dbf_bit_budget.json")
     m, n, r = g["shape_m"], g["shape_n"], g["r"]
