@@ -23,9 +23,10 @@ import os
 import torch
 
 __all__ = [
-    "BrqError", "lib", "library_path", "pack", "gemm", "gemm_lr", "dbf_gemm", "moe_ffn", "moe_dbf_ffn",
+    "BrqError", "lib", "library_path", "pack", "gemm", "gemm_lr", "dbf_gemm", "dbf_gemm_q8", "moe_ffn", "moe_dbf_ffn",
     "kron_rotate", "DbfFactors", "moe_dbf_workspace_bytes",
-    "gemm_workspace_bytes", "gemm_lr_workspace_bytes", "dbf_workspace_bytes", "moe_workspace_bytes",
+    "gemm_workspace_bytes", "gemm_lr_workspace_bytes", "dbf_workspace_bytes", "dbf_q8_workspace_bytes",
+    "moe_workspace_bytes",
     "sign_words", "scale_count",
     "BRQ_BF16", "BRQ_F32", "ABI_FUNCTIONS",
 ]
@@ -55,6 +56,8 @@ ABI_FUNCTIONS = {
     "brq_gemm_lr": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _sz, _vp]),
     "brq_dbf_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "brq_dbf_gemm": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "brq_dbf_q8_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "brq_dbf_gemm_q8": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
     "brq_moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "brq_moe_ffn": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int,
                            _vp, _vp, _vp, _sz, _vp]),
@@ -150,6 +153,10 @@ def dbf_workspace_bytes(M: int, m: int, n: int, r: int) -> int:
     return lib().brq_dbf_workspace_bytes(M, m, n, r)
 
 
+def dbf_q8_workspace_bytes(M: int, m: int, n: int, r: int) -> int:
+    return lib().brq_dbf_q8_workspace_bytes(M, m, n, r)
+
+
 def moe_workspace_bytes(T: int, H: int, I: int, E: int, top_k: int) -> int:
     return lib().brq_moe_workspace_bytes(T, H, I, E, top_k)
 
@@ -230,6 +237,27 @@ def dbf_gemm(x, d_in, v, d_mid, u, d_out, m: int, n: int, r: int, out_dtype=torc
                               _dev(u, "u", torch.int64), _dev(d_out, "d_out", torch.float16),
                               _dev(y, "y", out_dtype), code, _dev(ws, "ws") if ws is not None else None, wsb,
                               _stream()), "brq_dbf_gemm")
+    return y
+
+
+def dbf_gemm_q8(x, d_in, v, d_mid, u, d_out, m: int, n: int, r: int, out_dtype=torch.bfloat16, y=None, ws=None):
+    """brq_dbf_gemm_q8: the DBF chain with both binary products over per-row Q8 activation codes."""
+    M = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != n:
+        raise BrqError(f"x must be [M, {n}]")
+    if v.numel() != r * n // 64 or u.numel() != m * r // 64:
+        raise BrqError("v must be r x n and u m x r sign planes")
+    if d_in.numel() != n or d_mid.numel() != r or d_out.numel() != m:
+        raise BrqError("diagonal lengths must be n, r, m")
+    code = _out_code(out_dtype)
+    if y is None:
+        y = torch.empty((M, m), dtype=out_dtype, device=x.device)
+    ws, wsb = _ws(dbf_q8_workspace_bytes(M, m, n, r), x.device, ws)
+    _check(lib().brq_dbf_gemm_q8(_dev(x, "x", torch.bfloat16), M, m, n, r, _dev(d_in, "d_in", torch.float16),
+                                 _dev(v, "v", torch.int64), _dev(d_mid, "d_mid", torch.float16),
+                                 _dev(u, "u", torch.int64), _dev(d_out, "d_out", torch.float16),
+                                 _dev(y, "y", out_dtype), code, _dev(ws, "ws") if ws is not None else None, wsb,
+                                 _stream()), "brq_dbf_gemm_q8")
     return y
 
 

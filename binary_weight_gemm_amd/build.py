@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbrq.so")
 
-SOURCES = ["abi.hip", "pack.hip", "dec.hip", "tile.hip", "pf.hip", "dbf.hip", "moe.hip", "kron.hip", "mid.hip", "lr.hip"]
+SOURCES = ["abi.hip", "pack.hip", "dec.hip", "tile.hip", "pf.hip", "dbf.hip", "moe.hip", "kron.hip", "mid.hip", "lr.hip", "q8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

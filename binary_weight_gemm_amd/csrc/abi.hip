@@ -210,6 +210,42 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
                     "brq_dbf_gemm");
 }
 
+size_t brq_dbf_q8_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
+  if (M < 1 || m < 1 || n < 128 || r < 128 || n % 128 || r % 128 || M > kMaxDim || m > kMaxDim || n > kMaxDim ||
+      r > kMaxDim)
+    return 0;
+  return brq::dbf_q8_ws_bytes(M, m, n, r);
+}
+
+brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, int64_t r, const uint16_t* d_in,
+                           const uint64_t* v, const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out,
+                           void* y, brq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !d_in || !v || !d_mid || !u || !d_out || !y)
+    return fail(BRQ_E_NULL, "brq_dbf_gemm_q8: x, d_in, v, d_mid, u, d_out and y must not be NULL");
+  if (M < 1 || m < 1 || M > kMaxDim || m > kMaxDim)
+    return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: M=%lld m=%lld out of range", (long long)M, (long long)m);
+  if (n < 128 || r < 128 || n > kMaxDim || r > kMaxDim || n % 128 || r % 128)
+    return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: n=%lld and r=%lld must be positive multiples of 128", (long long)n,
+                (long long)r);
+  const int64_t wide = m > r ? m : r;
+  if (((M + 127) / 128) * ((wide + 127) / 128) > (int64_t)INT32_MAX)
+    return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: M=%lld with max(m, r)=%lld needs more than 2^31 tiles", (long long)M,
+                (long long)wide);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm_q8: unknown y_dtype %d", (int)y_dtype);
+  if (!aligned(x, 2) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, y_dtype == BRQ_BF16 ? 2 : 4) || !aligned(d_in, 2) ||
+      !aligned(d_mid, 2) || !aligned(d_out, 2))
+    return fail(BRQ_E_ALIGN, "brq_dbf_gemm_q8: v and u must be 16-byte aligned, the others aligned to their element");
+  const size_t need = brq::dbf_q8_ws_bytes(M, m, n, r);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(BRQ_E_WORKSPACE, "brq_dbf_gemm_q8: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  brq_status s = check_device();
+  if (s != BRQ_OK) return s;
+  return hip_result(brq::launch_dbf_q8(x, (int)M, (int)m, (int)n, (int)r, d_in, v, d_mid, u, d_out, y,
+                                       y_dtype == BRQ_BF16, ws, (hipStream_t)stream),
+                    "brq_dbf_gemm_q8");
+}
+
 size_t brq_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k) {
   if (T < 1 || T > 256 || H < 128 || I < 128 || H > 32768 || I > 2048 || H % 128 || I % 128 || E < 1 ||
       E > 1024 || top_k < 1 ||

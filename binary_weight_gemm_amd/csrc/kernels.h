@@ -61,6 +61,12 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
                       const uint64_t* v, const uint16_t* d_mid, const uint64_t* u,
                       const uint16_t* d_out, void* y, int y_bf16, void* ws, hipStream_t st);
 size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
+// the same chain over Q8 activation codes (int8 matrix cores, exact integer
+// reductions, one exponent per row)
+hipError_t launch_dbf_q8(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
+                         const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
+                         void* ws, hipStream_t st);
+size_t dbf_q8_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
 
 // ---- routed MoE ------------------------------------------------------------
 size_t moe_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k);

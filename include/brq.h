@@ -173,6 +173,32 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * brq_dbf_gemm_q8 -- the same DBF chain as brq_dbf_gemm with both binary
+ * products taken over sign-magnitude Q8 activation codes, the prompt-side
+ * formulation of "LLM binarization, Episode 01: DBF" (section 5, item 4: one
+ * exponent per reduction row, a sign and seven magnitude bits, an exact
+ * integer reduction against the weight signs, then one shared scale; item 1
+ * names the same integer as a signed int8 dot product against +-1 weights).
+ * Per row of the product's input v (x_s = D_in x, exact in fp32, for V; h_s
+ * for U): e = the smallest integer with max|v| <= 127 * 2^e (0 for an all-zero
+ * row); q = round-half-to-even(v / 2^e), |q| <= 127. Then
+ *   h   = (q1 . V^T) * 2^e1            (an exact integer times a power of two)
+ *   h_s = fp32(d_mid * h)              (one fp32 rounding)
+ *   y   = d_out * (q2 . U^T) * 2^e2    (one fp32 rounding, then y_dtype)
+ * The codes and exponents are decided in fp32, where every input to them is
+ * exact, so they match an fp64 evaluation of the same definition bit for bit.
+ * Arguments, layouts and limits are those of brq_dbf_gemm; the workspace
+ * holds the two code planes, the row exponents and h_s (fp32 [M][r]).
+ * Alignment: v and u 16 bytes, the others their element size.
+ */
+size_t brq_dbf_q8_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
+brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, int64_t r,
+                           const uint16_t* d_in, const uint64_t* v, const uint16_t* d_mid,
+                           const uint64_t* u, const uint16_t* d_out,
+                           void* y, brq_dtype y_dtype,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * brq_moe_ffn -- routed mixture-of-experts SwiGLU layer on group-128 experts:
  *   for each token t: ids = the top_k experts by descending fp32 router logit
  *   (ties to the lower expert index); w = softmax over the top_k selected

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(brq.ABI_FUNCTIONS)
@@ -152,6 +152,32 @@ def test_dbf_validation(L):
     assert f(*bad) == E_DTYPE
     bad = list(args); bad[13] = 16
     assert f(*bad) == E_WORKSPACE
+
+
+def test_dbf_q8_validation(L):
+    f = L.brq_dbf_gemm_q8
+    args = [P, 1, 4096, 4096, 2048, P, P, P, P, P, P, 0, P, 1 << 30, None]
+    bad = list(args); bad[6] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[1] = 0
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[3] = 4000
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[4] = 100
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[6] = PMIS
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[10] = PMIS; bad[11] = 1           # fp32 y needs 4-byte alignment
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[11] = 5
+    assert f(*bad) == E_DTYPE
+    bad = list(args); bad[13] = 16
+    assert f(*bad) == E_WORKSPACE
+    bad = list(args); bad[12] = PMIS
+    assert f(*bad) == E_WORKSPACE
+    # codes [M][n] int8, exponents [M], h_s [M][r] fp32, codes [M][r], exponents [M]
+    assert L.brq_dbf_q8_workspace_bytes(512, 4096, 4096, 2048) == 512 * 4096 + 2048 + 512 * 2048 * 4 + 512 * 2048 + 2048
+    assert L.brq_dbf_q8_workspace_bytes(1, 4096, 4096, 100) == 0
 
 
 def test_moe_validation(L):

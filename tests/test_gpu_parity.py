@@ -415,6 +415,106 @@ def test_dbf_device_packed_factors():
 
 
 # ---------------------------------------------------------------------------
+# DBF chain over Q8 activation codes
+# ---------------------------------------------------------------------------
+
+# The codes and exponents are decided from values that are exact in fp32 on
+# both sides, the integer reductions are exact, and the only roundings are
+# h_s to fp32 (the same single rounding on both sides) and the final product
+# with d_out: the fp32 output is within one rounding (2^-24, relative,
+# elementwise) of the oracle's fp64 value.
+Q8_REL = 2.0 ** -24 * 1.01
+
+
+def check_q8(y, o, what):
+    g = f64(y)
+    err = np.abs(g - o)
+    bad = err > Q8_REL * np.abs(o)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements off, worst {float(err.max()):.3e}"
+
+
+def _q8_inputs(M, m, n, r, key):
+    v = datagen.pm1_f32((75, key, 0), (r, n))
+    u = datagen.pm1_f32((75, key, 1), (m, r))
+    d_in = datagen.f16_lognormal((75, key, 2), (n,))
+    d_mid = datagen.f16_lognormal((75, key, 3), (r,))
+    d_out = datagen.f16_lognormal((75, key, 4), (m,))
+    x = datagen.bf16_normal((75, key, 5), (M, n))
+    return x, d_in, oracle.pack_sign1_only(v), d_mid, oracle.pack_sign1_only(u), d_out
+
+
+def _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r, out=torch.float32):
+    y = brq().dbf_gemm_q8(dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r, out_dtype=out)
+    torch.cuda.synchronize()
+    return y
+
+
+# several 128 x 128 tiles with ragged row and column tails, 64-wide k-steps
+@pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (5, 200, 384, 256), (127, 128, 256, 128),
+                                     (130, 300, 640, 384), (300, 96, 512, 640)])
+def test_dbf_q8_small(M, m, n, r):
+    say("dbf q8", M, m, n, r)
+    x, d_in, vw, d_mid, uw, d_out = _q8_inputs(M, m, n, r, M + m + n + r)
+    if M > 1:
+        x[M // 2] = 0                      # an all-zero row: exponent 0, codes 0, output 0
+    o = oracle.dbf_chain_q8(oracle.bf16_to_f64(x), d_in, vw, d_mid, uw, d_out, m, n, r)
+    y = _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r)
+    check_q8(y, o, f"dbf q8 {M},{m},{n},{r}")
+    if M > 1:
+        assert not f64(y)[M // 2].any()
+    # bf16 output: the fp32 value (one rounding of the exact d_out * integer
+    # * 2^e) rounded to nearest even bf16, bit for bit
+    yb = _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r, out=torch.bfloat16)
+    want = datagen.bf16_bits_from_f32(o.astype(np.float32))
+    assert np.array_equal(host_bits(yb), want), f"dbf q8 {M},{m},{n},{r} bf16"
+
+
+def test_dbf_q8_ties_and_exponent_edges():
+    """Rows whose values land exactly on half codes (round half to even), a row
+    whose maximum is exactly 127 * 2^e (code 127 at that exponent) and one a
+    half step above it (the next exponent up), with unit d_in so that x_s = x."""
+    say("dbf q8 ties")
+    M, m, n, r = 6, 128, 256, 128
+    x, _, vw, d_mid, uw, d_out = _q8_inputs(M, m, n, r, 11)
+    d_in = np.ones(n, np.float16)
+    half = datagen.rng(75, 99).integers(-126, 127, size=(M, n)).astype(np.float32) + 0.5
+    rows = np.zeros((M, n), np.float32)
+    rows[0] = half[0] * 2.0 ** -3
+    rows[0, 7] = 127 * 2.0 ** -3            # max exactly 127 * 2^-3: codes are half[0] rounded to even
+    rows[1] = half[1] * 2.0 ** 5
+    rows[1, 3] = -127 * 2.0 ** 5
+    rows[2] = np.round(half[2]) * 2.0 ** -9
+    rows[2, 0] = 127.5 * 2.0 ** -9           # just past 127 * 2^-9: exponent -8
+    rows[3] = half[3]
+    rows[3, 5] = 127                        # exponent 0: the ties themselves
+    rows[4, 9] = -3.0                       # one non-zero value
+    rows[5] = half[5] * 2.0 ** -20
+    rows[5, 1] = 127 * 2.0 ** -20
+    x = datagen.bf16_bits_from_f32(rows)
+    assert np.array_equal(oracle.bf16_to_f64(x), rows.astype(np.float64))   # every value is exact in bf16
+    o = oracle.dbf_chain_q8(oracle.bf16_to_f64(x), d_in, vw, d_mid, uw, d_out, m, n, r)
+    y = _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r)
+    check_q8(y, o, "dbf q8 ties")
+
+
+# the full-size case at the launch configuration the benchmark times (all 512
+# rows computed), compared on sampled rows: rows are independent in the chain
+# (each has its own exponents), so the oracle runs on those rows alone
+def test_dbf_q8_c3_sampled_rows():
+    say("C3 dbf q8 M=512 sampled rows")
+    d = datagen.C3(512)
+    vw, uw = oracle.pack_sign1_only(d["v"]), oracle.pack_sign1_only(d["u"])
+    m, n, r = d["m"], d["n"], d["r"]
+    y = _q8_run(d["x"], d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
+    rows = np.array([0, 1, 127, 128, 255, 300, 383, 511])
+    o = oracle.dbf_chain_q8(oracle.bf16_to_f64(d["x"][rows]), d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
+    check_q8(y[torch.from_numpy(rows).to(y.device)], o, "C3 q8 sampled")
+    # and the distance to the unquantised chain on those rows stays at the Q8 level
+    full = oracle.dbf_chain(oracle.bf16_to_f64(d["x"][rows]), d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
+    assert 1e-3 < l2rel(f64(y)[rows], full) < 5e-2
+
+
+# ---------------------------------------------------------------------------
 # S5 / S6 MoE
 # ---------------------------------------------------------------------------
 
