@@ -210,9 +210,13 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
                     "brq_dbf_gemm");
 }
 
+// longest Q8 reduction: 127 * 131072 < 2^24, so every integer sum converts to
+// fp32 exactly
+constexpr int64_t kMaxQ8Red = 131072;
+
 size_t brq_dbf_q8_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
-  if (M < 1 || m < 1 || n < 128 || r < 128 || n % 128 || r % 128 || M > kMaxDim || m > kMaxDim || n > kMaxDim ||
-      r > kMaxDim)
+  if (M < 1 || m < 1 || n < 128 || r < 128 || n % 128 || r % 128 || M > kMaxDim || m > kMaxDim || n > kMaxQ8Red ||
+      r > kMaxQ8Red)
     return 0;
   return brq::dbf_q8_ws_bytes(M, m, n, r);
 }
@@ -224,17 +228,18 @@ brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, i
     return fail(BRQ_E_NULL, "brq_dbf_gemm_q8: x, d_in, v, d_mid, u, d_out and y must not be NULL");
   if (M < 1 || m < 1 || M > kMaxDim || m > kMaxDim)
     return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: M=%lld m=%lld out of range", (long long)M, (long long)m);
-  if (n < 128 || r < 128 || n > kMaxDim || r > kMaxDim || n % 128 || r % 128)
-    return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: n=%lld and r=%lld must be positive multiples of 128", (long long)n,
-                (long long)r);
+  if (n < 128 || r < 128 || n > kMaxQ8Red || r > kMaxQ8Red || n % 128 || r % 128)
+    return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: n=%lld and r=%lld must be multiples of 128 in [128, 131072]",
+                (long long)n, (long long)r);
   const int64_t wide = m > r ? m : r;
   if (((M + 127) / 128) * ((wide + 127) / 128) > (int64_t)INT32_MAX)
     return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: M=%lld with max(m, r)=%lld needs more than 2^31 tiles", (long long)M,
                 (long long)wide);
   if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm_q8: unknown y_dtype %d", (int)y_dtype);
-  if (!aligned(x, 2) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, y_dtype == BRQ_BF16 ? 2 : 4) || !aligned(d_in, 2) ||
-      !aligned(d_mid, 2) || !aligned(d_out, 2))
-    return fail(BRQ_E_ALIGN, "brq_dbf_gemm_q8: v and u must be 16-byte aligned, the others aligned to their element");
+  if (!aligned(x, 16) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, y_dtype == BRQ_BF16 ? 2 : 4) ||
+      !aligned(d_in, 16) || !aligned(d_mid, 16) || !aligned(d_out, 2))
+    return fail(BRQ_E_ALIGN, "brq_dbf_gemm_q8: x, v, u, d_in and d_mid must be 16-byte aligned, y and d_out aligned "
+                "to their element");
   const size_t need = brq::dbf_q8_ws_bytes(M, m, n, r);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(BRQ_E_WORKSPACE, "brq_dbf_gemm_q8: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,

@@ -26,18 +26,28 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // ---- quantisation of rows ---------------------------------------------------
 
-template <bool FROM_BF16>
-__global__ __launch_bounds__(256) void k_q8_rows(const void* __restrict__ src, const uint16_t* __restrict__ d_in,
-                                                 int K, int8_t* __restrict__ q, int* __restrict__ rexp) {
+enum { SRC_XDIN, SRC_F32, SRC_PART };
+
+// SRC_XDIN: v = x * d_in (bf16 x fp16, exact in fp32); SRC_F32: v = h_s;
+// SRC_PART: v = h_s = fp32(d_mid * (s * 2^e1)), s the sum of the nsplit int32
+// K-slice partials of the first product (exact: |s| < 2^24)
+template <int SRC>
+__global__ __launch_bounds__(256) void k_q8_rows(const void* __restrict__ src, const uint16_t* __restrict__ diag,
+                                                 const int* __restrict__ rexp_in, int nsplit, int M, int K,
+                                                 int8_t* __restrict__ q, int* __restrict__ rexp) {
   __shared__ uint32_t s_max[4];
   const int t = blockIdx.x, tid = threadIdx.x;
-  // value k of the row (exact in fp32)
+  const int e_in = SRC == SRC_PART ? rexp_in[t] : 0;
   auto val = [&](int k) -> float {
-    if (FROM_BF16) {
+    if (SRC == SRC_XDIN) {
       const uint16_t* x = reinterpret_cast<const uint16_t*>(src) + (size_t)t * K;
-      return bf16_to_f32(x[k]) * f16_bits_to_f32(d_in[k]);
+      return bf16_to_f32(x[k]) * f16_bits_to_f32(diag[k]);
     }
-    return reinterpret_cast<const float*>(src)[(size_t)t * K + k];
+    if (SRC == SRC_F32) return reinterpret_cast<const float*>(src)[(size_t)t * K + k];
+    const int* part = reinterpret_cast<const int*>(src) + (size_t)t * K + k;
+    int sum = 0;
+    for (int s = 0; s < nsplit; ++s) sum += part[(size_t)s * M * K];
+    return f16_bits_to_f32(diag[k]) * __builtin_amdgcn_ldexpf((float)sum, e_in);
   };
   uint32_t mx = 0;
   for (int k = tid; k < K; k += 256) mx = max(mx, __float_as_uint(val(k)) & 0x7fffffffu);
@@ -56,6 +66,129 @@ __global__ __launch_bounds__(256) void k_q8_rows(const void* __restrict__ src, c
     q[(size_t)t * K + k] = (int8_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(val(k), -e));
 }
 
+// The same quantisation with the row held in registers: thread tid takes the
+// 8-element groups tid, tid + 256, ... (NG of them, K <= 2048 NG), read with
+// 16-byte loads and written as 8-byte codes.
+template <int SRC, int NG>
+__global__ __launch_bounds__(256) void k_q8_rows_reg(const void* __restrict__ src, const uint16_t* __restrict__ diag,
+                                                     const int* __restrict__ rexp_in, int nsplit, int M, int K,
+                                                     int8_t* __restrict__ q, int* __restrict__ rexp) {
+  __shared__ uint32_t s_max[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  f32x4 v[NG][2];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int k = (g * 256 + tid) * 8;
+    v[g][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    v[g][1] = v[g][0];
+    if (k >= K) continue;
+    const size_t o = (size_t)t * K + k;
+    if (SRC == SRC_XDIN) {
+      const uint4 xb = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + o);
+      const uint4 db = *reinterpret_cast<const uint4*>(diag + k);
+      const uint32_t xw[4] = {xb.x, xb.y, xb.z, xb.w}, dw[4] = {db.x, db.y, db.z, db.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[g][h >> 1][2 * (h & 1)] = bf16_to_f32(xw[h] & 0xFFFFu) * f16_bits_to_f32(dw[h] & 0xFFFFu);
+        v[g][h >> 1][2 * (h & 1) + 1] = bf16_to_f32(xw[h] >> 16) * f16_bits_to_f32(dw[h] >> 16);
+      }
+    } else if (SRC == SRC_F32) {
+      const float* hs = reinterpret_cast<const float*>(src) + o;
+      v[g][0] = *reinterpret_cast<const f32x4*>(hs);
+      v[g][1] = *reinterpret_cast<const f32x4*>(hs + 4);
+    } else {
+      const int* part = reinterpret_cast<const int*>(src) + o;
+      i32x4 s0 = *reinterpret_cast<const i32x4*>(part), s1 = *reinterpret_cast<const i32x4*>(part + 4);
+      for (int sl = 1; sl < nsplit; ++sl) {
+        s0 += *reinterpret_cast<const i32x4*>(part + (size_t)sl * M * K);
+        s1 += *reinterpret_cast<const i32x4*>(part + (size_t)sl * M * K + 4);
+      }
+      const int e_in = rexp_in[t];
+      const uint4 db = *reinterpret_cast<const uint4*>(diag + k);
+      const uint32_t dw[4] = {db.x, db.y, db.z, db.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int a0 = (h < 2 ? s0 : s1)[2 * (h & 1)], a1 = (h < 2 ? s0 : s1)[2 * (h & 1) + 1];
+        v[g][h >> 1][2 * (h & 1)] = f16_bits_to_f32(dw[h] & 0xFFFFu) * __builtin_amdgcn_ldexpf((float)a0, e_in);
+        v[g][h >> 1][2 * (h & 1) + 1] = f16_bits_to_f32(dw[h] >> 16) * __builtin_amdgcn_ldexpf((float)a1, e_in);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = max(mx, __float_as_uint(v[g][h][c]) & 0x7fffffffu);
+  }
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+  __syncthreads();
+  mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const float m = __uint_as_float(mx);
+  int e = 0;
+  if (m > 0.f) {
+    const int E = ilogbf(m);  // 2^E <= m < 2^(E+1)
+    e = (m <= __builtin_amdgcn_ldexpf(127.f, E - 6)) ? E - 6 : E - 5;
+  }
+  if (tid == 0) rexp[t] = e;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int k = (g * 256 + tid) * 8;
+    if (k >= K) continue;
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        b |= ((uint32_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(v[g][h][c], -e)) & 0xFFu) << (8 * c);
+      w[h] = b;
+    }
+    *reinterpret_cast<uint2*>(q + (size_t)t * K + k) = make_uint2(w[0], w[1]);
+  }
+}
+
+template <int SRC>
+static void launch_q8_rows(const void* src, const uint16_t* diag, const int* rexp_in, int nsplit, int M, int K,
+                           int8_t* q, int* rexp, hipStream_t st) {
+  const int ng = (K + 2047) / 2048;
+  const dim3 g(M), b(256);
+  if (ng <= 1)
+    hipLaunchKernelGGL((k_q8_rows_reg<SRC, 1>), g, b, 0, st, src, diag, rexp_in, nsplit, M, K, q, rexp);
+  else if (ng <= 2)
+    hipLaunchKernelGGL((k_q8_rows_reg<SRC, 2>), g, b, 0, st, src, diag, rexp_in, nsplit, M, K, q, rexp);
+  else if (ng <= 4)
+    hipLaunchKernelGGL((k_q8_rows_reg<SRC, 4>), g, b, 0, st, src, diag, rexp_in, nsplit, M, K, q, rexp);
+  else if (ng <= 8)
+    hipLaunchKernelGGL((k_q8_rows_reg<SRC, 8>), g, b, 0, st, src, diag, rexp_in, nsplit, M, K, q, rexp);
+  else
+    hipLaunchKernelGGL(k_q8_rows<SRC>, g, b, 0, st, src, diag, rexp_in, nsplit, M, K, q, rexp);
+}
+
+// y = fp32(d_out * (s * 2^e2)), s the sum of the nsplit int32 partials of the
+// second product; four consecutive outputs per thread
+__global__ __launch_bounds__(256) void k_q8_out(const int* __restrict__ part, int nsplit, int M, int N,
+                                                const int* __restrict__ rexp, const uint16_t* __restrict__ diag,
+                                                void* __restrict__ y, int y_bf16) {
+  const size_t MN = (size_t)M * N;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  if ((N & 3) == 0) {  // the four share a row; 16-byte loads
+    i32x4 sum = *reinterpret_cast<const i32x4*>(part + i);
+    for (int s = 1; s < nsplit; ++s) sum += *reinterpret_cast<const i32x4*>(part + (size_t)s * MN + i);
+    const int row = (int)(i / N), col = (int)(i % N), e = rexp[row];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      store_out(y, i + j, f16_bits_to_f32(diag[col + j]) * __builtin_amdgcn_ldexpf((float)sum[j], e), y_bf16);
+    return;
+  }
+  for (int j = 0; j < 4 && i + j < MN; ++j) {
+    int sum = 0;
+    for (int s = 0; s < nsplit; ++s) sum += part[(size_t)s * MN + i + j];
+    const int row = (int)((i + j) / N), col = (int)((i + j) % N);
+    store_out(y, i + j, f16_bits_to_f32(diag[col]) * __builtin_amdgcn_ldexpf((float)sum, rexp[row]), y_bf16);
+  }
+}
+
 // ---- product of codes with a sign plane --------------------------------------
 
 // four sign bits (bit i -> weight i) as four bytes: 0xFF (bit set: -1) or 0x01
@@ -66,7 +199,12 @@ __device__ __forceinline__ uint32_t signs4_to_bytes(uint32_t nib) {
   return mask | 0x01010101u;
 }
 
-template <bool STAGE2>
+enum { OUT_HS, OUT_Y, OUT_PART };
+
+// OUT_HS: h_s = fp32(diag * (acc * 2^e)) as fp32 [M][N]; OUT_Y: the same
+// value as y_dtype; OUT_PART: the raw int32 sums of K-slice blockIdx.y into
+// part[blockIdx.y][M][N]
+template <int OUT>
 __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, const int* __restrict__ rexp, int M,
                                                  int N, int K, const uint32_t* __restrict__ signs,
                                                  const uint16_t* __restrict__ diag, void* __restrict__ out,
@@ -78,20 +216,28 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   const int wr = wave >> 1, wc = wave & 1;
   const int tiles_n = (N + BN - 1) / BN;
   const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
-  const int nk = K / BK;
+  const int nk = K / BK / gridDim.y;  // k-steps of this K-slice
+  const int kt0 = blockIdx.y * nk;
   const int KW = K >> 5;  // sign dwords per weight row
 
   // staging: thread tid moves A bytes [row tid/2][32 (tid%2) .. +32) (two
-  // 16-byte loads) and the sign dword of column tid/2, k-half tid%2
+  // 16-byte loads) and the sign dword of column tid/2, k-half tid%2. Two
+  // register sets (P, Q) keep the loads two k-steps ahead of their LDS store.
   const int srow = tid >> 1, shalf = tid & 1;
   const int gm = m0 + srow < M ? m0 + srow : M - 1;  // rows past M repeat the last (never stored)
   const int gn = n0 + srow < N ? n0 + srow : N - 1;  // columns past N repeat the last (never stored)
-  const int8_t* asrc = a + (size_t)gm * K + 32 * shalf;
-  const uint32_t* wsrc = signs + (size_t)gn * KW + shalf;
+  const int8_t* asrc = a + (size_t)gm * K + (size_t)kt0 * BK + 32 * shalf;
+  const uint32_t* wsrc = signs + (size_t)gn * KW + 2 * kt0 + shalf;
   const int lofs = srow * LDB + 32 * shalf;
-  uint4 ra0 = *reinterpret_cast<const uint4*>(asrc), ra1 = *reinterpret_cast<const uint4*>(asrc + 16);
-  uint32_t rw = *wsrc;
-#define Q8_STORE_STAGE(buf)                                                                                   \
+  uint4 pa0, pa1, qa0, qa1;
+  uint32_t pw, qw;
+#define Q8_LOAD(ra0, ra1, rw, kt)                                      \
+  {                                                                    \
+    ra0 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK);           \
+    ra1 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK + 16);      \
+    rw = wsrc[(kt) * 2];                                               \
+  }
+#define Q8_STORE(ra0, ra1, rw, buf)                                                                          \
   {                                                                                                          \
     uint4* da = reinterpret_cast<uint4*>(&As[buf][lofs]);                                                    \
     da[0] = ra0;                                                                                             \
@@ -111,15 +257,7 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  Q8_STORE_STAGE(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      ra0 = *reinterpret_cast<const uint4*>(asrc + (kt + 1) * BK);
-      ra1 = *reinterpret_cast<const uint4*>(asrc + (kt + 1) * BK + 16);
-      rw = wsrc[(kt + 1) * 2];
-    }
+  auto mfma_step = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       // lane l: row (column) l%32 of its 32-tile, bytes k = 32 ks + 16 (l/32) .. +15
@@ -127,19 +265,42 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
       i32x4 af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(&As[cur][(wr * 64 + 32 * i + (lane & 31)) * LDB + kofs]);
+        af[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wr * 64 + 32 * i + (lane & 31)) * LDB + kofs]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(&Bs[cur][(wc * 64 + 32 * j + (lane & 31)) * LDB + kofs]);
+        bf[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wc * 64 + 32 * j + (lane & 31)) * LDB + kofs]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) Q8_STORE_STAGE(cur ^ 1);
+  };
+
+  // k-step kt computes from LDS buffer kt % 2 and stores step kt + 1 (held in
+  // P for even kt, Q for odd) into the other buffer, then reloads that set
+  // with step kt + 3
+  Q8_LOAD(pa0, pa1, pw, 0);
+  Q8_STORE(pa0, pa1, pw, 0);
+  if (nk > 1) Q8_LOAD(pa0, pa1, pw, 1);
+  if (nk > 2) Q8_LOAD(qa0, qa1, qw, 2);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    mfma_step(0);
+    if (kt + 1 < nk) {
+      Q8_STORE(pa0, pa1, pw, 1);
+      if (kt + 3 < nk) Q8_LOAD(pa0, pa1, pw, kt + 3);
+    }
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    mfma_step(1);
+    if (kt + 2 < nk) {
+      Q8_STORE(qa0, qa1, qw, 0);
+      if (kt + 4 < nk) Q8_LOAD(qa0, qa1, qw, kt + 4);
+    }
     __syncthreads();
   }
-#undef Q8_STORE_STAGE
+#undef Q8_LOAD
+#undef Q8_STORE
 
   // epilogue: lane l holds, in item r, row 8(r/4) + 4(l/32) + r%4 of column l%32
 #pragma unroll
@@ -148,30 +309,57 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wc * 64 + 32 * j + (lane & 31);
       if (col >= N) continue;
-      const float dg = f16_bits_to_f32(diag[col]);
+      const float dg = OUT == OUT_PART ? 0.f : f16_bits_to_f32(diag[col]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wr * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= M) continue;
-        const float v = dg * __builtin_amdgcn_ldexpf((float)acc[i][j][r], rexp[row]);
-        if (STAGE2)
-          store_out(out, (size_t)row * N + col, v, out_bf16);
-        else
-          reinterpret_cast<float*>(out)[(size_t)row * N + col] = v;
+        const size_t o = (size_t)row * N + col;
+        if (OUT == OUT_PART) {
+          reinterpret_cast<int*>(out)[(size_t)blockIdx.y * M * N + o] = acc[i][j][r];
+        } else {
+          const float v = dg * __builtin_amdgcn_ldexpf((float)acc[i][j][r], rexp[row]);
+          if (OUT == OUT_Y)
+            store_out(out, o, v, out_bf16);
+          else
+            reinterpret_cast<float*>(out)[o] = v;
+        }
       }
     }
 }
 
-// workspace: q1 int8 [M][n], e1 [M], h_s fp32 [M][r], q2 int8 [M][r], e2 [M]
+// K-slices of a product with `tiles` output tiles and nk 64-wide k-steps:
+// doubled while the grid stays within 256 workgroups and every slice keeps
+// at least 8 k-steps
+int q8_ksplit(int tiles, int nk) {
+  int ks = 1;
+  while (tiles * ks * 2 <= 256 && nk % (2 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
+  return ks;
+}
+
+// workspace: q1 int8 [M][n], e1 [M], h_s fp32 [M][r], q2 int8 [M][r], e2 [M],
+// int32 K-slice partials [max(ks1 r, ks2 m)][M]
+static void q8_splits(int64_t M, int64_t m, int64_t n, int64_t r, int& ks1, int& ks2) {
+  const int mt = (int)((M + 127) / 128);
+  ks1 = q8_ksplit(mt * (int)((r + 127) / 128), (int)(n / 64));
+  ks2 = q8_ksplit(mt * (int)((m + 127) / 128), (int)(r / 64));
+}
+
 size_t dbf_q8_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
-  (void)m;
+  int ks1, ks2;
+  q8_splits(M, m, n, r, ks1, ks2);
+  size_t part = 0;
+  if (ks1 > 1) part = (size_t)ks1 * M * r * 4;
+  if (ks2 > 1 && (size_t)ks2 * M * m * 4 > part) part = (size_t)ks2 * M * m * 4;
   return align256((size_t)M * n) + align256((size_t)M * 4) + align256((size_t)M * r * 4) + align256((size_t)M * r) +
-         align256((size_t)M * 4);
+         align256((size_t)M * 4) + align256(part);
 }
 
 hipError_t launch_dbf_q8(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
                          const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
                          void* ws, hipStream_t st) {
+  int ks1, ks2;
+  q8_splits(M, m, n, r, ks1, ks2);
   char* p = reinterpret_cast<char*>(ws);
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
   int8_t* q1 = reinterpret_cast<int8_t*>(take((size_t)M * n));
@@ -179,14 +367,28 @@ hipError_t launch_dbf_q8(const uint16_t* x, int M, int m, int n, int r, const ui
   float* hs = reinterpret_cast<float*>(take((size_t)M * r * 4));
   int8_t* q2 = reinterpret_cast<int8_t*>(take((size_t)M * r));
   int* e2 = reinterpret_cast<int*>(take((size_t)M * 4));
+  int* part = reinterpret_cast<int*>(p);
   const uint32_t* v32 = reinterpret_cast<const uint32_t*>(v);
   const uint32_t* u32 = reinterpret_cast<const uint32_t*>(u);
-  hipLaunchKernelGGL(k_q8_rows<true>, dim3(M), dim3(256), 0, st, x, d_in, n, q1, e1);
-  const int t1 = ((M + 127) / 128) * ((r + 127) / 128);
-  hipLaunchKernelGGL(k_tile_q8<false>, dim3(t1), dim3(256), 0, st, q1, e1, M, r, n, v32, d_mid, hs, 0);
-  hipLaunchKernelGGL(k_q8_rows<false>, dim3(M), dim3(256), 0, st, hs, nullptr, r, q2, e2);
-  const int t2 = ((M + 127) / 128) * ((m + 127) / 128);
-  hipLaunchKernelGGL(k_tile_q8<true>, dim3(t2), dim3(256), 0, st, q2, e2, M, m, r, u32, d_out, y, y_bf16);
+  const int mt = (M + 127) / 128;
+  launch_q8_rows<SRC_XDIN>(x, d_in, nullptr, 1, M, n, q1, e1, st);
+  const dim3 g1(mt * ((r + 127) / 128), ks1);
+  if (ks1 == 1) {
+    hipLaunchKernelGGL(k_tile_q8<OUT_HS>, g1, dim3(256), 0, st, q1, e1, M, r, n, v32, d_mid, hs, 0);
+    launch_q8_rows<SRC_F32>(hs, nullptr, nullptr, 1, M, r, q2, e2, st);
+  } else {
+    hipLaunchKernelGGL(k_tile_q8<OUT_PART>, g1, dim3(256), 0, st, q1, e1, M, r, n, v32, d_mid, part, 0);
+    launch_q8_rows<SRC_PART>(part, d_mid, e1, ks1, M, r, q2, e2, st);
+  }
+  const dim3 g2(mt * ((m + 127) / 128), ks2);
+  if (ks2 == 1) {
+    hipLaunchKernelGGL(k_tile_q8<OUT_Y>, g2, dim3(256), 0, st, q2, e2, M, m, r, u32, d_out, y, y_bf16);
+  } else {
+    hipLaunchKernelGGL(k_tile_q8<OUT_PART>, g2, dim3(256), 0, st, q2, e2, M, m, r, u32, d_out, part, 0);
+    const size_t quads = ((size_t)M * m + 3) / 4;
+    hipLaunchKernelGGL(k_q8_out, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part, ks2, M, m, e2, d_out,
+                       y, y_bf16);
+  }
   return hipGetLastError();
 }
 

@@ -187,9 +187,12 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
  *   y   = d_out * (q2 . U^T) * 2^e2    (one fp32 rounding, then y_dtype)
  * The codes and exponents are decided in fp32, where every input to them is
  * exact, so they match an fp64 evaluation of the same definition bit for bit.
- * Arguments, layouts and limits are those of brq_dbf_gemm; the workspace
- * holds the two code planes, the row exponents and h_s (fp32 [M][r]).
- * Alignment: v and u 16 bytes, the others their element size.
+ * Arguments and layouts are those of brq_dbf_gemm, with n and r at most
+ * 131072 (so that 127 * n < 2^24 and every integer sum is exact in fp32). The
+ * workspace holds the two code planes, the row exponents, h_s (fp32 [M][r])
+ * and, when few output tiles split the reductions along k, their int32
+ * partial sums (added exactly, in any order).
+ * Alignment: x, v, u, d_in and d_mid 16 bytes; y and d_out their element size.
  */
 size_t brq_dbf_q8_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
 brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, int64_t r,

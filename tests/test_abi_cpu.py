@@ -165,7 +165,11 @@ def test_dbf_q8_validation(L):
     assert f(*bad) == E_SHAPE
     bad = list(args); bad[4] = 100
     assert f(*bad) == E_SHAPE
+    bad = list(args); bad[3] = 131072 + 128                 # 127 n must stay below 2^24
+    assert f(*bad) == E_SHAPE
     bad = list(args); bad[6] = PMIS
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[7] = PMIS                         # d_mid is read 8 values at a time
     assert f(*bad) == E_ALIGN
     bad = list(args); bad[10] = PMIS; bad[11] = 1           # fp32 y needs 4-byte alignment
     assert f(*bad) == E_ALIGN
@@ -175,8 +179,13 @@ def test_dbf_q8_validation(L):
     assert f(*bad) == E_WORKSPACE
     bad = list(args); bad[12] = PMIS
     assert f(*bad) == E_WORKSPACE
-    # codes [M][n] int8, exponents [M], h_s [M][r] fp32, codes [M][r], exponents [M]
-    assert L.brq_dbf_q8_workspace_bytes(512, 4096, 4096, 2048) == 512 * 4096 + 2048 + 512 * 2048 * 4 + 512 * 2048 + 2048
+    # codes [M][n] int8, exponents [M], h_s [M][r] fp32, codes [M][r], exponents [M]; 4096 rows fill
+    # 512 tiles and split no reduction
+    assert L.brq_dbf_q8_workspace_bytes(4096, 4096, 4096, 2048) == (4096 * 4096 + 4 * 4096 + 4096 * 2048 * 4
+                                                                    + 4096 * 2048 + 4 * 4096)
+    # 512 rows: 64 tiles of the first product in 4 K-slices, 128 of the second in 2: int32 partials
+    base = 512 * 4096 + 2048 + 512 * 2048 * 4 + 512 * 2048 + 2048
+    assert L.brq_dbf_q8_workspace_bytes(512, 4096, 4096, 2048) == base + max(4 * 512 * 2048, 2 * 512 * 4096) * 4
     assert L.brq_dbf_q8_workspace_bytes(1, 4096, 4096, 100) == 0
 
 
