@@ -3,19 +3,22 @@
 // activation row is denormalised to one shared exponent and encoded in 8 bits
 // (a sign and seven magnitude bits), the binary product of a row is an exact
 // integer reduction of weight signs times activation codes, and one shared
-// scale follows. The pages evaluate that reduction with XOR + AND + POPCOUNT +
-// SHIFT + ADD over bitplanes; on gfx950 the same integer comes from the int8
-// matrix cores (v_mfma_i32_32x32x32_i8) with the weights as +-1 bytes, exact
-// in int32.
+// scale follows. The pages evaluate that reduction over bitplanes with masked
+// population counts; on gfx950 the same integer comes from the int8 matrix
+// cores (v_mfma_i32_32x32x32_i8) with the weights as +-1 bytes, exact in int32
+// (section 5, item 1 names that form of the reduction).
 //
-//   k_q8_rows: one workgroup per row: v = x * d_in (bf16 x fp16, exact in
-//     fp32) or v = h_s (fp32); e = the smallest integer with max|v| <= 127 *
-//     2^e; q = round-half-even(v / 2^e) as int8, natural order.
+//   k_q8_rows_reg / k_q8_rows: one workgroup per row: v = x * d_in (bf16 x
+//     fp16, exact in fp32), v = h_s (fp32), or h_s from int32 K-slice sums;
+//     e = the smallest integer with max|v| <= 127 * 2^e; q = round-half-even
+//     (v / 2^e) as int8, stored in the k order shared with the weight bytes.
 //   k_tile_q8: 128 x 128 output tiles of the product of the codes with a +-1
 //     sign plane, 64-wide k-steps, four waves of 64 x 64 (2 x 2 MFMAs of 32 x
-//     32 x 32); the sign words of a k-step become +-1 bytes in LDS (a byte
-//     permute with the 0x00 / 0xFF selectors per four signs). Epilogue:
-//     h_s = fp32(d_mid * (acc * 2^e)) (stage 1) or y = d_out * (acc * 2^e).
+//     32 x 32); each sign dword of a k-step becomes eight dwords of +-1 bytes
+//     in LDS, one AND and one byte permute each. Epilogue: h_s = fp32(d_mid *
+//     (acc * 2^e)) (first product), y = d_out * (acc * 2^e) (second), or the
+//     raw int32 sums of a K-slice.
+//   k_q8_out: y from the K-slice sums of the second product.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,6 +26,19 @@ namespace brq {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// Codes and weight bytes share a k order inside every 32-wide group: byte
+// p = 4 d + j of the group holds k = 8 j + d (dword d gathers k = d, d + 8,
+// d + 16, d + 24). In that order dword d of the weight bytes of a 32-bit sign
+// word w is one byte permute of the selector w & (0x01010101 << d): a
+// selector byte is 0 (bit clear: byte 0 of 0x00FFFF01, 0x01) or 2^d (set:
+// 1 -> byte 1, 2 -> byte 2, 4 -> byte 4 = the low byte of 0x000000FF, 8 -> the
+// sign of bit 15 of 0x00FFFF01, 16 and above -> 0xFF), so -1 or +1.
+__device__ __forceinline__ int q8_pos(int k) { return (k & ~31) + 4 * (k & 7) + ((k >> 3) & 3); }
+
+__device__ __forceinline__ uint32_t signs_to_bytes(uint32_t w, int d) {
+  return __builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & (0x01010101u << d));
+}
 
 // ---- quantisation of rows ---------------------------------------------------
 
@@ -63,7 +79,7 @@ __global__ __launch_bounds__(256) void k_q8_rows(const void* __restrict__ src, c
   }
   if (tid == 0) rexp[t] = e;
   for (int k = tid; k < K; k += 256)
-    q[(size_t)t * K + k] = (int8_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(val(k), -e));
+    q[(size_t)t * K + q8_pos(k)] = (int8_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(val(k), -e));
 }
 
 // The same quantisation with the row held in registers: thread tid takes the
@@ -74,6 +90,7 @@ __global__ __launch_bounds__(256) void k_q8_rows_reg(const void* __restrict__ sr
                                                      const int* __restrict__ rexp_in, int nsplit, int M, int K,
                                                      int8_t* __restrict__ q, int* __restrict__ rexp) {
   __shared__ uint32_t s_max[4];
+  __shared__ __attribute__((aligned(16))) int8_t s_code[NG * 2048];
   const int t = blockIdx.x, tid = threadIdx.x;
   f32x4 v[NG][2];
   uint32_t mx = 0;
@@ -130,20 +147,22 @@ __global__ __launch_bounds__(256) void k_q8_rows_reg(const void* __restrict__ sr
     e = (m <= __builtin_amdgcn_ldexpf(127.f, E - 6)) ? E - 6 : E - 5;
   }
   if (tid == 0) rexp[t] = e;
+  // the codes go to their positions in the shared k order through LDS (byte
+  // p of a 32-wide group gathers from four threads), then out 8 bytes a thread
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const int k = (g * 256 + tid) * 8;
     if (k >= K) continue;
-    uint32_t w[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t b = 0;
+    for (int i = 0; i < 8; ++i)
+      s_code[q8_pos(k + i)] = (int8_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(v[g][i >> 2][i & 3], -e));
+  }
+  __syncthreads();
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        b |= ((uint32_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(v[g][h][c], -e)) & 0xFFu) << (8 * c);
-      w[h] = b;
-    }
-    *reinterpret_cast<uint2*>(q + (size_t)t * K + k) = make_uint2(w[0], w[1]);
+  for (int g = 0; g < NG; ++g) {
+    const int k = (g * 256 + tid) * 8;
+    if (k >= K) continue;
+    *reinterpret_cast<uint2*>(q + (size_t)t * K + k) = *reinterpret_cast<const uint2*>(&s_code[k]);
   }
 }
 
@@ -191,15 +210,9 @@ __global__ __launch_bounds__(256) void k_q8_out(const int* __restrict__ part, in
 
 // ---- product of codes with a sign plane --------------------------------------
 
-// four sign bits (bit i -> weight i) as four bytes: 0xFF (bit set: -1) or 0x01
-__device__ __forceinline__ uint32_t signs4_to_bytes(uint32_t nib) {
-  const uint32_t spread = (nib * 0x00204081u) & 0x01010101u;  // bit i -> byte i
-  // byte permute: selector 0x0C gives 0x00, 0x0D gives 0xFF
-  const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, 0x0C0C0C0Cu + spread);
-  return mask | 0x01010101u;
-}
-
 enum { OUT_HS, OUT_Y, OUT_PART };
+
+__device__ __forceinline__ int q8_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // OUT_HS: h_s = fp32(diag * (acc * 2^e)) as fp32 [M][N]; OUT_Y: the same
 // value as y_dtype; OUT_PART: the raw int32 sums of K-slice blockIdx.y into
@@ -209,9 +222,13 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
                                                  int N, int K, const uint32_t* __restrict__ signs,
                                                  const uint16_t* __restrict__ diag, void* __restrict__ out,
                                                  int out_bf16) {
-  constexpr int BM = 128, BN = 128, BK = 64, LDB = BK + 16;  // LDS row: 64 bytes + 16 against bank conflicts
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * LDB];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * LDB];
+  // LDS rows of 64 bytes; the 16-byte chunk c of row r sits at chunk
+  // c ^ q8_swz(r), which keeps both the fragment reads (32 rows, one chunk)
+  // and the staging writes (two chunks of each of 4 or 8 rows per group of
+  // lanes) on distinct banks
+  constexpr int BM = 128, BN = 128, BK = 64;
+  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int tiles_n = (N + BN - 1) / BN;
@@ -228,7 +245,8 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   const int gn = n0 + srow < N ? n0 + srow : N - 1;  // columns past N repeat the last (never stored)
   const int8_t* asrc = a + (size_t)gm * K + (size_t)kt0 * BK + 32 * shalf;
   const uint32_t* wsrc = signs + (size_t)gn * KW + 2 * kt0 + shalf;
-  const int lofs = srow * LDB + 32 * shalf;
+  const int lofs0 = srow * BK + 16 * ((2 * shalf) ^ q8_swz(srow));
+  const int lofs1 = srow * BK + 16 * ((2 * shalf + 1) ^ q8_swz(srow));
   uint4 pa0, pa1, qa0, qa1;
   uint32_t pw, qw;
 #define Q8_LOAD(ra0, ra1, rw, kt)                                      \
@@ -239,14 +257,12 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   }
 #define Q8_STORE(ra0, ra1, rw, buf)                                                                          \
   {                                                                                                          \
-    uint4* da = reinterpret_cast<uint4*>(&As[buf][lofs]);                                                    \
-    da[0] = ra0;                                                                                             \
-    da[1] = ra1;                                                                                             \
-    uint4* db = reinterpret_cast<uint4*>(&Bs[buf][lofs]);                                                    \
-    db[0] = make_uint4(signs4_to_bytes(rw & 0xFu), signs4_to_bytes((rw >> 4) & 0xFu),                        \
-                       signs4_to_bytes((rw >> 8) & 0xFu), signs4_to_bytes((rw >> 12) & 0xFu));               \
-    db[1] = make_uint4(signs4_to_bytes((rw >> 16) & 0xFu), signs4_to_bytes((rw >> 20) & 0xFu),               \
-                       signs4_to_bytes((rw >> 24) & 0xFu), signs4_to_bytes(rw >> 28));                       \
+    *reinterpret_cast<uint4*>(&As[buf][lofs0]) = ra0;                                                        \
+    *reinterpret_cast<uint4*>(&As[buf][lofs1]) = ra1;                                                        \
+    *reinterpret_cast<uint4*>(&Bs[buf][lofs0]) = make_uint4(signs_to_bytes(rw, 0), signs_to_bytes(rw, 1),     \
+                                                            signs_to_bytes(rw, 2), signs_to_bytes(rw, 3));    \
+    *reinterpret_cast<uint4*>(&Bs[buf][lofs1]) = make_uint4(signs_to_bytes(rw, 4), signs_to_bytes(rw, 5),     \
+                                                            signs_to_bytes(rw, 6), signs_to_bytes(rw, 7));    \
   }
 
   i32x16 acc[2][2];
@@ -257,18 +273,21 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
+  // lane l reads row (column) l%32 of a 32-row block, chunk 2 ks + l/32 (bytes
+  // k = 32 ks + 16 (l/32) .. +15); the blocks start at multiples of 32 rows,
+  // so the swizzle depends on l%32 alone
+  const int rsw = q8_swz(lane & 31), rofs = (lane & 31) * BK;
   auto mfma_step = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      // lane l: row (column) l%32 of its 32-tile, bytes k = 32 ks + 16 (l/32) .. +15
-      const int kofs = 32 * ks + 16 * (lane >> 5);
+      const int kofs = rofs + 16 * ((2 * ks + (lane >> 5)) ^ rsw);
       i32x4 af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wr * 64 + 32 * i + (lane & 31)) * LDB + kofs]);
+        af[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wr * 64 + 32 * i) * BK + kofs]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wc * 64 + 32 * j + (lane & 31)) * LDB + kofs]);
+        bf[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wc * 64 + 32 * j) * BK + kofs]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -278,25 +297,24 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 
   // k-step kt computes from LDS buffer kt % 2 and stores step kt + 1 (held in
   // P for even kt, Q for odd) into the other buffer, then reloads that set
-  // with step kt + 3
+  // with step kt + 3. Every K-slice has an even number of k-steps (at least
+  // 2), so the loop runs whole pairs; the loads past the slice's last step
+  // repeat that step (the copies are never read), which keeps every load and
+  // store unconditional.
+  const int last = nk - 1;
   Q8_LOAD(pa0, pa1, pw, 0);
   Q8_STORE(pa0, pa1, pw, 0);
-  if (nk > 1) Q8_LOAD(pa0, pa1, pw, 1);
-  if (nk > 2) Q8_LOAD(qa0, qa1, qw, 2);
+  Q8_LOAD(pa0, pa1, pw, 1);
+  Q8_LOAD(qa0, qa1, qw, min(2, last));
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     mfma_step(0);
-    if (kt + 1 < nk) {
-      Q8_STORE(pa0, pa1, pw, 1);
-      if (kt + 3 < nk) Q8_LOAD(pa0, pa1, pw, kt + 3);
-    }
+    Q8_STORE(pa0, pa1, pw, 1);
+    Q8_LOAD(pa0, pa1, pw, min(kt + 3, last));
     __syncthreads();
-    if (kt + 1 >= nk) break;
     mfma_step(1);
-    if (kt + 2 < nk) {
-      Q8_STORE(qa0, qa1, qw, 0);
-      if (kt + 4 < nk) Q8_LOAD(qa0, qa1, qw, kt + 4);
-    }
+    Q8_STORE(qa0, qa1, qw, 0);
+    Q8_LOAD(qa0, qa1, qw, min(kt + 4, last));
     __syncthreads();
   }
 #undef Q8_LOAD
@@ -328,12 +346,12 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
     }
 }
 
-// K-slices of a product with `tiles` output tiles and nk 64-wide k-steps:
-// doubled while the grid stays within 256 workgroups and every slice keeps
-// at least 8 k-steps
+// K-slices of a product with `tiles` output tiles and nk 64-wide k-steps (nk
+// even): doubled while the grid stays within 256 workgroups and every slice
+// keeps an even number of k-steps (the loop runs whole pairs), at least 8
 int q8_ksplit(int tiles, int nk) {
   int ks = 1;
-  while (tiles * ks * 2 <= 256 && nk % (2 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
+  while (tiles * ks * 2 <= 256 && nk % (4 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
   return ks;
 }
 

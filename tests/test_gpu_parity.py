@@ -450,11 +450,13 @@ def _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r, out=torch.float32):
 
 
 # several 128 x 128 tiles with ragged row and column tails, 64-wide k-steps;
-# the last three have few tiles and long reductions, which split along k into
-# 2 or 4 int32 partial sums (m = 99: the output pass off 4-element rows)
+# three with few tiles and long reductions, which split along k into 2 or 4
+# int32 partial sums (m = 99: the output pass off 4-element rows); rows longer
+# than 16384 (n or r = 16512) take the quantiser that re-reads its row
 @pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (5, 200, 384, 256), (127, 128, 256, 128),
                                      (130, 300, 640, 384), (300, 96, 512, 640), (3, 130, 1024, 1280),
-                                     (70, 100, 2048, 1024), (9, 99, 1024, 1024)])
+                                     (70, 100, 2048, 1024), (9, 99, 1024, 1024), (3, 64, 16512, 256),
+                                     (2, 64, 256, 16512)])
 def test_dbf_q8_small(M, m, n, r):
     say("dbf q8", M, m, n, r)
     x, d_in, vw, d_mid, uw, d_out = _q8_inputs(M, m, n, r, M + m + n + r)
