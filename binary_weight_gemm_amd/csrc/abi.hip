@@ -236,10 +236,9 @@ brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, i
     return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: M=%lld with max(m, r)=%lld needs more than 2^31 tiles", (long long)M,
                 (long long)wide);
   if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm_q8: unknown y_dtype %d", (int)y_dtype);
-  if (!aligned(x, 16) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, y_dtype == BRQ_BF16 ? 2 : 4) ||
-      !aligned(d_in, 16) || !aligned(d_mid, 16) || !aligned(d_out, 2))
-    return fail(BRQ_E_ALIGN, "brq_dbf_gemm_q8: x, v, u, d_in and d_mid must be 16-byte aligned, y and d_out aligned "
-                "to their element");
+  if (!aligned(x, 16) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, 4) || !aligned(d_in, 16) ||
+      !aligned(d_mid, 16) || !aligned(d_out, 2))
+    return fail(BRQ_E_ALIGN, "brq_dbf_gemm_q8: x, v, u, d_in and d_mid must be 16-byte aligned, y 4-byte");
   const size_t need = brq::dbf_q8_ws_bytes(M, m, n, r);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(BRQ_E_WORKSPACE, "brq_dbf_gemm_q8: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,

@@ -36,9 +36,6 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 // sign of bit 15 of 0x00FFFF01, 16 and above -> 0xFF), so -1 or +1.
 __device__ __forceinline__ int q8_pos(int k) { return (k & ~31) + 4 * (k & 7) + ((k >> 3) & 3); }
 
-__device__ __forceinline__ uint32_t signs_to_bytes(uint32_t w, int d) {
-  return __builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & (0x01010101u << d));
-}
 
 // ---- quantisation of rows ---------------------------------------------------
 
@@ -222,48 +219,76 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
                                                  int N, int K, const uint32_t* __restrict__ signs,
                                                  const uint16_t* __restrict__ diag, void* __restrict__ out,
                                                  int out_bf16) {
-  // LDS rows of 64 bytes; the 16-byte chunk c of row r sits at chunk
-  // c ^ q8_swz(r), which keeps both the fragment reads (32 rows, one chunk)
-  // and the staging writes (two chunks of each of 4 or 8 rows per group of
-  // lanes) on distinct banks
+  // LDS holds the code tile (rows of 64 bytes; the 16-byte chunk c of row r
+  // at chunk c ^ q8_swz(r), which keeps both the fragment reads (32 rows, one
+  // chunk) and the staging writes (two chunks of each of 4 or 8 rows per
+  // group of lanes) on distinct banks) and the packed sign dwords of the
+  // tile's columns; the +-1 weight fragments are built in registers.
   constexpr int BM = 128, BN = 128, BK = 64;
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
+  __shared__ __attribute__((aligned(16))) int8_t As[4][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint32_t Ws[4][BN * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int tiles_n = (N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
-  const int nk = K / BK / gridDim.y;  // k-steps of this K-slice
+  // tile id -> (row tile, column tile). Workgroups go to the 8 XCDs in turn
+  // (id % 8); the first 8 floor(T / 8) ids are renumbered so that each XCD
+  // takes a contiguous run of tiles, i.e. few activation row blocks per L2
+  const int tiles_n = (N + BN - 1) / BN, ntiles = gridDim.x, per = ntiles >> 3;
+  int bid = blockIdx.x;
+  if (bid < 8 * per) bid = (bid & 7) * per + (bid >> 3);
+  const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
+  const int nk = K / BK / gridDim.y;  // k-steps of this K-slice (even)
   const int kt0 = blockIdx.y * nk;
   const int KW = K >> 5;  // sign dwords per weight row
 
-  // staging: thread tid moves A bytes [row tid/2][32 (tid%2) .. +32) (two
-  // 16-byte loads) and the sign dword of column tid/2, k-half tid%2. Two
-  // register sets (P, Q) keep the loads two k-steps ahead of their LDS store.
+  // staging: thread tid moves code bytes [row tid/2][32 (tid%2) .. +32) of a
+  // k-step (two 16-byte loads) and the sign dword of column tid/2, k-half
+  // tid%2; two register sets (P, Q) hold the two k-steps of the next pair
   const int srow = tid >> 1, shalf = tid & 1;
   const int gm = m0 + srow < M ? m0 + srow : M - 1;  // rows past M repeat the last (never stored)
   const int gn = n0 + srow < N ? n0 + srow : N - 1;  // columns past N repeat the last (never stored)
   const int8_t* asrc = a + (size_t)gm * K + (size_t)kt0 * BK + 32 * shalf;
   const uint32_t* wsrc = signs + (size_t)gn * KW + 2 * kt0 + shalf;
+  // epilogue operands, fetched before the k-loop: the row exponents of the
+  // tile (LDS, visible after the first barrier) and this lane's column scales
+  __shared__ int s_rexp[BM];
+  float dgv[2] = {0.f, 0.f};
+  if (OUT != OUT_PART) {
+    if (tid < BM) s_rexp[tid] = rexp[m0 + tid < M ? m0 + tid : M - 1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = n0 + wc * 64 + 32 * j + (lane & 31);
+      dgv[j] = f16_bits_to_f32(diag[c < N ? c : N - 1]);
+    }
+  }
   const int lofs0 = srow * BK + 16 * ((2 * shalf) ^ q8_swz(srow));
   const int lofs1 = srow * BK + 16 * ((2 * shalf + 1) ^ q8_swz(srow));
   uint4 pa0, pa1, qa0, qa1;
   uint32_t pw, qw;
-#define Q8_LOAD(ra0, ra1, rw, kt)                                      \
-  {                                                                    \
-    ra0 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK);           \
-    ra1 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK + 16);      \
-    rw = wsrc[(kt) * 2];                                               \
+#define Q8_LOAD(ra0, ra1, rw, kt)                                 \
+  {                                                               \
+    ra0 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK);      \
+    ra1 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK + 16); \
+    rw = wsrc[(kt) * 2];                                          \
   }
-#define Q8_STORE(ra0, ra1, rw, buf)                                                                          \
-  {                                                                                                          \
-    *reinterpret_cast<uint4*>(&As[buf][lofs0]) = ra0;                                                        \
-    *reinterpret_cast<uint4*>(&As[buf][lofs1]) = ra1;                                                        \
-    *reinterpret_cast<uint4*>(&Bs[buf][lofs0]) = make_uint4(signs_to_bytes(rw, 0), signs_to_bytes(rw, 1),     \
-                                                            signs_to_bytes(rw, 2), signs_to_bytes(rw, 3));    \
-    *reinterpret_cast<uint4*>(&Bs[buf][lofs1]) = make_uint4(signs_to_bytes(rw, 4), signs_to_bytes(rw, 5),     \
-                                                            signs_to_bytes(rw, 6), signs_to_bytes(rw, 7));    \
+#define Q8_STORE(ra0, ra1, rw, buf)                               \
+  {                                                               \
+    *reinterpret_cast<uint4*>(&As[buf][lofs0]) = ra0;             \
+    *reinterpret_cast<uint4*>(&As[buf][lofs1]) = ra1;             \
+    Ws[buf][tid] = rw;                                            \
   }
+
+  // weight fragments: lane l takes column 32 j + l%32 of its wave's 64, and
+  // of the 32-wide group of a half k-step the bytes 16 (l/32) .. +15, i.e.
+  // dwords d = 4 (l/32) .. +3 of the expanded sign dword
+  uint32_t msk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) msk[i] = 0x01010101u << (4 * (lane >> 5) + i);
+  auto bfrag = [&](uint32_t w) {
+    return i32x4{(int)__builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & msk[0]),
+                 (int)__builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & msk[1]),
+                 (int)__builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & msk[2]),
+                 (int)__builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & msk[3])};
+  };
 
   i32x16 acc[2][2];
 #pragma unroll
@@ -273,21 +298,22 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // lane l reads row (column) l%32 of a 32-row block, chunk 2 ks + l/32 (bytes
-  // k = 32 ks + 16 (l/32) .. +15); the blocks start at multiples of 32 rows,
-  // so the swizzle depends on l%32 alone
+  // lane l reads row l%32 of a 32-row block, chunk 2 ks + l/32; the blocks
+  // start at multiples of 32 rows, so the swizzle depends on l%32 alone
   const int rsw = q8_swz(lane & 31), rofs = (lane & 31) * BK;
   auto mfma_step = [&](int buf) {
+    uint2 sd[2];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
+    for (int j = 0; j < 2; ++j) sd[j] = *reinterpret_cast<const uint2*>(&Ws[buf][2 * (wc * 64 + 32 * j + (lane & 31))]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
       const int kofs = rofs + 16 * ((2 * ks + (lane >> 5)) ^ rsw);
       i32x4 af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         af[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wr * 64 + 32 * i) * BK + kofs]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wc * 64 + 32 * j) * BK + kofs]);
+      for (int j = 0; j < 2; ++j) bf[j] = bfrag(ks == 0 ? sd[j].x : sd[j].y);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -295,63 +321,96 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
     }
   };
 
-  // k-step kt computes from LDS buffer kt % 2 and stores step kt + 1 (held in
-  // P for even kt, Q for odd) into the other buffer, then reloads that set
-  // with step kt + 3. Every K-slice has an even number of k-steps (at least
-  // 2), so the loop runs whole pairs; the loads past the slice's last step
-  // repeat that step (the copies are never read), which keeps every load and
-  // store unconditional.
+  // Four LDS buffers: pair kt, kt + 1 computes from buffers b, b + 1 (b = 0
+  // or 2 by pair parity) while P and Q (steps kt + 2, kt + 3, loaded during
+  // the previous pair) go to the other two and reload with steps kt + 4 and
+  // kt + 5; one barrier per pair. Every K-slice has an even number of k-steps
+  // (at least 2), so the loop runs whole pairs; the loads past the slice's
+  // last step repeat that step (the copies are never read), which keeps every
+  // load and store unconditional.
   const int last = nk - 1;
   Q8_LOAD(pa0, pa1, pw, 0);
+  Q8_LOAD(qa0, qa1, qw, 1);
   Q8_STORE(pa0, pa1, pw, 0);
-  Q8_LOAD(pa0, pa1, pw, 1);
-  Q8_LOAD(qa0, qa1, qw, min(2, last));
+  Q8_STORE(qa0, qa1, qw, 1);
+  Q8_LOAD(pa0, pa1, pw, min(2, last));
+  Q8_LOAD(qa0, qa1, qw, min(3, last));
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    mfma_step(0);
-    Q8_STORE(pa0, pa1, pw, 1);
-    Q8_LOAD(pa0, pa1, pw, min(kt + 3, last));
-    __syncthreads();
-    mfma_step(1);
-    Q8_STORE(qa0, qa1, qw, 0);
-    Q8_LOAD(qa0, qa1, qw, min(kt + 4, last));
+    const int b = kt & 2, o = 2 - b;
+    mfma_step(b);
+    mfma_step(b + 1);
+    Q8_STORE(pa0, pa1, pw, o);
+    Q8_STORE(qa0, qa1, qw, o + 1);
+    Q8_LOAD(pa0, pa1, pw, min(kt + 4, last));
+    Q8_LOAD(qa0, qa1, qw, min(kt + 5, last));
     __syncthreads();
   }
 #undef Q8_LOAD
 #undef Q8_STORE
 
-  // epilogue: lane l holds, in item r, row 8(r/4) + 4(l/32) + r%4 of column l%32
+  // epilogue: lane l holds, in item r, row 8(r/4) + 4(l/32) + r%4 of column
+  // l%32. A bf16 y trades one item of each pair (r, r + 1) (adjacent rows)
+  // with the neighbouring lane: the even lane then writes columns c, c + 1 of
+  // row r, the odd lane columns c - 1, c of row r + 1, four bytes each.
+  const bool odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wc * 64 + 32 * j + (lane & 31);
+      const int rbase = wr * 64 + 32 * i + 4 * (lane >> 5);  // tile row of item 0
+      if (OUT == OUT_Y) {
+        if (out_bf16) {
+          const int col0 = col & ~1;  // the pair's first column
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const int tr = rbase + 8 * (r >> 2) + (r & 3);
+            const float a0 = dgv[j] * __builtin_amdgcn_ldexpf((float)acc[i][j][r], s_rexp[tr]);
+            const float a1 = dgv[j] * __builtin_amdgcn_ldexpf((float)acc[i][j][r + 1], s_rexp[tr + 1]);
+            const float got = __shfl_xor(odd ? a0 : a1, 1);
+            const int row = m0 + tr + (odd ? 1 : 0);
+            if (row >= M || col0 >= N) continue;
+            const uint32_t lo = f32_to_bf16_bits(odd ? got : a0), hi = f32_to_bf16_bits(odd ? a1 : got);
+            uint16_t* yp = reinterpret_cast<uint16_t*>(out);
+            const size_t e = (size_t)row * N + col0;
+            if (col0 + 1 >= N) {  // odd N: the last column alone
+              yp[e] = (uint16_t)lo;
+            } else if ((e & 1) == 0) {
+              *reinterpret_cast<uint32_t*>(yp + e) = lo | (hi << 16);
+            } else {  // odd N, odd row: the pair straddles a 4-byte boundary
+              yp[e] = (uint16_t)lo;
+              yp[e + 1] = (uint16_t)hi;
+            }
+          }
+          continue;
+        }
+      }
       if (col >= N) continue;
-      const float dg = OUT == OUT_PART ? 0.f : f16_bits_to_f32(diag[col]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wr * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int tr = rbase + 8 * (r >> 2) + (r & 3);
+        const int row = m0 + tr;
         if (row >= M) continue;
         const size_t o = (size_t)row * N + col;
         if (OUT == OUT_PART) {
           reinterpret_cast<int*>(out)[(size_t)blockIdx.y * M * N + o] = acc[i][j][r];
         } else {
-          const float v = dg * __builtin_amdgcn_ldexpf((float)acc[i][j][r], rexp[row]);
-          if (OUT == OUT_Y)
-            store_out(out, o, v, out_bf16);
-          else
-            reinterpret_cast<float*>(out)[o] = v;
+          const float v = dgv[j] * __builtin_amdgcn_ldexpf((float)acc[i][j][r], s_rexp[tr]);
+          reinterpret_cast<float*>(out)[o] = v;
         }
       }
     }
 }
 
 // K-slices of a product with `tiles` output tiles and nk 64-wide k-steps (nk
-// even): doubled while the grid stays within 256 workgroups and every slice
-// keeps an even number of k-steps (the loop runs whole pairs), at least 8
+// even): doubled while the grid stays within 128 workgroups and every slice
+// keeps an even number of k-steps (the loop runs whole pairs), at least 8.
+// The int32 partials cost a write and a read of ks M N words, so few slices
+// are taken (measured at 512 x 4096 x 4096 x 2048: 128 beats 64, 256, 512)
 int q8_ksplit(int tiles, int nk) {
   int ks = 1;
-  while (tiles * ks * 2 <= 256 && nk % (4 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
+  while (tiles * ks * 2 <= 128 && nk % (4 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
   return ks;
 }
 

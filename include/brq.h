@@ -192,7 +192,7 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
  * workspace holds the two code planes, the row exponents, h_s (fp32 [M][r])
  * and, when few output tiles split the reductions along k, their int32
  * partial sums (added exactly, in any order).
- * Alignment: x, v, u, d_in and d_mid 16 bytes; y and d_out their element size.
+ * Alignment: x, v, u, d_in and d_mid 16 bytes; y 4 bytes; d_out 2 bytes.
  */
 size_t brq_dbf_q8_workspace_bytes(int64_t M, int64_t m, int64_t n, int64_t r);
 brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, int64_t r,

@@ -451,9 +451,10 @@ def _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r, out=torch.float32):
 
 # several 128 x 128 tiles with ragged row and column tails, 64-wide k-steps;
 # three with few tiles and long reductions, which split along k into 2 or 4
-# int32 partial sums (m = 99: the output pass off 4-element rows); rows longer
-# than 16384 (n or r = 16512) take the quantiser that re-reads its row
-@pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (5, 200, 384, 256), (127, 128, 256, 128),
+# int32 partial sums (m = 99: the output pass off 4-element rows, and bf16
+# pairs that straddle 4-byte boundaries); rows longer than 16384 (n or r =
+# 16512) take the quantiser that re-reads its row
+@pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (5, 201, 384, 256), (127, 128, 256, 128),
                                      (130, 300, 640, 384), (300, 96, 512, 640), (3, 130, 1024, 1280),
                                      (70, 100, 2048, 1024), (9, 99, 1024, 1024), (3, 64, 16512, 256),
                                      (2, 64, 256, 16512)])
