@@ -405,8 +405,12 @@ def run_moe_dbf(brq, torch, Ts, iters=50):
     return out
 
 
-def run_dbf(brq, torch, Ms, iters=50):
+def run_dbf(brq, torch, Ms, iters=50, q8=False):
+    """The DBF chain at the DBF workload's shapes; q8 selects the path over Q8
+    activation codes (int8 matrix cores) instead of the fp16-piece path."""
     import datagen
+    gemm = brq.dbf_gemm_q8 if q8 else brq.dbf_gemm
+    ws_bytes = brq.dbf_q8_workspace_bytes if q8 else brq.dbf_workspace_bytes
     out = {}
     for M in Ms:
         d = datagen.C3(M)
@@ -419,14 +423,14 @@ def run_dbf(brq, torch, Ms, iters=50):
         x = dev_np(d["x"])
         di, dm, do = (torch.from_numpy(d[k]).cuda() for k in ("d_in", "d_mid", "d_out"))
         y = torch.empty((M, m), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(brq.dbf_workspace_bytes(M, m, n, r), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(ws_bytes(M, m, n, r), dtype=torch.uint8, device="cuda")
         for i in range(5):
-            brq.dbf_gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
+            gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
         torch.cuda.synchronize()
 
         def timed():
             for i in range(iters):
-                brq.dbf_gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
+                gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
 
         ms = graph_time(torch, timed, iters) / iters
         nbytes = wbytes + M * n * 2 + M * m * 2
@@ -620,6 +624,8 @@ def main():
         extra["moe_dbf"] = run_moe_dbf(brq, torch, (1, 64))
         log("[bench] DBF")
         extra["dbf"] = run_dbf(brq, torch, (1, 512))
+        log("[bench] DBF over Q8 activation codes")
+        extra["dbf_q8"] = run_dbf(brq, torch, (512, 4096), q8=True)
         log("[bench] prefill")
         extra["prefill"] = run_prefill(brq, torch)
     cpu = None
