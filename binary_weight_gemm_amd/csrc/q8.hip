@@ -209,7 +209,10 @@ __global__ __launch_bounds__(256) void k_q8_out(const int* __restrict__ part, in
 
 enum { OUT_HS, OUT_Y, OUT_PART };
 
-__device__ __forceinline__ int q8_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// chunk slot of row r in a stage row of eight 16-byte chunks: 8 consecutive
+// rows (one 128-byte bank line each) and 16 consecutive rows (pairs sharing
+// a 256-byte line) both land on distinct slots
+__device__ __forceinline__ int q8_swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 // OUT_HS: h_s = fp32(diag * (acc * 2^e)) as fp32 [M][N]; OUT_Y: the same
 // value as y_dtype; OUT_PART: the raw int32 sums of K-slice blockIdx.y into
@@ -219,14 +222,22 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
                                                  int N, int K, const uint32_t* __restrict__ signs,
                                                  const uint16_t* __restrict__ diag, void* __restrict__ out,
                                                  int out_bf16) {
-  // LDS holds the code tile (rows of 64 bytes; the 16-byte chunk c of row r
-  // at chunk c ^ q8_swz(r), which keeps both the fragment reads (32 rows, one
-  // chunk) and the staging writes (two chunks of each of 4 or 8 rows per
-  // group of lanes) on distinct banks) and the packed sign dwords of the
-  // tile's columns; the +-1 weight fragments are built in registers.
-  constexpr int BM = 128, BN = 128, BK = 64;
-  __shared__ __attribute__((aligned(16))) int8_t As[4][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint32_t Ws[4][BN * 2];
+  // Stages of 128 k move global -> LDS by direct loads (no registers), three
+  // stages deep, so that the loads run two stages ahead of the products even
+  // at one workgroup per compute unit. A stage holds the code tile (128 rows
+  // of 128 bytes; the 16-byte chunk c of row r sits at chunk c ^ q8_swz8(r),
+  // which keeps the fragment reads of 32 rows on distinct banks) and the
+  // packed sign dwords of the tile's columns (4 per column); the +-1 weight
+  // fragments are built in registers.
+  constexpr int BM = 128, BN = 128, BKS = 128;  // BKS: k per stage
+  constexpr int A_ST = BM * BKS, W_ST = BN * 4;  // bytes, dwords per stage
+  // one variable per stage buffer: each gets its own alias scope, so that the
+  // fragment reads of one buffer need not wait for the direct loads into
+  // another (the stage loop is unrolled so that every access names its buffer)
+  __shared__ __attribute__((aligned(16))) int8_t A0[A_ST], A1[A_ST], A2[A_ST];
+  __shared__ __attribute__((aligned(16))) uint32_t W0[W_ST], W1[W_ST], W2[W_ST];
+#define Q8_ABUF(b) ((b) == 0 ? A0 : (b) == 1 ? A1 : A2)
+#define Q8_WBUF(b) ((b) == 0 ? W0 : (b) == 1 ? W1 : W2)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   // tile id -> (row tile, column tile). Workgroups go to the 8 XCDs in turn
@@ -236,18 +247,10 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   int bid = blockIdx.x;
   if (bid < 8 * per) bid = (bid & 7) * per + (bid >> 3);
   const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
-  const int nk = K / BK / gridDim.y;  // k-steps of this K-slice (even)
-  const int kt0 = blockIdx.y * nk;
+  const int ns = K / BKS / gridDim.y;  // stages of this K-slice
+  const int k0 = blockIdx.y * ns * BKS;
   const int KW = K >> 5;  // sign dwords per weight row
 
-  // staging: thread tid moves code bytes [row tid/2][32 (tid%2) .. +32) of a
-  // k-step (two 16-byte loads) and the sign dword of column tid/2, k-half
-  // tid%2; two register sets (P, Q) hold the two k-steps of the next pair
-  const int srow = tid >> 1, shalf = tid & 1;
-  const int gm = m0 + srow < M ? m0 + srow : M - 1;  // rows past M repeat the last (never stored)
-  const int gn = n0 + srow < N ? n0 + srow : N - 1;  // columns past N repeat the last (never stored)
-  const int8_t* asrc = a + (size_t)gm * K + (size_t)kt0 * BK + 32 * shalf;
-  const uint32_t* wsrc = signs + (size_t)gn * KW + 2 * kt0 + shalf;
   // epilogue operands, fetched before the k-loop: the row exponents of the
   // tile (LDS, visible after the first barrier) and this lane's column scales
   __shared__ int s_rexp[BM];
@@ -260,25 +263,37 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
       dgv[j] = f16_bits_to_f32(diag[c < N ? c : N - 1]);
     }
   }
-  const int lofs0 = srow * BK + 16 * ((2 * shalf) ^ q8_swz(srow));
-  const int lofs1 = srow * BK + 16 * ((2 * shalf + 1) ^ q8_swz(srow));
-  uint4 pa0, pa1, qa0, qa1;
-  uint32_t pw, qw;
-#define Q8_LOAD(ra0, ra1, rw, kt)                                 \
-  {                                                               \
-    ra0 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK);      \
-    ra1 = *reinterpret_cast<const uint4*>(asrc + (kt) * BK + 16); \
-    rw = wsrc[(kt) * 2];                                          \
+  // direct loads of a stage. Codes: wave w, load i writes rows 32 w + 8 i ..
+  // +7 (1 KB); lane L takes row 32 w + 8 i + L/8, physical chunk L%8, i.e.
+  // logical chunk (L%8) ^ q8_swz8(row). Signs: load t of wave w writes dword
+  // slots 256 t + 64 w + L: column slot/4, dword slot%4 of the stage.
+  const int8_t* a_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    const int gr = m0 + r < M ? m0 + r : M - 1;  // rows past M repeat the last (never stored)
+    a_src[i] = a + (size_t)gr * K + k0 + 16 * ((lane & 7) ^ q8_swz8(r));
   }
-#define Q8_STORE(ra0, ra1, rw, buf)                               \
-  {                                                               \
-    *reinterpret_cast<uint4*>(&As[buf][lofs0]) = ra0;             \
-    *reinterpret_cast<uint4*>(&As[buf][lofs1]) = ra1;             \
-    Ws[buf][tid] = rw;                                            \
+  const uint32_t* w_src[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int slot = 256 * t + 64 * wave + lane, c = n0 + (slot >> 2);
+    w_src[t] = signs + (size_t)(c < N ? c : N - 1) * KW + (k0 >> 5) + (slot & 3);
   }
+  auto issue = [&](int p, int buf) {  // stage p (clamped to the slice) into buffer buf
+    const int q = p < ns ? p : ns - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a_src[i] + (size_t)q * BKS),
+                                       Q8_ABUF(buf) + (32 * wave + 8 * i) * BKS, 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(w_src[t] + 4 * q),
+                                       Q8_WBUF(buf) + 256 * t + 64 * wave, 4, 0, 0);
+  };
 
   // weight fragments: lane l takes column 32 j + l%32 of its wave's 64, and
-  // of the 32-wide group of a half k-step the bytes 16 (l/32) .. +15, i.e.
+  // of the 32-wide group of a sub-step the bytes 16 (l/32) .. +15, i.e.
   // dwords d = 4 (l/32) .. +3 of the expanded sign dword
   uint32_t msk[4];
 #pragma unroll
@@ -298,22 +313,30 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // lane l reads row l%32 of a 32-row block, chunk 2 ks + l/32; the blocks
-  // start at multiples of 32 rows, so the swizzle depends on l%32 alone
-  const int rsw = q8_swz(lane & 31), rofs = (lane & 31) * BK;
-  auto mfma_step = [&](int buf) {
-    uint2 sd[2];
+  // fragment reads: lane l takes row wr 64 + 32 i + l%32, logical chunk
+  // 2 u + l/32 of sub-step u
+  int a_row[2], a_swz[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sd[j] = *reinterpret_cast<const uint2*>(&Ws[buf][2 * (wc * 64 + 32 * j + (lane & 31))]);
+  for (int i = 0; i < 2; ++i) {
+    const int r = wr * 64 + 32 * i + (lane & 31);
+    a_row[i] = r * BKS;
+    a_swz[i] = q8_swz8(r);
+  }
+  auto compute = [&](int buf) {
+    const int8_t* ab = Q8_ABUF(buf);
+    const uint32_t* wb = Q8_WBUF(buf);
+    uint4 sw[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kofs = rofs + 16 * ((2 * ks + (lane >> 5)) ^ rsw);
+    for (int j = 0; j < 2; ++j) sw[j] = *reinterpret_cast<const uint4*>(wb + 4 * (wc * 64 + 32 * j + (lane & 31)));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       i32x4 af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wr * 64 + 32 * i) * BK + kofs]);
+        af[i] = *reinterpret_cast<const i32x4*>(ab + a_row[i] + 16 * ((2 * u + (lane >> 5)) ^ a_swz[i]));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = bfrag(ks == 0 ? sd[j].x : sd[j].y);
+      for (int j = 0; j < 2; ++j)
+        bf[j] = bfrag(u == 0 ? sw[j].x : u == 1 ? sw[j].y : u == 2 ? sw[j].z : sw[j].w);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -321,33 +344,32 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
     }
   };
 
-  // Four LDS buffers: pair kt, kt + 1 computes from buffers b, b + 1 (b = 0
-  // or 2 by pair parity) while P and Q (steps kt + 2, kt + 3, loaded during
-  // the previous pair) go to the other two and reload with steps kt + 4 and
-  // kt + 5; one barrier per pair. Every K-slice has an even number of k-steps
-  // (at least 2), so the loop runs whole pairs; the loads past the slice's
-  // last step repeat that step (the copies are never read), which keeps every
-  // load and store unconditional.
-  const int last = nk - 1;
-  Q8_LOAD(pa0, pa1, pw, 0);
-  Q8_LOAD(qa0, qa1, qw, 1);
-  Q8_STORE(pa0, pa1, pw, 0);
-  Q8_STORE(qa0, qa1, qw, 1);
-  Q8_LOAD(pa0, pa1, pw, min(2, last));
-  Q8_LOAD(qa0, qa1, qw, min(3, last));
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    const int b = kt & 2, o = 2 - b;
-    mfma_step(b);
-    mfma_step(b + 1);
-    Q8_STORE(pa0, pa1, pw, o);
-    Q8_STORE(qa0, qa1, qw, o + 1);
-    Q8_LOAD(pa0, pa1, pw, min(kt + 4, last));
-    Q8_LOAD(qa0, qa1, qw, min(kt + 5, last));
-    __syncthreads();
+  // stage p computes from buffer p % 3. Before it, each wave waits for its own
+  // loads of stage p (those of stage p + 1, six per wave, may stay in flight)
+  // and meets the others at a barrier: stage p is then complete in LDS and
+  // every wave is done with stage p - 1, whose buffer takes stage p + 2.
+  auto stage = [&](int p, int d) {  // d = p % 3, a constant after unrolling
+    // s_waitcnt vmcnt(6) expcnt(7) lgkmcnt(0) as a builtin, which the
+    // compiler's own wait placement takes into account; the barrier in asm
+    // with a memory clobber keeps the LDS accesses on their side of it
+    __builtin_amdgcn_s_waitcnt(0x0076);
+    asm volatile("s_barrier" ::: "memory");
+    issue(p + 2, (d + 2) % 3);
+    compute(d);
+  };
+  issue(0, 0);
+  issue(1, 1);
+  // whole rounds of three stages with no branch inside, then the last one or two
+  int p = 0;
+  for (; p + 3 <= ns; p += 3) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) stage(p + d, d);
   }
-#undef Q8_LOAD
-#undef Q8_STORE
+  if (p < ns) stage(p, 0);
+  if (p + 1 < ns) stage(p + 1, 1);
+  __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
+#undef Q8_ABUF
+#undef Q8_WBUF
 
   // epilogue: lane l holds, in item r, row 8(r/4) + 4(l/32) + r%4 of column
   // l%32. A bf16 y trades one item of each pair (r, r + 1) (adjacent rows)
