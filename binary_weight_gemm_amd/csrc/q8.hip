@@ -322,32 +322,50 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
     a_row[i] = r * BKS;
     a_swz[i] = q8_swz8(r);
   }
+  // one stage: 4 sub-steps of 32 k, each 4 MFMAs; the fragment reads and
+  // the weight expansion of sub-step u + 1 are placed between the MFMAs of
+  // sub-step u (scheduling-group barriers), so that one wave per SIMD keeps
+  // its matrix core busy while they complete
   auto compute = [&](int buf) {
     const int8_t* ab = Q8_ABUF(buf);
     const uint32_t* wb = Q8_WBUF(buf);
     uint4 sw[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) sw[j] = *reinterpret_cast<const uint4*>(wb + 4 * (wc * 64 + 32 * j + (lane & 31)));
+    auto wdw = [&](int j, int u) { return u == 0 ? sw[j].x : u == 1 ? sw[j].y : u == 2 ? sw[j].z : sw[j].w; };
+    i32x4 af[2][2], bf[2][2];  // [buffer][block]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      af[0][i] = *reinterpret_cast<const i32x4*>(ab + a_row[i] + 16 * ((lane >> 5) ^ a_swz[i]));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bf[0][j] = bfrag(wdw(j, 0));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      i32x4 af[2], bf[2];
+      const int c = u & 1, n = c ^ 1;
+      if (u < 3) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[n][i] = *reinterpret_cast<const i32x4*>(ab + a_row[i] + 16 * ((2 * (u + 1) + (lane >> 5)) ^ a_swz[i]));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[n][j] = bfrag(wdw(j, u + 1));
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(ab + a_row[i] + 16 * ((2 * u + (lane >> 5)) ^ a_swz[i]));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = bfrag(u == 0 ? sw[j].x : u == 1 ? sw[j].y : u == 2 ? sw[j].z : sw[j].w);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+      if (u < 3) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int m = 0; m < 4; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+          if (m < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);               // four VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  // stage p computes from buffer p % 3. Before it, each wave waits for its own
-  // loads of stage p (those of stage p + 1, six per wave, may stay in flight)
-  // and meets the others at a barrier: stage p is then complete in LDS and
-  // every wave is done with stage p - 1, whose buffer takes stage p + 2.
   auto stage = [&](int p, int d) {  // d = p % 3, a constant after unrolling
     // s_waitcnt vmcnt(6) expcnt(7) lgkmcnt(0) as a builtin, which the
     // compiler's own wait placement takes into account; the barrier in asm
