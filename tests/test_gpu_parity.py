@@ -790,7 +790,7 @@ def test_c5_prefill_sampled_columns():
 # ---------------------------------------------------------------------------
 
 def test_graph_capture_replay():
-    say("graph capture of gemm (decode + tiled), dbf, moe")
+    say("graph capture of gemm (decode + tiled), dbf, dbf over Q8 codes, moe")
     b = brq()
     N, K = 1024, 2048
     w = datagen.normal_f32((76, 0), (N, K), 0.02)
@@ -805,6 +805,11 @@ def test_graph_capture_replay():
     packs = [[oracle.pack_sign1(f(e)) for f in (cfg.gate, cfg.up, cfg.down)] for e in range(cfg.E)]
     mw = [dev(np.stack([pk[p][i] for pk in packs])) for p in range(3) for i in range(2)]
     xm, lg = dev(cfg.x(2)), dev(cfg.logits(2))
+    # Q8 chain with both reductions split into int32 slices (9 rows, 99 outputs)
+    qx, qdi, qv, qdm, qu, qdo = _q8_inputs(9, 99, 1024, 1024, 76)
+    qargs = (dev(qx), dev(qdi), dev(qv), dev(qdm), dev(qu), dev(qdo), 99, 1024, 1024)
+    yq = torch.empty((9, 99), dtype=torch.bfloat16, device="cuda")
+    wsq = torch.empty(b.dbf_q8_workspace_bytes(9, 99, 1024, 1024), dtype=torch.uint8, device="cuda")
     y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
     y2 = torch.empty((96, N), dtype=torch.float32, device="cuda")
     yd = torch.empty((1, 256), dtype=torch.float32, device="cuda")
@@ -816,11 +821,12 @@ def test_graph_capture_replay():
         b.gemm(x1, S, SC, N, K, out_dtype=torch.float32, y=y1)
         b.gemm(x2, S, SC, N, K, out_dtype=torch.float32, y=y2)
         b.dbf_gemm(*dargs, out_dtype=torch.float32, y=yd, ws=wsd)
+        b.dbf_gemm_q8(*qargs, out_dtype=torch.bfloat16, y=yq, ws=wsq)
         b.moe_ffn(xm, lg, *mw, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32, y=ym, ws=wsm)
 
     work()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (y1, y2, yd, ym)]
+    ref = [t.clone() for t in (y1, y2, yd, ym, yq)]
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -830,12 +836,12 @@ def test_graph_capture_replay():
     with torch.cuda.graph(g):
         work()
     for rep in range(3):
-        for t in (y1, y2, yd, ym):
+        for t in (y1, y2, yd, ym, yq):
             t.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, r in zip((y1, y2, yd, ym), ref):
+        for a, r in zip((y1, y2, yd, ym, yq), ref):
             assert torch.equal(a, r), f"replay {rep} differs"
         work()  # eager work between replays
         torch.cuda.synchronize()
