@@ -31,7 +31,7 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def maxrel(g: np.ndarray, o: np.ndarray) -> float:
-    """max_i |g_i - o_i| / max_i |o_i|  (the spec error measure)."""
+    """max_i |g_i - o_i| / max_i |o_i|: the largest error relative to the largest reference magnitude."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     den = np.max(np.abs(o))
