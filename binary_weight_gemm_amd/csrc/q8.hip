@@ -217,7 +217,8 @@ __device__ __forceinline__ int q8_swz8(int r) { return (r ^ (r >> 3)) & 7; }
 // OUT_HS: h_s = fp32(diag * (acc * 2^e)) as fp32 [M][N]; OUT_Y: the same
 // value as y_dtype; OUT_PART: the raw int32 sums of K-slice blockIdx.y into
 // part[blockIdx.y][M][N]
-template <int OUT>
+// BM = 128 (waves of 64 x 64) or 64 (waves of 32 x 64), 128 columns per tile
+template <int OUT, int BM>
 __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, const int* __restrict__ rexp, int M,
                                                  int N, int K, const uint32_t* __restrict__ signs,
                                                  const uint16_t* __restrict__ diag, void* __restrict__ out,
@@ -229,8 +230,15 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   // which keeps the fragment reads of 32 rows on distinct banks) and the
   // packed sign dwords of the tile's columns (4 per column); the +-1 weight
   // fragments are built in registers.
-  constexpr int BM = 128, BN = 128, BKS = 128;  // BKS: k per stage
-  constexpr int A_ST = BM * BKS, W_ST = BN * 4;  // bytes, dwords per stage
+  constexpr int BN = 128, BKS = 128;  // BKS: k per stage
+  constexpr int NI = BM / 64;         // 32-row blocks per wave
+  constexpr int WROWS = BM / 2;       // rows per wave row
+  constexpr int ALD = BM / 32;        // code loads per wave and stage (8 rows each)
+  static_assert(ALD == 4 || ALD == 2, "tile height 128 or 64");
+  // bytes, dwords per stage; the LDS arrays are sized for 128-row tiles
+  // whatever BM (shared arrays of a size that depends on a template parameter
+  // leave the host compiler without a launch stub for the kernel)
+  constexpr int A_ST = 128 * BKS, W_ST = BN * 4;
   // one variable per stage buffer: each gets its own alias scope, so that the
   // fragment reads of one buffer need not wait for the direct loads into
   // another (the stage loop is unrolled so that every access names its buffer)
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 
   // epilogue operands, fetched before the k-loop: the row exponents of the
   // tile (LDS, visible after the first barrier) and this lane's column scales
-  __shared__ int s_rexp[BM];
+  __shared__ int s_rexp[128];
   float dgv[2] = {0.f, 0.f};
   if (OUT != OUT_PART) {
     if (tid < BM) s_rexp[tid] = rexp[m0 + tid < M ? m0 + tid : M - 1];
@@ -263,14 +271,14 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
       dgv[j] = f16_bits_to_f32(diag[c < N ? c : N - 1]);
     }
   }
-  // direct loads of a stage. Codes: wave w, load i writes rows 32 w + 8 i ..
-  // +7 (1 KB); lane L takes row 32 w + 8 i + L/8, physical chunk L%8, i.e.
-  // logical chunk (L%8) ^ q8_swz8(row). Signs: load t of wave w writes dword
+  // direct loads of a stage. Codes: wave w, load i writes rows (BM/4) w + 8 i
+  // .. +7 (1 KB); lane L takes row (BM/4) w + 8 i + L/8, physical chunk L%8,
+  // i.e. logical chunk (L%8) ^ q8_swz8(row). Signs: load t of wave w writes dword
   // slots 256 t + 64 w + L: column slot/4, dword slot%4 of the stage.
-  const int8_t* a_src[4];
+  const int8_t* a_src[ALD];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 32 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < ALD; ++i) {
+    const int r = (BM / 4) * wave + 8 * i + (lane >> 3);
     const int gr = m0 + r < M ? m0 + r : M - 1;  // rows past M repeat the last (never stored)
     a_src[i] = a + (size_t)gr * K + k0 + 16 * ((lane & 7) ^ q8_swz8(r));
   }
@@ -283,9 +291,9 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   auto issue = [&](int p, int buf) {  // stage p (clamped to the slice) into buffer buf
     const int q = p < ns ? p : ns - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < ALD; ++i)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a_src[i] + (size_t)q * BKS),
-                                       Q8_ABUF(buf) + (32 * wave + 8 * i) * BKS, 16, 0, 0);
+                                       Q8_ABUF(buf) + ((BM / 4) * wave + 8 * i) * BKS, 16, 0, 0);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(w_src[t] + 4 * q),
@@ -305,20 +313,20 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
                  (int)__builtin_amdgcn_perm(0x000000FFu, 0x00FFFF01u, w & msk[3])};
   };
 
-  i32x16 acc[2][2];
+  i32x16 acc[NI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // fragment reads: lane l takes row wr 64 + 32 i + l%32, logical chunk
+  // fragment reads: lane l takes row wr BM/2 + 32 i + l%32, logical chunk
   // 2 u + l/32 of sub-step u
-  int a_row[2], a_swz[2];
+  int a_row[NI], a_swz[NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wr * 64 + 32 * i + (lane & 31);
+  for (int i = 0; i < NI; ++i) {
+    const int r = wr * WROWS + 32 * i + (lane & 31);
     a_row[i] = r * BKS;
     a_swz[i] = q8_swz8(r);
   }
@@ -333,9 +341,9 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
 #pragma unroll
     for (int j = 0; j < 2; ++j) sw[j] = *reinterpret_cast<const uint4*>(wb + 4 * (wc * 64 + 32 * j + (lane & 31)));
     auto wdw = [&](int j, int u) { return u == 0 ? sw[j].x : u == 1 ? sw[j].y : u == 2 ? sw[j].z : sw[j].w; };
-    i32x4 af[2][2], bf[2][2];  // [buffer][block]
+    i32x4 af[2][NI], bf[2][2];  // [buffer][block]
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
       af[0][i] = *reinterpret_cast<const i32x4*>(ab + a_row[i] + 16 * ((lane >> 5) ^ a_swz[i]));
 #pragma unroll
     for (int j = 0; j < 2; ++j) bf[0][j] = bfrag(wdw(j, 0));
@@ -344,21 +352,21 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
       const int c = u & 1, n = c ^ 1;
       if (u < 3) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
           af[n][i] = *reinterpret_cast<const i32x4*>(ab + a_row[i] + 16 * ((2 * (u + 1) + (lane >> 5)) ^ a_swz[i]));
 #pragma unroll
         for (int j = 0; j < 2; ++j) bf[n][j] = bfrag(wdw(j, u + 1));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
       if (u < 3) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 2 * NI; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
-          if (m < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+          if (m < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);               // four VALU
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -366,11 +374,18 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
     }
   };
 
+  // stage p computes from buffer p % 3. Before it, each wave waits for its
+  // own loads of stage p (those of stage p + 1, ALD + 2 per wave, may stay in
+  // flight) and meets the others at a barrier: stage p is then complete in
+  // LDS and every wave is done with stage p - 1, whose buffer takes p + 2.
   auto stage = [&](int p, int d) {  // d = p % 3, a constant after unrolling
-    // s_waitcnt vmcnt(6) expcnt(7) lgkmcnt(0) as a builtin, which the
+    // s_waitcnt vmcnt(ALD + 2) expcnt(7) lgkmcnt(0) as a builtin, which the
     // compiler's own wait placement takes into account; the barrier in asm
     // with a memory clobber keeps the LDS accesses on their side of it
-    __builtin_amdgcn_s_waitcnt(0x0076);
+    if constexpr (ALD == 4)
+      __builtin_amdgcn_s_waitcnt(0x0076);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0074);
     asm volatile("s_barrier" ::: "memory");
     issue(p + 2, (d + 2) % 3);
     compute(d);
@@ -395,11 +410,11 @@ __global__ __launch_bounds__(256) void k_tile_q8(const int8_t* __restrict__ a, c
   // row r, the odd lane columns c - 1, c of row r + 1, four bytes each.
   const bool odd = lane & 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wc * 64 + 32 * j + (lane & 31);
-      const int rbase = wr * 64 + 32 * i + 4 * (lane >> 5);  // tile row of item 0
+      const int rbase = wr * WROWS + 32 * i + 4 * (lane >> 5);  // tile row of item 0
       if (OUT == OUT_Y) {
         if (out_bf16) {
           const int col0 = col & ~1;  // the pair's first column
@@ -454,12 +469,33 @@ int q8_ksplit(int tiles, int nk) {
   return ks;
 }
 
+// tile height and K-slices of an M x N product with reduction length K:
+// 64-row tiles when 128-row tiles would not give every compute unit one
+struct Q8Plan {
+  int bm, ks, tiles;
+};
+static Q8Plan q8_plan(int64_t M, int64_t N, int64_t K) {
+  const int tn = (int)((N + 127) / 128);
+  const int bm = ((M + 127) / 128) * tn < 256 ? 64 : 128;
+  const int tiles = (int)((M + bm - 1) / bm) * tn;
+  return Q8Plan{bm, q8_ksplit(tiles, (int)(K / 64)), tiles};
+}
+
 // workspace: q1 int8 [M][n], e1 [M], h_s fp32 [M][r], q2 int8 [M][r], e2 [M],
 // int32 K-slice partials [max(ks1 r, ks2 m)][M]
 static void q8_splits(int64_t M, int64_t m, int64_t n, int64_t r, int& ks1, int& ks2) {
-  const int mt = (int)((M + 127) / 128);
-  ks1 = q8_ksplit(mt * (int)((r + 127) / 128), (int)(n / 64));
-  ks2 = q8_ksplit(mt * (int)((m + 127) / 128), (int)(r / 64));
+  ks1 = q8_plan(M, r, n).ks;
+  ks2 = q8_plan(M, m, r).ks;
+}
+
+template <int OUT>
+static void launch_tile_q8(const Q8Plan& pl, const int8_t* a, const int* rexp, int M, int N, int K,
+                           const uint32_t* signs, const uint16_t* diag, void* out, int out_bf16, hipStream_t st) {
+  const dim3 g(pl.tiles, pl.ks), b(256);
+  if (pl.bm == 64)
+    hipLaunchKernelGGL((k_tile_q8<OUT, 64>), g, b, 0, st, a, rexp, M, N, K, signs, diag, out, out_bf16);
+  else
+    hipLaunchKernelGGL((k_tile_q8<OUT, 128>), g, b, 0, st, a, rexp, M, N, K, signs, diag, out, out_bf16);
 }
 
 size_t dbf_q8_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
@@ -475,8 +511,6 @@ size_t dbf_q8_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
 hipError_t launch_dbf_q8(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
                          const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
                          void* ws, hipStream_t st) {
-  int ks1, ks2;
-  q8_splits(M, m, n, r, ks1, ks2);
   char* p = reinterpret_cast<char*>(ws);
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
   int8_t* q1 = reinterpret_cast<int8_t*>(take((size_t)M * n));
@@ -487,23 +521,21 @@ hipError_t launch_dbf_q8(const uint16_t* x, int M, int m, int n, int r, const ui
   int* part = reinterpret_cast<int*>(p);
   const uint32_t* v32 = reinterpret_cast<const uint32_t*>(v);
   const uint32_t* u32 = reinterpret_cast<const uint32_t*>(u);
-  const int mt = (M + 127) / 128;
+  const Q8Plan p1 = q8_plan(M, r, n), p2 = q8_plan(M, m, r);
   launch_q8_rows<SRC_XDIN>(x, d_in, nullptr, 1, M, n, q1, e1, st);
-  const dim3 g1(mt * ((r + 127) / 128), ks1);
-  if (ks1 == 1) {
-    hipLaunchKernelGGL(k_tile_q8<OUT_HS>, g1, dim3(256), 0, st, q1, e1, M, r, n, v32, d_mid, hs, 0);
+  if (p1.ks == 1) {
+    launch_tile_q8<OUT_HS>(p1, q1, e1, M, r, n, v32, d_mid, hs, 0, st);
     launch_q8_rows<SRC_F32>(hs, nullptr, nullptr, 1, M, r, q2, e2, st);
   } else {
-    hipLaunchKernelGGL(k_tile_q8<OUT_PART>, g1, dim3(256), 0, st, q1, e1, M, r, n, v32, d_mid, part, 0);
-    launch_q8_rows<SRC_PART>(part, d_mid, e1, ks1, M, r, q2, e2, st);
+    launch_tile_q8<OUT_PART>(p1, q1, e1, M, r, n, v32, d_mid, part, 0, st);
+    launch_q8_rows<SRC_PART>(part, d_mid, e1, p1.ks, M, r, q2, e2, st);
   }
-  const dim3 g2(mt * ((m + 127) / 128), ks2);
-  if (ks2 == 1) {
-    hipLaunchKernelGGL(k_tile_q8<OUT_Y>, g2, dim3(256), 0, st, q2, e2, M, m, r, u32, d_out, y, y_bf16);
+  if (p2.ks == 1) {
+    launch_tile_q8<OUT_Y>(p2, q2, e2, M, m, r, u32, d_out, y, y_bf16, st);
   } else {
-    hipLaunchKernelGGL(k_tile_q8<OUT_PART>, g2, dim3(256), 0, st, q2, e2, M, m, r, u32, d_out, part, 0);
+    launch_tile_q8<OUT_PART>(p2, q2, e2, M, m, r, u32, d_out, part, 0, st);
     const size_t quads = ((size_t)M * m + 3) / 4;
-    hipLaunchKernelGGL(k_q8_out, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part, ks2, M, m, e2, d_out,
+    hipLaunchKernelGGL(k_q8_out, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part, p2.ks, M, m, e2, d_out,
                        y, y_bf16);
   }
   return hipGetLastError();

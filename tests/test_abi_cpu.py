@@ -183,9 +183,12 @@ def test_dbf_q8_validation(L):
     # 512 tiles and split no reduction
     assert L.brq_dbf_q8_workspace_bytes(4096, 4096, 4096, 2048) == (4096 * 4096 + 4 * 4096 + 4096 * 2048 * 4
                                                                     + 4096 * 2048 + 4 * 4096)
-    # 512 rows: 64 tiles of the first product in 2 K-slices (int32 partials), 128 of the second in one
-    base = 512 * 4096 + 2048 + 512 * 2048 * 4 + 512 * 2048 + 2048
-    assert L.brq_dbf_q8_workspace_bytes(512, 4096, 4096, 2048) == base + 2 * 512 * 2048 * 4
+    # 512 rows: 64-row tiles, 128 and 256 of them, no K-split
+    assert L.brq_dbf_q8_workspace_bytes(512, 4096, 4096, 2048) == (512 * 4096 + 2048 + 512 * 2048 * 4
+                                                                   + 512 * 2048 + 2048)
+    # one row: 16 tiles of the first product in 8 K-slices, 32 of the second in 4 (int32 partials)
+    assert L.brq_dbf_q8_workspace_bytes(1, 4096, 4096, 2048) == (4096 + 256 + 2048 * 4 + 2048 + 256
+                                                                 + max(8 * 2048, 4 * 4096) * 4)
     assert L.brq_dbf_q8_workspace_bytes(1, 4096, 4096, 100) == 0
 
 

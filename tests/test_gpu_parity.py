@@ -506,14 +506,17 @@ def test_dbf_q8_ties_and_exponent_edges():
 # the full-size case at the launch configuration the benchmark times (all 512
 # rows computed), compared on sampled rows: rows are independent in the chain
 # (each has its own exponents), so the oracle runs on those rows alone
-@pytest.mark.parametrize("M", [1, 512])
+# 1 and 512 rows are the DBF workload's sizes (64-row tiles; one row splits
+# both reductions); 4096 rows run the 128-row tiles the benchmark times
+@pytest.mark.parametrize("M", [1, 512, 4096])
 def test_dbf_q8_c3_sampled_rows(M):
     say("C3 dbf q8 sampled rows", M)
     d = datagen.C3(M)
     vw, uw = oracle.pack_sign1_only(d["v"]), oracle.pack_sign1_only(d["u"])
     m, n, r = d["m"], d["n"], d["r"]
     y = _q8_run(d["x"], d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
-    rows = np.array([0, 1, 127, 128, 255, 300, 383, 511]) if M == 512 else np.array([0])
+    rows = {1: np.array([0]), 512: np.array([0, 1, 127, 128, 255, 300, 383, 511]),
+            4096: np.array([0, 1, 127, 128, 2047, 2048, 4094, 4095])}[M]
     o = oracle.dbf_chain_q8(oracle.bf16_to_f64(d["x"][rows]), d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
     check_q8(y[torch.from_numpy(rows).to(y.device)], o, f"C3 q8 M={M} sampled")
     # and the distance to the unquantised chain stays at the level of two 7-bit
