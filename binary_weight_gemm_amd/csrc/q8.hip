@@ -12,12 +12,14 @@
 //     fp16, exact in fp32), v = h_s (fp32), or h_s from int32 K-slice sums;
 //     e = the smallest integer with max|v| <= 127 * 2^e; q = round-half-even
 //     (v / 2^e) as int8, stored in the k order shared with the weight bytes.
-//   k_tile_q8: 128 x 128 output tiles of the product of the codes with a +-1
-//     sign plane, 64-wide k-steps, four waves of 64 x 64 (2 x 2 MFMAs of 32 x
-//     32 x 32); each sign dword of a k-step becomes eight dwords of +-1 bytes
-//     in LDS, one AND and one byte permute each. Epilogue: h_s = fp32(d_mid *
-//     (acc * 2^e)) (first product), y = d_out * (acc * 2^e) (second), or the
-//     raw int32 sums of a K-slice.
+//   k_tile_q8: output tiles of 128 columns by 128 rows (four waves of 64 x
+//     64) or 64 rows (32 x 64) of the product of the codes with a +-1 sign
+//     plane on MFMAs of 32 x 32 x 32; codes and packed sign dwords move to
+//     LDS by direct loads, three stages of 128 k deep; each lane turns a sign
+//     dword into its four dwords of +-1 bytes with one AND and one byte
+//     permute each. Epilogue: h_s = fp32(d_mid * (acc * 2^e)) (first
+//     product), y = d_out * (acc * 2^e) (second), or the raw int32 sums of a
+//     K-slice.
 //   k_q8_out: y from the K-slice sums of the second product.
 #include "common.h"
 #include "kernels.h"
