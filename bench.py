@@ -4,8 +4,10 @@ Headline (value): decode-shaped binary GEMV at M=1 -- one step is y = x . Wq^T
 for both decode matrices, W 4096x14336 and 14336x4096 in the group-128 sign +
 fp16 scale format, bf16 activations, bf16 outputs. Throughput is algorithmic
 HBM bytes (packed weights + activations in + outputs out) per second. The
-weights rotate through a ring of copies larger than twice the 256 MB
-Infinity Cache, so every call streams its weights from HBM.
+timed steps walk a ring of distinct weight copies (larger than twice the 256 MB
+Infinity Cache; a copy comes back only after more than 512 MB of others), and
+the caches are scrubbed before every timed replay, so every call streams its
+weights from HBM.
 
 Also reported (extra): device facts and reference rates (a 1 GiB device copy,
 the vendor library's bf16 GEMM); the 1024 x 1024 single GEMV (cache resident);
@@ -142,10 +144,26 @@ def setup_c2(brq, torch, M):
     return ring, xs, ys, wss, step_bytes
 
 
+_SCRUB = []
+
+
+def scrub_caches(torch):
+    """Read a buffer of twice the Infinity Cache's size (untimed), so that
+    whatever an earlier replay left in the caches has been evicted: the next
+    replay's first weight reads come from HBM."""
+    if not _SCRUB:
+        _SCRUB.append(torch.ones(2 * MALL_BYTES // 4, dtype=torch.float32, device="cuda"))
+    _SCRUB.append(_SCRUB[0].sum())
+    del _SCRUB[1:]
+
+
 def graph_time(torch, fn, n_items, replays=5):
     """Capture fn() (which enqueues n_items kernel launches) in a HIP graph,
     replay it `replays` times and return ms per replay (median), GPU time only:
-    no host submission gaps between the captured launches."""
+    no host submission gaps between the captured launches. Before each timed
+    replay the caches are scrubbed (scrub_caches), so a replay never finds
+    weights that the previous one left in the Infinity Cache; inside a replay
+    the callers walk a ring of distinct weight copies."""
     warm_gpu(torch, 0.3)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -163,6 +181,7 @@ def graph_time(torch, fn, n_items, replays=5):
     for _ in range(replays):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        scrub_caches(torch)
         torch.cuda.synchronize()
         e0.record()
         g.replay()

@@ -123,17 +123,25 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 // A weight operand of +-1 needs only its sign, and fp4 (e2m1) has no infinity
 // or NaN: OR-ing 0b0111 onto a nibble whose top bit is a sign bit gives +-6.0.
 // So one shift-or turns a 32-bit sign word into 8 fp4 operands (dword t of a
-// lane's 32-k block holds, in nibble q, the sign of k = 4q + t). The
-// activation row is split per wave into two fp8 (e4m3) pieces, p0 = RNE(v)
-// and p1 = RNE((v - p0)*16) with v = x*2^-a and 2^a chosen from the slice
-// maximum so |v| < 256. A bf16 value has 8 significant bits and each piece
-// carries 4, so the pieces add up to x exactly for every element within 2^13
-// of the slice maximum; smaller ones are off by at most 2^-21 of the maximum.
-// Rows 0/1 of v_mfma_scale_f32_16x16x128_f8f6f4 take them with block
-// exponents a and a-4. One MFMA covers one scale group of 16 columns; the
-// group scale and the 1/6 are applied in fp32 afterwards. (These matrix cores
-// add every 8 products with about 13 significant bits relative to the largest
-// of them, which bounds the accuracy more than a third piece would help.)
+// lane's 32-k block holds, in nibble q, the sign of k = 4q + t).
+//
+// These matrix cores add each run of 8 products after aligning them to the
+// largest one and truncating whatever falls more than 13 bits below it, so
+// floating-point pieces of the activations would lose the low bits of small
+// values next to large ones. The activations therefore enter as fixed-point
+// digits, which makes every product and every partial sum exact: per wave
+// slice, with 2^e the largest power of two in the slice (biased exponent
+// ebs), each |x| is written as X * 2^(ebs - 150) with X = its 8-bit
+// significand shifted into a 24-bit field (bits shifted out below are
+// dropped: less than 2^-23 of the slice maximum), and the six 4-bit digits of
+// X (most significant first) go to A rows 0..5 as sign-magnitude e4m3 codes.
+// An e4m3 code c in 0..15 is the value c * 2^-9 (subnormals and the first
+// normal binade), so the code of a digit is the digit itself plus the sign
+// bit. Row p carries block exponent ebs - 2 - 4p and the weights 135, which
+// puts row p's product at 6 * sum(+-digit_p) * 2^(ebs - 130 - 4p): integers
+// times one power of two, exact in fp32. Rows 6..15 repeat row 5 and are not
+// used. One MFMA covers one scale group of 16 columns; the group scale and
+// the 1/6 are applied in fp32 afterwards.
 //
 // Layout facts of that MFMA (fp8 A, fp4 B): A lane l supplies row l%16 with
 // bytes 0..15 = k 16*(l/16).. and bytes 16..31 = k 64+16*(l/16)..; B lane l
@@ -141,9 +149,11 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 // (row r, k block b) comes from lane r + 16b; D as for the 16x16 f16 MFMA.
 // A lane loads group 4c+kb of its column; four permlane swaps transpose the
 // 4 x 4 (group, word) block of the four lanes of a column so that MFMA i gets
-// word kb of group 4c+i.
+// word kb of group i.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-constexpr int F4_CHUNK = 4 * 2 * 128;  // LDS bytes of one chunk: 4 groups x 2 pieces x 128
+constexpr int F4_DIGITS = 6;
+constexpr int F4_GROUP = F4_DIGITS * 128;  // LDS bytes of one group: six digit rows of 128 codes
+constexpr int F4_CHUNK = 4 * F4_GROUP;     // LDS bytes of one chunk of four groups
 
 // (group, word) transpose across the four 16-lane rows: on entry register w
 // of row g holds word w of group g; on exit register i of row b holds word b
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
   const int G = K >> 7;
   const int nchunks = (G + 3) >> 2;
   const int c0 = wave * CPW;
-  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * CPW * F4_CHUNK;  // [chunk][group][piece][128]
+  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * CPW * F4_CHUNK;  // [chunk][group][digit][128]
   float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * CPW * F4_CHUNK);
   float acc[NT];
 #pragma unroll
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
         sc[t][c] = *reinterpret_cast<const uint2*>(scales + row[t] + (gs < G ? gs : 0));
       }
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
-    // ---- block exponents from the slice maximum
+    // ---- slice exponent: biased exponent of the largest |x| of the wave slice
     uint32_t mx = 0;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
@@ -211,36 +221,47 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
       for (int h = 0; h < 4; ++h) mx = max(mx, max(w4[h] & 0x7fffu, (w4[h] >> 16) & 0x7fffu));
     }
     mx = wave_max_u32(mx);
-    int sh = (int)(mx >> 7) - 7;  // E8M0 exponent of piece 0: 2^(e_max - 7)
-    sh = sh < 5 ? 5 : (sh > 253 ? 253 : sh);
-    const float mh = __uint_as_float((uint32_t)(254 - sh) << 23);  // 2^(127 - sh)
-    // ---- pieces in the operand order: lane L's 8 values are k = 8L .. 8L+7 of
-    // the chunk (group L/16, word (L%16)/4); value e lands at in-word position
-    // 8*(e%4) + 2*(L%4) + e/4
+    // at least 24, so that a zero (or bf16 subnormal, dropped: below 2^-126)
+    // shifts its implicit bit out of the field entirely
+    const uint32_t ebs = max(mx >> 7, 24u);
+    // ---- digit codes in the operand order: lane L's 8 values are k = 8L .. 8L+7
+    // of the chunk (group L/16, word (L%16)/4); value e lands at in-word
+    // position 8*(e%4) + 2*(L%4) + e/4 of each digit row
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const uint32_t w4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-      float v[8];
+      uint32_t lo[8], hi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (e & 1) ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16);
-        v[e] = __uint_as_float(h) * mh;
+        const uint32_t wp = (e & 1) ? w4[e >> 1] : (w4[e >> 1] << 16);  // the bf16 in bits 16..31
+        const uint32_t sh = min(ebs - ((wp >> 23) & 0xffu), 31u);
+        const uint32_t X = ((wp & 0x7f0000u) | 0x800000u) >> sh;          // 24-bit magnitude field
+        const uint32_t sr = (wp >> 31) * 0x808080u;                        // sign bit of each code byte
+        lo[e] = (X & 0x0f0f0fu) | sr;         // nibbles 0, 2, 4 -> bytes 0, 1, 2
+        hi[e] = ((X >> 4) & 0x0f0f0fu) | sr;  // nibbles 1, 3, 5 -> bytes 0, 1, 2
       }
-      uint8_t* base = xw + c * F4_CHUNK + (lane >> 4) * 256 + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
+      uint8_t* base = xw + c * F4_CHUNK + (lane >> 4) * F4_GROUP + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[t], v[t + 4], 0, false);
-        const float r0 = (v[t] - __builtin_amdgcn_cvt_f32_fp8(p0, 0)) * 16.f;
-        const float r1 = (v[t + 4] - __builtin_amdgcn_cvt_f32_fp8(p0, 1)) * 16.f;
-        const int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-        *reinterpret_cast<uint16_t*>(base + 8 * t) = (uint16_t)p0;
-        *reinterpret_cast<uint16_t*>(base + 128 + 8 * t) = (uint16_t)p1;
+        // values t and t+4 side by side: byte permutes pair their codes per nibble
+        const uint32_t l02 = __builtin_amdgcn_perm(lo[t + 4], lo[t], 0x05010400u);
+        const uint32_t l4 = __builtin_amdgcn_perm(lo[t + 4], lo[t], 0x0c0c0602u);
+        const uint32_t h13 = __builtin_amdgcn_perm(hi[t + 4], hi[t], 0x05010400u);
+        const uint32_t h5 = __builtin_amdgcn_perm(hi[t + 4], hi[t], 0x0c0c0602u);
+        // digit p (most significant first) is nibble 5 - p
+        auto put = [&](int nib, uint32_t v16) {
+          *reinterpret_cast<uint16_t*>(base + (F4_DIGITS - 1 - nib) * 128 + 8 * t) = (uint16_t)v16;
+        };
+        put(0, l02);
+        put(2, l02 >> 16);
+        put(4, l4);
+        put(1, h13);
+        put(3, h13 >> 16);
+        put(5, h5);
       }
     }
-    // A row j holds piece min(j, 1) (rows past 1 repeat piece 1 and are not
-    // used) with block exponent sh - 4 * piece
-    const int prow = j < 1 ? j : 1;
-    const int sa = sh - 4 * prow;
+    const int prow = j < F4_DIGITS ? j : F4_DIGITS - 1;
+    const int sa = (int)ebs - 2 - 4 * prow;
     // ---- products
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
@@ -253,8 +274,8 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
         const uint32_t s4[4] = {sc[t][c].x & 0xffffu, sc[t][c].x >> 16, sc[t][c].y & 0xffffu, sc[t][c].y >> 16};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(ab + i * 256);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ab + i * 256 + 64);
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(ab + i * F4_GROUP);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ab + i * F4_GROUP + 64);
           i32x8 A, B;
           A[0] = a0[0]; A[1] = a0[1]; A[2] = a0[2]; A[3] = a0[3];
           A[4] = a1[0]; A[5] = a1[1]; A[6] = a1[2]; A[7] = a1[3];
@@ -264,15 +285,19 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
           B[3] = (int)(wi[i] | 0x77777777u);
           B[4] = 0; B[5] = 0; B[6] = 0; B[7] = 0;
           const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
-                                                                           sa, 0, 127);
+                                                                           sa, 0, 135);
           const bool ok = cok[t] && (4 * (c0 + c) + i < G);
           const float s = ok ? f16_bits_to_f32(s4[i]) : 0.f;
-          acc[t] = fmaf(s, d[0] + d[1], acc[t]);
+          // lanes 0..15 hold digit rows 0..3 of column j, lanes 16..31 rows 4..7
+          const float part = kb == 0 ? (d[0] + d[1]) + (d[2] + d[3]) : kb == 1 ? d[0] + d[1] : 0.f;
+          acc[t] = fmaf(s, part, acc[t]);
         }
       }
     }
   }
-  // lanes 0..15 hold the partial sums of columns j of the NT tiles
+  // digit rows 4 and 5 (lanes 16..31) join rows 0..3 (lanes 0..15)
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] += __shfl_down(acc[t], 16, 64);
   if (wave > 0 && kb == 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[((wave - 1) * NT + t) * 16 + j] = acc[t];
@@ -336,34 +361,54 @@ static void gemm_dec_lds(const uint16_t* x, int M, int N, int K, const uint4* s4
 }
 
 // The fp8 x fp4 path takes M = 1 when the scale groups come in whole chunks
-// of four (K % 512 == 0); it splits K like the one-launch fp16 path. Two
-// column tiles per workgroup when that still leaves well over one workgroup
-// per compute unit (the activation pieces are then shared by both tiles).
+// of four (K % 512 == 0) and the digit rows of the workgroup's slices fit the
+// LDS (K <= 26624: up to 52 chunks); longer rows take the fp16 one-launch
+// path. Two column tiles per workgroup when that still leaves well over one
+// workgroup per compute unit (the activation digits are then shared by both
+// tiles). One chunk per wave up to 16 waves (the less a wave computes after
+// its last sign word lands, the shorter the tail), more beyond.
+constexpr size_t kF4Lds = 160 * 1024;
+
+static bool f4_split(int64_t K, int64_t N, DecSplit& sp, int& nt, size_t& lds) {
+  if (K % 512 != 0) return false;
+  const int64_t chunks = K / 512;
+  const int64_t cpw = chunks <= 16 ? 1 : (chunks + 15) / 16;
+  if (cpw > 8) return false;
+  sp.cpw = (int)cpw;
+  sp.waves = (int)((chunks + cpw - 1) / cpw);
+  const int64_t tiles = (N + 15) / 16;
+  nt = tiles >= 768 ? 2 : 1;
+  lds = (size_t)sp.waves * sp.cpw * F4_CHUNK + (size_t)(sp.waves - 1) * nt * 16 * 4;
+  return lds <= kF4Lds;
+}
+
 static void gemm_dec_f4(const uint16_t* x, int N, int K, const uint4* s4, const uint16_t* scales, void* y,
                         int y_bf16, hipStream_t st) {
-  // one chunk per wave up to 16 waves (the less a wave computes after its
-  // last sign word lands, the shorter the tail), two beyond
-  const int chunks = K / 512;
   DecSplit sp;
-  sp.cpw = chunks <= 16 ? 1 : (chunks + 15) / 16;
-  sp.waves = (chunks + sp.cpw - 1) / sp.cpw;
+  int nt;
+  size_t lds;
+  f4_split(K, N, sp, nt, lds);
   const int tiles = (N + 15) / 16;
-  const int nt = tiles >= 768 ? 2 : 1;
-  const size_t lds = (size_t)sp.waves * sp.cpw * F4_CHUNK + (size_t)(sp.waves - 1) * nt * 16 * 4;
   const dim3 grid((tiles + nt - 1) / nt), block(64 * sp.waves);
+  auto opt_in = [&](const void* fn) {
+    if (lds > 64 * 1024) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  };
   if (nt == 2) {
-    BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 2>), grid, block, lds, st, x, N, K, s4, scales, y,
-                                              y_bf16));
+    BRQ_CPW_SWITCH(sp.cpw, opt_in(reinterpret_cast<const void*>(&k_gemm_dec_f4<CPW, 2>));
+                   hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 2>), grid, block, lds, st, x, N, K, s4, scales, y, y_bf16));
   } else {
-    BRQ_CPW_SWITCH(sp.cpw, hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 1>), grid, block, lds, st, x, N, K, s4, scales, y,
-                                              y_bf16));
+    BRQ_CPW_SWITCH(sp.cpw, opt_in(reinterpret_cast<const void*>(&k_gemm_dec_f4<CPW, 1>));
+                   hipLaunchKernelGGL((k_gemm_dec_f4<CPW, 1>), grid, block, lds, st, x, N, K, s4, scales, y, y_bf16));
   }
 }
 
 hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                            void* y, int y_bf16, void* ws, hipStream_t st) {
   const uint4* s4 = reinterpret_cast<const uint4*>(signs);
-  if (M == 1 && K % 512 == 0 && gemm_dec_in_lds(M, K)) {
+  DecSplit sp;
+  int nt;
+  size_t lds;
+  if (M == 1 && f4_split(K, N, sp, nt, lds)) {
     gemm_dec_f4(x, N, K, s4, scales, y, y_bf16, st);
     return hipGetLastError();
   }

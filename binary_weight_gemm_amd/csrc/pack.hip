@@ -1,7 +1,7 @@
 // Quantiser: fp32 weights -> SIGN1 sign plane (+ one fp16 scale per group of 128).
 //
-// Format of "Behaviour-Relearned Quantization" (item 02, group-128 signs plus
-// scales) and "Banyan ..." (Abstract, 1.125 bits per weight); sign convention
+// Format of "Behaviour-Relearned Quantization" (item 02: sign bits with one scale
+// per 128 of them) and "Banyan ..." (Abstract, 1.125 bits per weight); sign convention
 // and 64-sign words of "LLM binarization, Episode 01: DBF" (sections 1, 3).
 //
 // Mapping: a row-major [rows][cols] matrix with cols % 128 == 0 is a flat run of

@@ -18,7 +18,7 @@
  *                   sections 1 and 3).
  *  group-128     -- a SIGN1 plane plus one fp16 scale per run of 128 consecutive
  *                   weights of a row ("Behaviour-Relearned Quantization", item 02:
- *                   group-128 signs plus scales; "Banyan: Converting Pretrained
+ *                   sign bits with one scale per 128 of them; "Banyan: Converting Pretrained
  *                   Language Models to 1-Bit Weights ...", Abstract: one sign per
  *                   weight and one shared scale per small group, 1.125 bits per
  *                   weight). Scale of row n, group g at index n*(cols/128) + g.
@@ -30,7 +30,14 @@
  * Numerics: every product multiplies exactly representable operands and
  * accumulates in fp32. Activations are carried as fp16 inside the products;
  * bf16 activations must satisfy |x| < 65504 (values below 2^-14 are kept on
- * fp16's subnormal grid, an absolute change of at most 2^-25). fp32
+ * fp16's subnormal grid, an absolute change of at most 2^-25). The one
+ * exception is brq_gemm with M = 1 and K % 512 == 0 (K <= 26624), which runs
+ * on the fp8 x fp4 matrix cores: there each activation is a 24-bit
+ * fixed-point field under the largest power of two of its slice of the row
+ * (a change of less than 2^-23 of that slice's maximum; bf16 subnormals count
+ * as zero), split into six 4-bit digits whose products and partial sums are
+ * exact, so no magnitude limit below fp32's range applies and the result
+ * agrees with the M > 1 paths to fp32 rounding. fp32
  * intermediates (DBF h, MoE SwiGLU output) are stored as fp32 and enter the
  * next product as two fp16 pieces of v * 2^s, s a power of two that puts the
  * largest magnitude of the staged slice (or row) near 2^14: about 22

@@ -13,7 +13,8 @@ sums out with ``math.fsum`` for tiny shapes.
 
 Sources (the pages):
 * "Behaviour-Relearned Quantization" (technical report page), item 02
-  "Binarize experts": routed experts stored as group-128 signs plus scales.
+  "Binarize experts": routed experts kept as sign bits with one scale per
+  128 of them.
 * "Banyan: Converting Pretrained Language Models to 1-Bit Weights with Homotopy
   On-Policy Distillation", Abstract: one sign per weight, one scale shared by a
   small group, 1.125 bits per weight, about a fourteenth of a 16-bit parent.

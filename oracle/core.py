@@ -15,7 +15,8 @@ __all__ = [
     "packed_bytes", "bits_per_weight",
 ]
 
-#: weights per scale group along the reduction axis ("group-128 signs plus scales")
+#: weights per scale group along the reduction axis: one fp16 scale per 128 signs
+#: ("Behaviour-Relearned Quantization", item 02)
 GROUP = 128
 
 PINS = {
@@ -26,7 +27,9 @@ PINS = {
     "dbf_chain": "dense reconstruction + Sylvester-Hadamard identity",
     "dbf_bpe": "worked example of the DBF post, section 1.1",
     "q8_rows": "rounding bound + minimal exponent + exact codes for representable rows + zero row",
-    "dbf_chain_q8": "Sylvester-Hadamard closed form + odd symmetry + power-of-two equivariance + distance to the unquantised chain",
+    "dbf_chain_q8": "Sylvester-Hadamard closed form + odd symmetry + power-of-two equivariance + distance to the unquantised chain"
+                    " + a hand-built row whose codes differ unless h_s is rounded once to fp32",
+    "silu": "logistic identities: silu(0) = 0, silu(z) - silu(-z) = z, silu(ln 3) = (3/4) ln 3, slope 1/2 at 0, limits",
     "route_topk": "brute-force ordering + softmax invariants",
     "moe_ffn": "identical-experts reduction + single-route dense FFN + loops",
     "moe_dbf_ffn": "dense reconstruction of every chain + identical-experts reduction + single route",

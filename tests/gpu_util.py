@@ -1,5 +1,8 @@
 """Helpers for the GPU parity tests: moving seeded numpy inputs to the device
 and comparing device results with the fp64 oracle."""
+import os
+import sys
+
 import numpy as np
 import torch
 
@@ -49,9 +52,37 @@ def bf16_ulps(g_bits: np.ndarray, o64: np.ndarray) -> np.ndarray:
     return np.abs(_ordered(np.asarray(g_bits, dtype=np.uint16)) - _ordered(ref))
 
 
-def check_f32(g, o, tol, what=""):
+#: the products' specified accuracy, as a per-element relative error
+SPEC_TOL = 2e-3
+
+
+def elemrel(g: np.ndarray, o: np.ndarray, floor: float = 1e-3) -> float:
+    """max_i |g_i - o_i| / max(|o_i|, floor * rms(o)): the error of every element
+    relative to its own reference value, with a floor of 1e-3 of the rms so that
+    outputs at (or crossing) zero do not divide by nothing."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(o * o))) if o.size else 0.0
+    if rms == 0.0:
+        return 0.0 if np.array_equal(g, o) else float("inf")
+    den = np.maximum(np.abs(o), floor * rms)
+    return float(np.max(np.abs(g - o) / den))
+
+
+def check_f32(g, o, tol, what="", elementwise=True):
+    """fp32 outputs: max_i |g_i - o_i| / max_i |o_i| <= tol (the tight bar that
+    one flipped sign or one dropped group fails) and, element by element,
+    |g_i - o_i| / max(|o_i|, 1e-3 rms(o)) <= SPEC_TOL. `elementwise=False`
+    only where the device and the oracle legitimately start from different
+    inputs (an end-to-end chain whose intermediate is an output rounded on
+    each side), which a per-element bar on the product does not describe."""
     e = maxrel(g, o)
+    ee = elemrel(g, o)
+    if os.environ.get("BRQ_REPORT_ERRORS"):
+        print(f"[err] {what}: maxrel {e:.3e} elemrel {ee:.3e}", file=sys.stderr, flush=True)
     assert e <= tol, f"{what}: max rel error {e:.3e} > {tol:.1e}"
+    if elementwise:
+        assert ee <= SPEC_TOL, f"{what}: per-element rel error {ee:.3e} > {SPEC_TOL:.1e}"
     return e
 
 

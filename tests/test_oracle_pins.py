@@ -376,6 +376,58 @@ def test_dbf_chain_q8_symmetries_and_distance():
     assert np.all(rel < 5e-2) and np.all(rel > 1e-3)
 
 
+def test_dbf_chain_q8_rounds_h_s_once_to_fp32():
+    """h_s = fp32(d_mid * h) before it is quantised, checked on a hand-built
+    row whose codes differ under every other precision of that step.
+
+    x = integer codes (max 127, so e1 = 0), d_in = 1, and three rows of V
+    give h = 127, 20083 and 49. With d_mid = 1, 1723 * 2^-21 and
+    1839 * 2^-14 the exact products are
+      h_s[0] = 127                     (the row maximum: e2 = 0)
+      h_s[1] = 16.5 + 2^-21            (fp64 -> code 17; fp32 rounds it to the
+                                        midpoint 16.5 -> 16, ties to even;
+                                        fp16 and bf16 also give 16.5 -> 16)
+      h_s[2] = 5.5 - 2^-14             (exact in fp32 -> 5; fp16 and bf16
+                                        round it to 5.5 -> 6; fp64 -> 5)
+    so only fp32 gives the codes (127, 16, 5). Rows 0..2 of U read them out:
+    y = (q0 + q1 + q2, q0 - q1 + q2, q0 + q1 - q2)."""
+    n, r, m = 256, 64, 3
+    q1 = np.array([127.0] * 248 + [64, 32, 16, 8, 4, 2, 1, 0])
+
+    def v_row(h):
+        # h = 127 * (2p - 248) + f with f odd in [-127, 127]: p coarse +1s, then
+        # the binary expansion of f over the fine codes 64 .. 1
+        k = int(round((h - 1) / 254.0)) * 2
+        f = h - 127 * k
+        assert f % 2 == 1 and -127 <= f <= 127
+        p = (k + 248) // 2
+        u = (f + 127) // 2
+        row = np.array([1.0] * p + [-1.0] * (248 - p)
+                       + [1.0 if (u >> i) & 1 else -1.0 for i in (6, 5, 4, 3, 2, 1, 0)] + [1.0])
+        assert row @ q1 == h
+        return row
+
+    V = np.ones((r, n), dtype=np.float32)
+    for j, h in enumerate((127, 20083, 49)):
+        V[j] = v_row(h)
+    d_mid = np.zeros(r, dtype=np.float16)
+    d_mid[:3] = [1.0, 1723 * 2.0 ** -21, 1839 * 2.0 ** -14]
+    assert d_mid[1] == 1723 * 2.0 ** -21 and d_mid[2] == 1839 * 2.0 ** -14   # exact fp16 values
+    exact = np.array([127.0, 1723 * 20083 * 2.0 ** -21, 1839 * 49 * 2.0 ** -14])
+    assert exact[1] == 16.5 + 2.0 ** -21 and exact[2] == 5.5 - 2.0 ** -14
+    U = np.ones((m, r), dtype=np.float32)
+    U[1, 1] = -1.0
+    U[2, 2] = -1.0
+    ones_n, ones_m = np.ones(n, np.float16), np.ones(m, np.float16)
+    y = oracle.dbf_chain_q8(q1[None, :], ones_n, oracle.pack_sign1_only(V), d_mid,
+                            oracle.pack_sign1_only(U), ones_m, m, n, r)
+    assert np.array_equal(y[0], [127 + 16 + 5, 127 - 16 + 5, 127 + 16 - 5])
+    # the codes the other precisions would give, for the record
+    assert list(oracle.q8_rows(exact)[0]) == [127, 17, 5]                                    # fp64
+    assert list(oracle.q8_rows(exact.astype(np.float16).astype(np.float64))[0]) == [127, 16, 6]  # fp16
+    assert list(oracle.q8_rows(oracle.round_bf16(exact))[0]) == [127, 16, 6]                  # bf16
+
+
 def test_dbf_bit_budget_worked_example():
     g = _gold("dbf_bit_budget.json")
     m, n, r = g["shape_m"], g["shape_n"], g["r"]
@@ -437,6 +489,28 @@ def _dense_ffn(p, x, H, I):
     Wd = oracle.dequantize(dw, ds, H, I)
     g = x @ Wg.T
     return (g / (1 + np.exp(-g)) * (x @ Wu.T)) @ Wd.T
+
+
+def test_silu_values_fixed_by_the_mathematics():
+    """silu(z) = z * sigmoid(z), pinned by values that follow from the
+    definition of the logistic function rather than by its formula:
+    silu(0) = 0; silu(z) - silu(-z) = z (sigmoid(z) + sigmoid(-z) = 1);
+    sigmoid(ln 3) = 3/4, so silu(ln 3) = (3/4) ln 3 and silu(-ln 3) = -(1/4) ln 3;
+    slope 1/2 at 0; silu(z) -> z for large z and -> 0 from below for large -z."""
+    assert oracle.silu(0.0) == 0.0
+    z = np.linspace(-30.0, 30.0, 1201)
+    assert np.allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=1e-14, atol=1e-14)
+    l3 = math.log(3.0)
+    assert math.isclose(float(oracle.silu(l3)), 0.75 * l3, rel_tol=1e-15)
+    assert math.isclose(float(oracle.silu(-l3)), -0.25 * l3, rel_tol=1e-15)
+    assert math.isclose(float(oracle.silu(1e-9)) / 1e-9, 0.5, rel_tol=1e-9)
+    assert float(oracle.silu(40.0)) == 40.0
+    s = float(oracle.silu(-40.0))
+    assert s < 0.0 and math.isclose(s, -40.0 * math.exp(-40.0), rel_tol=1e-12)
+    # sigmoid(ln(p / (1 - p))) = p for any p in (0, 1)
+    p = np.array([0.1, 0.2, 0.5, 0.9, 0.99])
+    t = np.log(p / (1.0 - p))
+    assert np.allclose(oracle.silu(t), t * p, rtol=1e-14, atol=1e-15)
 
 
 def test_moe_identical_experts_and_single_route():
