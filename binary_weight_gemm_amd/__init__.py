@@ -61,6 +61,8 @@ ABI_FUNCTIONS = {
     "brq_moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "brq_moe_ffn": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int,
                            _vp, _vp, _vp, _sz, _vp]),
+    "brq_moe_ffn_noalloc": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _int, _vp, _vp, _vp]),
     "brq_moe_dbf_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "brq_moe_dbf_ffn": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _vp, _vp,
                                _vp, _sz, _vp]),
@@ -291,6 +293,40 @@ def moe_ffn(x, logits, gate_s, gate_sc, up_s, up_sc, down_s, down_sc, E: int, H:
                              _dev(ws, "ws"), wsb, _stream()), "brq_moe_ffn")
     if return_routing:
         return y, ids, wts
+    return y
+
+
+#: bytes of the scratch array brq_moe_ffn_noalloc uses (BRQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_ffn_noalloc(x, logits, gate_s, gate_sc, up_s, up_sc, down_s, down_sc, E: int, H: int, I: int, top_k: int,
+                    out_dtype=torch.bfloat16, y=None, ids=None, wts=None):
+    """brq_moe_ffn_noalloc: the routed layer of moe_ffn with the library's own
+    scratch array as workspace (the call allocates no device memory; pass y,
+    and ids / wts if the routing is wanted, to allocate nothing here either)."""
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != H or logits.shape != (T, E):
+        raise BrqError("x must be [T, H] and logits [T, E]")
+    if gate_s.numel() != E * I * H // 64 or up_s.numel() != E * I * H // 64 or down_s.numel() != E * H * I // 64:
+        raise BrqError("expert sign planes do not match E, H, I")
+    if gate_sc.numel() != E * I * H // 128 or up_sc.numel() != E * I * H // 128 or down_sc.numel() != E * H * I // 128:
+        raise BrqError("expert scales do not match E, H, I")
+    code = _out_code(out_dtype)
+    if y is None:
+        y = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    if (ids is None) != (wts is None):
+        raise BrqError("pass both ids and wts, or neither")
+    if ids is not None and (ids.shape != (T, top_k) or wts.shape != (T, top_k)):
+        raise BrqError("ids and wts must be [T, top_k]")
+    _check(lib().brq_moe_ffn_noalloc(_dev(x, "x", torch.bfloat16), _dev(logits, "logits", torch.float32), T, H, I, E,
+                                     top_k, _dev(gate_s, "gate_s", torch.int64),
+                                     _dev(gate_sc, "gate_sc", torch.float16), _dev(up_s, "up_s", torch.int64),
+                                     _dev(up_sc, "up_sc", torch.float16), _dev(down_s, "down_s", torch.int64),
+                                     _dev(down_sc, "down_sc", torch.float16), _dev(y, "y", out_dtype), code,
+                                     _dev(ids, "ids", torch.int32) if ids is not None else None,
+                                     _dev(wts, "w", torch.float32) if wts is not None else None, _stream()),
+           "brq_moe_ffn_noalloc")
     return y
 
 

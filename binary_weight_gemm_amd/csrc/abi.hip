@@ -78,6 +78,12 @@ size_t gemm_ws(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+namespace brq {
+// for entry points defined in other source files of the library
+brq_status report(brq_status s, const char* msg) { return s == BRQ_OK ? ok() : fail(s, "%s", msg); }
+brq_status device_ok() { return check_device(); }
+}  // namespace brq
+
 extern "C" {
 
 int brq_abi_version(void) { return BRQ_ABI_VERSION; }

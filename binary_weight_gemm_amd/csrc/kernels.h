@@ -94,4 +94,13 @@ hipError_t launch_kron(const uint16_t* x, int M, const float* H, const float* R,
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Status reporting shared by the entry points (abi.hip): report(s, msg) sets
+// the calling thread's last-error text for a non-OK status and returns s;
+// device_ok() checks that the current device is a gfx950.
+}  // namespace brq
+#include "../../include/brq.h"
+namespace brq {
+brq_status report(brq_status s, const char* msg);
+brq_status device_ok();
+
 }  // namespace brq

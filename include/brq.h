@@ -240,6 +240,29 @@ brq_status brq_moe_ffn(const uint16_t* x, const float* logits,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * brq_moe_ffn_noalloc -- brq_moe_ffn without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc). The workspace is a scratch array of
+ * BRQ_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call allocates nothing.
+ *
+ *   arguments as for brq_moe_ffn, minus ws and ws_bytes
+ *   BRQ_E_WORKSPACE when brq_moe_workspace_bytes(T, H, I, E, top_k) exceeds
+ *   BRQ_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. T <= 64 at H = 4096, I = 2048,
+ *   top_k = 8); every other status as for brq_moe_ffn.
+ * All calls on one GPU share its array: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.
+ */
+#define BRQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+brq_status brq_moe_ffn_noalloc(const uint16_t* x, const float* logits,
+                               int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k,
+                               const uint64_t* gate_s, const uint16_t* gate_sc,
+                               const uint64_t* up_s, const uint16_t* up_sc,
+                               const uint64_t* down_s, const uint16_t* down_sc,
+                               void* y, brq_dtype y_dtype,
+                               int32_t* ids, float* w, void* stream);
+
+/*
  * One DBF chain record (the five tensors of a routed expert projection,
  * "LLM binarization, Episode 01: DBF", section 4): for E experts of an m x n
  * projection with inner dimension r,

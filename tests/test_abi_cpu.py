@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(brq.ABI_FUNCTIONS)
@@ -232,3 +232,18 @@ def test_binding_refuses_host_tensors():
     w = torch.zeros((4, 128), dtype=torch.float32)
     with pytest.raises(brq.BrqError):
         brq.pack(w)
+
+
+def test_moe_noalloc_validation(L):
+    f = L.brq_moe_ffn_noalloc
+    args = [P, P, 1, 2048, 512, 256, 8, P, P, P, P, P, P, P, 0, None, None, None]
+    bad = list(args); bad[1] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[2] = 0
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[3] = 2000
+    assert f(*bad) == E_SHAPE
+    # beyond the library's scratch array: refused before any device call
+    big = list(args); big[2] = 256; big[3] = 4096; big[4] = 2048; big[6] = 16
+    assert f(*big) == E_WORKSPACE
+    assert b"scratch" in L.brq_last_error()
