@@ -263,6 +263,60 @@ def achievable_peaks(torch, reps=10):
                 bf16_gemm_tflops=gemm_tflops, bf16_gemm_frac=gemm_tflops / MFMA_F16_PEAK_TFLOPS)
 
 
+def reference_kernels(torch, brq):
+    """Rates of this device's own reference kernels (libbrq_ref.so, not the
+    product): a plain streaming read of 8.26 MB (the packed size of one decode
+    matrix) on a cold ring of copies, one launch per copy, graph-timed like the
+    headline (launch overhead included); the same read of 1 GiB; and a loop of
+    independent 32x32x16 fp16 matrix-core products (1024 workgroups of 4 waves)."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "binary_weight_gemm_amd", "libbrq_ref.so"))
+    L.brq_ref_stream_blocks.restype = ctypes.c_uint
+    L.brq_ref_stream_blocks.argtypes = [ctypes.c_size_t]
+    L.brq_ref_stream_read.restype = ctypes.c_int
+    L.brq_ref_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.brq_ref_mfma_loop.restype = ctypes.c_int
+    L.brq_ref_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    out = {}
+    nbytes = packed_bytes(14336, 4096)
+    nbytes -= nbytes % 16
+    copies = ring_copies(nbytes)
+    ring = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(max(L.brq_ref_stream_blocks(nbytes), 1), dtype=torch.int32, device="cuda")
+
+    def stream():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for t in ring:
+            assert L.brq_ref_stream_read(ctypes.c_void_p(t.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), st) == 0
+
+    ms = graph_time(torch, stream, copies) / copies
+    out["stream_read_8mb"] = dict(bytes=nbytes, us_per_launch=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9)
+    del ring
+    big = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(L.brq_ref_stream_blocks(1 << 30), dtype=torch.int32, device="cuda")
+
+    def stream_big():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert L.brq_ref_stream_read(ctypes.c_void_p(big.data_ptr()), 1 << 30, ctypes.c_void_p(sink.data_ptr()), st) == 0
+
+    ms = graph_time(torch, stream_big, 1)
+    out["stream_read_1gib"] = dict(us=ms * 1e3, gbs=(1 << 30) / (ms * 1e-3) / 1e9)
+    del big
+    blocks, iters = 1024, 4000
+    fsink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert L.brq_ref_mfma_loop(blocks, iters, ctypes.c_void_p(fsink.data_ptr()), st) == 0
+
+    ms = graph_time(torch, mfma, 1)
+    flops = blocks * 4 * 8 * iters * 32768.0
+    out["mfma_f16_loop"] = dict(us=ms * 1e3, tflops=flops / (ms * 1e-3) / 1e12,
+                                frac_of_peak=flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS)
+    torch.cuda.empty_cache()
+    return out
+
+
 def isolated_call_us(brq, torch, reps=20):
     """One decode product (M = 1, the 14336 x 4096 matrix) launched on its own
     between two synchronisations, median of `reps`: launch overhead included."""
@@ -372,13 +426,14 @@ def run_moe(brq, torch, Ts, iters=50):
     return out
 
 
-def run_moe_dbf(brq, torch, Ts, iters=50):
+def run_moe_dbf(brq, torch, Ts, iters=50, geometry=None):
     """The DBF-expert MoE layer at the deployed shape (256 experts, top-8,
-    gate/up 512x2048, down 2048x512, r = 1024): random sign words and fp16
+    gate/up 512x2048, down 2048x512, r = 1024), or at one of the named
+    geometries of datagen.MOE_GEOMETRIES: random sign words and fp16
     log-normal diagonals on the device (timing does not depend on their
     values), D_mid at 2^-12 as in the parity inputs."""
     import datagen
-    cfg = datagen.C4D()
+    cfg = datagen.C4D() if geometry is None else datagen.C4D(**datagen.MOE_GEOMETRIES[geometry], top_k=8)
     E, H, I, r, k = cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
@@ -424,15 +479,15 @@ def run_moe_dbf(brq, torch, Ts, iters=50):
     return out
 
 
-def run_dbf(brq, torch, Ms, iters=50, q8=False):
-    """The DBF chain at the DBF workload's shapes; q8 selects the path over Q8
-    activation codes (int8 matrix cores) instead of the fp16-piece path."""
+def run_dbf(brq, torch, Ms, iters=50, q8=False, r=2048):
+    """The DBF chain at the DBF workload's shapes (rank r); q8 selects the path
+    over Q8 activation codes (int8 matrix cores) instead of the fp16-piece path."""
     import datagen
     gemm = brq.dbf_gemm_q8 if q8 else brq.dbf_gemm
     ws_bytes = brq.dbf_q8_workspace_bytes if q8 else brq.dbf_workspace_bytes
     out = {}
     for M in Ms:
-        d = datagen.C3(M)
+        d = datagen.C3(M, r=r)
         m, n, r = d["m"], d["n"], d["r"]
         v, _ = brq.pack(torch.from_numpy(d["v"]).cuda(), scales=False)
         u, _ = brq.pack(torch.from_numpy(d["u"]).cuda(), scales=False)
@@ -627,6 +682,8 @@ def main():
         extra["device"] = device_facts(torch)
         log("[bench] achievable peaks")
         extra["achievable"] = achievable_peaks(torch)
+        log("[bench] reference kernels")
+        extra["reference_kernels"] = reference_kernels(torch, brq)
         log("[bench] C1")
         extra["c1"] = run_c1(brq, torch)
         extra["isolated_decode_call_us"] = isolated_call_us(brq, torch)
@@ -638,11 +695,15 @@ def main():
         log("[bench] pack")
         extra["pack"] = run_pack(brq, torch)
         log("[bench] MoE")
-        extra["moe"] = run_moe(brq, torch, (1, 64))
+        extra["moe"] = run_moe(brq, torch, (1, 4, 16, 64))
         log("[bench] MoE with DBF experts")
         extra["moe_dbf"] = run_moe_dbf(brq, torch, (1, 64))
+        log("[bench] MoE with DBF experts, DeepSeek-V4-Flash geometry")
+        extra["moe_dbf_deepseek_v4_flash"] = run_moe_dbf(brq, torch, (1, 4), geometry="DeepSeek-V4-Flash")
         log("[bench] DBF")
         extra["dbf"] = run_dbf(brq, torch, (1, 512))
+        log("[bench] DBF, r = 4096")
+        extra["dbf_r4096"] = run_dbf(brq, torch, (1, 512), r=4096)
         log("[bench] DBF over Q8 activation codes")
         extra["dbf_q8"] = run_dbf(brq, torch, (512, 4096), q8=True)
         log("[bench] prefill")

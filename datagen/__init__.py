@@ -65,6 +65,14 @@ def pm1_f32(key, shape) -> np.ndarray:
     return np.where(g.integers(0, 2, size=shape, dtype=np.int8) == 0, 1.0, -1.0).astype(np.float32)
 
 
+def sign_words(key, rows: int, cols: int) -> np.ndarray:
+    """Uniform random signs of a rows x cols matrix as SIGN1 words (uint64
+    [rows * cols / 64], 64 signs per word): every bit an independent fair coin."""
+    g = rng(*key)
+    return g.integers(0, 2 ** 63, size=rows * cols // 64, dtype=np.int64).view(np.uint64) ^ \
+        (g.integers(0, 2, size=rows * cols // 64, dtype=np.int64).view(np.uint64) << np.uint64(63))
+
+
 def haar_orthogonal(key, n: int) -> np.ndarray:
     """Haar-distributed n x n orthogonal matrix (fp64): QR of a Gaussian matrix,
     with the columns' signs fixed by the signs of R's diagonal."""
@@ -89,6 +97,14 @@ def C1():
     x = bf16_normal((1, 1), (1, 1024))
     return w, x
 
+
+#: the named MoE geometries (experts, hidden, expert intermediate) with the
+#: DBF rank used for them here: r = 2048, the most the layer accepts
+MOE_GEOMETRIES = {
+    "GLM-4.5-Air": dict(E=128, H=4096, I=1408, r=2048),
+    "MiniMax-M2.5": dict(E=256, H=3072, I=1536, r=2048),
+    "DeepSeek-V4-Flash": dict(E=256, H=4096, I=2048, r=2048),
+}
 
 #: decode-shaped matrices, stored [N_out, K_in]
 C2_SHAPES = ((4096, 14336), (14336, 4096))
@@ -158,6 +174,17 @@ class C4D:
         key = (6, self.layer, e, p)
         d_mid = (np.exp(rng(*key, 3).standard_normal(size=(self.r,)) * 0.5) * 2.0 ** -12).astype(np.float16)
         return dict(v=pm1_f32(key + (0,), (self.r, n)), u=pm1_f32(key + (1,), (m, self.r)),
+                    d_in=f16_lognormal(key + (2,), (n,)), d_mid=d_mid, d_out=f16_lognormal(key + (4,), (m,)),
+                    m=m, n=n)
+
+    def proj_packed(self, e: int, p: int):
+        """As proj, with V and U drawn directly as SIGN1 words (uniform random
+        bits are uniform +-1 signs): the layer's named geometries have factors
+        too large to draw as fp32 and pack on the host per test."""
+        m, n = (self.I, self.H) if p < 2 else (self.H, self.I)
+        key = (6, self.layer, e, p)
+        d_mid = (np.exp(rng(*key, 3).standard_normal(size=(self.r,)) * 0.5) * 2.0 ** -12).astype(np.float16)
+        return dict(v=sign_words((7,) + key + (0,), self.r, n), u=sign_words((7,) + key + (1,), m, self.r),
                     d_in=f16_lognormal(key + (2,), (n,)), d_mid=d_mid, d_out=f16_lognormal(key + (4,), (m,)),
                     m=m, n=n)
 

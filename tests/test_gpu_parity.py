@@ -395,6 +395,22 @@ def test_dbf_small_intermediates(M):
     check_f32(f64(y), o, F32_TOL, f"dbf small h_s M={M}")
 
 
+# the DBF workload at about 2 bits per element: r = 4096 on 4096 x 4096
+# (2.0117 bpe, section 1.1's bit budget), decode and tiled paths
+@pytest.mark.parametrize("M", [1, 512])
+def test_dbf_c3_rank4096(M):
+    say("C3 dbf r=4096", M)
+    d = datagen.C3(M, r=4096)
+    vw, uw = oracle.pack_sign1_only(d["v"]), oracle.pack_sign1_only(d["u"])
+    m, n, r = d["m"], d["n"], d["r"]
+    o = oracle.dbf_chain(oracle.bf16_to_f64(d["x"]), d["d_in"], vw, d["d_mid"], uw, d["d_out"], m, n, r)
+    args = (dev(d["x"]), dev(d["d_in"]), dev(vw), dev(d["d_mid"]), dev(uw), dev(d["d_out"]), m, n, r)
+    y = brq().dbf_gemm(*args, out_dtype=torch.float32)
+    check_f32(f64(y), o, F32_TOL, f"C3 r=4096 M={M}")
+    yb = brq().dbf_gemm(*args, out_dtype=torch.bfloat16)
+    check_bf16(yb, o, f"C3 r=4096 M={M} bf16")
+
+
 @pytest.mark.parametrize("M", [1, 512])
 def test_dbf_c3(M):
     say("C3 dbf", M)
@@ -716,6 +732,51 @@ def test_moe_dbf_deployed_shape_t64_sampled_tokens():
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
     check_f32(f64(y)[toks], o[toks], F32_TOL, "moe dbf deployed T=64")
+
+
+def _dbf_moe_packed(cfg, experts):
+    """Device records [E, ...] per projection (the experts' factors from
+    C4D.proj_packed, zeros for the others) and the oracle's expert lookup,
+    both from the same arrays."""
+    E, H, I, r = cfg.E, cfg.H, cfg.I, cfg.r
+    recs, host = [], {e: [] for e in experts}
+    for p, (m, n) in enumerate(((I, H), (I, H), (H, I))):
+        d_in = np.zeros((E, n), np.float16)
+        v = np.zeros((E, r, n // 64), np.uint64)
+        d_mid = np.zeros((E, r), np.float16)
+        u = np.zeros((E, m, r // 64), np.uint64)
+        d_out = np.zeros((E, m), np.float16)
+        for e in experts:
+            d = cfg.proj_packed(e, p)
+            d_in[e], d_mid[e], d_out[e] = d["d_in"], d["d_mid"], d["d_out"]
+            v[e] = d["v"].reshape(r, n // 64)
+            u[e] = d["u"].reshape(m, r // 64)
+            host[e].append((d["d_in"], d["v"], d["d_mid"], d["u"], d["d_out"]))
+        recs.append(tuple(dev(a) for a in (d_in, v, d_mid, u, d_out)))
+    return recs, lambda e: tuple(host[e])
+
+
+# the other MoE geometries the DBF post names (its section 9), full projection
+# shapes with top-8 routing and r = 2048 (the most the layer accepts); only
+# the selected experts are built. T = 1 and 3 take the few-token path, T = 5
+# the grouped one.
+@pytest.mark.parametrize("name,T", [("GLM-4.5-Air", 1), ("MiniMax-M2.5", 3), ("DeepSeek-V4-Flash", 5)])
+def test_moe_dbf_named_geometries(name, T):
+    say("moe dbf geometry", name, T)
+    g = datagen.MOE_GEOMETRIES[name]
+    cfg = datagen.C4D(E=g["E"], H=g["H"], I=g["I"], r=g["r"], top_k=8, layer=11)
+    x, lg = cfg.x(T), cfg.logits(T)
+    ids_o, _ = oracle.route_topk(lg, cfg.top_k)
+    recs, ex = _dbf_moe_packed(cfg, sorted(set(int(e) for e in ids_o.ravel())))
+    o, oids, ow = oracle.moe_dbf_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, cfg.r, cfg.top_k)
+    y, ids, w = brq().moe_dbf_ffn(dev(x), dev(lg), *recs, cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k,
+                                  out_dtype=torch.float32, return_routing=True)
+    yb = brq().moe_dbf_ffn(dev(x), dev(lg), *recs, cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=1e-7)
+    check_f32(f64(y), o, F32_TOL, f"moe dbf {name} T={T}")
+    check_bf16(yb, o, f"moe dbf {name} T={T} bf16")
 
 
 # the ABI limits of the routed layers: T = 256 tokens, E = 1024 experts,
