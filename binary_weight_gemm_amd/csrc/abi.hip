@@ -73,7 +73,7 @@ bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K) {
   if (M <= 64) return brq::gemm_dec_ws_bytes(M, N, K);
-  return brq::align256((size_t)M * K * 2);
+  return brq::pf_ws_bytes(M, K);
 }
 
 }  // namespace

@@ -42,8 +42,8 @@ __global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ 
   f32x4 acc[1][TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  WaveStage<ST_BF16, CPW, MAXR> sx;
   if (c0 < nchunks) {
-    WaveStage<ST_BF16, CPW, MAXR> sx;
     WaveStage<ST_F16, CPW, 1> sd;
     sx.load(M, n, c0, [&](int m) { return x + (size_t)m * n; });
     sd.load(1, n, c0, [&](int) { return d_in; });
@@ -61,6 +61,9 @@ __global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ 
       return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
     };
     b_compute<BM_PERK, 1, TT, CPW>(bp, kp, G, c0, 1, aop, acc);
+    static_assert(TT == 1, "one tile of up to 8 rows");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], sx.unscale(i));
   }
   __syncthreads();
   reduce_waves<1, TT>(acc, reinterpret_cast<f32x4*>(smem));

@@ -38,6 +38,75 @@ __global__ __launch_bounds__(256) void k_prep(const uint16_t* __restrict__ src, 
   d[3] = make_uint4(o[12], o[13], o[14], o[15]);
 }
 
+// One workgroup per row: the row's runs of 32 stay in registers (up to 4 per
+// thread, K <= 32768) while the row's largest |x| is found; when it lies
+// outside [2^-8, 2^15) the row is staged as fp16(x * 2^s) with s = 14 - its
+// exponent (the largest value then in [2^14, 2^15), every bf16 value exact in
+// fp16 or on its subnormal grid far below 2^-24 of the maximum), else s = 0;
+// s goes to rexp[row] for the product's epilogue to undo. scale = 0 keeps
+// every s at 0 (callers that add unscaled terms into the same accumulator).
+__global__ __launch_bounds__(256) void k_prep_rows(const uint16_t* __restrict__ src, int K,
+                                                   uint16_t* __restrict__ dst, int* __restrict__ rexp, int scale) {
+  __shared__ uint32_t s_max[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int runs = K >> 5;
+  const uint16_t* xr = src + (size_t)row * K;
+  uint16_t* dr = dst + (size_t)row * K;
+  uint4 q[4][4];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = tid + 256 * u;
+    const uint4* s4 = reinterpret_cast<const uint4*>(xr + 32 * (t < runs ? t : 0));
+#pragma unroll
+    for (int h = 0; h < 4; ++h) q[u][h] = s4[h];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (tid + 256 * u >= runs) continue;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t w4[4] = {q[u][h].x, q[u][h].y, q[u][h].z, q[u][h].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = max(mx, max(w4[e] & 0x7fffu, (w4[e] >> 16) & 0x7fffu));
+    }
+  }
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+  __syncthreads();
+  mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const int e = (int)(mx >> 7) - 127;  // exponent of the row's largest |x| (-127: all zero)
+  const int sc = (scale && mx != 0 && (e >= 15 || e < -8)) ? 14 - e : 0;
+  if (tid == 0) rexp[row] = sc;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = tid + 256 * u;
+    if (t >= runs) continue;
+    const uint32_t v[16] = {q[u][0].x, q[u][0].y, q[u][0].z, q[u][0].w, q[u][1].x, q[u][1].y, q[u][1].z, q[u][1].w,
+                            q[u][2].x, q[u][2].y, q[u][2].z, q[u][2].w, q[u][3].x, q[u][3].y, q[u][3].z, q[u][3].w};
+    uint32_t o[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      // element b lives in word b/2 (half b%2); element 16+b in word 8+b/2
+      const uint32_t lo = (b & 1) ? (v[b >> 1] & 0xffff0000u) : (v[b >> 1] << 16);
+      const uint32_t hi = (b & 1) ? (v[8 + (b >> 1)] & 0xffff0000u) : (v[8 + (b >> 1)] << 16);
+      o[b] = (uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(lo), sc)) |
+             ((uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(hi), sc)) << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(dr + 32 * t);
+    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    d[2] = make_uint4(o[8], o[9], o[10], o[11]);
+    d[3] = make_uint4(o[12], o[13], o[14], o[15]);
+  }
+}
+
+hipError_t launch_prep_rows(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, int* rexp, int scale,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_prep_rows, dim3((unsigned)rows), dim3(256), 0, st, x, (int)K, xp, rexp, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st) {
   const int64_t runs = rows * (K / 32);
   hipLaunchKernelGGL(k_prep, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, st, x, runs, xp);
@@ -103,6 +172,8 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
       return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
     };
     b_compute<BM_GROUP, 1, 1, CPW, true>(bp, nullptr, G, c0, 1, aop, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], ws.unscale(i));
   }
   // lane (kb, j) holds rows 4*kb .. 4*kb+3 of column j
   const bool holds = 4 * kb < M;

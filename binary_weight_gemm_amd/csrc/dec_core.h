@@ -141,6 +141,13 @@ __device__ __forceinline__ void b_compute(const BPre<NB, CPW>& bp, const u32x4* 
 template <int MODE, int CPW, int MAXR>
 struct WaveStage {
   uint2 lo[CPW][MAXR], hi[CPW][MAXR];
+  // ST_BF16: each row of the wave's slice is staged as fp16(x * 2^s), s a
+  // power of two that puts the row's largest |x| in [2^14, 2^15): a bf16 value
+  // is exact in fp16 there whatever its magnitude (no overflow at 65504, no
+  // loss below 2^-14); us[i] = -s of the row whose MFMA output this lane
+  // holds in element i (rows 4kb .. 4kb+3 for lane l = 16kb + j), undone
+  // exactly by unscale(). Other modes stage unscaled (us = 0).
+  int us[4];
 
   template <class ROWPTR>
   __device__ __forceinline__ void load(int rows, int K, int c0, ROWPTR&& rowptr) {
@@ -166,7 +173,28 @@ struct WaveStage {
 
   __device__ __forceinline__ void store(uint4* xs) {
     const int lane = threadIdx.x & 63;
-    const int run = lane >> 2;
+    const int run = lane >> 2, kb = lane >> 4;
+    int sm[MAXR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) us[i] = 0;
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) {
+      sm[m] = 0;
+      if (MODE == ST_BF16) {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+          const uint32_t w4[4] = {lo[c][m].x, lo[c][m].y, hi[c][m].x, hi[c][m].y};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) mx = max(mx, max(w4[h] & 0x7fffu, (w4[h] >> 16) & 0x7fffu));
+        }
+        mx = wave_max_u32(mx);
+        sm[m] = 14 - ((int)(mx >> 7) - 127);  // an all-zero row gets 141: harmless, every value is 0
+        // selected from scalars, not from an indexed array (which would go to scratch)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) us[i] = (4 * kb + i == m) ? -sm[m] : us[i];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
@@ -181,8 +209,8 @@ struct WaveStage {
             if (MODE == ST_BF16) {
               const uint32_t a = (t & 1) ? (l2[t >> 1] & 0xffff0000u) : (l2[t >> 1] << 16);
               const uint32_t b = (t & 1) ? (h2[t >> 1] & 0xffff0000u) : (h2[t >> 1] << 16);
-              o[t] = (uint32_t)f32_to_f16_bits(__uint_as_float(a)) |
-                     ((uint32_t)f32_to_f16_bits(__uint_as_float(b)) << 16);
+              o[t] = (uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(a), sm[m])) |
+                     ((uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(b), sm[m])) << 16);
             } else {
               const uint32_t a = (t & 1) ? (l2[t >> 1] >> 16) : (l2[t >> 1] & 0xffffu);
               const uint32_t b = (t & 1) ? (h2[t >> 1] >> 16) : (h2[t >> 1] & 0xffffu);
@@ -193,6 +221,9 @@ struct WaveStage {
         xs[(c * MAXR + m) * 64 + run * 4 + (lane & 3)] = make_uint4(o[0], o[1], o[2], o[3]);
       }
   }
+
+  // exponent that scales this lane's MFMA output element i back
+  __device__ __forceinline__ int unscale(int i) const { return us[i]; }
 };
 
 // Per-wave staging of fp32 rows (intermediate vectors of a chain) as scaled

@@ -15,6 +15,11 @@ hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, uint64_t* sig
 // ---- activation staging --------------------------------------------------
 // bf16 [rows][K] -> fp16 [rows][K] in the permuted operand order.
 hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st);
+// The same, one workgroup per row (K <= 32768), each row scaled by 2^rexp[row]
+// (a power of two, 0 for rows whose largest |x| is in [2^-8, 2^15); scale = 0:
+// always 0) so that every bf16 value is exact in fp16 whatever the row's range.
+hipError_t launch_prep_rows(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, int* rexp, int scale,
+                            hipStream_t st);
 // fp16 vector [K] -> fp16 [K] in the permuted operand order.
 
 // ---- group-128 product ----------------------------------------------------
@@ -39,8 +44,10 @@ hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_
 // Many activation rows: LDS-tiled matrix-core kernel, bf16 activations read directly.
 hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                             const uint16_t* scales, void* y, int y_bf16, hipStream_t st);
-// Many activation rows (prefill): x staged to `ws` (M*K*2 bytes) as permuted
-// fp16, then the 256 x 256 direct-to-LDS matrix-core kernel.
+// Many activation rows (prefill): x staged to `ws` (pf_ws_bytes) as permuted
+// fp16 with a power-of-two scale per row, then the 256 x 256 direct-to-LDS
+// matrix-core kernel, which undoes the scales in its epilogue.
+size_t pf_ws_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                           const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 // The same with one extra k-step per tile that adds a rank-r correction:

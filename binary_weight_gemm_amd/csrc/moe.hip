@@ -310,8 +310,8 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
     auto tile = [&](auto sr) {
       constexpr int SR = decltype(sr)::value;
       uint4* xw = smem + (size_t)wave * CPW * SR * 64;
+      WaveStage<ST_BF16, CPW, SR> sx;
       if (c0 < nchunks) {
-        WaveStage<ST_BF16, CPW, SR> sx;
         sx.load(rows, H, c0, [&](int rr) { return x + (size_t)ws.route_tok[r0 + tb + rr] * H; });
         sx.store(xw);
       }
@@ -326,6 +326,16 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
         for (int cb = 0; cb < CB; ++cb) {
           pin_signs(bp[cb]);
           b_compute<BM_GROUP, 2, 1, CPW>(bp[cb], nullptr, G, c0, 1, aop, acc[cb]);
+        }
+        // back from the rows' staging scales (exact powers of two)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int u = sx.unscale(i);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            acc[cb][0][0][i] = __builtin_amdgcn_ldexpf(acc[cb][0][0][i], u);
+            acc[cb][1][0][i] = __builtin_amdgcn_ldexpf(acc[cb][1][0][i], u);
+          }
         }
       }
     };
@@ -574,6 +584,11 @@ __global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict_
       return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
     };
     b_compute<BM_GROUP, 2, 1, CPW, true>(bp, nullptr, G, c0, 1, aop, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], sx.unscale(i));
+      acc[1][0][i] = __builtin_amdgcn_ldexpf(acc[1][0][i], sx.unscale(i));
+    }
   }
   const bool holds = 4 * kb < cnt;
   if (wave > 0 && holds) {
@@ -829,6 +844,7 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) acc[q][cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     WaveStageF32<CPW, RT> sf0, sf1;  // the two inputs of stage 1 (gate, up); sf0 elsewhere
+    WaveStage<ST_BF16, CPW, SR> sx;  // stage 0: the routes' token rows
     if (c0 < nchunks) {
       if constexpr (PIECES) {
         sf0.load(routes, K, c0, [&](int m) { return a.in[0] + (size_t)(r0 + tb + m) * K; });
@@ -836,7 +852,6 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
         sf0.store(xw);
         if constexpr (NIN == 2) sf1.store(xw + CPW * SR * 64);
       } else {
-        WaveStage<ST_BF16, CPW, SR> sx;
         sx.load(rows, K, c0, [&](int rr) { return x + (size_t)ws.route_tok[r0 + tb + rr] * H; });
         sx.store(xw);
       }
@@ -853,14 +868,12 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
         const u32x4* kp = PERK ? reinterpret_cast<const u32x4*>(dw + q * CPW * 64) - (size_t)c0 * 64 : nullptr;
         pin_signs(bp[q]);
         b_compute<BMODE, CB, 1, CPW>(bp[q], kp, G, c0, 1, aop, acc[q]);
-        if constexpr (PIECES) {
-          // back from the wave's scaled pieces (exact powers of two)
+        // back from the wave's scaled pieces or rows (exact powers of two)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int us = (NIN == 2 && q == 1) ? sf1.unscale(i) : sf0.unscale(i);
+        for (int i = 0; i < 4; ++i) {
+          const int us = !PIECES ? sx.unscale(i) : (NIN == 2 && q == 1) ? sf1.unscale(i) : sf0.unscale(i);
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) acc[q][cb][0][i] = __builtin_amdgcn_ldexpf(acc[q][cb][0][i], us);
-          }
+          for (int cb = 0; cb < CB; ++cb) acc[q][cb][0][i] = __builtin_amdgcn_ldexpf(acc[q][cb][0][i], us);
         }
       }
     }

@@ -53,7 +53,7 @@ template <bool OUT_BF16, int BN, bool LR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf(
     const uint16_t* __restrict__ xp, int M, int N, int K, const uint32_t* __restrict__ signs,
     const uint16_t* __restrict__ scales, void* __restrict__ y, int n_base, int tiles_n,
-    const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_u) {
+    const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_u, const int* __restrict__ rexp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // [2][PF_TILE]
   constexpr int NJ = BN / 64;  // 32-column tiles per wave
 
@@ -68,6 +68,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int bid = blockIdx.x;
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   const int m0 = (bid / tiles_n) * PF_BM, n0 = n_base + (bid % tiles_n) * BN;
+  // staging exponents of this wave's 128 output rows (lane l: rows l and 64 + l
+  // of the half); the rows were staged as x * 2^s, undone in the epilogue
+  int rs0 = 0, rs1 = 0;
+  if (rexp) {
+    const int ra = m0 + wr * 128 + lane, rb = ra + 64;
+    rs0 = rexp[ra < M ? ra : M - 1];
+    rs1 = rexp[rb < M ? rb : M - 1];
+  }
   const int nk = K / PF_BK;  // k-steps = scale groups
   const int KW = K >> 5;     // 32-bit sign words per weight row
 
@@ -258,6 +266,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   }
 
+  // ---- undo the rows' staging scales (rare: rows outside [2^-8, 2^15))
+  if (__any((rs0 | rs1) != 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = 32 * i + 4 * fh + 8 * (r >> 2) + (r & 3);  // row within the wave's half
+        const int sr = __shfl(i < 2 ? rs0 : rs1, q & 63, 64);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j][r] = __builtin_amdgcn_ldexpf(acc[i][j][r], -sr);
+      }
+  }
+
   // ---- epilogue: lane writes column fr of each 32 x 32 tile, rows in runs of 4
   const bool full = (m0 + PF_BM <= M) && (n0 + BN <= N);
   auto put = [&](size_t idx, float v) {
@@ -296,7 +317,7 @@ size_t pf_lds_bytes() { return 2 * (size_t)PF_TILE; }
 template <bool OUT_BF16, int BN, bool LR>
 static hipError_t pf_launch(const uint16_t* xp, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                             void* y, int n_base, int tiles_n, const uint16_t* lr_t, const uint16_t* lr_u,
-                            hipStream_t st) {
+                            const int* rexp, hipStream_t st) {
   // 128 KiB of dynamic LDS needs the per-function opt-in (set on every call:
   // the attribute is per device and cheap to repeat)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf<OUT_BF16, BN, LR>),
@@ -304,7 +325,7 @@ static hipError_t pf_launch(const uint16_t* xp, int M, int N, int K, const uint6
   if (e != hipSuccess) return e;
   const int tiles = ((M + PF_BM - 1) / PF_BM) * tiles_n;
   hipLaunchKernelGGL((k_pf<OUT_BF16, BN, LR>), dim3(tiles), dim3(256), pf_lds_bytes(), st, xp, M, N, K,
-                     reinterpret_cast<const uint32_t*>(signs), scales, y, n_base, tiles_n, lr_t, lr_u);
+                     reinterpret_cast<const uint32_t*>(signs), scales, y, n_base, tiles_n, lr_t, lr_u, rexp);
   return hipGetLastError();
 }
 
@@ -332,7 +353,8 @@ void pf_plan(int M, int N, int cus, int& big_n, int& small_n) {
 
 template <bool LR>
 static hipError_t pf_run(const uint16_t* xp, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
-                         void* y, int y_bf16, const uint16_t* lr_t, const uint16_t* lr_u, hipStream_t st) {
+                         void* y, int y_bf16, const uint16_t* lr_t, const uint16_t* lr_u, const int* rexp,
+                         hipStream_t st) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -341,31 +363,41 @@ static hipError_t pf_run(const uint16_t* xp, int M, int N, int K, const uint64_t
   pf_plan(M, N, cus, big_n, small_n);
   hipError_t e = hipSuccess;
   if (big_n > 0) {
-    e = y_bf16 ? pf_launch<true, 256, LR>(xp, M, N, K, signs, scales, y, 0, big_n, lr_t, lr_u, st)
-               : pf_launch<false, 256, LR>(xp, M, N, K, signs, scales, y, 0, big_n, lr_t, lr_u, st);
+    e = y_bf16 ? pf_launch<true, 256, LR>(xp, M, N, K, signs, scales, y, 0, big_n, lr_t, lr_u, rexp, st)
+               : pf_launch<false, 256, LR>(xp, M, N, K, signs, scales, y, 0, big_n, lr_t, lr_u, rexp, st);
     if (e != hipSuccess) return e;
   }
   if (small_n > 0)
-    e = y_bf16 ? pf_launch<true, 128, LR>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, lr_t, lr_u, st)
-               : pf_launch<false, 128, LR>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, lr_t, lr_u, st);
+    e = y_bf16 ? pf_launch<true, 128, LR>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, lr_t, lr_u, rexp,
+                                          st)
+               : pf_launch<false, 128, LR>(xp, M, N, K, signs, scales, y, big_n * 256, small_n, lr_t, lr_u, rexp,
+                                           st);
   return e;
 }
+
+// workspace: the staged rows (fp16 [M][K]), then one staging exponent per row
+size_t pf_ws_bytes(int64_t M, int64_t K) { return align256((size_t)M * K * 2) + align256((size_t)M * 4); }
 
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                           void* y, int y_bf16, void* ws, hipStream_t st) {
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-  const hipError_t e = launch_prep_bf16(x, M, K, xp, st);
+  int* rexp = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
+  // rows of up to 32768 values are staged with a power-of-two scale per row;
+  // longer rows unscaled (|x| < 65504)
+  const bool rows = K <= 32768;
+  const hipError_t e = rows ? launch_prep_rows(x, M, K, xp, rexp, 1, st) : launch_prep_bf16(x, M, K, xp, st);
   if (e != hipSuccess) return e;
-  return pf_run<false>(xp, M, N, K, signs, scales, y, y_bf16, nullptr, nullptr, st);
+  return pf_run<false>(xp, M, N, K, signs, scales, y, y_bf16, nullptr, nullptr, rows ? rexp : nullptr, st);
 }
 
 hipError_t launch_gemm_pf_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                              const uint16_t* lr_t, const uint16_t* lr_u, void* y, int y_bf16, void* ws,
                              hipStream_t st) {
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
+  // unscaled staging: the correction x V^T enters the same accumulator unscaled
   const hipError_t e = launch_prep_bf16(x, M, K, xp, st);
   if (e != hipSuccess) return e;
-  return pf_run<true>(xp, M, N, K, signs, scales, y, y_bf16, lr_t, lr_u, st);
+  return pf_run<true>(xp, M, N, K, signs, scales, y, y_bf16, lr_t, lr_u, nullptr, st);
 }
 
 }  // namespace brq

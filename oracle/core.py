@@ -327,8 +327,11 @@ def route_topk(logits, k: int):
 
 
 def silu(z):
+    """z * sigmoid(z) = z / (1 + e^-z); for z below about -709 e^-z overflows to
+    inf and the quotient is the limit -0 (no warning raised for it)."""
     z = np.asarray(z, dtype=np.float64)
-    return z / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def moe_ffn(x, logits, expert, H: int, I: int, k: int):

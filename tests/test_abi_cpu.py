@@ -52,7 +52,7 @@ def test_size_queries(L):
     assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 14 * 32 * 64 * 128 * 4
     # one K-slice (K = 512 over 256 tiles of 128 columns): no workspace
     assert L.brq_gemm_workspace_bytes(64, 32768, 512) == 0
-    assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 4096 * 4096 * 2   # staged activations
+    assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 4096 * 4096 * 2 + 4096 * 4   # staged rows, exponents
     assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0
     assert L.brq_dbf_workspace_bytes(1, 4096, 4096, 2048) > 0
     assert L.brq_moe_workspace_bytes(1, 2048, 512, 256, 8) > 0

@@ -185,6 +185,82 @@ def test_gemm_few_rows_wide_range(M, N, K):
             check_f32(y[m], o[m], F32_TOL, f"row {m} of {M}x{N}x{K}")
 
 
+# activation rows far outside fp16's range (|x| ~ 1e5, 1e30, 1e-30) next to
+# ordinary and all-zero rows: the paths that stage bf16 rows as fp16 (decode
+# rows M <= 8, prefill M > 64) scale each row (or wave slice of a row) by a
+# power of two first, so every row matches the oracle and the single-row path
+# to the fp32 bar, whatever its magnitude
+_RANGE_SCALES = (1e5, 1e30, 0.0, 1e-30, 1.0, 3e4, 2.0 ** -20, 1e-3)
+
+
+# the routed layer's SwiGLU squares the magnitude: scales whose fp32
+# intermediates stay finite and normal
+_RANGE_SCALES_MOE = (1e5, 3e8, 0.0, 1e-10, 1.0, 3e4, 2.0 ** -20, 1e-3)
+
+
+def _range_rows(M, K, key, scales=_RANGE_SCALES):
+    g = datagen.rng(79, M, K, key)
+    base = g.standard_normal((M, K)).astype(np.float32)
+    rows = np.stack([base[m] * np.float32(scales[m % len(scales)]) for m in range(M)])
+    return datagen.bf16_bits_from_f32(rows)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 96, 1024), (8, 130, 2048), (300, 520, 1024)])
+def test_gemm_activation_range(M, N, K):
+    say("gemm activation range", M, N, K)
+    w = datagen.normal_f32((79, N, K), (N, K), 0.02)
+    ow, osc = oracle.pack_sign1(w)
+    xb = _range_rows(M, K, 0)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(xb), ow, osc, N, K)
+    S, SC = dev(ow), dev(osc)
+    y = f64(brq().gemm(dev(xb), S, SC, N, K, out_dtype=torch.float32))
+    assert np.all(np.isfinite(y))
+    for m in range(M):
+        if not np.any(o[m]):
+            assert not np.any(y[m])
+            continue
+        check_f32(y[m], o[m], F32_TOL, f"row {m} (scale {_RANGE_SCALES[m % len(_RANGE_SCALES)]:g}) of {M}x{N}x{K}")
+    # each row alone (the single-row path) agrees with its row of the batch
+    for m in range(min(M, len(_RANGE_SCALES))):
+        if not np.any(o[m]):
+            continue
+        y1 = f64(brq().gemm(dev(xb[m:m + 1]), S, SC, N, K, out_dtype=torch.float32))[0]
+        assert maxrel(y1, y[m]) <= F32_TOL, f"row {m}: single-row and batch differ"
+
+
+def test_dbf_and_moe_activation_range():
+    say("dbf decode + moe small/grouped, activation range")
+    m_, n_, r_ = 128, 512, 256
+    v = datagen.pm1_f32((79, 1, 0), (r_, n_))
+    u = datagen.pm1_f32((79, 1, 1), (m_, r_))
+    d_in, d_mid, d_out = (datagen.f16_lognormal((79, 1, 2 + i), (s_,)) for i, s_ in enumerate((n_, r_, m_)))
+    vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
+    xb = _range_rows(4, n_, 1)
+    o = oracle.dbf_chain(oracle.bf16_to_f64(xb), d_in, vw, d_mid, uw, d_out, m_, n_, r_)
+    y = f64(brq().dbf_gemm(dev(xb), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m_, n_, r_,
+                           out_dtype=torch.float32))
+    for t in range(4):
+        if np.any(o[t]):
+            check_f32(y[t], o[t], F32_TOL, f"dbf row {t}")
+        else:
+            assert not np.any(y[t])
+    cfg = datagen.C4(E=16, H=256, I=128, top_k=4, layer=79)
+    ex = _Experts(cfg)
+    for T in (3, 9):  # few-token path, grouped path
+        xt = _range_rows(T, cfg.H, 2 + T, _RANGE_SCALES_MOE)
+        lg = cfg.logits(T)
+        om, oids, _ = oracle.moe_ffn(oracle.bf16_to_f64(xt), lg, ex, cfg.H, cfg.I, cfg.top_k)
+        ym, ids, _ = brq().moe_ffn(dev(xt), dev(lg), *ex.d, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32,
+                                   return_routing=True)
+        ym = f64(ym)
+        assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+        for t in range(T):
+            if np.any(om[t]):
+                check_f32(ym[t], om[t], F32_TOL, f"moe T={T} token {t}")
+            else:
+                assert not np.any(ym[t])
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 40, 640), (64, 96, 1024)])
 def test_gemm_decode_bf16(M, N, K):
     say("gemm decode bf16", M, N, K)
