@@ -660,6 +660,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 512 MiB device copies (counter calibration) and exit")
+    ap.add_argument("--only", choices=["prefill", "decode64", "moe1", "dbf1", "q8"],
+                    help="run one extra section alone and print its result (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
@@ -672,6 +674,16 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         print(json.dumps(copy_calibration(torch)))
+        return
+    if args.only:
+        sections = {
+            "prefill": lambda: run_prefill(brq, torch),
+            "decode64": lambda: run_c2(brq, torch, 64, 50, 10),
+            "moe1": lambda: run_moe(brq, torch, (1,)),
+            "dbf1": lambda: run_dbf(brq, torch, (1,)),
+            "q8": lambda: run_dbf(brq, torch, (512,), q8=True),
+        }
+        print(json.dumps({args.only: sections[args.only]()}, default=float))
         return
 
     log("[bench] headline C2 decode M=1")
