@@ -383,7 +383,9 @@ def run_pack(brq, torch, iters=10):
                 frac_of_hbm=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
-def run_moe(brq, torch, Ts, iters=50):
+def run_moe(brq, torch, Ts, iters=50, fusion=0):
+    """The routed MoE layer at the C4 shape; fusion selects the single-launch
+    setting (brq.set_decode_fusion) for the timed calls."""
     import datagen
     cfg = datagen.C4()
     E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.top_k
@@ -410,6 +412,7 @@ def run_moe(brq, torch, Ts, iters=50):
         for it in range(iters):
             ids = np.argsort(-cfg.logits(T, it), axis=1, kind="stable")[:, :k]
             nbytes += len(np.unique(ids)) * 3 * packed_bytes(I, H) + T * (H * 2 * 2 + E * 4)
+        brq.set_decode_fusion(fusion)
         for it in range(5):
             brq.moe_ffn(x, lgs[it], *ring[it % copies], E, H, I, k, y=y, ws=ws)
         torch.cuda.synchronize()
@@ -419,6 +422,7 @@ def run_moe(brq, torch, Ts, iters=50):
                 brq.moe_ffn(x, lgs[it], *ring[it % copies], E, H, I, k, y=y, ws=ws)
 
         ms = graph_time(torch, timed, iters) / iters
+        brq.set_decode_fusion(brq.FUSION_DEFAULT)
         out[f"T={T}"] = dict(us_per_layer=ms * 1e3, gbs=nbytes / iters / (ms * 1e-3) / 1e9,
                              tokens_per_s=T / (ms * 1e-3), ring_copies=copies)
     del ring, gs, gsc, us, usc, ds, dsc
@@ -479,9 +483,10 @@ def run_moe_dbf(brq, torch, Ts, iters=50, geometry=None):
     return out
 
 
-def run_dbf(brq, torch, Ms, iters=50, q8=False, r=2048):
+def run_dbf(brq, torch, Ms, iters=50, q8=False, r=2048, fusion=0):
     """The DBF chain at the DBF workload's shapes (rank r); q8 selects the path
-    over Q8 activation codes (int8 matrix cores) instead of the fp16-piece path."""
+    over Q8 activation codes (int8 matrix cores) instead of the fp16-piece path;
+    fusion the single-launch setting (brq.set_decode_fusion)."""
     import datagen
     gemm = brq.dbf_gemm_q8 if q8 else brq.dbf_gemm
     ws_bytes = brq.dbf_q8_workspace_bytes if q8 else brq.dbf_workspace_bytes
@@ -498,6 +503,7 @@ def run_dbf(brq, torch, Ms, iters=50, q8=False, r=2048):
         di, dm, do = (torch.from_numpy(d[k]).cuda() for k in ("d_in", "d_mid", "d_out"))
         y = torch.empty((M, m), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(ws_bytes(M, m, n, r), dtype=torch.uint8, device="cuda")
+        brq.set_decode_fusion(fusion)
         for i in range(5):
             gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
         torch.cuda.synchronize()
@@ -507,6 +513,7 @@ def run_dbf(brq, torch, Ms, iters=50, q8=False, r=2048):
                 gemm(x, di, ring[i % copies][0], dm, ring[i % copies][1], do, m, n, r, y=y, ws=ws)
 
         ms = graph_time(torch, timed, iters) / iters
+        brq.set_decode_fusion(brq.FUSION_DEFAULT)
         nbytes = wbytes + M * n * 2 + M * m * 2
         flops = 2.0 * M * (r * n + m * r)
         out[f"M={M}"] = dict(us=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
@@ -660,7 +667,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 512 MiB device copies (counter calibration) and exit")
-    ap.add_argument("--only", choices=["prefill", "decode64", "moe1", "dbf1", "q8"],
+    ap.add_argument("--only", choices=["prefill", "decode64", "moe1", "dbf1", "q8", "fusion"],
                     help="run one extra section alone and print its result (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -682,6 +689,11 @@ def main():
             "moe1": lambda: run_moe(brq, torch, (1,)),
             "dbf1": lambda: run_dbf(brq, torch, (1,)),
             "q8": lambda: run_dbf(brq, torch, (512,), q8=True),
+            "fusion": lambda: {
+                "moe_one_launch": run_moe(brq, torch, (1, 2, 4), fusion=brq.FUSION_ON),
+                "moe_multi_launch": run_moe(brq, torch, (1, 2, 4), fusion=brq.FUSION_OFF),
+                "dbf_one_launch": run_dbf(brq, torch, (1, 4), fusion=brq.FUSION_ON),
+                "dbf_multi_launch": run_dbf(brq, torch, (1, 4), fusion=brq.FUSION_OFF)},
         }
         print(json.dumps({args.only: sections[args.only]()}, default=float))
         return
@@ -708,6 +720,13 @@ def main():
         extra["pack"] = run_pack(brq, torch)
         log("[bench] MoE")
         extra["moe"] = run_moe(brq, torch, (1, 4, 16, 64))
+        log("[bench] single-launch decode chains: MoE T = 1, 2, 4 and DBF M = 1, 4, one launch and multi-launch")
+        extra["decode_fusion"] = {
+            "moe_one_launch": run_moe(brq, torch, (1, 2, 4), fusion=brq.FUSION_ON),
+            "moe_multi_launch": run_moe(brq, torch, (1, 2, 4), fusion=brq.FUSION_OFF),
+            "dbf_one_launch": run_dbf(brq, torch, (1, 4), fusion=brq.FUSION_ON),
+            "dbf_multi_launch": run_dbf(brq, torch, (1, 4), fusion=brq.FUSION_OFF),
+        }
         log("[bench] MoE with DBF experts")
         extra["moe_dbf"] = run_moe_dbf(brq, torch, (1, 64))
         log("[bench] MoE with DBF experts, DeepSeek-V4-Flash geometry")

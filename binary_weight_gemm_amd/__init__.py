@@ -28,7 +28,7 @@ __all__ = [
     "gemm_workspace_bytes", "gemm_lr_workspace_bytes", "dbf_workspace_bytes", "dbf_q8_workspace_bytes",
     "moe_workspace_bytes",
     "sign_words", "scale_count",
-    "BRQ_BF16", "BRQ_F32", "ABI_FUNCTIONS",
+    "BRQ_BF16", "BRQ_F32", "ABI_FUNCTIONS", "set_decode_fusion", "FUSION_DEFAULT", "FUSION_OFF", "FUSION_ON",
 ]
 
 BRQ_BF16 = 0
@@ -47,6 +47,7 @@ ABI_FUNCTIONS = {
     "brq_abi_version": (_int, []),
     "brq_status_str": (ctypes.c_char_p, [_int]),
     "brq_last_error": (ctypes.c_char_p, []),
+    "brq_set_decode_fusion": (_int, [_int, ctypes.c_uint32]),
     "brq_sign_words": (_sz, [_i64, _i64]),
     "brq_scale_count": (_sz, [_i64, _i64]),
     "brq_pack": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
@@ -137,6 +138,16 @@ def _ws(nbytes: int, device, ws):
     if ws.numel() * ws.element_size() < nbytes:
         raise BrqError(f"workspace of {ws.numel() * ws.element_size()} bytes, {nbytes} needed")
     return ws, nbytes
+
+
+FUSION_DEFAULT, FUSION_OFF, FUSION_ON = 0, 1, 2
+
+
+def set_decode_fusion(mode: int, spin_limit: int = 0) -> None:
+    """brq_set_decode_fusion: single-launch decode chains (DBF at M <= 8, MoE at
+    T <= 4): FUSION_DEFAULT (the library's per-path choice), FUSION_OFF or
+    FUSION_ON; spin_limit bounds the grid-wide wait (0: default)."""
+    _check(lib().brq_set_decode_fusion(int(mode), int(spin_limit)), "brq_set_decode_fusion")
 
 
 def sign_words(rows: int, cols: int) -> int:

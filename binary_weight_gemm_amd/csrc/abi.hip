@@ -11,6 +11,7 @@
 
 #include "../../include/brq.h"
 #include "kernels.h"
+#include "gsync.h"
 
 namespace {
 
@@ -103,6 +104,13 @@ const char* brq_status_str(brq_status s) {
 }
 
 const char* brq_last_error(void) { return g_last_error.c_str(); }
+
+brq_status brq_set_decode_fusion(brq_fusion mode, uint32_t spin_limit) {
+  if (mode != BRQ_FUSION_DEFAULT && mode != BRQ_FUSION_OFF && mode != BRQ_FUSION_ON)
+    return fail(BRQ_E_SHAPE, "brq_set_decode_fusion: unknown mode %d", (int)mode);
+  brq::set_fusion((int)mode, spin_limit);
+  return ok();
+}
 
 size_t brq_sign_words(int64_t rows, int64_t cols) {
   if (rows < 1 || cols < 64 || cols % 64) return 0;

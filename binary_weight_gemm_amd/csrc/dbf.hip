@@ -133,6 +133,123 @@ __global__ __launch_bounds__(1024) void k_dbf2_dec(const float* __restrict__ hs,
     }
 }
 
+// Decode path in one launch (the joint kernel of section 7 of the DBF post):
+// workgroup b computes stage 1 for rows 16b .. 16b+15 of V (if b < r/16)
+// and, after a grid-wide wait for every workgroup's h_s, stage 2 for rows
+// 16b .. 16b+15 of U (if b < m/16). Its U sign words are loaded before stage 1
+// starts, so the second product issues no weight load after the wait. The
+// stage bodies and their sums are those of k_dbf1_dec and k_dbf2_dec (the
+// results are the same bits); h_s crosses the wait through the coherence
+// point (gsync.h). The launch is sized so that every workgroup is resident.
+template <int CPW1, int CPW2, int MAXR1, int MAXR2>
+__global__ __launch_bounds__(1024) void k_dbf_fused(const uint16_t* __restrict__ x, int M, int m, int n, int r,
+                                                    int waves1, int waves2, const uint4* __restrict__ v,
+                                                    const uint16_t* __restrict__ d_in,
+                                                    const uint16_t* __restrict__ d_mid, const uint4* __restrict__ u,
+                                                    const uint16_t* __restrict__ d_out, float* __restrict__ hs,
+                                                    void* __restrict__ y, int y_bf16, uint32_t* __restrict__ slot,
+                                                    uint32_t spin) {
+  extern __shared__ uint4 smem[];
+  const uint32_t epoch = grid_epoch(slot);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int col = blockIdx.x * 16 + j;
+  const bool do1 = (int)blockIdx.x * 16 < r, do2 = (int)blockIdx.x * 16 < m;  // uniform per workgroup
+  const int G1 = n >> 7, nch1 = (G1 + 3) >> 2, c01 = wave * CPW1;
+  const int G2 = r >> 7, nch2 = (G2 + 3) >> 2, c02 = wave * CPW2;
+  // waves of each stage: those of the two-launch kernels (the rest idle)
+  const bool act1 = do1 && wave < waves1 && c01 < nch1, act2 = do2 && wave < waves2 && c02 < nch2;
+  uint4* xw = smem + (size_t)wave * CPW1 * MAXR1 * 64;
+  uint4* dw = smem + (size_t)waves1 * CPW1 * MAXR1 * 64 + (size_t)wave * CPW1 * 64;
+  BPre<1, CPW2> bp2;
+  const uint16_t* nsc[1] = {nullptr};
+  if (act2) {  // stage 2 weight words first: they do not depend on stage 1
+    const uint4* wsig2[1] = {u + (size_t)(col < m ? col : 0) * G2};
+    const bool rok2[1] = {col < m};
+    b_prefetch<BM_ONE, 1, CPW2>(wsig2, nsc, rok2, G2, c02, 1, bp2);
+  }
+  f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+  WaveStage<ST_BF16, CPW1, MAXR1> sx;
+  BPre<1, CPW1> bp1;
+  if (act1) {
+    const uint4* wsig[1] = {v + (size_t)(col < r ? col : 0) * G1};
+    const bool rok[1] = {col < r};
+    WaveStage<ST_F16, CPW1, 1> sd;
+    sx.load(M, n, c01, [&](int q) { return x + (size_t)q * n; });
+    sd.load(1, n, c01, [&](int) { return d_in; });
+    b_prefetch<BM_PERK, 1, CPW1>(wsig, nsc, rok, G1, c01, 1, bp1);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sx.store(xw);
+    sd.store(dw);
+  }
+  __syncthreads();
+  if (act1) {
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(dw) - (size_t)c01 * 64;
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int q = min(j, M - 1);
+      return xs[(((g >> 2) - c01) * MAXR1 + q) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_PERK, 1, 1, CPW1>(bp1, kp, G1, c01, 1, aop, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], sx.unscale(i));
+  }
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  if (do1) {  // the partials of stage 1's waves, added in wave order as reduce_waves does
+    if (wave > 0 && wave < waves1) red[(wave - 1) * 64 + lane] = acc[0][0];
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < waves1; ++w) acc[0][0] += red[(w - 1) * 64 + lane];
+      if (col < r) {
+        const float dm = f16_bits_to_f32(d_mid[col]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 4 * (lane >> 4) + i;
+          if (q < M) coh_storef(hs + (size_t)q * r + col, acc[0][0][i] * dm);
+        }
+      }
+    }
+  }
+  // ---- every workgroup's h_s is at the coherence point after this
+  const bool ok = grid_wait(slot, epoch, spin);
+  if (!do2) return;  // uniform per workgroup
+  if (!ok) {
+    if (wave == 0 && lane < 16 && col < m)
+      for (int t = 0; t < M; ++t) store_out(y, (size_t)t * m + col, __builtin_nanf(""), y_bf16);
+    return;
+  }
+  // ---- stage 2: h_s as scaled fp16 piece rows, U operands +-1, D_out
+  acc[0][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rows = 2 * M;
+  uint4* pw = smem + (size_t)wave * CPW2 * MAXR2 * 64;
+  WaveStageF32<CPW2, MAXR2 / 2> sh;
+  if (act2) {
+    sh.template load<true>(M, r, c02, [&](int t) { return hs + (size_t)t * r; });
+    sh.store(pw);
+    const u32x4* xs = reinterpret_cast<const u32x4*>(pw);
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int pr = min(j, rows - 1);  // piece row: token pr/2, piece pr%2
+      return xs[(((g >> 2) - c02) * MAXR2 + pr) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_ONE, 1, 1, CPW2>(bp2, nullptr, G2, c02, 1, aop, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], sh.unscale(i));
+  }
+  __syncthreads();
+  if (wave > 0 && wave < waves2) red[(wave - 1) * 64 + lane] = acc[0][0];
+  __syncthreads();
+  if (wave != 0) return;
+  for (int w = 1; w < waves2; ++w) acc[0][0] += red[(w - 1) * 64 + lane];
+  if (col >= m) return;
+  const float dg = f16_bits_to_f32(d_out[col]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 2 * (lane >> 4) + h;
+    if (t < M) store_out(y, (size_t)t * m + col, (acc[0][0][2 * h] + acc[0][0][2 * h + 1]) * dg, y_bf16);
+  }
+}
+
 // Decode path: per-wave staging of the x slice plus d_in (stage 1) and of the
 // 2M h_s piece rows (stage 2) within the LDS budget, M <= 8.
 static bool dbf_split(int64_t rows, int64_t K, DecSplit& sp) {
@@ -149,6 +266,15 @@ static int dbf_maxr(int64_t M) { return M <= 1 ? 1 : M <= 4 ? 4 : 8; }
 static bool dbf_decode_path(int64_t M, int64_t n, int64_t r) {
   DecSplit a, b;
   return M <= 8 && dbf_split(dbf_maxr(M) + 1, n, a) && dbf_split(2 * dbf_maxr(M), r, b);
+}
+
+// Single-launch chains: on when the caller asked for them (mode 2); by default
+// (mode 0) off, two graph launches having measured faster on this chip (the
+// grid-wide wait costs about what the kernel boundary does, and the first
+// stage's workgroups are as slow either way).
+static bool dbf_fusion_wanted(int M) {
+  (void)M;
+  return fusion_mode() == 2;
 }
 
 // Tiled path, between the stages: one workgroup per h_s row adds the row's
@@ -281,10 +407,55 @@ size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
   return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4);
 }
 
+// Single-launch decode chain: taken when the caller asked for it (or the
+// library's default does) and every workgroup (one per 16 rows of the longer
+// of V and U) fits the device at once. Returns false when not taken.
+template <int MAXR1, int MAXR2>
+static bool dbf_fused(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
+                      const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
+                      float* hs, hipStream_t st, hipError_t& err) {
+  if (!dbf_fusion_wanted(M)) return false;
+  DecSplit s1, s2;
+  dbf_split(MAXR1 + 1, n, s1);
+  dbf_split(MAXR2, r, s2);
+  const int waves = s1.waves > s2.waves ? s1.waves : s2.waves;
+  const int64_t blocks = ((int64_t)(r > m ? r : m) + 15) / 16;
+  size_t lds = (size_t)s1.waves * s1.cpw * (MAXR1 + 1) * 1024;
+  const size_t l2 = (size_t)s2.waves * s2.cpw * MAXR2 * 1024, rd = (size_t)(waves - 1) * 64 * 16;
+  lds = lds > l2 ? lds : l2;
+  lds = lds > rd ? lds : rd;
+  const void* fn = nullptr;
+#define BRQ_FUSED_FN(C1, C2) reinterpret_cast<const void*>(&k_dbf_fused<C1, C2, MAXR1, MAXR2>)
+  if (s1.cpw == 1 && s2.cpw == 1) fn = BRQ_FUSED_FN(1, 1);
+  else if (s1.cpw == 2 && s2.cpw == 1) fn = BRQ_FUSED_FN(2, 1);
+  else if (s1.cpw == 1 && s2.cpw == 2) fn = BRQ_FUSED_FN(1, 2);
+  else if (s1.cpw == 2 && s2.cpw == 2) fn = BRQ_FUSED_FN(2, 2);
+#undef BRQ_FUSED_FN
+  if (!fn || !grid_fits(fn, 64 * waves, lds, blocks)) return false;
+  uint32_t* slot = nullptr;
+  err = grid_slot(&slot);
+  if (err != hipSuccess) return true;
+  const uint4* v4 = reinterpret_cast<const uint4*>(v);
+  const uint4* u4 = reinterpret_cast<const uint4*>(u);
+  const uint32_t spin = grid_spin_limit();
+#define BRQ_FUSED(C1, C2)                                                                                    \
+  hipLaunchKernelGGL((k_dbf_fused<C1, C2, MAXR1, MAXR2>), dim3((unsigned)blocks), dim3(64 * waves), lds, st, x, M, \
+                     m, n, r, s1.waves, s2.waves, v4, d_in, d_mid, u4, d_out, hs, y, y_bf16, slot, spin)
+  if (s1.cpw == 1 && s2.cpw == 1) BRQ_FUSED(1, 1);
+  else if (s1.cpw == 2 && s2.cpw == 1) BRQ_FUSED(2, 1);
+  else if (s1.cpw == 1 && s2.cpw == 2) BRQ_FUSED(1, 2);
+  else BRQ_FUSED(2, 2);
+#undef BRQ_FUSED
+  err = hipGetLastError();
+  return true;
+}
+
 template <int MAXR1, int MAXR2>
 static hipError_t dbf_decode(const uint16_t* x, int M, int m, int n, int r, const uint16_t* d_in, const uint64_t* v,
                              const uint16_t* d_mid, const uint64_t* u, const uint16_t* d_out, void* y, int y_bf16,
                              float* hs, hipStream_t st) {
+  hipError_t fe = hipSuccess;
+  if (dbf_fused<MAXR1, MAXR2>(x, M, m, n, r, d_in, v, d_mid, u, d_out, y, y_bf16, hs, st, fe)) return fe;
   DecSplit s1, s2;
   dbf_split(MAXR1 + 1, n, s1);
   dbf_split(MAXR2, r, s2);

@@ -23,6 +23,7 @@
 #pragma once
 
 #include "common.h"
+#include "gsync.h"
 
 namespace brq {
 
@@ -243,7 +244,9 @@ struct WaveStageF32 {
   int us[2];  // -s of the rows 2kb and 2kb+1 (lane l = 16kb + j), the MFMA
               // output rows 4kb .. 4kb+3 of this lane being their pieces
 
-  template <class ROWPTR>
+  // COH: the rows were written by other workgroups of the same launch before a
+  // grid-wide wait (gsync.h), so they are read at the device's coherence point
+  template <bool COH = false, class ROWPTR>
   __device__ __forceinline__ void load(int rows, int K, int c0, ROWPTR&& rowptr) {
     const int lane = threadIdx.x & 63;
     const int run = lane >> 2, b0 = (lane & 3) * 4;
@@ -254,8 +257,14 @@ struct WaveStageF32 {
         const int kr = (c0 + c) * 512 + 32 * run;
         const int kc = kr < K ? kr : 0;
         const float* src = rowptr(m < rows ? m : rows - 1) + kc;
-        a[c][m] = *reinterpret_cast<const f32x4*>(src + b0);
-        b[c][m] = *reinterpret_cast<const f32x4*>(src + 16 + b0);
+        if (COH) {
+          const float4 u = coh_load4(src + b0), v = coh_load4(src + 16 + b0);
+          a[c][m] = f32x4{u.x, u.y, u.z, u.w};
+          b[c][m] = f32x4{v.x, v.y, v.z, v.w};
+        } else {
+          a[c][m] = *reinterpret_cast<const f32x4*>(src + b0);
+          b[c][m] = *reinterpret_cast<const f32x4*>(src + 16 + b0);
+        }
       }
   }
 

@@ -499,6 +499,44 @@ constexpr int MOE_SMALL_T = 4;
 constexpr int moe_cb_gu(int cpw) { return cpw == 1 ? 4 : cpw == 2 ? 2 : 1; }
 constexpr int moe_cb_dn(int cpw) { return cpw == 1 ? 4 : cpw == 2 ? 2 : 1; }
 
+// The want-th distinct expert (ascending id) among the R = T*k <= 64 routes
+// in s_ids, and its routes in ascending (token, slot) order, by one wave with
+// no serial loop: lane q holds route q; a distinct expert's rank is the
+// number of set bits of s_bits (the routed experts) below its id, from an
+// exclusive prefix of the words' bit counts (lane w holding word w, E/32 <= 32
+// words). Lane 0 writes the expert (-1 if fewer than want+1 are routed) and
+// its route count.
+__device__ __forceinline__ void route_pick(const int* s_ids, const uint32_t* s_bits, int R, int E, int k, int want,
+                                           int* s_tok, int* s_slot, int& s_e, int& s_cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t bw = lane < ((E + 31) >> 5) ? s_bits[lane] : 0u;
+  int inc = __popc(bw);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  const int excl = inc - __popc(bw);
+  const int id = lane < R ? s_ids[lane] : 0;
+  const int before = __shfl(excl, id >> 5, 64);
+  const uint32_t word = (uint32_t)__shfl((int)bw, id >> 5, 64);
+  const int rank = before + __popc(word & ((1u << (id & 31)) - 1u));
+  const bool mine = lane < R && rank == want;
+  const uint64_t bm = __ballot(mine);
+  const int cnt = __popcll(bm);
+  const int e = cnt ? __shfl(id, __ffsll((unsigned long long)bm) - 1, 64) : -1;
+  if (mine) {
+    const int pos = __popcll(bm & ((1ull << lane) - 1ull));
+    const int t = lane / k;
+    s_tok[pos] = t;
+    s_slot[pos] = lane - t * k;
+  }
+  if (lane == 0) {
+    s_e = e;
+    s_cnt = cnt;
+  }
+}
+
 template <int CPW, int MAXR>
 __global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict__ x, const float* __restrict__ logits,
                                                      int T, int E, int k, int H, int I,
@@ -527,27 +565,7 @@ __global__ __launch_bounds__(512) void k_moe_a_small(const uint16_t* __restrict_
   __syncthreads();
   for (int r = tid; r < T * k; r += blockDim.x) atomicOr(&s_bits[s_ids[r] >> 5], 1u << (s_ids[r] & 31));
   __syncthreads();
-  if (tid == 0) {
-    // the blockIdx.y-th set bit, and the routes (ascending token) of that expert
-    int want = blockIdx.y, e = -1;
-    for (int q = 0; q < (E + 31) / 32 && e < 0; ++q) {
-      uint32_t b = s_bits[q];
-      const int c = __popc(b);
-      if (want < c) {
-        for (int i = 0; i < want; ++i) b &= b - 1u;
-        e = 32 * q + __ffs(b) - 1;
-      } else {
-        want -= c;
-      }
-    }
-    int cnt = 0;
-    if (e >= 0)
-      for (int t = 0; t < T; ++t)
-        for (int j = 0; j < k; ++j)
-          if (s_ids[t * k + j] == e) { s_tok[cnt] = t; s_slot[cnt] = j; ++cnt; }
-    s_e = e;
-    s_cnt = cnt;
-  }
+  if (wave == 0) route_pick(s_ids, s_bits, T * k, E, k, blockIdx.y, s_tok, s_slot, s_e, s_cnt);
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int r = tid; r < T * k; r += blockDim.x) {
       ws.ids[r] = s_ids[r];
@@ -654,6 +672,170 @@ __global__ __launch_bounds__(1024) void k_moe_b_token(int H, int I, int k, const
   store_out(y, (size_t)t * H + n, sum, y_bf16);
 }
 
+// The decode path in one launch (the persistent gate/up -> SwiGLU -> down
+// kernel of section 7 of the DBF post): every workgroup routes the T <= 4
+// tokens itself; workgroup (x, a) then does the gate/up work of
+// k_moe_a_small's workgroup (x, a) and, after a grid-wide wait, workgroup
+// number b = a * gridDim.x + x < (H/16) * T does the down work of
+// k_moe_b_token's workgroup (b % (H/16), b / (H/16)). The down weight words
+// are loaded right after routing, before the gate/up products, so the second
+// half issues no weight load after the wait. Arithmetic and sum orders are
+// those of the two-launch path (the same bits); the SwiGLU rows cross the
+// wait through the coherence point (gsync.h). WA waves do gate/up, k waves
+// (one per slot) do down.
+template <int CPW, int MAXR, int CPWB>
+__global__ __launch_bounds__(1024) void k_moe_fused_small(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ logits, int T, int E, int k,
+                                                          int H, int I, int WA, const uint4* __restrict__ gs,
+                                                          const uint16_t* __restrict__ gsc,
+                                                          const uint4* __restrict__ us,
+                                                          const uint16_t* __restrict__ usc,
+                                                          const uint4* __restrict__ ds,
+                                                          const uint16_t* __restrict__ dsc, MoeWs ws,
+                                                          int32_t* __restrict__ ids_user, float* __restrict__ w_user,
+                                                          void* __restrict__ y, int y_bf16, uint32_t* __restrict__ slot,
+                                                          uint32_t spin) {
+  extern __shared__ uint4 smem[];
+  __shared__ int s_ids[MOE_SMALL_T * 16];
+  __shared__ float s_w[MOE_SMALL_T * 16];
+  __shared__ uint32_t s_bits[MOE_MAX_E / 32];
+  __shared__ int s_tok[MOE_SMALL_T], s_slot[MOE_SMALL_T];
+  __shared__ int s_e, s_cnt;
+  const uint32_t epoch = grid_epoch(slot);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  // ---- routing of every token (as k_moe_a_small)
+  for (int i = tid; i < MOE_MAX_E / 32; i += blockDim.x) s_bits[i] = 0u;
+  for (int t = wave; t < T; t += nw) {
+    int id;
+    float w;
+    if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, id, w);
+    else wave_route<16>(logits + (size_t)t * E, E, k, id, w);
+    if (lane < k) {
+      s_ids[t * k + lane] = id;
+      s_w[t * k + lane] = w;
+    }
+  }
+  __syncthreads();
+  for (int q = tid; q < T * k; q += blockDim.x) atomicOr(&s_bits[s_ids[q] >> 5], 1u << (s_ids[q] & 31));
+  __syncthreads();
+  if (wave == 0) route_pick(s_ids, s_bits, T * k, E, k, blockIdx.y, s_tok, s_slot, s_e, s_cnt);
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int q = tid; q < T * k; q += blockDim.x) {
+      if (ids_user) ids_user[q] = s_ids[q];
+      if (w_user) w_user[q] = s_w[q];
+    }
+  }
+  __syncthreads();
+  // ---- down weight words of this workgroup's second half (wave = slot)
+  const int HB = (H + 15) / 16;
+  const int b2 = blockIdx.y * gridDim.x + blockIdx.x;
+  const bool do2 = b2 < HB * T;  // uniform per workgroup
+  const int t2 = do2 ? b2 / HB : 0;
+  const int n2 = (b2 - t2 * HB) * 16 + j;
+  const bool act2 = do2 && wave < k;  // uniform per wave
+  const int GI = I >> 7;
+  BPre<1, CPWB> bpd;
+  if (act2) {
+    const int e2 = s_ids[t2 * k + wave];
+    const bool rok = n2 < H;
+    const size_t row = (size_t)e2 * H + (rok ? n2 : 0);
+    const uint4* wsig[1] = {ds + row * GI};
+    const uint16_t* wsc[1] = {dsc + row * GI};
+    const bool rk[1] = {rok};
+    b_prefetch<BM_GROUP, 1, CPWB>(wsig, wsc, rk, GI, 0, 1, bpd);
+  }
+  // ---- gate/up of (16 intermediate columns, active expert), as k_moe_a_small
+  const int e = s_e, cnt = s_cnt;
+  const int n = blockIdx.x * 16 + j;
+  const int G = H >> 7, nchunks = (G + 3) >> 2;
+  const int c0 = wave * CPW;
+  const bool rok = n < I;
+  uint4* xw = smem + (size_t)wave * CPW * MAXR * 64;
+  f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)WA * CPW * MAXR * 64);
+  f32x4 acc[2][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}, {f32x4{0.f, 0.f, 0.f, 0.f}}};
+  if (e >= 0 && wave < WA && c0 < nchunks) {
+    const size_t row = (size_t)e * I + (rok ? n : 0);
+    const uint4* wsig[2] = {gs + row * G, us + row * G};
+    const uint16_t* wsc[2] = {gsc + row * G, usc + row * G};
+    const bool rk[2] = {rok, rok};
+    WaveStage<ST_BF16, CPW, MAXR> sx;
+    sx.load(cnt, H, c0, [&](int q) { return x + (size_t)s_tok[q] * H; });
+    BPre<2, CPW> bp;
+    b_prefetch<BM_GROUP, 2, CPW>(wsig, wsc, rk, G, c0, 1, bp);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    sx.store(xw);
+    const u32x4* xs = reinterpret_cast<const u32x4*>(xw);
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int m = min(j, cnt - 1);
+      return xs[(((g >> 2) - c0) * MAXR + m) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_GROUP, 2, 1, CPW, true>(bp, nullptr, G, c0, 1, aop, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[0][0][i] = __builtin_amdgcn_ldexpf(acc[0][0][i], sx.unscale(i));
+      acc[1][0][i] = __builtin_amdgcn_ldexpf(acc[1][0][i], sx.unscale(i));
+    }
+  }
+  const bool holds = 4 * kb < cnt;
+  if (e >= 0 && wave > 0 && wave < WA && holds) {
+    red[(2 * (wave - 1)) * 64 + lane] = acc[0][0];
+    red[(2 * (wave - 1) + 1) * 64 + lane] = acc[1][0];
+  }
+  __syncthreads();
+  if (e >= 0 && wave == 0 && holds && rok) {
+    for (int w = 1; w < WA; ++w) {
+      acc[0][0] += red[(2 * (w - 1)) * 64 + lane];
+      acc[1][0] += red[(2 * (w - 1) + 1) * 64 + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 4 * kb + i;
+      if (q < cnt) {
+        const float g = acc[0][0][i], uu = acc[1][0][i];
+        coh_storef(ws.ap + ((size_t)s_tok[q] * k + s_slot[q]) * I + n, g / (1.0f + expf(-g)) * uu);
+      }
+    }
+  }
+  // ---- every route's SwiGLU row is at the coherence point after this
+  const bool ok = grid_wait(slot, epoch, spin);
+  if (!do2) return;
+  if (!ok) {
+    if (wave == 0 && lane < 16 && n2 < H) store_out(y, (size_t)t2 * H + n2, __builtin_nanf(""), y_bf16);
+    return;
+  }
+  // ---- down of (16 hidden columns, token t2), one wave per slot, as k_moe_b_token
+  uint4* pw = smem + (size_t)wave * CPWB * 2 * 64;
+  float* part = reinterpret_cast<float*>(smem + (size_t)k * CPWB * 2 * 64);  // [k][16]
+  if (act2) {
+    const int r2 = t2 * k + wave;
+    f32x4 ad[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+    WaveStageF32<CPWB, 1> sa;
+    sa.template load<true>(1, I, 0, [&](int) { return ws.ap + (size_t)r2 * I; });
+    sa.store(pw);
+    const u32x4* xs = reinterpret_cast<const u32x4*>(pw);
+    auto aop = [&](int, int g, int i) -> u32x4 {
+      const int p = min(j, 1);
+      return xs[((g >> 2) * 2 + p) * 64 + (g & 3) * 16 + i];
+    };
+    b_compute<BM_GROUP, 1, 1, CPWB, true>(bpd, nullptr, GI, 0, 1, aop, ad);
+    if (kb == 0) part[wave * 16 + j] = __builtin_amdgcn_ldexpf(ad[0][0][0] + ad[0][0][1], sa.unscale(0));
+  }
+  __syncthreads();
+  if (wave != 0 || kb != 0 || n2 >= H) return;
+  float sum = 0.f;
+  for (int q = 0; q < k; ++q) sum = fmaf(s_w[t2 * k + q], part[q * 16 + j], sum);
+  store_out(y, (size_t)t2 * H + n2, sum, y_bf16);
+}
+
+// Single-launch layers: on when the caller asked for them (mode 2); by
+// default (mode 0) off: two graph launches measured as fast or faster on this
+// chip (the grid-wide wait costs about what the kernel boundary does).
+static bool moe_fusion_wanted(int T) {
+  (void)T;
+  return fusion_mode() == 2;
+}
+
 // The decode path applies when the per-wave staging of both launches fits.
 static bool moe_small_path(int T, int H, int I, int k, DecSplit& sa, int& maxr, int& cpwb) {
   if (T > MOE_SMALL_T) return false;
@@ -676,6 +858,60 @@ static int moe_tile_rows(const DecSplit& sp, int T, int E, int k) {
   return (r > 4 && (int64_t)T * k <= 3 * (int64_t)E) ? 4 : r;
 }
 
+using MoeFusedFn = void (*)(const uint16_t*, const float*, int, int, int, int, int, int, const uint4*,
+                           const uint16_t*, const uint4*, const uint16_t*, const uint4*, const uint16_t*, MoeWs,
+                           int32_t*, float*, void*, int, uint32_t*, uint32_t);
+template <int C, int MR>
+static MoeFusedFn moe_fused_fn_cb(int cpwb) {
+  switch (cpwb) {
+    case 1: return &k_moe_fused_small<C, MR, 1>;
+    case 2: return &k_moe_fused_small<C, MR, 2>;
+    case 3: return &k_moe_fused_small<C, MR, 3>;
+    default: return &k_moe_fused_small<C, MR, 4>;
+  }
+}
+template <int C>
+static MoeFusedFn moe_fused_fn_mr(int maxr, int cpwb) {
+  return maxr == 1 ? moe_fused_fn_cb<C, 1>(cpwb) : maxr == 2 ? moe_fused_fn_cb<C, 2>(cpwb) : moe_fused_fn_cb<C, 4>(cpwb);
+}
+static MoeFusedFn moe_fused_fn(int cpw, int maxr, int cpwb) {
+  return cpw == 1 ? moe_fused_fn_mr<1>(maxr, cpwb) : moe_fused_fn_mr<2>(maxr, cpwb);
+}
+
+// Single-launch decode layer: taken when the caller asked for it (or the
+// library's default does) and every workgroup fits the device at once.
+// Returns false when not taken.
+static bool moe_fused(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k, int maxact,
+                      const DecSplit& sa, int maxr, int cpwb, const uint64_t* gate_s, const uint16_t* gate_sc,
+                      const uint64_t* up_s, const uint16_t* up_sc, const uint64_t* down_s, const uint16_t* down_sc,
+                      void* y, int y_bf16, int32_t* ids, float* w, const MoeWs& ws, hipStream_t st,
+                      hipError_t& err) {
+  if (!moe_fusion_wanted(T)) return false;
+  const int waves = sa.waves > k ? sa.waves : k;
+  const int gx = (I + 15) / 16, hb = (H + 15) / 16;
+  int gy = maxact;
+  if ((int64_t)gx * gy < (int64_t)hb * T) gy = (int)(((int64_t)hb * T + gx - 1) / gx);
+  const size_t la = (size_t)sa.waves * sa.cpw * maxr * 1024 + (size_t)(sa.waves - 1) * 2 * 64 * 16;
+  const size_t lb = (size_t)k * cpwb * 2 * 1024 + (size_t)k * 16 * 4;
+  const size_t lds = la > lb ? la : lb;
+  // instantiated for 1 or 2 chunks per gate/up wave (H <= 8192), 1, 2 or 4
+  // staged token rows and 1 .. 4 down chunks (I <= 2048)
+  if (sa.cpw > 2 || maxr > 4 || cpwb > 4) return false;
+  MoeFusedFn fn = moe_fused_fn(sa.cpw, maxr, cpwb);
+  if (!grid_fits(reinterpret_cast<const void*>(fn), 64 * waves, lds, (int64_t)gx * gy)) return false;
+  uint32_t* slot = nullptr;
+  err = grid_slot(&slot);
+  if (err != hipSuccess) return true;
+  const uint32_t spin = grid_spin_limit();
+  const uint4* g4 = reinterpret_cast<const uint4*>(gate_s);
+  const uint4* u4 = reinterpret_cast<const uint4*>(up_s);
+  const uint4* d4 = reinterpret_cast<const uint4*>(down_s);
+  hipLaunchKernelGGL(fn, dim3(gx, gy), dim3(64 * waves), lds, st, x, logits, T, E, k, H, I, sa.waves, g4, gate_sc, u4,
+                     up_sc, d4, down_sc, ws, ids, w, y, y_bf16, slot, spin);
+  err = hipGetLastError();
+  return true;
+}
+
 hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int I, int E, int top_k,
                       const uint64_t* gate_s, const uint16_t* gate_sc, const uint64_t* up_s,
                       const uint16_t* up_sc, const uint64_t* down_s, const uint16_t* down_sc, void* y,
@@ -686,6 +922,10 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
     DecSplit sa;
     int maxr, cpwb;
     if (moe_small_path(T, H, I, top_k, sa, maxr, cpwb)) {
+      hipError_t fe = hipSuccess;
+      if (moe_fused(x, logits, T, H, I, E, top_k, maxact, sa, maxr, cpwb, gate_s, gate_sc, up_s, up_sc, down_s,
+                    down_sc, y, y_bf16, ids, w, ws, st, fe))
+        return fe;
       const size_t la = (size_t)sa.waves * sa.cpw * maxr * 1024 + (size_t)(sa.waves - 1) * 2 * 64 * 16;
       const dim3 ga((I + 15) / 16, maxact), ba(64 * sa.waves);
       const uint4* g4 = reinterpret_cast<const uint4*>(gate_s);

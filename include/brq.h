@@ -4,8 +4,11 @@
  * C ABI of libbrq.so. Every pointer argument named as device memory must be a
  * device (or device-accessible) pointer; every call enqueues its kernels on
  * `stream` (a hipStream_t passed as void*, NULL = the null stream) and returns
- * without synchronising the host. The library keeps no device memory of its
- * own: buffers and workspaces are owned by the caller. A call that returns a
+ * without synchronising the host. Buffers and workspaces are owned by the
+ * caller; the library's own device memory is two arrays that every GPU it runs
+ * on holds until the process ends: the scratch of brq_moe_ffn_noalloc
+ * (BRQ_NOALLOC_SCRATCH_BYTES) and the wait counters of the single-launch
+ * chains (brq_set_decode_fusion, 272 KiB). A call that returns a
  * status other than BRQ_OK has enqueued nothing and written nothing, except
  * BRQ_E_HIP, which reports a failed launch.
  *
@@ -86,6 +89,35 @@ const char* brq_status_str(brq_status s);
 /* Text describing the last non-OK status returned on the calling thread
    ("" if none). Valid until the next brq_* call on the same thread. */
 const char* brq_last_error(void);
+
+/*
+ * brq_set_decode_fusion -- single-launch decode chains ("LLM binarization,
+ * Episode 01: DBF", section 7: a joint V - D_mid - U kernel with one grid-wide
+ * synchronisation between the products, and a persistent MoE kernel running
+ * gate/up, SwiGLU and down in one launch). brq_dbf_gemm with M <= 8 and
+ * brq_moe_ffn / brq_moe_ffn_noalloc with T <= 4 can each run as one launch
+ * whose workgroups (all resident on the device at once) wait for one another
+ * once, instead of two launches. The result bits are the same either way.
+ *
+ *   mode        BRQ_FUSION_DEFAULT: the library's choice per path, the one
+ *               that measured faster on MI355X (today the multi-launch path
+ *               everywhere: the grid-wide wait costs about what a kernel
+ *               boundary inside a HIP graph does); BRQ_FUSION_OFF: always the
+ *               multi-launch path; BRQ_FUSION_ON: one launch wherever all its
+ *               workgroups fit the device at once.
+ *   spin_limit  polls of the grid-wide wait before a workgroup gives up (0:
+ *               the default, 2^22, about a second); a wait that gives up
+ *               writes NaN to the outputs that workgroup owns. It ends only
+ *               when the device cannot run all workgroups of the launch at
+ *               once (see below).
+ * Process-wide; applies to calls issued after it returns. A single-launch
+ * chain needs all its workgroups resident at once: a caller that runs two of
+ * them concurrently on one device (two streams), or one beside a kernel that
+ * holds compute units until it ends, can see that wait give up.
+ * BRQ_E_SHAPE for an unknown mode.
+ */
+typedef enum { BRQ_FUSION_DEFAULT = 0, BRQ_FUSION_OFF = 1, BRQ_FUSION_ON = 2 } brq_fusion;
+brq_status brq_set_decode_fusion(brq_fusion mode, uint32_t spin_limit);
 
 /* Number of uint64_t words of a SIGN1 plane of rows x cols (cols % 64 == 0). */
 size_t brq_sign_words(int64_t rows, int64_t cols);

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(brq.ABI_FUNCTIONS)
@@ -40,6 +40,18 @@ def test_version_and_status_strings(L):
     assert L.brq_status_str(E_SHAPE) == b"BRQ_E_SHAPE"
     assert L.brq_status_str(OK) == b"BRQ_OK"
     assert L.brq_status_str(99) == b"BRQ_E_UNKNOWN"
+
+
+def test_decode_fusion_setting(L):
+    """brq_set_decode_fusion takes the three modes (host state only, no device
+    call) and rejects any other value with BRQ_E_SHAPE."""
+    for mode in (1, 2, 0):
+        assert L.brq_set_decode_fusion(mode, 0) == OK
+    assert L.brq_set_decode_fusion(2, 1000) == OK
+    assert L.brq_set_decode_fusion(0, 0) == OK
+    assert L.brq_set_decode_fusion(3, 0) == E_SHAPE
+    assert b"unknown mode" in L.brq_last_error()
+    assert L.brq_set_decode_fusion(-1, 0) == E_SHAPE
 
 
 def test_size_queries(L):

@@ -1,0 +1,220 @@
+"""GPU: the single-launch decode chains (brq_set_decode_fusion) against the
+multi-launch paths and the fp64 oracle.
+
+The one-launch DBF chain (M <= 8) and MoE layer (T <= 4) run the stage bodies
+and sum orders of the multi-launch kernels, so their outputs and routing must
+be the same bits; they are also checked against the oracle directly. The
+bounded grid-wide wait is exercised from the host with a spin limit of one
+poll: every workgroup then either finds the others arrived or gives up and
+writes NaN, and each kernel still ends normally.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_util import check_f32, dev, f64, host_bits
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 2e-5
+
+
+def brq():
+    import binary_weight_gemm_amd as b
+    return b
+
+
+def say(*a):
+    import sys
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _default_fusion():
+    yield
+    brq().set_decode_fusion(brq().FUSION_DEFAULT)
+
+
+def _dbf_inputs(M, m, n, r, key):
+    v = datagen.pm1_f32((91, key, 0), (r, n))
+    u = datagen.pm1_f32((91, key, 1), (m, r))
+    d_in = datagen.f16_lognormal((91, key, 2), (n,))
+    d_mid = datagen.f16_lognormal((91, key, 3), (r,))
+    d_out = datagen.f16_lognormal((91, key, 4), (m,))
+    x = datagen.bf16_normal((91, key, 5), (M, n))
+    return x, d_in, oracle.pack_sign1_only(v), d_mid, oracle.pack_sign1_only(u), d_out
+
+
+def _dbf_run(args, m, n, r, mode, out):
+    b = brq()
+    b.set_decode_fusion(mode)
+    x, d_in, vw, d_mid, uw, d_out = args
+    y = b.dbf_gemm(dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r, out_dtype=out)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (1, 48, 256, 384), (3, 200, 512, 256), (8, 130, 1024, 512),
+                                     (1, 4096, 4096, 2048), (4, 4000, 4096, 2048), (1, 4096, 4096, 4096)])
+def test_dbf_one_launch_same_bits(M, m, n, r):
+    say("dbf one launch", M, m, n, r)
+    args = _dbf_inputs(M, m, n, r, M + m + n + r)
+    o = oracle.dbf_chain(oracle.bf16_to_f64(args[0]), args[1], args[2], args[3], args[4], args[5], m, n, r)
+    for out in (torch.float32, torch.bfloat16):
+        y_on = _dbf_run(args, m, n, r, brq().FUSION_ON, out)
+        y_off = _dbf_run(args, m, n, r, brq().FUSION_OFF, out)
+        assert np.array_equal(host_bits(y_on), host_bits(y_off)), f"one launch != two launches ({out})"
+    y32 = _dbf_run(args, m, n, r, brq().FUSION_ON, torch.float32)
+    check_f32(f64(y32), o, F32_TOL, f"dbf one launch {M},{m},{n},{r}")
+
+
+class _DevExperts:
+    """Group-128 experts as device tensors: random sign words and fp16
+    lognormal scales drawn directly (no fp32 weights), for geometries whose
+    full expert set the oracle would take too long to pack."""
+
+    def __init__(self, E, H, I, key):
+        self.E, self.H, self.I = E, H, I
+        self.d = [dev(datagen.sign_words((92, key, 0), E * I, H)), dev(datagen.f16_lognormal((92, key, 1), (E * I * H // 128,))),
+                  dev(datagen.sign_words((92, key, 2), E * I, H)), dev(datagen.f16_lognormal((92, key, 3), (E * I * H // 128,))),
+                  dev(datagen.sign_words((92, key, 4), E * H, I)), dev(datagen.f16_lognormal((92, key, 5), (E * H * I // 128,)))]
+
+
+def _moe_run(ex, x, lg, k, mode, out):
+    b = brq()
+    b.set_decode_fusion(mode)
+    c = getattr(ex, "cfg", ex)
+    y, ids, w = b.moe_ffn(dev(x), dev(lg), *ex.d, c.E, c.H, c.I, k, out_dtype=out, return_routing=True)
+    torch.cuda.synchronize()
+    return host_bits(y), ids.cpu().numpy(), w.cpu().numpy().view(np.uint32)
+
+
+@pytest.fixture(scope="module")
+def c4_experts():
+    from test_gpu_parity import _Experts
+    return _Experts(datagen.C4())
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_moe_one_launch_c4(c4_experts, T):
+    say("moe one launch C4", T)
+    ex = c4_experts
+    cfg = ex.cfg
+    x, lg = cfg.x(T), cfg.logits(T, 3)
+    o, oids, ow = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, cfg.top_k)
+    for out in (torch.float32, torch.bfloat16):
+        on = _moe_run(ex, x, lg, cfg.top_k, brq().FUSION_ON, out)
+        off = _moe_run(ex, x, lg, cfg.top_k, brq().FUSION_OFF, out)
+        for a, b_, what in zip(on, off, ("y", "ids", "w")):
+            assert np.array_equal(a, b_), f"one launch != two launches: {what} ({out})"
+    brq().set_decode_fusion(brq().FUSION_ON)
+    y, ids, w = brq().moe_ffn(dev(x), dev(lg), *ex.d, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32,
+                              return_routing=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=1e-7)
+    check_f32(f64(y), o, F32_TOL, f"moe one launch T={T}")
+
+
+# the named geometries at T = 1 and 4 (I = 1408 has 11 groups: three down
+# chunks per slot; H = 3072 six gate/up waves). Where the one-launch grid does
+# not fit the device at once (T = 4 here) or the layer's down staging exceeds
+# the decode budget (I = 2048), both settings take the multi-launch path.
+@pytest.mark.parametrize("name", ["GLM-4.5-Air", "MiniMax-M2.5", "DeepSeek-V4-Flash"])
+@pytest.mark.parametrize("T", [1, 4])
+def test_moe_one_launch_named_geometries(name, T):
+    g = datagen.MOE_GEOMETRIES[name]
+    say("moe one launch", name, T)
+    ex = _DevExperts(g["E"], g["H"], g["I"], sorted(datagen.MOE_GEOMETRIES).index(name))
+    x = datagen.bf16_normal((93, T), (T, g["H"]))
+    lg = datagen.router_logits((94, T), T, g["E"])
+    for out in (torch.float32, torch.bfloat16):
+        on = _moe_run(ex, x, lg, 8, brq().FUSION_ON, out)
+        off = _moe_run(ex, x, lg, 8, brq().FUSION_OFF, out)
+        for a, b_, what in zip(on, off, ("y", "ids", "w")):
+            assert np.array_equal(a, b_), f"{name} T={T}: one launch != two launches: {what} ({out})"
+        if out == torch.float32:
+            assert np.isfinite(on[0].view(np.float32)).all()
+
+
+def test_one_launch_wait_guard():
+    """Spin limit of one poll: every workgroup either sees the wait released
+    or gives up and writes NaN over its own outputs; every other output keeps
+    the two-launch bits, the kernels end, and the next default call is
+    unaffected (the wait slots stay consistent)."""
+    say("one launch wait guard")
+    b = brq()
+    M, m, n, r = 1, 4096, 4096, 2048
+    args = _dbf_inputs(M, m, n, r, 7)
+    ref = host_bits(_dbf_run(args, m, n, r, b.FUSION_OFF, torch.float32)).view(np.float32)
+    b.set_decode_fusion(b.FUSION_ON, 1)
+    x, d_in, vw, d_mid, uw, d_out = args
+    y = b.dbf_gemm(dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    g = host_bits(y).view(np.float32)
+    nan = np.isnan(g)
+    assert np.array_equal(g[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    # NaN only in whole 16-column blocks (one workgroup's outputs)
+    assert np.array_equal(nan.reshape(M, -1, 16).all(axis=2), nan.reshape(M, -1, 16).any(axis=2))
+    from test_gpu_parity import _Experts
+    ex = _Experts(datagen.C4(E=16, H=256, I=128, top_k=4, layer=3))
+    xm, lgm = ex.cfg.x(1), ex.cfg.logits(1)
+    refm = _moe_run(ex, xm, lgm, 4, b.FUSION_OFF, torch.float32)
+    b.set_decode_fusion(b.FUSION_ON, 1)
+    ym = b.moe_ffn(dev(xm), dev(lgm), *ex.d, 16, 256, 128, 4, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gm = host_bits(ym).view(np.float32)
+    nm = np.isnan(gm)
+    assert np.array_equal(gm[~nm].view(np.uint32), refm[0].view(np.float32)[~nm].view(np.uint32))
+    # default settings again: the same slots serve correct launches
+    b.set_decode_fusion(b.FUSION_ON)
+    y2 = _dbf_run(args, m, n, r, b.FUSION_ON, torch.float32)
+    assert np.array_equal(host_bits(y2).view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(_moe_run(ex, xm, lgm, 4, b.FUSION_ON, torch.float32)[0], refm[0])
+
+
+def test_one_launch_graph_replay():
+    """The one-launch chains captured in a HIP graph and replayed three times,
+    with eager work between replays: every replay gives the eager bits."""
+    say("one launch graph replay")
+    b = brq()
+    b.set_decode_fusion(b.FUSION_ON)
+    M, m, n, r = 1, 4096, 4096, 2048
+    x, d_in, vw, d_mid, uw, d_out = (dev(a) for a in _dbf_inputs(M, m, n, r, 8))
+    from test_gpu_parity import _Experts
+    ex = _Experts(datagen.C4(E=16, H=256, I=128, top_k=4, layer=4))
+    xm, lgm = dev(ex.cfg.x(1)), dev(ex.cfg.logits(1))
+    ws_d = torch.empty(b.dbf_workspace_bytes(M, m, n, r), dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(b.moe_workspace_bytes(1, 256, 128, 16, 4), dtype=torch.uint8, device="cuda")
+    yd = torch.empty((M, m), dtype=torch.float32, device="cuda")
+    ym = torch.empty((1, 256), dtype=torch.float32, device="cuda")
+
+    def run():
+        b.dbf_gemm(x, d_in, vw, d_mid, uw, d_out, m, n, r, out_dtype=torch.float32, y=yd, ws=ws_d)
+        b.moe_ffn(xm, lgm, *ex.d, 16, 256, 128, 4, out_dtype=torch.float32, y=ym, ws=ws_m)
+
+    run()
+    torch.cuda.synchronize()
+    ref_d, ref_m = host_bits(yd), host_bits(ym)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for it in range(3):
+        yd.fill_(float("nan"))
+        ym.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(yd), ref_d), f"dbf replay {it}"
+        assert np.array_equal(host_bits(ym), ref_m), f"moe replay {it}"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+    del g
