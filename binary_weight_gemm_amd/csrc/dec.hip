@@ -206,13 +206,17 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 // significand shifted into a 24-bit field (bits shifted out below are
 // dropped: less than 2^-23 of the slice maximum), and the six 4-bit digits of
 // X (most significant first) go to A rows 0..5 as sign-magnitude e4m3 codes.
+// X is formed as the truncating fp32 -> u32 conversion of |x| * 2^(150 - ebs)
+// (exact: a power-of-two scaling of a bf16 value, below 2^24), the same
+// integer as shifting the 8-bit significand right by ebs - e.
 // An e4m3 code c in 0..15 is the value c * 2^-9 (subnormals and the first
 // normal binade), so the code of a digit is the digit itself plus the sign
 // bit. Row p carries block exponent ebs - 2 - 4p and the weights 135, which
 // puts row p's product at 6 * sum(+-digit_p) * 2^(ebs - 130 - 4p): integers
-// times one power of two, exact in fp32. Rows 6..15 repeat row 5 and are not
-// used. One MFMA covers one scale group of 16 columns; the group scale and
-// the 1/6 are applied in fp32 afterwards.
+// times one power of two, exact in fp32. Rows 6..15 read an all-zero LDS row,
+// so every lane simply adds its four output rows. One MFMA covers one scale
+// group of 16 columns; the group scale and the 1/6 are applied in fp32
+// afterwards.
 //
 // Layout facts of that MFMA (fp8 A, fp4 B): A lane l supplies row l%16 with
 // bytes 0..15 = k 16*(l/16).. and bytes 16..31 = k 64+16*(l/16)..; B lane l
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_lds(const uint16_t* __restric
 // word kb of group i.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int F4_DIGITS = 6;
-constexpr int F4_GROUP = F4_DIGITS * 128;  // LDS bytes of one group: six digit rows of 128 codes
+constexpr int F4_GROUP = (F4_DIGITS + 1) * 128;  // LDS bytes of one group: six digit rows of 128 codes, a zero row
 constexpr int F4_CHUNK = 4 * F4_GROUP;     // LDS bytes of one chunk of four groups
 
 // (group, word) transpose across the four 16-lane rows: on entry register w
@@ -261,7 +265,6 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
     uint4 xv[CPW];
     uint4 sg[NT][CPW];
     uint2 sc[NT][CPW];
-    bool cok[NT];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int k0 = (c0 + c) * 512 + 8 * lane;
@@ -271,7 +274,6 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int n = (blockIdx.x * NT + t) * 16 + j;
-      cok[t] = n < N;
       row[t] = (size_t)(n < N ? n : 0) * G;
     }
 #pragma unroll
@@ -295,6 +297,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
     // at least 24, so that a zero (or bf16 subnormal, dropped: below 2^-126)
     // shifts its implicit bit out of the field entirely
     const uint32_t ebs = max(mx >> 7, 24u);
+    const float S = __uint_as_float((277u - ebs) << 23);  // 2^(150 - ebs), a normal fp32 for ebs in 24..254
     // ---- digit codes in the operand order: lane L's 8 values are k = 8L .. 8L+7
     // of the chunk (group L/16, word (L%16)/4); value e lands at in-word
     // position 8*(e%4) + 2*(L%4) + e/4 of each digit row
@@ -304,13 +307,15 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
       uint32_t lo[8], hi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t wp = (e & 1) ? w4[e >> 1] : (w4[e >> 1] << 16);  // the bf16 in bits 16..31
-        const uint32_t sh = min(ebs - ((wp >> 23) & 0xffu), 31u);
-        const uint32_t X = ((wp & 0x7f0000u) | 0x800000u) >> sh;          // 24-bit magnitude field
+        const uint32_t wp = (e & 1) ? (w4[e >> 1] & 0xffff0000u) : (w4[e >> 1] << 16);  // the bf16 as fp32
+        const uint32_t X = (uint32_t)(fabsf(__uint_as_float(wp)) * S);  // 24-bit magnitude field
         const uint32_t sr = (wp >> 31) * 0x808080u;                        // sign bit of each code byte
         lo[e] = (X & 0x0f0f0fu) | sr;         // nibbles 0, 2, 4 -> bytes 0, 1, 2
         hi[e] = ((X >> 4) & 0x0f0f0fu) | sr;  // nibbles 1, 3, 5 -> bytes 0, 1, 2
       }
+      if (lane < 32)  // the zero row of each group: 16 bytes per lane
+        *reinterpret_cast<uint4*>(xw + c * F4_CHUNK + (lane >> 3) * F4_GROUP + F4_DIGITS * 128 + 16 * (lane & 7)) =
+            make_uint4(0u, 0u, 0u, 0u);
       uint8_t* base = xw + c * F4_CHUNK + (lane >> 4) * F4_GROUP + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
         put(5, h5);
       }
     }
-    const int prow = j < F4_DIGITS ? j : F4_DIGITS - 1;
+    const int prow = j < F4_DIGITS ? j : F4_DIGITS;  // lanes 6..15 read the zero row
     const int sa = (int)ebs - 2 - 4 * prow;
     // ---- products
 #pragma unroll
@@ -357,11 +362,10 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
           B[4] = 0; B[5] = 0; B[6] = 0; B[7] = 0;
           const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
                                                                            sa, 0, 135);
-          const bool ok = cok[t] && (4 * (c0 + c) + i < G);
-          const float s = ok ? f16_bits_to_f32(s4[i]) : 0.f;
-          // lanes 0..15 hold digit rows 0..3 of column j, lanes 16..31 rows 4..7
-          const float part = kb == 0 ? (d[0] + d[1]) + (d[2] + d[3]) : kb == 1 ? d[0] + d[1] : 0.f;
-          acc[t] = fmaf(s, part, acc[t]);
+          // K % 512 == 0: every group of the chunk exists; columns past N read
+          // row 0 (finite) and are never stored. Lanes 0..15 hold digit rows
+          // 0..3 of column j, lanes 16..31 rows 4..7 (6, 7 zero), the rest zeros.
+          acc[t] = fmaf(f16_bits_to_f32(s4[i]), (d[0] + d[1]) + (d[2] + d[3]), acc[t]);
         }
       }
     }
@@ -433,7 +437,7 @@ static void gemm_dec_lds(const uint16_t* x, int M, int N, int K, const uint4* s4
 
 // The fp8 x fp4 path takes M = 1 when the scale groups come in whole chunks
 // of four (K % 512 == 0) and the digit rows of the workgroup's slices fit the
-// LDS (K <= 26624: up to 52 chunks); longer rows take the fp16 one-launch
+// LDS (K <= 23040: up to 45 chunks of 3.5 KiB); longer rows take the fp16 one-launch
 // path. Two column tiles per workgroup when that still leaves well over one
 // workgroup per compute unit (the activation digits are then shared by both
 // tiles). One chunk per wave up to 16 waves (the less a wave computes after

@@ -34,7 +34,7 @@
  * accumulates in fp32. Activations are carried as fp16 inside the products;
  * bf16 activations must satisfy |x| < 65504 (values below 2^-14 are kept on
  * fp16's subnormal grid, an absolute change of at most 2^-25). The one
- * exception is brq_gemm with M = 1 and K % 512 == 0 (K <= 26624), which runs
+ * exception is brq_gemm with M = 1 and K % 512 == 0 (K <= 23040), which runs
  * on the fp8 x fp4 matrix cores: there each activation is a 24-bit
  * fixed-point field under the largest power of two of its slice of the row
  * (a change of less than 2^-23 of that slice's maximum; bf16 subnormals count

@@ -113,14 +113,15 @@ def _gemm_case(M, N, K, key, out=torch.float32):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (1, 40, 640), (3, 48, 1024), (16, 33, 256), (17, 64, 512),
                                    (64, 32, 2048), (5, 16, 14336), (1, 1024, 1024), (9, 16, 128),
-                                   (33, 130, 4480), (40, 2000, 3200), (20, 32768, 512), (64, 4100, 1280)])
+                                   (33, 130, 4480), (40, 2000, 3200), (20, 32768, 512), (64, 4100, 1280),
+                                   (1, 48, 23552)])
 def test_gemm_decode_f32(M, N, K):
     say("gemm decode f32", M, N, K)
     y, o = _gemm_case(M, N, K, M * 1000 + N)
     check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("N,K", [(40, 512), (1000, 1536), (2049, 4096)])
+@pytest.mark.parametrize("N,K", [(40, 512), (1000, 1536), (2049, 4096), (48, 23040)])
 def test_gemm_single_row_wide_range(N, K):
     """A single activation row with K % 512 == 0 runs on the fp8 x fp4 matrix
     cores with the activations as fixed-point digit rows: ragged column tiles,
@@ -129,7 +130,9 @@ def test_gemm_single_row_wide_range(N, K):
     the largest of 8 products; the digit rows keep every product an integer
     times one power of two, so nothing is truncated and each output is held to
     the fp32 bar and, element by element, to the bound single_row_bound
-    derives from the representation."""
+    derives from the representation. K = 23040 is the longest row the digit
+    rows fit the LDS for (45 chunks, three per wave); 23552 takes the fp16
+    one-launch path (test_gemm_decode_f32)."""
     say("gemm single row, wide range", N, K)
     w = datagen.normal_f32((73, N, K), (N, K), 0.02)
     ow, osc = oracle.pack_sign1(w)
