@@ -55,12 +55,50 @@ def _link(objs, out):
     shutil.move(tmp, out)
 
 
+#: the host layer (argument checks, status and error text, per-device state)
+#: built again with AddressSanitizer and UndefinedBehaviorSanitizer on its
+#: host code only (device code is unchanged), linked with the other objects
+#: into a library of its own that a CPU test loads with the sanitizer runtime
+#: preloaded; never loaded by the product
+SAN_SOURCES = ["abi.hip", "noalloc.hip", "gsync.hip"]
+SAN_LIB = os.path.join(BUILD, "libbrq_hostsan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the compiler hipcc uses."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang++")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def _compile_san(src: str) -> str:
+    obj = os.path.join(BUILD, "san_" + os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (host sanitizers) failed for {src}:\n{r.stderr}")
+    return obj
+
+
 def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES + REF_SOURCES))
+        futs = [ex.submit(_compile, s) for s in SOURCES + REF_SOURCES]
+        sans = [ex.submit(_compile_san, s) for s in SAN_SOURCES]
+        objs = [f.result() for f in futs]
+        san_objs = [f.result() for f in sans]
     _link(objs[:len(SOURCES)], LIB)
     _link(objs[len(SOURCES):], REF_LIB)
+    plain = [o for o, s in zip(objs[:len(SOURCES)], SOURCES) if s not in SAN_SOURCES]
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-shared-libsan", "-o", tmp, *san_objs, *plain]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (host sanitizers) failed:\n{r.stderr}")
+    shutil.move(tmp, SAN_LIB)
     return LIB
 
 

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -40,7 +41,20 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every index inside 32-bi
 std::mutex g_dev_mu;
 int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
 
+// launch-failure injection (brq_debug_fail_launches): calls still to fail
+std::atomic<int> g_inject{0};
+
+bool take_injected() {
+  int n = g_inject.load(std::memory_order_relaxed);
+  while (n > 0)
+    if (g_inject.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) return true;
+  return false;
+}
+
+// Every entry point calls this after its arguments passed and right before it
+// enqueues anything.
 brq_status check_device() {
+  if (take_injected()) return fail(BRQ_E_HIP, "injected launch failure (brq_debug_fail_launches)");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
@@ -70,7 +84,21 @@ brq_status hip_result(hipError_t e, const char* what) {
   return ok();
 }
 
-bool dtype_ok(brq_dtype d) { return d == BRQ_BF16 || d == BRQ_F32; }
+// An enum argument from a C caller can hold any int; reading it as the C++
+// enum type is only defined for the enumerators' range, so the raw value is
+// taken from the argument's bytes and checked as an int.
+template <class E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool dtype_ok(const brq_dtype& d) {
+  const int v = enum_value(d);
+  return v == BRQ_BF16 || v == BRQ_F32;
+}
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K) {
   if (M <= 64) return brq::gemm_dec_ws_bytes(M, N, K);
@@ -90,7 +118,7 @@ extern "C" {
 int brq_abi_version(void) { return BRQ_ABI_VERSION; }
 
 const char* brq_status_str(brq_status s) {
-  switch (s) {
+  switch (enum_value(s)) {
     case BRQ_OK: return "BRQ_OK";
     case BRQ_E_NULL: return "BRQ_E_NULL";
     case BRQ_E_SHAPE: return "BRQ_E_SHAPE";
@@ -105,10 +133,17 @@ const char* brq_status_str(brq_status s) {
 
 const char* brq_last_error(void) { return g_last_error.c_str(); }
 
+brq_status brq_debug_fail_launches(int32_t count) {
+  if (count < 0) return fail(BRQ_E_SHAPE, "brq_debug_fail_launches: count %d < 0", (int)count);
+  g_inject.store(count, std::memory_order_relaxed);
+  return ok();
+}
+
 brq_status brq_set_decode_fusion(brq_fusion mode, uint32_t spin_limit) {
-  if (mode != BRQ_FUSION_DEFAULT && mode != BRQ_FUSION_OFF && mode != BRQ_FUSION_ON)
-    return fail(BRQ_E_SHAPE, "brq_set_decode_fusion: unknown mode %d", (int)mode);
-  brq::set_fusion((int)mode, spin_limit);
+  const int m = enum_value(mode);
+  if (m != BRQ_FUSION_DEFAULT && m != BRQ_FUSION_OFF && m != BRQ_FUSION_ON)
+    return fail(BRQ_E_SHAPE, "brq_set_decode_fusion: unknown mode %d", m);
+  brq::set_fusion(m, spin_limit);
   return ok();
 }
 
@@ -149,7 +184,7 @@ brq_status brq_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K, const ui
     return fail(BRQ_E_SHAPE, "brq_gemm: M=%lld N=%lld out of range", (long long)M, (long long)N);
   if (K < 128 || K > kMaxDim || K % 128)
     return fail(BRQ_E_SHAPE, "brq_gemm: K=%lld must be a positive multiple of 128", (long long)K);
-  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm: unknown y_dtype %d", enum_value(y_dtype));
   if (!aligned(x, 16) || !aligned(signs, 16) || !aligned(scales, 16) || !aligned(y, 16))
     return fail(BRQ_E_ALIGN, "brq_gemm: x, signs, scales and y must be 16-byte aligned");
   const size_t need = gemm_ws(M, N, K);
@@ -179,7 +214,7 @@ brq_status brq_gemm_lr(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
   if (K < 128 || K > kMaxDim || K % 128)
     return fail(BRQ_E_SHAPE, "brq_gemm_lr: K=%lld must be a positive multiple of 128", (long long)K);
   if (r < 1 || r > 64) return fail(BRQ_E_SHAPE, "brq_gemm_lr: rank r=%lld must be in 1..64", (long long)r);
-  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm_lr: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_gemm_lr: unknown y_dtype %d", enum_value(y_dtype));
   if (!aligned(x, 16) || !aligned(signs, 16) || !aligned(scales, 16) || !aligned(y, 16) || !aligned(v, 2) ||
       !aligned(u, 2))
     return fail(BRQ_E_ALIGN, "brq_gemm_lr: x, signs, scales and y must be 16-byte aligned, v and u 2-byte");
@@ -209,7 +244,7 @@ brq_status brq_dbf_gemm(const uint16_t* x, int64_t M, int64_t m, int64_t n, int6
   if (n < 128 || r < 128 || n > kMaxDim || r > kMaxDim || n % 128 || r % 128)
     return fail(BRQ_E_SHAPE, "brq_dbf_gemm: n=%lld and r=%lld must be positive multiples of 128", (long long)n,
                 (long long)r);
-  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm: unknown y_dtype %d", enum_value(y_dtype));
   if (!aligned(x, 16) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, 16) || !aligned(d_in, 16) ||
       !aligned(d_mid, 2) || !aligned(d_out, 2))
     return fail(BRQ_E_ALIGN, "brq_dbf_gemm: x, v, u, y and d_in must be 16-byte aligned");
@@ -249,7 +284,7 @@ brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, i
   if (((M + 127) / 128) * ((wide + 127) / 128) > (int64_t)INT32_MAX)
     return fail(BRQ_E_SHAPE, "brq_dbf_gemm_q8: M=%lld with max(m, r)=%lld needs more than 2^31 tiles", (long long)M,
                 (long long)wide);
-  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm_q8: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_dbf_gemm_q8: unknown y_dtype %d", enum_value(y_dtype));
   if (!aligned(x, 16) || !aligned(v, 16) || !aligned(u, 16) || !aligned(y, 4) || !aligned(d_in, 16) ||
       !aligned(d_mid, 16) || !aligned(d_out, 2))
     return fail(BRQ_E_ALIGN, "brq_dbf_gemm_q8: x, v, u, d_in and d_mid must be 16-byte aligned, y 4-byte");
@@ -285,7 +320,7 @@ brq_status brq_moe_ffn(const uint16_t* x, const float* logits, int64_t T, int64_
   if (H < 128 || I < 128 || H > 32768 || I > 2048 || H % 128 || I % 128)
     return fail(BRQ_E_SHAPE, "brq_moe_ffn: H=%lld and I=%lld must be multiples of 128, H <= 32768, I <= 2048",
                 (long long)H, (long long)I);
-  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_ffn: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_ffn: unknown y_dtype %d", enum_value(y_dtype));
   if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(gate_s, 16) || !aligned(up_s, 16) || !aligned(down_s, 16) ||
       !aligned(gate_sc, 16) || !aligned(up_sc, 16) || !aligned(down_sc, 16) || !aligned(y, 16) ||
       (ids && !aligned(ids, 4)) || (w && !aligned(w, 4)))
@@ -326,7 +361,7 @@ brq_status brq_moe_dbf_ffn(const uint16_t* x, const float* logits, int64_t T, in
                 "brq_moe_dbf_ffn: H=%lld, I=%lld, r=%lld must be multiples of 128 with H <= 4096, I <= 2048, "
                 "r <= 2048",
                 (long long)H, (long long)I, (long long)r);
-  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_dbf_ffn: unknown y_dtype %d", (int)y_dtype);
+  if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_dbf_ffn: unknown y_dtype %d", enum_value(y_dtype));
   bool al = aligned(x, 16) && aligned(logits, 4) && aligned(y, 16) && (!ids || aligned(ids, 4)) && (!w || aligned(w, 4));
   for (const brq_dbf_factors* f : recs)
     al = al && aligned(f->v, 16) && aligned(f->u, 16) && aligned(f->d_in, 16) && aligned(f->d_mid, 2) &&

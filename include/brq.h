@@ -119,6 +119,14 @@ const char* brq_last_error(void);
 typedef enum { BRQ_FUSION_DEFAULT = 0, BRQ_FUSION_OFF = 1, BRQ_FUSION_ON = 2 } brq_fusion;
 brq_status brq_set_decode_fusion(brq_fusion mode, uint32_t spin_limit);
 
+/*
+ * brq_debug_fail_launches -- test hook for callers' error handling: the next
+ * `count` calls of the process whose arguments pass validation return
+ * BRQ_E_HIP ("injected launch failure") instead of enqueueing their kernels;
+ * they enqueue and write nothing. 0 disarms it. BRQ_E_SHAPE if count < 0.
+ */
+brq_status brq_debug_fail_launches(int32_t count);
+
 /* Number of uint64_t words of a SIGN1 plane of rows x cols (cols % 64 == 0). */
 size_t brq_sign_words(int64_t rows, int64_t cols);
 

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(brq.ABI_FUNCTIONS)
@@ -40,6 +40,24 @@ def test_version_and_status_strings(L):
     assert L.brq_status_str(E_SHAPE) == b"BRQ_E_SHAPE"
     assert L.brq_status_str(OK) == b"BRQ_OK"
     assert L.brq_status_str(99) == b"BRQ_E_UNKNOWN"
+
+
+def test_injected_launch_failure(L):
+    """brq_debug_fail_launches: an armed call whose arguments pass returns
+    BRQ_E_HIP with its text and enqueues nothing (it fails before the device
+    check, so this runs without a GPU); invalid arguments still win and do not
+    use up an injection."""
+    x = ctypes.c_void_p(16)  # never dereferenced: every call below stops on the host
+    assert L.brq_debug_fail_launches(-1) == E_SHAPE
+    assert L.brq_debug_fail_launches(2) == OK
+    # argument errors are reported first and do not consume the injection
+    assert L.brq_gemm(None, 1, 16, 128, x, x, x, 0, None, 0, None) == E_NULL
+    assert L.brq_gemm(x, 1, 16, 128, x, x, x, 0, None, 0, None) == E_HIP
+    assert b"injected launch failure" in L.brq_last_error()
+    assert L.brq_kron_rotate(x, 1, x, 64, x, 64, ctypes.c_void_p(1 << 20), None) == E_HIP
+    # both injections spent; no further call with these placeholder pointers
+    # here (past the hook a call would reach the device)
+    assert L.brq_debug_fail_launches(0) == OK
 
 
 def test_decode_fusion_setting(L):

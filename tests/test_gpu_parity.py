@@ -560,11 +560,13 @@ def _q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r, out=torch.float32):
 # three with few tiles and long reductions, which split along k into 2 or 4
 # int32 partial sums (m = 99: the output pass off 4-element rows, and bf16
 # pairs that straddle 4-byte boundaries); rows longer than 16384 (n or r =
-# 16512) take the quantiser that re-reads its row
+# 16512) take the quantiser that re-reads its row; M = 1000 with m = 4001
+# gives the second product 8 x 32 tiles, enough for 128-row tiles, with a
+# 104-row tail, an odd column count and bf16 pairs straddling 4-byte words
 @pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (5, 201, 384, 256), (127, 128, 256, 128),
                                      (130, 300, 640, 384), (300, 96, 512, 640), (3, 130, 1024, 1280),
                                      (70, 100, 2048, 1024), (9, 99, 1024, 1024), (3, 64, 16512, 256),
-                                     (2, 64, 256, 16512)])
+                                     (2, 64, 256, 16512), (1000, 4001, 256, 256)])
 def test_dbf_q8_small(M, m, n, r):
     say("dbf q8", M, m, n, r)
     x, d_in, vw, d_mid, uw, d_out = _q8_inputs(M, m, n, r, M + m + n + r)
@@ -1002,3 +1004,24 @@ def test_graph_capture_replay():
             assert torch.equal(a, r), f"replay {rep} differs"
         work()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_injected_launch_failure_leaves_outputs():
+    """brq_debug_fail_launches on the device: the armed call raises the
+    BRQ_E_HIP status with its text and leaves y as it was; the next call runs
+    and matches the oracle."""
+    say("injected launch failure")
+    b = brq()
+    N, K = 64, 1024
+    w = datagen.normal_f32((79, 1), (N, K), 0.02)
+    x = datagen.bf16_normal((79, 2), (1, K))
+    ow, osc = oracle.pack_sign1(w)
+    y = torch.full((1, N), 7.0, dtype=torch.float32, device="cuda")
+    assert b.lib().brq_debug_fail_launches(1) == 0
+    with pytest.raises(b.BrqError, match="injected launch failure"):
+        b.gemm(dev(x), dev(ow), dev(osc), N, K, out_dtype=torch.float32, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    b.gemm(dev(x), dev(ow), dev(osc), N, K, out_dtype=torch.float32, y=y)
+    torch.cuda.synchronize()
+    check_f32(f64(y), oracle.bin_gemm(oracle.bf16_to_f64(x), ow, osc, N, K), F32_TOL, "after injection")
