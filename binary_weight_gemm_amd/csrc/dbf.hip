@@ -399,12 +399,14 @@ __global__ __launch_bounds__(256) void k_dbf_split_wide(const float* __restrict_
 }
 
 // workspace: h_s fp32 [M][r]; the tiled path holds one such partial per
-// K-slice of stage 1, then the pieces [2M][r] and the row exponents [M]
+// K-slice of stage 1, then the pieces [2M][r] and their exponents [M], then
+// the staged rows of x [M][n] fp16 and their staging exponents [M]
 size_t dbf_ws_bytes(int64_t M, int64_t m, int64_t n, int64_t r) {
   (void)m;
   if (dbf_decode_path(M, n, r)) return align256((size_t)M * r * 4);
   const size_t hs = align256((size_t)dbf1_ksplit((int)M, (int)r, (int)n) * M * r * 4);
-  return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4);
+  return hs + align256((size_t)2 * M * r * 2) + align256((size_t)M * 4) + align256((size_t)M * n * 2) +
+         align256((size_t)M * 4);
 }
 
 // Single-launch decode chain: taken when the caller asked for it (or the
@@ -487,10 +489,17 @@ hipError_t launch_dbf(const uint16_t* x, int M, int m, int n, int r, const uint1
   uint16_t* hp = reinterpret_cast<uint16_t*>(base);
   base += align256((size_t)2 * M * r * 2);
   int* rexp = reinterpret_cast<int*>(base);
+  base += align256((size_t)M * 4);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(base);
+  base += align256((size_t)M * n * 2);
+  int* xexp = reinterpret_cast<int*>(base);
+  // x staged as fp16 with a power of two per row (undone in stage 1's epilogue)
+  hipError_t e = launch_prep_rows(x, M, n, xp, xexp, 1, st);
+  if (e != hipSuccess) return e;
   TileArgs a1{};
-  a1.a = x; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kmag = d_in; a1.diag = d_mid; a1.out = hs;
-  a1.ksplit = ks;
-  hipError_t e = launch_tile_dbf1(a1, st);
+  a1.a = xp; a1.M = M; a1.N = r; a1.K = n; a1.signs = v; a1.kmag = d_in; a1.diag = d_mid; a1.rexp = xexp;
+  a1.out = hs; a1.ksplit = ks;
+  e = launch_tile_dbf1(a1, st);
   if (e != hipSuccess) return e;
   const int qpt = (r / 8 + 255) / 256;  // quads of 8 values per thread
   if (qpt <= 1)

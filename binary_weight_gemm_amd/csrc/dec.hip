@@ -8,36 +8,8 @@
 
 namespace brq {
 
-// One thread per run of 32: load 32 bf16 values, write them in the permuted
-// order slot 2b+h <- k = 16h+b, as fp16.
-__global__ __launch_bounds__(256) void k_prep(const uint16_t* __restrict__ src, int64_t runs,
-                                              uint16_t* __restrict__ dst) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= runs) return;
-  const uint4* s = reinterpret_cast<const uint4*>(src + t * 32);
-  uint32_t v[16];
-  const uint4 q0 = s[0], q1 = s[1], q2 = s[2], q3 = s[3];
-  v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
-  v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
-  v[8] = q2.x; v[9] = q2.y; v[10] = q2.z; v[11] = q2.w;
-  v[12] = q3.x; v[13] = q3.y; v[14] = q3.z; v[15] = q3.w;
-  uint32_t o[16];
-#pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    // element b lives in word b/2 (half b%2); element 16+b in word 8+b/2
-    const uint32_t lo16 = (b & 1) ? (v[b >> 1] >> 16) : (v[b >> 1] & 0xffffu);
-    const uint32_t hi16 = (b & 1) ? (v[8 + (b >> 1)] >> 16) : (v[8 + (b >> 1)] & 0xffffu);
-    const uint32_t a = f32_to_f16_bits(bf16_to_f32(lo16));
-    const uint32_t c = f32_to_f16_bits(bf16_to_f32(hi16));
-    o[b] = a | (c << 16);
-  }
-  uint4* d = reinterpret_cast<uint4*>(dst + t * 32);
-  d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  d[2] = make_uint4(o[8], o[9], o[10], o[11]);
-  d[3] = make_uint4(o[12], o[13], o[14], o[15]);
-}
-
+// Activation staging for the tiled products: bf16 rows -> fp16 in the
+// permuted operand order (slot 2b+h of each run of 32 <- k = 16h+b).
 // One workgroup per row: the row's runs of 32 stay in registers (up to 4 per
 // thread, K <= 32768) while the row's largest |x| is found; when it lies
 // outside [2^-8, 2^15) the row is staged as fp16(x * 2^s) with s = 14 - its
@@ -101,17 +73,65 @@ __global__ __launch_bounds__(256) void k_prep_rows(const uint16_t* __restrict__ 
   }
 }
 
+// Rows longer than 32768 values: the same in two passes over the row (the
+// largest |x| first, then the staging), runs of 32 per thread in turn; dst
+// NULL: only the exponents.
+__global__ __launch_bounds__(256) void k_prep_rows_long(const uint16_t* __restrict__ src, int K,
+                                                        uint16_t* __restrict__ dst, int* __restrict__ rexp) {
+  __shared__ uint32_t s_max[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int runs = K >> 5;
+  const uint16_t* xr = src + (size_t)row * K;
+  uint32_t mx = 0;
+  for (int t = tid; t < runs; t += 256) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(xr + 32 * t);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint4 q = s4[h];
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = max(mx, max(w4[e] & 0x7fffu, (w4[e] >> 16) & 0x7fffu));
+    }
+  }
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+  __syncthreads();
+  mx = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const int e = (int)(mx >> 7) - 127;
+  const int sc = (mx != 0 && (e >= 15 || e < -8)) ? 14 - e : 0;
+  if (tid == 0) rexp[row] = sc;
+  if (!dst) return;
+  uint16_t* dr = dst + (size_t)row * K;
+  for (int t = tid; t < runs; t += 256) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(xr + 32 * t);
+    const uint4 q0 = s4[0], q1 = s4[1], q2 = s4[2], q3 = s4[3];
+    const uint32_t v[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                            q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+    uint32_t o[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const uint32_t lo = (b & 1) ? (v[b >> 1] & 0xffff0000u) : (v[b >> 1] << 16);
+      const uint32_t hi = (b & 1) ? (v[8 + (b >> 1)] & 0xffff0000u) : (v[8 + (b >> 1)] << 16);
+      o[b] = (uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(lo), sc)) |
+             ((uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(hi), sc)) << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(dr + 32 * t);
+    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    d[2] = make_uint4(o[8], o[9], o[10], o[11]);
+    d[3] = make_uint4(o[12], o[13], o[14], o[15]);
+  }
+}
+
 hipError_t launch_prep_rows(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, int* rexp, int scale,
                             hipStream_t st) {
-  hipLaunchKernelGGL(k_prep_rows, dim3((unsigned)rows), dim3(256), 0, st, x, (int)K, xp, rexp, scale);
+  if (K <= 32768 && xp)
+    hipLaunchKernelGGL(k_prep_rows, dim3((unsigned)rows), dim3(256), 0, st, x, (int)K, xp, rexp, scale);
+  else
+    hipLaunchKernelGGL(k_prep_rows_long, dim3((unsigned)rows), dim3(256), 0, st, x, (int)K, xp, rexp);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st) {
-  const int64_t runs = rows * (K / 32);
-  hipLaunchKernelGGL(k_prep, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, st, x, runs, xp);
-  return hipGetLastError();
-}
 
 
 // One-launch product for M <= 8: wave w owns chunks w*CPW .. w*CPW+CPW-1 of

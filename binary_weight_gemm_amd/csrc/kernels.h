@@ -13,11 +13,11 @@ hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, uint64_t* sig
                        uint16_t* scales /* NULL: SIGN1 plane only */, hipStream_t st);
 
 // ---- activation staging --------------------------------------------------
-// bf16 [rows][K] -> fp16 [rows][K] in the permuted operand order.
-hipError_t launch_prep_bf16(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, hipStream_t st);
-// The same, one workgroup per row (K <= 32768), each row scaled by 2^rexp[row]
-// (a power of two, 0 for rows whose largest |x| is in [2^-8, 2^15); scale = 0:
-// always 0) so that every bf16 value is exact in fp16 whatever the row's range.
+// bf16 [rows][K] -> fp16 [rows][K] in the permuted operand order (slot 2b+h of
+// each run of 32 <- k = 16h+b), one workgroup per row, each row scaled by 2^rexp[row] (a power of
+// two, 0 for rows whose largest |x| is in [2^-8, 2^15); scale = 0: always 0)
+// so that every bf16 value is exact in fp16 whatever the row's range. xp
+// NULL: only the exponents (scale must be 1 then).
 hipError_t launch_prep_rows(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xp, int* rexp, int scale,
                             hipStream_t st);
 // fp16 vector [K] -> fp16 [K] in the permuted operand order.
@@ -26,14 +26,15 @@ hipError_t launch_prep_rows(const uint16_t* x, int64_t rows, int64_t K, uint16_t
 // Few activation rows (M <= 64): split-K inside a workgroup, 16 output columns
 // per workgroup. x: bf16 [M][K]. When M*K*2 <= kDecLdsBytes the activations
 // are staged in LDS by the product kernel itself (one launch, no workspace);
-// otherwise a staging kernel writes them to `ws` (M*K*2 bytes) first.
+// otherwise the split-K path below takes them.
 constexpr int64_t kDecLdsBytes = 64 * 1024;
 bool gemm_dec_in_lds(int64_t M, int64_t K);
 hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 // Rows not taken by the one-launch path (M <= 64): split-K matrix-core product
 // over 128-column tiles (+ a slice-sum launch when K is split); `ws` holds
-// mid_ws_bytes(M, N, K) bytes (0: no workspace).
+// mid_ws_bytes(M, N, K) bytes (the rows' staging exponents, then the
+// K-slice partials).
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K);
 // workspace of launch_gemm_dec (M <= 64)
 inline size_t gemm_dec_ws_bytes(int64_t M, int64_t N, int64_t K) {
@@ -41,20 +42,18 @@ inline size_t gemm_dec_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
-// Many activation rows: LDS-tiled matrix-core kernel, bf16 activations read directly.
-hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
-                            const uint16_t* scales, void* y, int y_bf16, hipStream_t st);
 // Many activation rows (prefill): x staged to `ws` (pf_ws_bytes) as permuted
 // fp16 with a power-of-two scale per row, then the 256 x 256 direct-to-LDS
 // matrix-core kernel, which undoes the scales in its epilogue.
 size_t pf_ws_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                           const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
-// The same with one extra k-step per tile that adds a rank-r correction:
-// lr_t [M][128] fp16 (x V^T as hi | lo), lr_u [N][64] fp16 (U padded).
-hipError_t launch_gemm_pf_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
-                             const uint16_t* scales, const uint16_t* lr_t, const uint16_t* lr_u, void* y,
-                             int y_bf16, void* ws, hipStream_t st);
+// The product on rows already staged by launch_prep_rows (xp, rexp), with one
+// extra k-step per tile that adds a rank-r correction: lr_t [M][128] fp16
+// ((x 2^rexp) V^T as hi | lo), lr_u [N][64] fp16 (U padded).
+hipError_t launch_gemm_pf_lr(const uint16_t* xp, const int* rexp, int M, int N, int K, const uint64_t* signs,
+                             const uint16_t* scales, const uint16_t* lr_t, const uint16_t* lr_u, void* y, int y_bf16,
+                             hipStream_t st);
 // y = x . (Wq + U V)^T, r <= 64; `ws` holds lr_ws_bytes(M, N, K) bytes.
 size_t lr_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs,

@@ -6,9 +6,11 @@
 // Launches:
 //  1. k_lr_prep: V padded to 64 rows (zeros past r); for M > 64 also U
 //     padded to [N][64] fp16.
-//  2. k_lr_t: t = x . V^T on the fp16 matrix cores (x converted to fp16 in
-//     registers, natural order; the eight waves of a workgroup split K), fp32
-//     accumulate.
+//  2. k_prep_rows: the rows' staging exponents s (and, for M > 64, the
+//     staged rows of the prefill product).
+//     k_lr_t: t = (x 2^s) . V^T on the fp16 matrix cores (x scaled and
+//     converted to fp16 in registers, natural order; the eight waves of a
+//     workgroup split K), fp32 accumulate; for M <= 64 scaled back by 2^-s.
 //     M > 64: stored as the fp16 hi/lo pair [M][128] that the prefill kernel
 //     takes as one extra k-step inside its epilogue; M <= 64: stored fp32.
 //  3. M > 64: the prefill product with the fused correction step (pf.hip).
@@ -31,6 +33,7 @@ struct LrWs {
   uint16_t* t16;    // [M][128] fp16 hi/lo of x V^T (M > 64)
   float* t32;       // [M][64] fp32 x V^T (M <= 64)
   float* y32;       // [M][N] fp32 product (M <= 64)
+  int* rexp;        // [M] staging exponents of the rows
   void* gemm_ws;    // workspace of the product itself
 };
 
@@ -44,6 +47,7 @@ size_t lr_carve(char* base, int64_t M, int64_t N, int64_t K, LrWs* w) {
   };
   LrWs l{};
   l.vb = reinterpret_cast<uint16_t*>(take((size_t)LR_MAX * K * 2));
+  l.rexp = reinterpret_cast<int*>(take((size_t)M * 4));
   if (M > 64) {
     l.u_pad = reinterpret_cast<uint16_t*>(take((size_t)N * LR_MAX * 2));
     l.t16 = reinterpret_cast<uint16_t*>(take((size_t)M * 2 * LR_MAX * 2));
@@ -89,8 +93,8 @@ __global__ __launch_bounds__(256) void k_lr_prep(const uint16_t* __restrict__ v,
 // HILO: store fp16 hi/lo pairs [M][128] (hi at i, lo at 64+i), else fp32 [M][64].
 template <bool HILO, int NC, int TT>
 __global__ __launch_bounds__(512) void k_lr_t(const uint16_t* __restrict__ x, int M, int K,
-                                              const uint16_t* __restrict__ vp, uint16_t* __restrict__ t16,
-                                              float* __restrict__ t32) {
+                                              const uint16_t* __restrict__ vp, const int* __restrict__ rexp,
+                                              uint16_t* __restrict__ t16, float* __restrict__ t32) {
   constexpr int BPR = NC <= 2 ? 4 : 2;  // blocks per round: the round's loads stay in registers
   constexpr int NW = 8;                 // waves: interleaved 64-k blocks
   __shared__ f32x4 red[NW - 1][TT][NC][64];
@@ -99,10 +103,12 @@ __global__ __launch_bounds__(512) void k_lr_t(const uint16_t* __restrict__ x, in
   const int m0 = blockIdx.x * 16 * TT;
   const int nblk = K >> 6;
   const uint16_t* xa[TT];
+  int xs[TT];  // staging exponent of the lane's A row in each row tile
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     const int row = m0 + 16 * t + j < M ? m0 + 16 * t + j : M - 1;
     xa[t] = x + (size_t)row * K + 8 * kb;
+    xs[t] = rexp[row];
   }
   const uint16_t* vr = vp + (size_t)j * K + 8 * kb;  // factor 16c + j at + 16c*K
   f32x4 acc[TT][NC];
@@ -140,8 +146,9 @@ __global__ __launch_bounds__(512) void k_lr_t(const uint16_t* __restrict__ x, in
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
             const uint32_t w = a[q][t][hh][d];
-            af[d] = (uint32_t)f32_to_f16_bits(__uint_as_float(w << 16)) |
-                    ((uint32_t)f32_to_f16_bits(__uint_as_float(w & 0xffff0000u)) << 16);
+            af[d] = (uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(w << 16), xs[t])) |
+                    ((uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(__uint_as_float(w & 0xffff0000u), xs[t]))
+                     << 16);
           }
 #pragma unroll
           for (int c = 0; c < NC; ++c) acc[t][c] = mfma16(af, use[q] ? v[q][c][hh] : z, acc[t][c]);
@@ -168,10 +175,11 @@ __global__ __launch_bounds__(512) void k_lr_t(const uint16_t* __restrict__ x, in
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + 16 * t + 4 * kb + i;
       if (m >= M) continue;
+      const int un = HILO ? 0 : -rexp[m];  // fp32 output: back to the unscaled row
 #pragma unroll
       for (int c = 0; c < LR_MAX / 16; ++c) {
         const int f = 16 * c + j;
-        const float val = c < NC ? acc[t][c < NC ? c : 0][i] : 0.f;
+        const float val = c < NC ? __builtin_amdgcn_ldexpf(acc[t][c < NC ? c : 0][i], un) : 0.f;
         if (HILO) {
           uint16_t hi, lo;
           split_f16(val, hi, lo);
@@ -219,8 +227,8 @@ hipError_t launch_gemm_lr(const uint16_t* x, int M, int N, int K, const uint64_t
   auto lr_t = [&](auto hilo) {
     constexpr bool H = decltype(hilo)::value;
 #define BRQ_LRT(NC)                                                                                   \
-  if (two) hipLaunchKernelGGL((k_lr_t<H, NC, 2>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32); \
-  else hipLaunchKernelGGL((k_lr_t<H, NC, 1>), tg, dim3(512), 0, st, x, M, K, w.vb, w.t16, w.t32)
+  if (two) hipLaunchKernelGGL((k_lr_t<H, NC, 2>), tg, dim3(512), 0, st, x, M, K, w.vb, w.rexp, w.t16, w.t32); \
+  else hipLaunchKernelGGL((k_lr_t<H, NC, 1>), tg, dim3(512), 0, st, x, M, K, w.vb, w.rexp, w.t16, w.t32)
     switch (nc) {
       case 1: BRQ_LRT(1); break;
       case 2: BRQ_LRT(2); break;
@@ -230,10 +238,14 @@ hipError_t launch_gemm_lr(const uint16_t* x, int M, int N, int K, const uint64_t
 #undef BRQ_LRT
     return hipGetLastError();
   };
+  // the rows' staging exponents (M > 64: with the staged rows themselves)
+  uint16_t* xp = many ? reinterpret_cast<uint16_t*>(w.gemm_ws) : nullptr;
+  e = launch_prep_rows(x, M, K, xp, w.rexp, 1, st);
+  if (e != hipSuccess) return e;
   if (many) {
     e = lr_t(std::true_type{});
     if (e != hipSuccess) return e;
-    return launch_gemm_pf_lr(x, M, N, K, signs, scales, w.t16, w.u_pad, y, y_bf16, w.gemm_ws, st);
+    return launch_gemm_pf_lr(xp, w.rexp, M, N, K, signs, scales, w.t16, w.u_pad, y, y_bf16, st);
   }
   e = lr_t(std::false_type{});
   if (e != hipSuccess) return e;

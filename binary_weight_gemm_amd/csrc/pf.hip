@@ -2,8 +2,9 @@
 // matrix cores ("LLM binarization, Episode 01: DBF", section 4: one matrix
 // applied to many vectors amortises the weight unpack over the rows).
 //
-// x is first written by k_prep as fp16 in the permuted operand order (the
-// pair order of the shift-and-or weight unpack, see common.h), so the main
+// x is first written by k_prep_rows as fp16 in the permuted operand order
+// (the pair order of the shift-and-or weight unpack, see common.h), each row
+// scaled by a power of two that the epilogue undoes, so the main
 // kernel moves activation tiles global -> LDS with direct loads
 // (global_load_lds_dwordx4), never through registers.
 //
@@ -382,22 +383,18 @@ hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t
                           void* y, int y_bf16, void* ws, hipStream_t st) {
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
   int* rexp = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
-  // rows of up to 32768 values are staged with a power-of-two scale per row;
-  // longer rows unscaled (|x| < 65504)
-  const bool rows = K <= 32768;
-  const hipError_t e = rows ? launch_prep_rows(x, M, K, xp, rexp, 1, st) : launch_prep_bf16(x, M, K, xp, st);
+  // the rows are staged with a power-of-two scale per row, undone in the epilogue
+  const hipError_t e = launch_prep_rows(x, M, K, xp, rexp, 1, st);
   if (e != hipSuccess) return e;
-  return pf_run<false>(xp, M, N, K, signs, scales, y, y_bf16, nullptr, nullptr, rows ? rexp : nullptr, st);
+  return pf_run<false>(xp, M, N, K, signs, scales, y, y_bf16, nullptr, nullptr, rexp, st);
 }
 
-hipError_t launch_gemm_pf_lr(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
-                             const uint16_t* lr_t, const uint16_t* lr_u, void* y, int y_bf16, void* ws,
+hipError_t launch_gemm_pf_lr(const uint16_t* xp, const int* rexp, int M, int N, int K, const uint64_t* signs,
+                             const uint16_t* scales, const uint16_t* lr_t, const uint16_t* lr_u, void* y, int y_bf16,
                              hipStream_t st) {
-  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-  // unscaled staging: the correction x V^T enters the same accumulator unscaled
-  const hipError_t e = launch_prep_bf16(x, M, K, xp, st);
-  if (e != hipSuccess) return e;
-  return pf_run<true>(xp, M, N, K, signs, scales, y, y_bf16, lr_t, lr_u, nullptr, st);
+  // xp and rexp from launch_prep_rows; lr_t was formed from the same scaled
+  // rows, so the epilogue undoes one power of two for both terms
+  return pf_run<true>(xp, M, N, K, signs, scales, y, y_bf16, lr_t, lr_u, rexp, st);
 }
 
 }  // namespace brq

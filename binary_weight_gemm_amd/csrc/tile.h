@@ -10,13 +10,14 @@ namespace brq {
 enum { EPI_Y = 0, EPI_HS32 = 1, EPI_PAIRSUM = 2 };
 
 struct TileArgs {
-  const void* a;            // activations: bf16 [M][K] (AMODE 0) or permuted fp16 [M][K] (AMODE 1)
+  const void* a;            // activations: permuted fp16 [M][K]
   int M, N, K;              // A rows, output columns, reduction length
   const uint64_t* signs;    // SIGN1 plane [N][K/64]
   const uint16_t* scales;   // group-128 scales [N][K/128] (BM_GROUP)
   const uint16_t* kmag;     // fp16 per-k magnitudes [K], natural order (BM_PERK)
   const uint16_t* diag;     // fp16 per-column diagonal (EPI_HS32, EPI_PAIRSUM)
-  const int* rexp;          // per-token exponent applied to the piece sum (EPI_PAIRSUM)
+  const int* rexp;          // EPI_PAIRSUM: per-token exponent applied to the piece sum (2^rexp);
+                            // EPI_HS32: per-row staging exponent undone (2^-rexp)
   void* out;
   int out_bf16;
   int ksplit = 1;           // K-slices (grid y); EPI_HS32 writes slice s at out + s*M*N

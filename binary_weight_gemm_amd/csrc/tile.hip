@@ -4,9 +4,9 @@
 //
 // Block tile BM x BN x 64 on 4 waves (2 x 2), each wave (BM/2) x (BN/2) of
 // v_mfma_f32_32x32x16_f16 tiles. Per k-step of 64:
-//   A: activations, bf16 read from global (AMODE 0) and converted to fp16, or
-//      fp16 already in the permuted order (AMODE 1); written to LDS in the
-//      permuted order.
+//   A: activations, fp16 already in the permuted order (staged by
+//      k_prep_rows, each row scaled by a power of two, or the DBF
+//      intermediate's pieces), copied to LDS.
 //   B: one 64-bit sign word per column; each pair of signs becomes an fp16
 //      pair +-c (c = group scale, per-k value or 1) with one shift and one
 //      and-or, written to LDS.
@@ -17,8 +17,9 @@
 // 8 consecutive k of block l/32; B lane l supplies column l%32 and the same k
 // block; D lane l holds, in item r, row 8*(r/4) + 4*(l/32) + r%4 of column l%32.
 //
-// Epilogues: EPI_Y writes y (fp32 or bf16); EPI_HS32 multiplies by a per-column
-// fp16 diagonal and writes fp32 rows (the DBF intermediate h_s); EPI_PAIRSUM
+// Epilogues: EPI_Y writes y (fp32 or bf16); EPI_HS32 undoes the rows' staging
+// scale (2^-rexp[row]), multiplies by a per-column fp16 diagonal and writes
+// fp32 rows (the DBF intermediate h_s); EPI_PAIRSUM
 // adds the two piece rows of every token, applies the token's power of two
 // (2^rexp, exact) and multiplies by a per-column diagonal (the DBF output).
 #include "common.h"
@@ -66,15 +67,9 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
       const int row = unit >> 2, q = (unit >> 1) & 1, b0 = (unit & 1) * 8;
       const int gm = m0 + row;
       if (gm < p.M) {
-        if (AMODE == 0) {
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.a) + (size_t)gm * p.K + k0 + 32 * q + b0;
-          ra[u][0] = *reinterpret_cast<const uint4*>(src);
-          ra[u][1] = *reinterpret_cast<const uint4*>(src + 16);
-        } else {
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.a) + (size_t)gm * p.K + k0 + 32 * q + 2 * b0;
-          ra[u][0] = *reinterpret_cast<const uint4*>(src);
-          ra[u][1] = *reinterpret_cast<const uint4*>(src + 8);
-        }
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(p.a) + (size_t)gm * p.K + k0 + 32 * q + 2 * b0;
+        ra[u][0] = *reinterpret_cast<const uint4*>(src);
+        ra[u][1] = *reinterpret_cast<const uint4*>(src + 8);
       } else {
         ra[u][0] = make_uint4(0, 0, 0, 0);
         ra[u][1] = make_uint4(0, 0, 0, 0);
@@ -111,20 +106,8 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
       const int unit = tid + 256 * u;
       const int row = unit >> 2, q = (unit >> 1) & 1, b0 = (unit & 1) * 8;
       uint32_t o[8];
-      if (AMODE == 0) {
-        const uint32_t lo[4] = {ra[u][0].x, ra[u][0].y, ra[u][0].z, ra[u][0].w};
-        const uint32_t hi[4] = {ra[u][1].x, ra[u][1].y, ra[u][1].z, ra[u][1].w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const uint32_t a = (t & 1) ? (lo[t >> 1] & 0xffff0000u) : (lo[t >> 1] << 16);
-          const uint32_t c = (t & 1) ? (hi[t >> 1] & 0xffff0000u) : (hi[t >> 1] << 16);
-          o[t] = (uint32_t)f32_to_f16_bits(__uint_as_float(a)) |
-                 ((uint32_t)f32_to_f16_bits(__uint_as_float(c)) << 16);
-        }
-      } else {
-        o[0] = ra[u][0].x; o[1] = ra[u][0].y; o[2] = ra[u][0].z; o[3] = ra[u][0].w;
-        o[4] = ra[u][1].x; o[5] = ra[u][1].y; o[6] = ra[u][1].z; o[7] = ra[u][1].w;
-      }
+      o[0] = ra[u][0].x; o[1] = ra[u][0].y; o[2] = ra[u][0].z; o[3] = ra[u][0].w;
+      o[4] = ra[u][1].x; o[5] = ra[u][1].y; o[6] = ra[u][1].z; o[7] = ra[u][1].w;
       uint4* dst = reinterpret_cast<uint4*>(&As[buf][row * LDK + 32 * q + 2 * b0]);
       dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
       dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -205,7 +188,7 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < p.M) hs[(size_t)row * p.N + col] = acc[i][j][r] * dm;
+          if (row < p.M) hs[(size_t)row * p.N + col] = __builtin_amdgcn_ldexpf(acc[i][j][r], -p.rexp[row]) * dm;
         }
       } else {  // EPI_PAIRSUM: rows 2t, 2t+1 are the two pieces of token t
         const float dg = f16_bits_to_f32(p.diag[col]);
@@ -239,18 +222,8 @@ int dbf1_ksplit(int M, int r, int n) {
   return s;
 }
 
-hipError_t launch_gemm_tile(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
-                            const uint16_t* scales, void* y, int y_bf16, hipStream_t st) {
-  TileArgs a{};
-  a.a = x; a.M = M; a.N = N; a.K = K; a.signs = signs; a.scales = scales;
-  a.out = y; a.out_bf16 = y_bf16;
-  const long mid = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (mid >= 256) return run_tile<128, 128, 0, BM_GROUP, EPI_Y>(a, st);
-  return run_tile<64, 64, 0, BM_GROUP, EPI_Y>(a, st);
-}
-
 hipError_t launch_tile_dbf1(const TileArgs& a, hipStream_t st) {
-  return run_tile<128, 128, 0, BM_PERK, EPI_HS32>(a, st);
+  return run_tile<128, 128, 1, BM_PERK, EPI_HS32>(a, st);
 }
 
 // DBF stage 2: 64 x 128 tiles (two or more workgroups per compute unit, so

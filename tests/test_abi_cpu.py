@@ -78,10 +78,11 @@ def test_size_queries(L):
     assert L.brq_sign_words(3, 65) == 0
     assert L.brq_scale_count(3, 64) == 0
     assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 0          # staged in LDS
-    # fp32 partial tiles: 14 K-slices of 8 k-steps x 32 tiles of 128 columns
-    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 14 * 32 * 64 * 128 * 4
-    # one K-slice (K = 512 over 256 tiles of 128 columns): no workspace
-    assert L.brq_gemm_workspace_bytes(64, 32768, 512) == 0
+    # the rows' staging exponents (64 x 4 B, one 256-byte block), then fp32
+    # partial tiles: 14 K-slices of 8 k-steps x 32 tiles of 128 columns
+    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 256 + 14 * 32 * 64 * 128 * 4
+    # one K-slice (K = 512 over 256 tiles of 128 columns): the exponents only
+    assert L.brq_gemm_workspace_bytes(64, 32768, 512) == 256
     assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 4096 * 4096 * 2 + 4096 * 4   # staged rows, exponents
     assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0
     assert L.brq_dbf_workspace_bytes(1, 4096, 4096, 2048) > 0
@@ -130,13 +131,15 @@ def test_gemm_lr_validation(L):
     assert g(*ok[:11], None, 0, None) == E_WORKSPACE
     assert L.brq_gemm_lr_workspace_bytes(4, 16, 256, 0) == 0
     assert L.brq_gemm_lr_workspace_bytes(4, 16, 256, 65) == 0
-    # decode rows: padded V (64 x K fp16) + x V^T (fp32 [M][64]) + fp32 product + the product's own workspace
+    # decode rows: padded V (64 x K fp16) + row exponents (256 B) + x V^T (fp32 [M][64]) + fp32 product
+    # + the product's own workspace
     M, N, K = 4, 4096, 14336
-    assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == (64 * K * 2 + 1024 + M * N * 4
+    assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == (64 * K * 2 + 256 + 1024 + M * N * 4
                                                           + L.brq_gemm_workspace_bytes(M, N, K))
-    # many rows: padded V + padded U (N x 64 fp16) + x V^T hi/lo (M x 128 fp16) + staged activations
+    # many rows: padded V + row exponents + padded U (N x 64 fp16) + x V^T hi/lo (M x 128 fp16)
+    # + staged activations
     M, N, K = 4096, 14336, 4096
-    assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == 64 * K * 2 + N * 128 + M * 256 + M * K * 2
+    assert L.brq_gemm_lr_workspace_bytes(M, N, K, 20) == 64 * K * 2 + M * 4 + N * 128 + M * 256 + M * K * 2
 
 
 def test_moe_dbf_validation(L):

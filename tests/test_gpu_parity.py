@@ -208,7 +208,8 @@ def _range_rows(M, K, key, scales=_RANGE_SCALES):
     return datagen.bf16_bits_from_f32(rows)
 
 
-@pytest.mark.parametrize("M,N,K", [(2, 96, 1024), (8, 130, 2048), (300, 520, 1024)])
+@pytest.mark.parametrize("M,N,K", [(2, 96, 1024), (8, 130, 2048), (16, 96, 1024), (64, 130, 2048),
+                                   (300, 520, 1024), (100, 130, 33280)])
 def test_gemm_activation_range(M, N, K):
     say("gemm activation range", M, N, K)
     w = datagen.normal_f32((79, N, K), (N, K), 0.02)
@@ -232,21 +233,22 @@ def test_gemm_activation_range(M, N, K):
 
 
 def test_dbf_and_moe_activation_range():
-    say("dbf decode + moe small/grouped, activation range")
+    say("dbf decode and tiled + moe small/grouped, activation range")
     m_, n_, r_ = 128, 512, 256
     v = datagen.pm1_f32((79, 1, 0), (r_, n_))
     u = datagen.pm1_f32((79, 1, 1), (m_, r_))
     d_in, d_mid, d_out = (datagen.f16_lognormal((79, 1, 2 + i), (s_,)) for i, s_ in enumerate((n_, r_, m_)))
     vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
-    xb = _range_rows(4, n_, 1)
-    o = oracle.dbf_chain(oracle.bf16_to_f64(xb), d_in, vw, d_mid, uw, d_out, m_, n_, r_)
-    y = f64(brq().dbf_gemm(dev(xb), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m_, n_, r_,
-                           out_dtype=torch.float32))
-    for t in range(4):
-        if np.any(o[t]):
-            check_f32(y[t], o[t], F32_TOL, f"dbf row {t}")
-        else:
-            assert not np.any(y[t])
+    for M in (4, 16, 300):  # decode path, tiled path (x staged per row)
+        xb = _range_rows(M, n_, M)
+        o = oracle.dbf_chain(oracle.bf16_to_f64(xb), d_in, vw, d_mid, uw, d_out, m_, n_, r_)
+        y = f64(brq().dbf_gemm(dev(xb), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m_, n_, r_,
+                               out_dtype=torch.float32))
+        for t in range(M):
+            if np.any(o[t]):
+                check_f32(y[t], o[t], F32_TOL, f"dbf M={M} row {t}")
+            else:
+                assert not np.any(y[t])
     cfg = datagen.C4(E=16, H=256, I=128, top_k=4, layer=79)
     ex = _Experts(cfg)
     for T in (3, 9):  # few-token path, grouped path
@@ -316,6 +318,28 @@ def test_gemm_lr(M, N, K, r):
     # M = 1 with K % 512 == 0 takes the single-row fp8 x fp4 product
     tol = F32_TOL
     check_f32(f64(y), o, tol, f"gemm lr {M}x{N}x{K} r={r}")
+
+
+@pytest.mark.parametrize("M", [4, 16, 300])
+def test_gemm_lr_activation_range(M):
+    """The low-rank path's rows are staged with a power of two per row too:
+    x V^T is formed from the same scaled rows (fp16 operands) and scaled back
+    with the product, so rows at 1e5 or 1e30 (or 1e-30) match the oracle."""
+    say("gemm lr activation range", M)
+    N, K, r = 130, 1024, 20
+    w = datagen.normal_f32((81, M, 0), (N, K), 0.02)
+    v = np.asarray(datagen.normal_f32((81, M, 2), (r, K), 0.05), dtype=np.float16)
+    u = np.asarray(datagen.normal_f32((81, M, 3), (N, r), 0.05), dtype=np.float16)
+    ow, osc = oracle.pack_sign1(w)
+    xb = _range_rows(M, K, 5)
+    o = oracle.bin_gemm_lr(oracle.bf16_to_f64(xb), ow, osc, v, u, N, K, r)
+    y = f64(brq().gemm_lr(dev(xb), dev(ow), dev(osc), dev(v), dev(u), N, K, r, out_dtype=torch.float32))
+    assert np.all(np.isfinite(y))
+    for m in range(M):
+        if np.any(o[m]):
+            check_f32(y[m], o[m], F32_TOL, f"lr M={M} row {m}")
+        else:
+            assert not np.any(y[m])
 
 
 @pytest.mark.parametrize("M", [8, 300])
