@@ -6,17 +6,14 @@
 // (one 128-byte line of every sign row). A workgroup (4 waves, 32 columns
 // each) first issues direct loads of all sign records of its slice into LDS
 // and reads its scales; the activations stream through registers: each wave
-// loads its share of the bf16 rows PREF k-steps ahead, converts them to fp16
-// in the permuted operand order and writes them to one of two LDS stages. Every
+// loads its share of the bf16 rows PREF k-steps ahead and writes them, as
+// they are, in the permuted operand order to one of two LDS stages. Every
 // wave multiplies all rows (TT tiles of 16) by its two 16-column groups with
-// v_mfma_f32_16x16x32_f16 on +-scale fp16 weight operands: one activation
-// operand serves two MFMAs and one weight operand serves TT.
-//
-// The activation rows enter scaled: a first launch (k_prep_rows_long, exponents
-// only) finds each row's power of two s (0 unless its largest |x| lies
-// outside [2^-8, 2^15)), the staging converts x * 2^s to fp16 (every bf16
-// value exact in fp16 whatever the row's range) and the epilogue scales the
-// row's sums back by 2^-s (exact).
+// v_mfma_f32_16x16x32_bf16 on +-1 weight operands (bf16 activations and +-1
+// are exact, so a k-step's MFMAs give the group's signed sums of x in fp32,
+// for x of any magnitude) and adds each group sum times its fp16 scale into
+// the fp32 result: one activation operand serves two MFMAs and one weight
+// operand serves TT.
 //
 // With several K-slices each workgroup writes its fp32 partial tile to the
 // workspace and a second launch adds the slices in slice order (deterministic).
@@ -58,13 +55,11 @@ MidPlan mid_plan(int64_t N, int64_t K) {
   return p;
 }
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// fp16 pair (lo, hi) from two bf16 values times 2^s, round to nearest even
-__device__ __forceinline__ uint32_t bf16x2_to_f16_pair(uint32_t lo_bits, uint32_t hi_bits, int s) {
-  const h2 v = {(_Float16)__builtin_amdgcn_ldexpf(__uint_as_float(lo_bits), s),
-                (_Float16)__builtin_amdgcn_ldexpf(__uint_as_float(hi_bits), s)};
-  return __builtin_bit_cast(uint32_t, v);
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
 }
 
 }  // namespace
@@ -73,7 +68,7 @@ template <int TT>
 __global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, int K,
                                              const uint32_t* __restrict__ signs, const uint16_t* __restrict__ scales,
                                              void* __restrict__ y, int y_bf16, float* __restrict__ part, int kps,
-                                             int S, const int* __restrict__ rexp) {
+                                             int S) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int PREF = mid_pref(TT), SB = 16 * TT * 256;
   constexpr int NB = MID_NB, BN = MID_BN;
@@ -122,14 +117,12 @@ __global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, in
   const int rr = lane >> 4, cc = lane & 15;
   const uint8_t* xr[TT];
   uint32_t a_dst[TT];
-  int xs[TT];  // staging exponents of the rows
 #pragma unroll
   for (int i = 0; i < TT; ++i) {
     const int r = 4 * TT * wave + 4 * i + rr;
     const int rg = r < M ? r : M - 1;
     xr[i] = reinterpret_cast<const uint8_t*>(x) + (size_t)rg * K * 2 + (cc >> 2) * 64 + (cc & 3) * 8;
     a_dst[i] = (uint32_t)(r * 256 + ((cc ^ (r & 15)) * 16));
-    xs[i] = rexp[rg];
   }
   uint2 ra[PREF][TT][2];
   // (x is not __restrict__: the prefetch loads must stay ahead of the
@@ -147,10 +140,11 @@ __global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, in
     for (int i = 0; i < TT; ++i) {
       const uint2 lo = src[i][0], hi = src[i][1];
       u32x4 o;
-      o[0] = bf16x2_to_f16_pair(lo.x << 16, hi.x << 16, xs[i]);
-      o[1] = bf16x2_to_f16_pair(lo.x & 0xffff0000u, hi.x & 0xffff0000u, xs[i]);
-      o[2] = bf16x2_to_f16_pair(lo.y << 16, hi.y << 16, xs[i]);
-      o[3] = bf16x2_to_f16_pair(lo.y & 0xffff0000u, hi.y & 0xffff0000u, xs[i]);
+      // pair (element b, element 16 + b): low halves, then high halves
+      o[0] = __builtin_amdgcn_perm(hi.x, lo.x, 0x05040100u);
+      o[1] = __builtin_amdgcn_perm(hi.x, lo.x, 0x07060302u);
+      o[2] = __builtin_amdgcn_perm(hi.y, lo.y, 0x05040100u);
+      o[3] = __builtin_amdgcn_perm(hi.y, lo.y, 0x07060302u);
       *reinterpret_cast<u32x4*>(l_a + st * SB + a_dst[i]) = o;
     }
   };
@@ -202,24 +196,32 @@ __global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, in
       for (int t = 0; t < TT; ++t)  // chunk 4s+kb of row 16t+j
         a[s][t] = *reinterpret_cast<const u32x4*>(base + (16 * t + j) * 256 + (((4 * s + kb) ^ j) * 16));
     u32x4 w4[NB];
-    uint32_t Sc[NB];
+    float sc[NB];
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
       w4[g] = *reinterpret_cast<const u32x4*>(l_sig + sg_off[g] + q * sg_step);
-      Sc[g] = l_sc[q * BN + 16 * (NB * wave + g) + j];
+      sc[g] = f16_bits_to_f32(l_sc[q * BN + 16 * (NB * wave + g) + j] & 0xffffu);
     }
+    f32x4 gs[TT][NB];  // the k-step's (one scale group's) signed sums
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int g = 0; g < NB; ++g) {
         const uint32_t w = w4[g][s] >> bsh;
-        u32x4 b;
+        u32x4 b;  // bf16 +-1 pairs
 #pragma unroll
-        for (int u = 0; u < 4; ++u) b[u] = ((w << (15 - u)) & 0x80008000u) | Sc[g];
+        for (int u = 0; u < 4; ++u) b[u] = ((w << (15 - u)) & 0x80008000u) | 0x3f803f80u;
 #pragma unroll
-        for (int t = 0; t < TT; ++t) acc[t][g] = mfma16(a[s][t], b, acc[t][g]);
+        for (int t = 0; t < TT; ++t)
+          gs[t][g] = mfma16_bf16(a[s][t], b, s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : gs[t][g]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][g][i] = fmaf(sc[g], gs[t][g][i], acc[t][g][i]);
     // the next stage's writes are in and every wave is done with this one
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
@@ -235,17 +237,7 @@ __global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, in
     if (q + d < nks) step(q + d, d);
   __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
 
-  // lane (kb, j) holds rows 16t + 4kb + i of column cw + 16g + j; undo the
-  // rows' staging scales
-#pragma unroll
-  for (int t = 0; t < TT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * t + 4 * kb + i;
-      const int un = -rexp[m < M ? m : M - 1];
-#pragma unroll
-      for (int g = 0; g < NB; ++g) acc[t][g][i] = __builtin_amdgcn_ldexpf(acc[t][g][i], un);
-    }
+  // lane (kb, j) holds rows 16t + 4kb + i of column cw + 16g + j
   const int cw = n0 + 16 * NB * wave;
   if (S == 1) {
 #pragma unroll
@@ -303,15 +295,14 @@ __global__ __launch_bounds__(256) void k_mid_sum(const float* __restrict__ part,
     if (c + i < N) store_out(y, (size_t)m * N + c + i, v[i], y_bf16);
 }
 
-// workspace: the rows' staging exponents [M], then the partial tiles
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const MidPlan p = mid_plan(N, K);
-  return align256((size_t)M * 4) + (p.slices > 1 ? align256((size_t)p.tiles * p.slices * M * MID_BN * 4) : 0);
+  return p.slices > 1 ? align256((size_t)p.tiles * p.slices * M * MID_BN * 4) : 0;
 }
 
 template <int TT>
 static hipError_t mid_launch(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
-                             void* y, int y_bf16, float* part, const int* rexp, const MidPlan& p, hipStream_t st) {
+                             void* y, int y_bf16, float* part, const MidPlan& p, hipStream_t st) {
   const int lds = mid_lds_bytes(TT);
   if (lds > 64 * 1024) {  // per-function opt-in beyond 64 KiB of dynamic LDS
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid<TT>),
@@ -319,7 +310,7 @@ static hipError_t mid_launch(const uint16_t* x, int M, int N, int K, const uint6
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_mid<TT>, dim3(p.tiles, p.slices), dim3(256), lds, st, x, M, N, K,
-                     reinterpret_cast<const uint32_t*>(signs), scales, y, y_bf16, part, p.kps, p.slices, rexp);
+                     reinterpret_cast<const uint32_t*>(signs), scales, y, y_bf16, part, p.kps, p.slices);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.slices == 1) return e;
   const int64_t n = (int64_t)p.tiles * M * MID_BN / 4;
@@ -331,15 +322,12 @@ static hipError_t mid_launch(const uint16_t* x, int M, int N, int K, const uint6
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                            void* y, int y_bf16, void* ws, hipStream_t st) {
   const MidPlan p = mid_plan(N, K);
-  int* rexp = reinterpret_cast<int*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * 4));
-  const hipError_t e = launch_prep_rows(x, M, K, nullptr, rexp, 1, st);
-  if (e != hipSuccess) return e;
+  float* part = reinterpret_cast<float*>(ws);
   switch ((M + 15) / 16) {
-    case 1: return mid_launch<1>(x, M, N, K, signs, scales, y, y_bf16, part, rexp, p, st);
-    case 2: return mid_launch<2>(x, M, N, K, signs, scales, y, y_bf16, part, rexp, p, st);
-    case 3: return mid_launch<3>(x, M, N, K, signs, scales, y, y_bf16, part, rexp, p, st);
-    default: return mid_launch<4>(x, M, N, K, signs, scales, y, y_bf16, part, rexp, p, st);
+    case 1: return mid_launch<1>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 2: return mid_launch<2>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 3: return mid_launch<3>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    default: return mid_launch<4>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
   }
 }
 
