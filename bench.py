@@ -231,15 +231,18 @@ def device_facts(torch):
 
 def achievable_peaks(torch, reps=10):
     """Reference rates on this device (not the product): a 1 GiB device copy
-    (read + write) for HBM, and the vendor library's 8192^3 bf16 GEMM
-    (hipBLASLt through torch.matmul) for the matrix cores; back-to-back calls
-    between two events."""
+    (read + write) for HBM, and the vendor library's 8192^3 bf16 and fp16
+    GEMMs (hipBLASLt through torch.matmul; fp16 is the operand type of the
+    prefill product) for the matrix cores; back-to-back calls between two
+    events."""
     n = 2 ** 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
     b = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
     c = torch.empty_like(a)
+    ah, bh = a.to(torch.float16), b.to(torch.float16)
+    ch = torch.empty_like(ah)
     warm_gpu(torch, 0.3)
 
     def timed(fn):
@@ -255,12 +258,15 @@ def achievable_peaks(torch, reps=10):
 
     copy_ms = timed(lambda: dst.copy_(src))
     gemm_ms = timed(lambda: torch.matmul(a, b, out=c))
-    del src, dst, a, b, c
+    gemm16_ms = timed(lambda: torch.matmul(ah, bh, out=ch))
+    del src, dst, a, b, c, ah, bh, ch
     torch.cuda.empty_cache()
     copy_gbs = 2 * n / (copy_ms * 1e-3) / 1e9
     gemm_tflops = 2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
+    gemm16_tflops = 2 * 8192 ** 3 / (gemm16_ms * 1e-3) / 1e12
     return dict(hbm_copy_gbs=copy_gbs, hbm_copy_frac=copy_gbs / HBM_PEAK_GBS,
-                bf16_gemm_tflops=gemm_tflops, bf16_gemm_frac=gemm_tflops / MFMA_F16_PEAK_TFLOPS)
+                bf16_gemm_tflops=gemm_tflops, bf16_gemm_frac=gemm_tflops / MFMA_F16_PEAK_TFLOPS,
+                f16_gemm_tflops=gemm16_tflops, f16_gemm_frac=gemm16_tflops / MFMA_F16_PEAK_TFLOPS)
 
 
 def reference_kernels(torch, brq):
