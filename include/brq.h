@@ -31,21 +31,29 @@
  *                   result rounded to nearest, ties to even.
  *
  * Numerics: every product multiplies exactly representable operands and
- * accumulates in fp32. Activations are carried as fp16 inside the products;
- * bf16 activations must satisfy |x| < 65504 (values below 2^-14 are kept on
- * fp16's subnormal grid, an absolute change of at most 2^-25). The one
- * exception is brq_gemm with M = 1 and K % 512 == 0 (K <= 23040), which runs
- * on the fp8 x fp4 matrix cores: there each activation is a 24-bit
- * fixed-point field under the largest power of two of its slice of the row
- * (a change of less than 2^-23 of that slice's maximum; bf16 subnormals count
- * as zero), split into six 4-bit digits whose products and partial sums are
- * exact, so no magnitude limit below fp32's range applies and the result
- * agrees with the M > 1 paths to fp32 rounding. fp32
- * intermediates (DBF h, MoE SwiGLU output) are stored as fp32 and enter the
- * next product as two fp16 pieces of v * 2^s, s a power of two that puts the
- * largest magnitude of the staged slice (or row) near 2^14: about 22
- * significant bits for every value down to 2^-18 of that maximum, whatever
- * its magnitude.
+ * accumulates in fp32; bf16 activations of any finite magnitude are accepted
+ * (brq_dbf_gemm_q8 aside, which quantises them by definition). How each path
+ * carries them:
+ *  - brq_gemm, M = 1, K % 512 == 0, K <= 23040: fp8 x fp4 matrix cores; each
+ *    activation is a 24-bit fixed-point field under the largest power of two
+ *    of its slice of the row (a change of less than 2^-23 of that slice's
+ *    maximum; bf16 subnormals count as zero), split into six 4-bit digits
+ *    whose products and partial sums are exact;
+ *  - brq_gemm with 9 <= M <= 64: bf16 matrix cores with +-1 weights (bf16
+ *    activations as they are), each scale group's sum scaled in fp32;
+ *  - every other product on the fp16 matrix cores takes the activations as
+ *    fp16(x * 2^s), s a power of two per row (per staged slice of a row on the
+ *    few-row paths) that puts the largest |x| in [2^14, 2^15) when it lies
+ *    outside [2^-8, 2^15), else 0, undone exactly after the product: every
+ *    bf16 value is exact in fp16 there or lies below 2^-24 of the row (slice)
+ *    maximum;
+ *  - fp32 intermediates (DBF h_s, the MoE SwiGLU output) are stored as fp32
+ *    and enter the next product as two fp16 pieces of v * 2^s (s as above for
+ *    the staged slice or row, the largest near 2^14): about 22 significant
+ *    bits for every value down to 2^-18 of that maximum.
+ * The paths differ only in fp32 rounding order, so one row gives the same
+ * result to fp32 rounding at any M. Results are deterministic (sums in a
+ * fixed order, no floating-point atomics). Inputs must be finite.
  *
  * Alignment: weight planes, scales and activation rows must be 16-byte
  * aligned; workspaces 256-byte aligned.
@@ -356,7 +364,9 @@ brq_status brq_moe_dbf_ffn(const uint16_t* x, const float* logits,
  *
  *   x   device, bf16 [M][n1*n2];  H device, fp32 [n1][n1];  R device, fp32 [n2][n2]
  *   y   device, out, bf16 [M][n1*n2]; must not overlap x
- *   M >= 1; n1 == n2 == 64.
+ *   M >= 1; n1 == n2 == 64 (the 4096-wide rows of the prefill workload; other
+ *   factor sizes, e.g. 32 x 64 or 48 x 64 for hidden sizes 2048 and 3072, are
+ *   not built and give BRQ_E_SHAPE).
  */
 brq_status brq_kron_rotate(const uint16_t* x, int64_t M, const float* H, int64_t n1,
                            const float* R, int64_t n2, uint16_t* y, void* stream);
