@@ -142,12 +142,15 @@ __device__ __forceinline__ void b_compute(const BPre<NB, CPW>& bp, const u32x4* 
 template <int MODE, int CPW, int MAXR>
 struct WaveStage {
   uint2 lo[CPW][MAXR], hi[CPW][MAXR];
-  // ST_BF16: each row of the wave's slice is staged as fp16(x * 2^s), s a
-  // power of two that puts the row's largest |x| in [2^14, 2^15): a bf16 value
-  // is exact in fp16 there whatever its magnitude (no overflow at 65504, no
-  // loss below 2^-14); us[i] = -s of the row whose MFMA output this lane
-  // holds in element i (rows 4kb .. 4kb+3 for lane l = 16kb + j), undone
-  // exactly by unscale(). Other modes stage unscaled (us = 0).
+  // ST_BF16: each row of the wave's slice is staged as fp16(x * 2^s): s = 0
+  // when the row's largest |x| lies in [2^-8, 2^15) (every bf16 value of at
+  // least 2^-17 is exact in fp16 there, smaller ones move by at most 2^-25),
+  // else the power of two that puts it in [2^14, 2^15) (no overflow at
+  // 65504 whatever the magnitude, the same relative grid for tiny rows).
+  // When every row is in that range (one wave maximum over the slice and one
+  // ballot per row say so) no per-row maximum is taken. us[i] = -s of the row
+  // whose MFMA output this lane holds in element i (rows 4kb .. 4kb+3 for lane
+  // l = 16kb + j), undone exactly by unscale(). Other modes stage unscaled.
   int us[4];
 
   template <class ROWPTR>
@@ -179,9 +182,12 @@ struct WaveStage {
 #pragma unroll
     for (int i = 0; i < 4; ++i) us[i] = 0;
 #pragma unroll
-    for (int m = 0; m < MAXR; ++m) {
-      sm[m] = 0;
-      if (MODE == ST_BF16) {
+    for (int m = 0; m < MAXR; ++m) sm[m] = 0;
+    if (MODE == ST_BF16) {
+      uint32_t lm[MAXR];  // this lane's largest |x| bits of each row
+      uint32_t tm = 0;
+#pragma unroll
+      for (int m = 0; m < MAXR; ++m) {
         uint32_t mx = 0;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
@@ -189,11 +195,23 @@ struct WaveStage {
 #pragma unroll
           for (int h = 0; h < 4; ++h) mx = max(mx, max(w4[h] & 0x7fffu, (w4[h] >> 16) & 0x7fffu));
         }
-        mx = wave_max_u32(mx);
-        sm[m] = 14 - ((int)(mx >> 7) - 127);  // an all-zero row gets 141: harmless, every value is 0
-        // selected from scalars, not from an indexed array (which would go to scratch)
+        lm[m] = mx;
+        tm = max(tm, mx);
+      }
+      // every row in range: the slice's largest below 2^15 and a value of at
+      // least 2^-8 in each row (bf16 exponent field 119 .. 141)
+      bool all_in = wave_max_u32(tm) < (142u << 7);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) us[i] = (4 * kb + i == m) ? -sm[m] : us[i];
+      for (int m = 0; m < MAXR; ++m) all_in = all_in && __ballot(lm[m] >= (119u << 7)) != 0;
+      if (!all_in) {  // uniform across the wave
+#pragma unroll
+        for (int m = 0; m < MAXR; ++m) {
+          const int e = (int)(wave_max_u32(lm[m]) >> 7);  // biased exponent of the row's largest |x|
+          sm[m] = (e >= 142 || e < 119) ? 141 - e : 0;   // an all-zero row gets 141: harmless
+          // selected from scalars, not from an indexed array (which would go to scratch)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) us[i] = (4 * kb + i == m) ? -sm[m] : us[i];
+        }
       }
     }
 #pragma unroll

@@ -272,8 +272,11 @@ __device__ __forceinline__ void reduce_waves_cb(f32x4 (&acc)[CB][NB][1], f32x4* 
 // gate/up: one workgroup per (CB blocks of 16 intermediate columns, active
 // expert). The sign words of all CB blocks are loaded first; the expert's
 // tokens are staged once per tile of up to tile_rows tokens (each wave its own
-// K-slice, bf16 -> permuted fp16) and multiplied by every block, so a
+// K-slice, bf16 -> permuted scaled fp16) and multiplied by every block, so a
 // workgroup keeps CB blocks' loads in flight and pays one staging per tile.
+// The tile body is specialised by the expert's count (1/2/4/8/16 staged rows,
+// section 7 item 1 of the DBF post: kernels chosen by the observed per-expert
+// counts), picked per workgroup at run time.
 template <int CPW, int MAXR, int CB>
 __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__ x, int H, int I,
                                                     const uint4* __restrict__ gs, const uint16_t* __restrict__ gsc,
@@ -339,7 +342,12 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
         }
       }
     };
-    if (MAXR > 4 && rows <= 4) tile(std::integral_constant<int, 4>{});
+    // the staged row slots follow the expert's count: 1, 2, 4, 8 or MAXR rows
+    // (each variant stages, converts and unscales only the rows it holds)
+    if (rows <= 1) tile(std::integral_constant<int, 1>{});
+    else if (MAXR > 2 && rows <= 2) tile(std::integral_constant<int, (MAXR > 2 ? 2 : MAXR)>{});
+    else if (MAXR > 4 && rows <= 4) tile(std::integral_constant<int, (MAXR > 4 ? 4 : MAXR)>{});
+    else if (MAXR > 8 && rows <= 8) tile(std::integral_constant<int, (MAXR > 8 ? 8 : MAXR)>{});
     else tile(std::integral_constant<int, MAXR>{});
     __syncthreads();
     reduce_waves_cb<CB, 2>(acc, reinterpret_cast<f32x4*>(smem));

@@ -44,9 +44,9 @@
  *  - every other product on the fp16 matrix cores takes the activations as
  *    fp16(x * 2^s), s a power of two per row (per staged slice of a row on the
  *    few-row paths) that puts the largest |x| in [2^14, 2^15) when it lies
- *    outside [2^-8, 2^15), else 0, undone exactly after the product: every
- *    bf16 value is exact in fp16 there or lies below 2^-24 of the row (slice)
- *    maximum;
+ *    outside [2^-8, 2^15), else 0, undone exactly after the product; every
+ *    staged value of at least 2^-17 is then exact, smaller ones move by at
+ *    most 2^-25 (at most 2^-17 of the row maximum);
  *  - fp32 intermediates (DBF h_s, the MoE SwiGLU output) are stored as fp32
  *    and enter the next product as two fp16 pieces of v * 2^s (s as above for
  *    the staged slice or row, the largest near 2^14): about 22 significant
