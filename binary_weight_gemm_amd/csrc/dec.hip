@@ -514,6 +514,7 @@ hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_
     else gemm_dec_lds<8>(x, M, N, K, s4, scales, y, y_bf16, st);
     return hipGetLastError();
   }
+  if (!mid_fits(M, N, K)) return launch_gemm_pf(x, M, N, K, signs, scales, y, y_bf16, ws, st);
   return launch_gemm_mid(x, M, N, K, signs, scales, y, y_bf16, ws, st);
 }
 

@@ -31,21 +31,25 @@ constexpr int64_t kDecLdsBytes = 64 * 1024;
 bool gemm_dec_in_lds(int64_t M, int64_t K);
 hipError_t launch_gemm_dec(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
-// Rows not taken by the one-launch path (M <= 64): split-K matrix-core product
-// over 128-column tiles (+ a slice-sum launch when K is split); `ws` holds
-// mid_ws_bytes(M, N, K) bytes (the rows' staging exponents, then the
-// K-slice partials).
+// Rows not taken by the one-launch path (M <= 64): bf16 matrix-core product
+// over 64-column tiles, K split over the waves of a workgroup and, where the
+// grid needs it, over workgroups (+ a slice-sum launch); `ws` holds
+// mid_ws_bytes(M, N, K) bytes (the K-slice partials). Shapes whose activations
+// or sign plane reach 4 GiB (mid_fits false) take the prefill path.
+bool mid_fits(int64_t M, int64_t N, int64_t K);
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K);
+size_t pf_ws_bytes(int64_t M, int64_t K);
 // workspace of launch_gemm_dec (M <= 64)
 inline size_t gemm_dec_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  return gemm_dec_in_lds(M, K) ? 0 : mid_ws_bytes(M, N, K);
+  if (gemm_dec_in_lds(M, K)) return 0;
+  return mid_fits(M, N, K) ? mid_ws_bytes(M, N, K) : pf_ws_bytes(M, K);
 }
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                            const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 // Many activation rows (prefill): x staged to `ws` (pf_ws_bytes) as permuted
 // fp16 with a power-of-two scale per row, then the 256 x 256 direct-to-LDS
-// matrix-core kernel, which undoes the scales in its epilogue.
-size_t pf_ws_bytes(int64_t M, int64_t K);
+// matrix-core kernel, which undoes the scales in its epilogue (pf_ws_bytes
+// above).
 hipError_t launch_gemm_pf(const uint16_t* x, int M, int N, int K, const uint64_t* signs,
                           const uint16_t* scales, void* y, int y_bf16, void* ws, hipStream_t st);
 // The product on rows already staged by launch_prep_rows (xp, rexp), with one

@@ -2,56 +2,62 @@
 // vector and the prefill tiles, "LLM binarization, Episode 01: DBF", section 4:
 // each matrix is now applied to a handful of vectors).
 //
-// The work is split into 128-column tiles x K-slices of at most 8 k-steps
-// (one 128-byte line of every sign row). A workgroup (4 waves, 32 columns
-// each) first issues direct loads of all sign records of its slice into LDS
-// and reads its scales; the activations stream through registers: each wave
-// loads its share of the bf16 rows PREF k-steps ahead and writes them, as
-// they are, in the permuted operand order to one of two LDS stages. Every
-// wave multiplies all rows (TT tiles of 16) by its two 16-column groups with
-// v_mfma_f32_16x16x32_bf16 on +-1 weight operands (bf16 activations and +-1
-// are exact, so a k-step's MFMAs give the group's signed sums of x in fp32,
-// for x of any magnitude) and adds each group sum times its fp16 scale into
-// the fp32 result: one activation operand serves two MFMAs and one weight
-// operand serves TT.
+// A workgroup owns 64 output columns and a range of at most 32 k-steps (one
+// k-step = 128 k = one scale group); its eight waves take every eighth k-step
+// of the range (wave w: steps w, w+8, ...), each for all 64 columns and all M
+// rows (two waves per SIMD hide each other's waits).
+//  - The workgroup's sign records (16 B per column and k-step) and fp16
+//    scales are loaded once, by all waves together, into LDS tables where
+//    each column's consecutive k-steps are contiguous, as they are in memory
+//    (every load instruction covers long contiguous runs); one barrier.
+//  - The activation rows stream global -> LDS with direct loads
+//    (global_load_lds_dwordx4) through a ring owned by each wave; a stage
+//    holds 1/sub of a k-step of every row (about 4 KiB), chunk c of staged row
+//    r at slot c ^ ((r / sub) % (16 / sub)), so the 16 lanes of one LDS pass
+//    hit 16 different bank groups.
+//  - v_mfma_f32_16x16x32_bf16 multiplies the bf16 rows as they are by +-1
+//    weights (both exact, so a k-step's four MFMAs give the group's signed sums
+//    of x in fp32 for x of any magnitude), and each group sum is added times
+//    its fp16 scale into the fp32 result. A lane's 8 k of a 32-k sub-step are
+//    consecutive in both operands: byte kb of the sub-step's sign word, with a
+//    copy shifted up by 15, gives each weight pair by one shift and one and-or.
+// At the end the waves' results meet in LDS and are added in wave order.
 //
-// With several K-slices each workgroup writes its fp32 partial tile to the
-// workspace and a second launch adds the slices in slice order (deterministic).
-// (Meeting inside the product launch instead -- last-arriving workgroup adds
-// the tile -- needs a device-scope release per workgroup, which writes back
-// the whole L2 of its chiplet and cost far more than the extra launch.)
+// When the k-steps are split over several workgroups (K-slices), each writes
+// its fp32 partial result to the workspace and a second launch adds the
+// slices in slice order (deterministic). The split is chosen so that the grid
+// is about one workgroup per compute unit, each wave has a k-step where K
+// allows it, and no workgroup has more than 32.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace brq {
 
 namespace {
 
-constexpr int MID_NB = 2;            // 16-column groups per wave
-constexpr int MID_BN = 64 * MID_NB;  // columns per workgroup
-constexpr int MID_KPS = 8;           // most k-steps per slice: 8 x 16 B = one 128-byte line of a sign row
-
-// k-steps of activations in flight in registers
-__host__ __device__ constexpr int mid_pref(int tt) { return tt <= 2 ? 4 : 2; }
-// dynamic LDS: the slice's sign records, its scale pairs, two activation stages
-__host__ __device__ constexpr int mid_lds_bytes(int tt) {
-  return MID_BN * MID_KPS * 16 + MID_BN * MID_KPS * 4 + 2 * 16 * tt * 256;
-}
+constexpr int MID_BN = 64;  // columns of a workgroup (four 16-column groups, each in every wave)
+constexpr int MID_NB = 4;   // 16-column groups per wave
+constexpr int MID_KPS = 32; // most k-steps of a workgroup
 
 struct MidPlan {
-  int tiles, slices, kps;  // column tiles, K-slices, k-steps per slice
+  int tiles, splits, kps;  // column tiles, K-slices, k-steps per K-slice
 };
 
-// Slices of 8 k-steps (each column's sign records of a slice are one 128-byte
-// line), halved while the grid has fewer than 256 workgroups.
+// About one workgroup per compute unit (at least 256 workgroups where K
+// allows one k-step per wave), and at most MID_KPS k-steps per workgroup.
 MidPlan mid_plan(int64_t N, int64_t K) {
   MidPlan p;
   const int nk = (int)(K / 128);
   p.tiles = (int)((N + MID_BN - 1) / MID_BN);
-  int kps = MID_KPS;
-  while (kps > 1 && (int64_t)p.tiles * ((nk + kps - 1) / kps) < 256) kps /= 2;
-  p.kps = kps;
-  p.slices = (nk + kps - 1) / kps;
+  const int need = (nk + MID_KPS - 1) / MID_KPS;
+  const int fill = std::max(1, 256 / p.tiles);
+  const int most = std::max(1, nk / 8);  // one k-step for each of the 8 waves
+  const int s = std::max(need, std::min(fill, most));
+  p.kps = (nk + s - 1) / s;
+  p.splits = (nk + p.kps - 1) / p.kps;
   return p;
 }
 
@@ -62,261 +68,315 @@ __device__ __forceinline__ f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  0, 0);
 }
 
+// wait until at most N vector memory operations are outstanding (a larger
+// count waits as for 63: later loads complete after earlier ones); compiler
+// fences keep every memory access on its side (s_waitcnt immediate: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  constexpr int n = N < 63 ? N : 63;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void lgkm_wait0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 }  // namespace
 
-template <int TT>
-__global__ __launch_bounds__(256) void k_mid(const uint16_t* x, int M, int N, int K,
-                                             const uint32_t* __restrict__ signs, const uint16_t* __restrict__ scales,
-                                             void* __restrict__ y, int y_bf16, float* __restrict__ part, int kps,
-                                             int S) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int PREF = mid_pref(TT), SB = 16 * TT * 256;
-  constexpr int NB = MID_NB, BN = MID_BN;
-  uint8_t* const l_sig = lds;                                                 // [2*kps blocks][1 KiB]
-  uint32_t* const l_sc = reinterpret_cast<uint32_t*>(lds + BN * MID_KPS * 16);  // [kps][BN] scale pairs
-  uint8_t* const l_a = lds + BN * MID_KPS * 20;                               // [2][16*TT rows][256 B]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 15, kb = lane >> 4;
-  const int tile = blockIdx.x, sl = blockIdx.y;
-  const int nk = K >> 7;
-  const int kt0 = sl * kps, kt1 = kt0 + kps < nk ? kt0 + kps : nk, nks = kt1 - kt0;
-  const int n0 = tile * BN;
-  const int KW = K >> 5;  // 32-bit sign words per weight row
-
-  // ---- the slice's sign records, one direct load per 64 x 16 B: block i
-  // holds columns C*i .. C*i+C-1 (C = 64/kps) for all kps steps, lane L ->
-  // column C*i + L % C, step L / C, at byte 16*L of the block. A column's
-  // records of the slice are contiguous in memory (one line when kps = 8).
-  // Columns past N repeat N-1 and steps past K repeat the last (never used).
-  {
-    const int C = 64 / kps;
-    const int c = lane % C, q = lane / C;
-    const int kt = kt0 + q < nk ? kt0 + q : nk - 1;
-    for (int i = wave; i < 2 * kps; i += 4) {
-      const int n = n0 + C * i + c < N ? n0 + C * i + c : N - 1;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(signs + (size_t)n * KW + 4 * kt), l_sig + i * 1024,
-                                       16, 0, 0);
-    }
-  }
-
-  // ---- the slice's scales: thread e -> (column e % BN, step e / BN)
-  uint32_t scv[MID_KPS * BN / 256];
+// The KW waves' results meet in LDS (reused: every wave is past its last
+// step) and are added in wave order: item (t, g, e) of lane L of wave w at
+// red[(w * IT + (t * NB + g) * 4 + e) * 64 + L]; then y (one K-slice) or this
+// slice's partial result.
+template <int TT, int KW>
+__device__ __forceinline__ void mid_reduce_store(const f32x4 (&acc)[TT][MID_NB], uint8_t* lds, void* y, int y_bf16,
+                                                 float* part, int M, int N, int n0, int S, int lane, int ks) {
+  constexpr int NB = MID_NB, IT = TT * NB * 4;
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < MID_KPS * BN / 256; ++i) {
-    const int e = tid + 256 * i, c = e % BN, q = e / BN;
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int g = 0; g < NB; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(ks * IT + (t * NB + g) * 4 + e) * 64 + lane] = acc[t][g][e];
+  __syncthreads();
+  // output (row, col) of the workgroup: MFMA lane (col % 16) + 16 * ((row % 16) / 4),
+  // item (row / 16, col / 16, row % 4)
+  const int np = gridDim.x * MID_BN;
+  for (int o = threadIdx.x; o < 16 * TT * MID_BN; o += 64 * KW) {
+    const int row = o >> 6, col = o & 63, n = n0 + col;
+    if (row >= M || n >= N) continue;
+    const int rr = row & 15;
+    const int it = ((row >> 4) * NB + (col >> 4)) * 4 + (rr & 3);
+    const int ln = (col & 15) + 16 * (rr >> 2);
+    float v = red[it * 64 + ln];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) v += red[(w * IT + it) * 64 + ln];
+    if (S == 1) store_out(y, (size_t)row * N + n, v, y_bf16);
+    else part[((size_t)blockIdx.y * M + row) * np + n] = v;
+  }
+}
+
+// Table row stride: P = kps | 1 entries (odd, so that 16 lanes reading 16
+// columns at one step hit 16 different 16-byte bank groups).
+// Eight waves per workgroup (two per SIMD, which hide each other's waits). A
+// ring stage holds 1/sub of a k-step of the TT row tiles (sub = 1, 2, 4: 256,
+// 128 or 64 bytes of each row), about 4 KiB, so that three or four stages per
+// wave fit beside the tables.
+__host__ __device__ constexpr int midt_kw(int) { return 8; }
+__host__ __device__ constexpr int midt_sub(int tt) { return tt == 1 ? 1 : tt == 2 ? 2 : 4; }
+__host__ __device__ constexpr int midt_da(int tt) { return tt == 3 ? 4 : 3; }
+__host__ __device__ constexpr int midt_sb(int tt) { return tt * 16 * 256 / midt_sub(tt); }
+__host__ __device__ constexpr int midt_tab_bytes(int kps) { return (64 * (kps | 1) * 18 + 15) & ~15; }
+// the tables and rings, or (reused at the end) the waves' results: kw x tt x
+// 16 rows x 64 columns of fp32
+__host__ __device__ constexpr int midt_lds_bytes(int tt, int kps) {
+  return midt_tab_bytes(kps) + midt_kw(tt) * midt_da(tt) * midt_sb(tt) > midt_kw(tt) * tt * 4096
+             ? midt_tab_bytes(kps) + midt_kw(tt) * midt_da(tt) * midt_sb(tt)
+             : midt_kw(tt) * tt * 4096;
+}
+static_assert(midt_lds_bytes(1, MID_KPS) <= 160 * 1024 && midt_lds_bytes(2, MID_KPS) <= 160 * 1024 &&
+                  midt_lds_bytes(3, MID_KPS) <= 160 * 1024 && midt_lds_bytes(4, MID_KPS) <= 160 * 1024,
+              "tables and rings exceed the LDS");
+
+// Activation loads a wave has issued after those of its stage unit u (unit
+// = k-step i * sub + h) when unit u's products start (everything issued before
+// the tables' barrier has landed by then): the refills of units p + DA issued
+// after the products of units p < u, counted from the one that brought u.
+__host__ __device__ constexpr int midt_wait(int tt, int units, int u) {
+  const int da = midt_da(tt), la = 4 * tt / midt_sub(tt);
+  int n = 0;
+  for (int p = 0; p < u; ++p)
+    if (p + da < units && p + da > u) n += la;
+  return n;
+}
+
+struct MidTab {
+  const uint8_t* xb;      // activations
+  uint32_t xo[4], xl[4];  // activation row offsets (full tiles; the last tile), per load of a tile
+  uint32_t rt[MID_NB];    // byte offset of column 16g + j's row in the record table
+  int q0, K, j, kb, sl0;  // first global / local k-step of the wave
+};
+
+template <int TT, int CNT>
+__device__ __forceinline__ void midt_steps(f32x4 (&acc)[TT][MID_NB], const MidTab& L, uint8_t* lds, uint8_t* aring,
+                                           const uint4* __restrict__ recs, const uint16_t* __restrict__ scales, int N,
+                                           int G, int n0, int kt0, int nks, int P, int lane, int ks) {
+  constexpr int DA = midt_da(TT), SB = midt_sb(TT), NB = MID_NB, KW = midt_kw(TT), SUB = midt_sub(TT);
+  constexpr int RB = 256 / SUB, LPT = 4 / SUB;  // bytes per staged row, direct loads per row tile
+  constexpr int UNITS = CNT * SUB;
+  const int j = L.j, kb = L.kb;
+  auto load_a = [&](int u) {
+    const int i = u / SUB, h = u % SUB;
+    const uint8_t* src = L.xb + (size_t)(L.q0 + KW * i) * 256 + h * RB;
+    uint8_t* dst = aring + (u % DA) * SB;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int r = 0; r < LPT; ++r) {
+        const void* g = t < TT - 1 ? src + (size_t)t * 32 * L.K + L.xo[r] : src + L.xl[r];
+        __builtin_amdgcn_global_load_lds(g, dst + (16 * t + (16 / LPT) * r) * RB, 16, 0, 0);
+      }
+  };
+#pragma unroll
+  for (int u = 0; u < DA && u < UNITS; ++u) load_a(u);
+  // the tables: entry e = c * P + s (column c, local step s; s >= nks repeats a valid step)
+  uint16_t* stab = reinterpret_cast<uint16_t*>(lds + 64 * P * 16);
+  for (int i = ks; i < P; i += KW) {
+    const int e = 64 * i + lane, c = e / P, sl = e - c * P;
     const int n = n0 + c < N ? n0 + c : N - 1;
-    const int kt = kt0 + q < nk ? kt0 + q : nk - 1;
-    scv[i] = q < kps ? scales[(size_t)n * nk + kt] : 0u;
+    const int q = kt0 + (sl < nks ? sl : nks - 1);
+    __builtin_amdgcn_global_load_lds(recs + (size_t)n * G + q, lds + 64 * i * 16, 16, 0, 0);
   }
+  for (int i = ks; i < P; i += KW) {
+    const int e = 64 * i + lane, c = e / P, sl = e - c * P;
+    const int n = n0 + c < N ? n0 + c : N - 1;
+    const int q = kt0 + (sl < nks ? sl : nks - 1);
+    stab[e] = scales[(size_t)n * G + q];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t one2;  // bf16 +1.0 pairs in a register: the and-or is then one instruction
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(one2));
+  // slot of chunk c of a staged row r: c ^ ((r / sub) % (16 / sub)) (the 16
+  // lanes of one pass, rows j, hit 16 different 16-byte bank groups)
+  const int swz = (j / SUB) & (16 / SUB - 1);
 
-  // ---- activations: lane (rr = L/16, c = L%16) of wave w stages rows
-  // r = 4*TT*w + 4i + rr (i < TT; rows past M repeat M-1, never stored),
-  // permuted 16-byte chunk c of each k-step: run c/4, pairs b = 4(c%4) + u,
-  // i.e. bf16 elements 4(c%4)+u (low halves) and 16+4(c%4)+u (high halves)
-  // of the run -- two 8-byte loads. The chunk goes to LDS slot c ^ (r%16).
-  const int rr = lane >> 4, cc = lane & 15;
-  const uint8_t* xr[TT];
-  uint32_t a_dst[TT];
+  u32x4 R[NB];
+  uint32_t C[NB];
+  f32x4 gs[TT][NB];
+  static_for<0, UNITS>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int i = u / SUB, h = u % SUB;
+    vm_wait<midt_wait(TT, UNITS, u)>();  // unit u's activations are in LDS
+    if constexpr (h == 0) {
+      const int sl = L.sl0 + KW * i;
 #pragma unroll
-  for (int i = 0; i < TT; ++i) {
-    const int r = 4 * TT * wave + 4 * i + rr;
-    const int rg = r < M ? r : M - 1;
-    xr[i] = reinterpret_cast<const uint8_t*>(x) + (size_t)rg * K * 2 + (cc >> 2) * 64 + (cc & 3) * 8;
-    a_dst[i] = (uint32_t)(r * 256 + ((cc ^ (r & 15)) * 16));
-  }
-  uint2 ra[PREF][TT][2];
-  // (x is not __restrict__: the prefetch loads must stay ahead of the
-  // barriers, which are memory clobbers)
-  auto load_step = [&](uint2 (&dst)[TT][2], int q) {
-    const size_t off = (size_t)(kt0 + (q < nks ? q : nks - 1)) * 256;
-#pragma unroll
-    for (int i = 0; i < TT; ++i) {
-      dst[i][0] = *reinterpret_cast<const uint2*>(xr[i] + off);
-      dst[i][1] = *reinterpret_cast<const uint2*>(xr[i] + off + 32);
+      for (int g = 0; g < NB; ++g) {
+        R[g] = *reinterpret_cast<const u32x4*>(lds + L.rt[g] + sl * 16);
+        C[g] = stab[(L.rt[g] >> 4) + sl];
+      }
     }
-  };
-  auto stage_step = [&](const uint2 (&src)[TT][2], int st) {
+    const uint8_t* as = aring + (u % DA) * SB + j * RB;
 #pragma unroll
-    for (int i = 0; i < TT; ++i) {
-      const uint2 lo = src[i][0], hi = src[i][1];
-      u32x4 o;
-      // pair (element b, element 16 + b): low halves, then high halves
-      o[0] = __builtin_amdgcn_perm(hi.x, lo.x, 0x05040100u);
-      o[1] = __builtin_amdgcn_perm(hi.x, lo.x, 0x07060302u);
-      o[2] = __builtin_amdgcn_perm(hi.y, lo.y, 0x05040100u);
-      o[3] = __builtin_amdgcn_perm(hi.y, lo.y, 0x07060302u);
-      *reinterpret_cast<u32x4*>(l_a + st * SB + a_dst[i]) = o;
+    for (int s2 = 0; s2 < 4 / SUB; ++s2) {
+      const int s = h * (4 / SUB) + s2;  // 32-k sub-step of the k-step
+      const int slot = ((4 * s2 + kb) ^ swz) * 16;
+      u32x4 a[TT];
+#pragma unroll
+      for (int t = 0; t < TT; ++t) a[t] = *reinterpret_cast<const u32x4*>(as + t * 16 * RB + slot);
+#pragma unroll
+      for (int g = 0; g < NB; ++g) {
+        // the lane's 8 weights: bits 8kb .. 8kb+7 of word s; pair w = bits 2w, 2w+1
+        const uint32_t w8 = __builtin_amdgcn_ubfe(R[g][s], 8 * kb, 8);
+        const uint32_t w16 = w8 | (w8 << 15);
+        u32x4 b;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) b[w] = ((w16 << (15 - 2 * w)) & 0x80008000u) | one2;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) gs[t][g] = mfma16_bf16(a[t], b, s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : gs[t][g]);
+      }
     }
-  };
+    if constexpr (h == SUB - 1) {
 #pragma unroll
-  for (int d = 0; d < PREF; ++d) load_step(ra[d], d);
+      for (int g = 0; g < NB; ++g) {
+        const float sc = f16_bits_to_f32(C[g]);
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][g][e] = fmaf(sc, gs[t][g][e], acc[t][g][e]);
+      }
+    }
+    lgkm_wait0();  // this unit's ring reads are done before a direct load refills the stage
+    if (u + DA < UNITS) load_a(u + DA);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  __builtin_amdgcn_s_waitcnt(0);
+}
 
+// Offsets of activations are 32-bit: M * K * 2 bytes are below 4 GiB on this
+// path (mid_fits).
+template <int TT>
+__global__ __launch_bounds__(64 * midt_kw(TT)) void k_midt(const uint16_t* __restrict__ x, int M, int N, int K,
+                                                           const uint4* __restrict__ recs,
+                                                           const uint16_t* __restrict__ scales, void* __restrict__ y,
+                                                           int y_bf16, float* __restrict__ part, int kps, int S) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int DA = midt_da(TT), SB = midt_sb(TT), NB = MID_NB, KW = midt_kw(TT), SUB = midt_sub(TT);
+  constexpr int LPT = 4 / SUB, RPL = 16 / LPT;  // direct loads per row tile, rows per load
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const int G = K >> 7;
+  const int kt0 = blockIdx.y * kps, nks = min(kps, G - kt0);
+  const int cnt = nks > ks ? (nks - ks + KW - 1) / KW : 0;  // this wave's k-steps
+  const int n0 = blockIdx.x * MID_BN;
+  const int P = kps | 1;
+
+  MidTab L;
+  L.j = lane & 15;
+  L.kb = lane >> 4;
+  L.K = K;
+  L.q0 = kt0 + ks;
+  L.sl0 = ks;
+  L.xb = reinterpret_cast<const uint8_t*>(x);
+  // direct load r of a row tile moves rows RPL*r .. RPL*r + RPL-1 of it: lane
+  // takes row RPL*r + lane / (16/SUB) and puts the chunk that belongs at slot
+  // lane % (16/SUB) there (the swizzle above)
 #pragma unroll
-  for (int i = 0; i < MID_KPS * BN / 256; ++i) {
-    const int e = tid + 256 * i;
-    l_sc[e] = scv[i] | (scv[i] << 16);
+  for (int r = 0; r < LPT; ++r) {
+    const int cpr = 16 / SUB;  // chunks per staged row
+    const int rr = RPL * r + lane / cpr, p = lane % cpr, rl = 16 * (TT - 1) + rr;
+    const int c = p ^ ((rr / SUB) & (cpr - 1));
+    L.xo[r] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(c * 16);
+    L.xl[r] = (uint32_t)(rl < M ? rl : M - 1) * (uint32_t)K * 2u + (uint32_t)(c * 16);
   }
-  stage_step(ra[0], 0);
-  load_step(ra[0], PREF);
-  // every older load of this wave -- its sign records included -- landed
-  // (only the activation loads of steps 1 .. PREF may be in flight), then
-  // every wave's stage-0 writes and sign records are in
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * TT * PREF) : "memory");
-
+#pragma unroll
+  for (int g = 0; g < NB; ++g) L.rt[g] = (uint32_t)((16 * g + L.j) * P * 16);
   f32x4 acc[TT][NB];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
 #pragma unroll
     for (int g = 0; g < NB; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int bsh = 4 * kb;  // the lane's k block takes pairs 4*kb .. 4*kb+3 of each half-run
-  // where this lane's columns sit in the sign blocks
-  int sg_off[NB];
-  {
-    const int C = 64 / kps;
-#pragma unroll
-    for (int g = 0; g < NB; ++g) {
-      const int cl = 16 * (NB * wave + g) + j;
-      sg_off[g] = (cl / C) * 1024 + (cl % C) * 16;
-    }
+  uint8_t* const aring = lds + midt_tab_bytes(kps) + ks * DA * SB;
+#define BRQ_MIDT(C) midt_steps<TT, C>(acc, L, lds, aring, recs, scales, N, G, n0, kt0, nks, P, lane, ks)
+  switch (cnt) {  // uniform across the wave; every wave loads its share of the tables
+    case 0: BRQ_MIDT(0); break;
+    case 1: BRQ_MIDT(1); break;
+    case 2: BRQ_MIDT(2); break;
+    case 3: BRQ_MIDT(3); break;
+    case 4: BRQ_MIDT(4); break;
+    case 5: if constexpr (KW == 4) BRQ_MIDT(5); break;
+    case 6: if constexpr (KW == 4) BRQ_MIDT(6); break;
+    case 7: if constexpr (KW == 4) BRQ_MIDT(7); break;
+    default: if constexpr (KW == 4) BRQ_MIDT(8); break;
   }
-  const int sg_step = (64 / kps) * 16;
-
-  // one k-step: stage step q+1 into the other LDS stage (every wave finished
-  // reading it before the last barrier) and refill its registers with step
-  // q+1+PREF (both unconditional: past the slice they repeat its last step,
-  // unused), then multiply step q. d = q % PREF picks the registers.
-  auto step = [&](const int q, const int d) {
-    stage_step(ra[(d + 1) % PREF], (q + 1) & 1);
-    load_step(ra[(d + 1) % PREF], q + 1 + PREF);
-    const uint8_t* base = l_a + (q & 1) * SB;
-    u32x4 a[4][TT];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < TT; ++t)  // chunk 4s+kb of row 16t+j
-        a[s][t] = *reinterpret_cast<const u32x4*>(base + (16 * t + j) * 256 + (((4 * s + kb) ^ j) * 16));
-    u32x4 w4[NB];
-    float sc[NB];
-#pragma unroll
-    for (int g = 0; g < NB; ++g) {
-      w4[g] = *reinterpret_cast<const u32x4*>(l_sig + sg_off[g] + q * sg_step);
-      sc[g] = f16_bits_to_f32(l_sc[q * BN + 16 * (NB * wave + g) + j] & 0xffffu);
-    }
-    f32x4 gs[TT][NB];  // the k-step's (one scale group's) signed sums
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int g = 0; g < NB; ++g) {
-        const uint32_t w = w4[g][s] >> bsh;
-        u32x4 b;  // bf16 +-1 pairs
-#pragma unroll
-        for (int u = 0; u < 4; ++u) b[u] = ((w << (15 - u)) & 0x80008000u) | 0x3f803f80u;
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-          gs[t][g] = mfma16_bf16(a[s][t], b, s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : gs[t][g]);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int g = 0; g < NB; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][g][i] = fmaf(sc[g], gs[t][g][i], acc[t][g][i]);
-    // the next stage's writes are in and every wave is done with this one
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  // whole rounds of PREF steps with no branch inside, so that the compiler's
-  // wait before each staging counts the PREF-1 younger steps in flight
-  int q = 0;
-  for (; q + PREF <= nks; q += PREF) {
-#pragma unroll
-    for (int d = 0; d < PREF; ++d) step(q + d, d);
-  }
-#pragma unroll
-  for (int d = 0; d < PREF - 1; ++d)
-    if (q + d < nks) step(q + d, d);
-  __builtin_amdgcn_s_waitcnt(0);  // nothing in flight when the workgroup ends
-
-  // lane (kb, j) holds rows 16t + 4kb + i of column cw + 16g + j
-  const int cw = n0 + 16 * NB * wave;
-  if (S == 1) {
-#pragma unroll
-    for (int g = 0; g < NB; ++g) {
-      const int col = cw + 16 * g + j;
-      if (col < N) {
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 16 * t + 4 * kb + i;
-            if (m < M) store_out(y, (size_t)m * N + col, acc[t][g][i], y_bf16);
-          }
-      }
-    }
-    return;
-  }
-  // this slice's partial tile [M][BN] at part[(tile*S + sl)*M*BN ...]; a
-  // second launch adds the slices
-  float* mine = part + ((size_t)tile * S + sl) * M * BN;
-#pragma unroll
-  for (int g = 0; g < NB; ++g)
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * t + 4 * kb + i;
-        if (m < M) mine[m * BN + 16 * (NB * wave + g) + j] = acc[t][g][i];
-      }
+#undef BRQ_MIDT
+  mid_reduce_store<TT, KW>(acc, lds, y, y_bf16, part, M, N, n0, S, lane, ks);
 }
 
-// y = the sum of the S partial tiles, in slice order (deterministic); one
-// thread per four columns of a tile row.
-__global__ __launch_bounds__(256) void k_mid_sum(const float* __restrict__ part, int M, int N, int tiles, int S,
+// y = the sum of the S partial results part[s][M][np], in slice order
+// (deterministic); one thread per four columns of a row.
+__global__ __launch_bounds__(256) void k_mid_sum(const float* __restrict__ part, int M, int N, int np, int S,
                                                  void* __restrict__ y, int y_bf16) {
-  const int n4 = M * MID_BN / 4;  // float4s per partial tile
+  const int n4 = np / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)tiles * n4) return;
-  const int tile = (int)(e / n4), r = (int)(e - (int64_t)tile * n4);
-  const f32x4* all = reinterpret_cast<const f32x4*>(part) + (size_t)tile * S * n4 + r;
-  f32x4 v = all[0];
-  int s2 = 1;
-  for (; s2 + 4 <= S; s2 += 4) {
-    const f32x4 p0 = all[(size_t)s2 * n4], p1 = all[(size_t)(s2 + 1) * n4];
-    const f32x4 p2 = all[(size_t)(s2 + 2) * n4], p3 = all[(size_t)(s2 + 3) * n4];
-    v += p0;
-    v += p1;
-    v += p2;
-    v += p3;
-  }
-  for (; s2 < S; ++s2) v += all[(size_t)s2 * n4];
-  const int m = (4 * r) / MID_BN, c = tile * MID_BN + 4 * r - m * MID_BN;
+  if (e >= (int64_t)M * n4) return;
+  const int m = (int)(e / n4), c = 4 * (int)(e - (int64_t)m * n4);
+  const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)m * np + c);
+  const size_t step = (size_t)M * n4;
+  f32x4 v = p[0];
+  for (int s = 1; s < S; ++s) v += p[s * step];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (c + i < N) store_out(y, (size_t)m * N + c + i, v[i], y_bf16);
 }
 
+bool mid_fits(int64_t M, int64_t N, int64_t K) {
+  return (uint64_t)M * (uint64_t)K * 2u < (1ull << 32) && (uint64_t)N * (uint64_t)(K / 8) < (1ull << 32);
+}
+
 size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const MidPlan p = mid_plan(N, K);
-  return p.slices > 1 ? align256((size_t)p.tiles * p.slices * M * MID_BN * 4) : 0;
+  return p.splits > 1 ? align256((size_t)p.splits * M * p.tiles * MID_BN * 4) : 0;
+}
+
+template <typename Kern>
+static hipError_t mid_run(Kern kern, int threads, int lds, const uint16_t* x, int M, int N, int K,
+                          const uint64_t* signs, const uint16_t* scales, void* y, int y_bf16, float* part,
+                          const MidPlan& p, hipStream_t st) {
+  if (lds > 64 * 1024) {  // per-function opt-in beyond 64 KiB of dynamic LDS
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.tiles, p.splits), dim3(threads), lds, st, x, M, N, K,
+                     reinterpret_cast<const uint4*>(signs), scales, y, y_bf16, part, p.kps, p.splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int np = p.tiles * MID_BN;
+  const int64_t n = (int64_t)M * np / 4;
+  hipLaunchKernelGGL(k_mid_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, M, N, np, p.splits, y,
+                     y_bf16);
+  return hipGetLastError();
 }
 
 template <int TT>
-static hipError_t mid_launch(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
-                             void* y, int y_bf16, float* part, const MidPlan& p, hipStream_t st) {
-  const int lds = mid_lds_bytes(TT);
-  if (lds > 64 * 1024) {  // per-function opt-in beyond 64 KiB of dynamic LDS
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid<TT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k_mid<TT>, dim3(p.tiles, p.slices), dim3(256), lds, st, x, M, N, K,
-                     reinterpret_cast<const uint32_t*>(signs), scales, y, y_bf16, part, p.kps, p.slices);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.slices == 1) return e;
-  const int64_t n = (int64_t)p.tiles * M * MID_BN / 4;
-  hipLaunchKernelGGL(k_mid_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, M, N, p.tiles, p.slices, y,
-                     y_bf16);
-  return hipGetLastError();
+static hipError_t midt_launch(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
+                              void* y, int y_bf16, float* part, const MidPlan& p, hipStream_t st) {
+  return mid_run(&k_midt<TT>, 64 * midt_kw(TT), midt_lds_bytes(TT, p.kps), x, M, N, K, signs, scales, y, y_bf16, part,
+                 p, st);
 }
 
 hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
@@ -324,10 +384,10 @@ hipError_t launch_gemm_mid(const uint16_t* x, int M, int N, int K, const uint64_
   const MidPlan p = mid_plan(N, K);
   float* part = reinterpret_cast<float*>(ws);
   switch ((M + 15) / 16) {
-    case 1: return mid_launch<1>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
-    case 2: return mid_launch<2>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
-    case 3: return mid_launch<3>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
-    default: return mid_launch<4>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 1: return midt_launch<1>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 2: return midt_launch<2>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    case 3: return midt_launch<3>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
+    default: return midt_launch<4>(x, M, N, K, signs, scales, y, y_bf16, part, p, st);
   }
 }
 

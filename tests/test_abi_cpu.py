@@ -78,9 +78,9 @@ def test_size_queries(L):
     assert L.brq_sign_words(3, 65) == 0
     assert L.brq_scale_count(3, 64) == 0
     assert L.brq_gemm_workspace_bytes(1, 4096, 14336) == 0          # staged in LDS
-    # fp32 partial tiles: 14 K-slices of 8 k-steps x 32 tiles of 128 columns
-    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 14 * 32 * 64 * 128 * 4
-    # one K-slice (K = 512 over 256 tiles of 128 columns): no workspace
+    # 64-column tiles; K = 14336 split over 4 workgroups: 4 partial results of 64 x 4096 fp32
+    assert L.brq_gemm_workspace_bytes(64, 4096, 14336) == 4 * 64 * 4096 * 4
+    # one K-slice (K = 512 over 512 tiles of 64 columns): no workspace
     assert L.brq_gemm_workspace_bytes(64, 32768, 512) == 0
     assert L.brq_gemm_workspace_bytes(4096, 14336, 4096) == 4096 * 4096 * 2 + 4096 * 4   # staged rows, exponents
     assert L.brq_gemm_workspace_bytes(1, 16, 100) == 0

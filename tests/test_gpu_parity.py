@@ -121,6 +121,18 @@ def test_gemm_decode_f32(M, N, K):
     check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
 
 
+# 9..64 rows over 64-column tiles: each wave of a workgroup takes every
+# fourth k-step; these shapes give the waves 3, 4, 5 and 6 k-steps (ragged N,
+# partial last row tile) where the cases above give 1, 2, 7 and 8
+@pytest.mark.parametrize("M,N,K", [(64, 16384, 1536), (48, 16384, 2048), (30, 16400, 2560), (12, 16384, 3072)])
+def test_gemm_mid_wave_steps(M, N, K):
+    say("gemm mid wave steps", M, N, K)
+    y, o = _gemm_case(M, N, K, M * 7 + N)
+    check_f32(f64(y), o, F32_TOL, f"gemm {M}x{N}x{K}")
+    yb, _ = _gemm_case(M, N, K, M * 7 + N, out=torch.bfloat16)
+    check_bf16(yb, o, f"gemm {M}x{N}x{K} bf16")
+
+
 @pytest.mark.parametrize("N,K", [(40, 512), (1000, 1536), (2049, 4096), (48, 23040)])
 def test_gemm_single_row_wide_range(N, K):
     """A single activation row with K % 512 == 0 runs on the fp8 x fp4 matrix
