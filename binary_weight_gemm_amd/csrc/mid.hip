@@ -97,41 +97,40 @@ __device__ __forceinline__ void static_for(F&& f) {
 }  // namespace
 
 // The KW waves' results meet in LDS (reused: every wave is past its last
-// step) and are added in wave order: item (t, g, e) of lane L of wave w at
-// red[(w * IT + (t * NB + g) * 4 + e) * 64 + L]; then y (one K-slice) or this
-// slice's partial result.
+// step) and are added in wave order: the four values (t, g, 0..3) of lane L
+// of wave w at red[((w * TT * NB + t * NB + g) * 64 + L) * 4 ..]; then y (one
+// K-slice) or this slice's partial result. A thread takes a lane slot (t, g,
+// L): rows 16t + 4(L / 16) .. +3 of column 16g + L % 16.
 template <int TT, int KW>
 __device__ __forceinline__ void mid_reduce_store(const f32x4 (&acc)[TT][MID_NB], uint8_t* lds, void* y, int y_bf16,
-                                                 float* part, int M, int N, int n0, int S, int lane, int ks) {
-  constexpr int NB = MID_NB, IT = TT * NB * 4;
-  float* red = reinterpret_cast<float*>(lds);
+                                                 float* part, int M, int N, int n0, int sl, int S, int lane,
+                                                 int ks) {
+  constexpr int NB = MID_NB, TG = TT * NB;
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TT; ++t)
 #pragma unroll
-    for (int g = 0; g < NB; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[(ks * IT + (t * NB + g) * 4 + e) * 64 + lane] = acc[t][g][e];
+    for (int g = 0; g < NB; ++g) red[(ks * TG + t * NB + g) * 64 + lane] = acc[t][g];
   __syncthreads();
-  // output (row, col) of the workgroup: MFMA lane (col % 16) + 16 * ((row % 16) / 4),
-  // item (row / 16, col / 16, row % 4)
   const int np = gridDim.x * MID_BN;
-  for (int o = threadIdx.x; o < 16 * TT * MID_BN; o += 64 * KW) {
-    const int row = o >> 6, col = o & 63, n = n0 + col;
-    if (row >= M || n >= N) continue;
-    const int rr = row & 15;
-    const int it = ((row >> 4) * NB + (col >> 4)) * 4 + (rr & 3);
-    const int ln = (col & 15) + 16 * (rr >> 2);
-    float v = red[it * 64 + ln];
+  for (int o = threadIdx.x; o < TG * 64; o += 64 * KW) {
+    const int tg = o >> 6, ln = o & 63;
+    f32x4 v = red[tg * 64 + ln];
 #pragma unroll
-    for (int w = 1; w < KW; ++w) v += red[(w * IT + it) * 64 + ln];
-    if (S == 1) store_out(y, (size_t)row * N + n, v, y_bf16);
-    else part[((size_t)blockIdx.y * M + row) * np + n] = v;
+    for (int w = 1; w < KW; ++w) v += red[(w * TG + tg) * 64 + ln];
+    const int n = n0 + 16 * (tg % NB) + (ln & 15), r0 = 16 * (tg / NB) + 4 * (ln >> 4);
+    if (n >= N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = r0 + e;
+      if (row >= M) break;
+      if (S == 1) store_out(y, (size_t)row * N + n, v[e], y_bf16);
+      else part[((size_t)sl * M + row) * np + n] = v[e];
+    }
   }
 }
 
-// Table row stride: P = kps | 1 entries (odd, so that 16 lanes reading 16
-// columns at one step hit 16 different 16-byte bank groups).
 // Eight waves per workgroup (two per SIMD, which hide each other's waits). A
 // ring stage holds 1/sub of a k-step of the TT row tiles (sub = 1, 2, 4: 256,
 // 128 or 64 bytes of each row), about 4 KiB, so that three or four stages per
@@ -140,41 +139,62 @@ __host__ __device__ constexpr int midt_kw(int) { return 8; }
 __host__ __device__ constexpr int midt_sub(int tt) { return tt == 1 ? 1 : tt == 2 ? 2 : 4; }
 __host__ __device__ constexpr int midt_da(int tt) { return tt == 3 ? 4 : 3; }
 __host__ __device__ constexpr int midt_sb(int tt) { return tt * 16 * 256 / midt_sub(tt); }
-__host__ __device__ constexpr int midt_tab_bytes(int kps) { return (64 * (kps | 1) * 18 + 15) & ~15; }
+// Tables in two halves (local k-steps 0..15 and 16..31), each 64 columns x 16
+// steps: sign records (16 KiB) then the 4-byte words holding the fp16 scales
+// (4 KiB). Entry (column c, step s) of a half sits at slot s ^ (c % 16) of
+// column c's 16 slots, so that 16 lanes reading 16 columns at one step hit 16
+// different bank groups, while every direct load instruction (64 slots, four
+// columns) reads four contiguous 256-byte runs of memory. A wave's steps are
+// ks, ks + 8 (first half) and ks + 16, ks + 24 (second half): its first two
+// steps run while the second half is still arriving.
+constexpr int MIDT_HALF = 16 * 1024 + 4 * 1024;
+constexpr int MIDT_TAB = 2 * MIDT_HALF;
 // the tables and rings, or (reused at the end) the waves' results: kw x tt x
 // 16 rows x 64 columns of fp32
-__host__ __device__ constexpr int midt_lds_bytes(int tt, int kps) {
-  return midt_tab_bytes(kps) + midt_kw(tt) * midt_da(tt) * midt_sb(tt) > midt_kw(tt) * tt * 4096
-             ? midt_tab_bytes(kps) + midt_kw(tt) * midt_da(tt) * midt_sb(tt)
+__host__ __device__ constexpr int midt_lds_bytes(int tt) {
+  return MIDT_TAB + midt_kw(tt) * midt_da(tt) * midt_sb(tt) > midt_kw(tt) * tt * 4096
+             ? MIDT_TAB + midt_kw(tt) * midt_da(tt) * midt_sb(tt)
              : midt_kw(tt) * tt * 4096;
 }
-static_assert(midt_lds_bytes(1, MID_KPS) <= 160 * 1024 && midt_lds_bytes(2, MID_KPS) <= 160 * 1024 &&
-                  midt_lds_bytes(3, MID_KPS) <= 160 * 1024 && midt_lds_bytes(4, MID_KPS) <= 160 * 1024,
+static_assert(midt_lds_bytes(1) <= 160 * 1024 && midt_lds_bytes(2) <= 160 * 1024 && midt_lds_bytes(3) <= 160 * 1024 &&
+                  midt_lds_bytes(4) <= 160 * 1024,
               "tables and rings exceed the LDS");
 
-// Activation loads a wave has issued after those of its stage unit u (unit
-// = k-step i * sub + h) when unit u's products start (everything issued before
-// the tables' barrier has landed by then): the refills of units p + DA issued
-// after the products of units p < u, counted from the one that brought u.
-__host__ __device__ constexpr int midt_wait(int tt, int units, int u) {
+// Issue order of a wave's direct loads: table half 0 (4 loads), the
+// activations of units 0 .. DA-1 (unit = k-step i * sub + h; la loads each),
+// table half 1 (4 loads), then after the products of unit p the activations
+// of unit p + DA (while the wave has that unit). Loads complete in order, so
+// an operation has landed once at most (the loads issued after it) are
+// outstanding. midt_pos* give issue positions (loads issued up to and
+// including the operation; before unit u's products for midt_pos_now).
+__host__ __device__ constexpr int midt_pos_a(int tt, int units, int u) {  // after A(u)
+  const int da = midt_da(tt), la = 4 * tt / midt_sub(tt), pro = da < units ? da : units;
+  if (u < da) return 4 + (u + 1) * la;
+  return 4 + pro * la + 4 + (u - da + 1) * la;
+}
+__host__ __device__ constexpr int midt_pos_h1(int tt, int units) {
+  const int da = midt_da(tt), la = 4 * tt / midt_sub(tt), pro = da < units ? da : units;
+  return 4 + pro * la + 4;
+}
+__host__ __device__ constexpr int midt_pos_now(int tt, int units, int u) {
   const int da = midt_da(tt), la = 4 * tt / midt_sub(tt);
-  int n = 0;
+  int n = midt_pos_h1(tt, units);
   for (int p = 0; p < u; ++p)
-    if (p + da < units && p + da > u) n += la;
+    if (p + da < units) n += la;
   return n;
 }
 
 struct MidTab {
   const uint8_t* xb;      // activations
   uint32_t xo[4], xl[4];  // activation row offsets (full tiles; the last tile), per load of a tile
-  uint32_t rt[MID_NB];    // byte offset of column 16g + j's row in the record table
+  uint32_t cpar;          // bit g: parity of (column 16g + j) * G + the wave's first k-step
   int q0, K, j, kb, sl0;  // first global / local k-step of the wave
 };
 
 template <int TT, int CNT>
 __device__ __forceinline__ void midt_steps(f32x4 (&acc)[TT][MID_NB], const MidTab& L, uint8_t* lds, uint8_t* aring,
                                            const uint4* __restrict__ recs, const uint16_t* __restrict__ scales, int N,
-                                           int G, int n0, int kt0, int nks, int P, int lane, int ks) {
+                                           int G, int n0, int kt0, int nks, int lane, int ks) {
   constexpr int DA = midt_da(TT), SB = midt_sb(TT), NB = MID_NB, KW = midt_kw(TT), SUB = midt_sub(TT);
   constexpr int RB = 256 / SUB, LPT = 4 / SUB;  // bytes per staged row, direct loads per row tile
   constexpr int UNITS = CNT * SUB;
@@ -191,24 +211,47 @@ __device__ __forceinline__ void midt_steps(f32x4 (&acc)[TT][MID_NB], const MidTa
         __builtin_amdgcn_global_load_lds(g, dst + (16 * t + (16 / LPT) * r) * RB, 16, 0, 0);
       }
   };
+  // a table half: instruction i (0..15; wave i % 8 issues it) fills slots
+  // 64i .. 64i+63, i.e. columns 4i .. 4i+3; slot p of column c holds step
+  // p ^ (c % 16) (steps past the slice repeat its last, columns past N repeat
+  // N - 1). The scale of an entry is taken as the aligned 4-byte word that
+  // holds it (the scale array is 16-byte aligned, so the word of its last
+  // scale lies in the same 16-byte block, never on another page). Only direct
+  // loads here: the compiler would make any wait for a register load also
+  // wait for every direct load.
+  static_assert(KW == 8, "table halves assume eight waves");
+  const uint32_t* sw = reinterpret_cast<const uint32_t*>(scales);
+  auto load_half = [&](int hf) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = ks + KW * k, e = 64 * i + lane, c = e >> 4, st = 16 * hf + ((e & 15) ^ (c & 15));
+      const int n = n0 + c < N ? n0 + c : N - 1;
+      const size_t rq = (size_t)n * G + kt0 + (st < nks ? st : nks - 1);
+      uint8_t* base = lds + hf * MIDT_HALF;
+      __builtin_amdgcn_global_load_lds(recs + rq, base + 64 * i * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sw + (rq >> 1), base + 16384 + 64 * i * 4, 4, 0, 0);
+    }
+  };
+  load_half(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);  // issue order: half 0, first stages, half 1
 #pragma unroll
   for (int u = 0; u < DA && u < UNITS; ++u) load_a(u);
-  // the tables: entry e = c * P + s (column c, local step s; s >= nks repeats a valid step)
-  uint16_t* stab = reinterpret_cast<uint16_t*>(lds + 64 * P * 16);
-  for (int i = ks; i < P; i += KW) {
-    const int e = 64 * i + lane, c = e / P, sl = e - c * P;
-    const int n = n0 + c < N ? n0 + c : N - 1;
-    const int q = kt0 + (sl < nks ? sl : nks - 1);
-    __builtin_amdgcn_global_load_lds(recs + (size_t)n * G + q, lds + 64 * i * 16, 16, 0, 0);
-  }
-  for (int i = ks; i < P; i += KW) {
-    const int e = 64 * i + lane, c = e / P, sl = e - c * P;
-    const int n = n0 + c < N ? n0 + c : N - 1;
-    const int q = kt0 + (sl < nks ? sl : nks - 1);
-    stab[e] = scales[(size_t)n * G + q];
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  load_half(1);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  // half 0 of every wave has landed: a bare barrier (__syncthreads would also
+  // wait for the loads still in flight)
+  vm_wait<midt_pos_h1(TT, UNITS) - 4>();
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  auto half1_ready = [&]() {
+    vm_wait<midt_pos_now(TT, UNITS, 2 * SUB < UNITS ? 2 * SUB : UNITS) - midt_pos_h1(TT, UNITS)>();
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
   uint32_t one2;  // bf16 +1.0 pairs in a register: the and-or is then one instruction
   asm("v_mov_b32 %0, 0x3f803f80" : "=v"(one2));
   // slot of chunk c of a staged row r: c ^ ((r / sub) % (16 / sub)) (the 16
@@ -221,13 +264,19 @@ __device__ __forceinline__ void midt_steps(f32x4 (&acc)[TT][MID_NB], const MidTa
   static_for<0, UNITS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
     constexpr int i = u / SUB, h = u % SUB;
-    vm_wait<midt_wait(TT, UNITS, u)>();  // unit u's activations are in LDS
+    if constexpr (u == 2 * SUB) half1_ready();  // steps 2, 3 read the second half
+    vm_wait<midt_pos_now(TT, UNITS, u) - midt_pos_a(TT, UNITS, u)>();  // unit u's activations are in LDS
     if constexpr (h == 0) {
+      // step sl = ks + 8i: table half sl / 16, slot (sl % 16) ^ j of column 16g + j
       const int sl = L.sl0 + KW * i;
+      const uint8_t* hb = lds + (i >> 1) * MIDT_HALF;
+      const int slot = (sl & 15) ^ j;
 #pragma unroll
       for (int g = 0; g < NB; ++g) {
-        R[g] = *reinterpret_cast<const u32x4*>(lds + L.rt[g] + sl * 16);
-        C[g] = stab[(L.rt[g] >> 4) + sl];
+        R[g] = *reinterpret_cast<const u32x4*>(hb + ((16 * g + j) * 16 + slot) * 16);
+        // the scale: half (parity of column * G + step) of its word; steps of a
+        // wave are KW apart (even), so the parity is the wave's first step's
+        C[g] = reinterpret_cast<const uint32_t*>(hb + 16384)[(16 * g + j) * 16 + slot] >> (16 * ((L.cpar >> g) & 1));
       }
     }
     const uint8_t* as = aring + (u % DA) * SB + j * RB;
@@ -264,6 +313,7 @@ __device__ __forceinline__ void midt_steps(f32x4 (&acc)[TT][MID_NB], const MidTa
     if (u + DA < UNITS) load_a(u + DA);
     __builtin_amdgcn_sched_barrier(0);
   });
+  if constexpr (UNITS <= 2 * SUB) half1_ready();  // every wave meets both barriers
   __builtin_amdgcn_s_waitcnt(0);
 }
 
@@ -277,12 +327,25 @@ __global__ __launch_bounds__(64 * midt_kw(TT)) void k_midt(const uint16_t* __res
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int DA = midt_da(TT), SB = midt_sb(TT), NB = MID_NB, KW = midt_kw(TT), SUB = midt_sub(TT);
   constexpr int LPT = 4 / SUB, RPL = 16 / LPT;  // direct loads per row tile, rows per load
-  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the wave (uniform)
   const int G = K >> 7;
-  const int kt0 = blockIdx.y * kps, nks = min(kps, G - kt0);
+  // workgroup -> (column tile, K-slice): consecutive workgroups go to
+  // different chiplets (XCDs, eight); when the slices divide the chiplets and
+  // their tiles evenly, each chiplet takes the tiles of one slice only, so its
+  // L2 holds one slice of the activations instead of all of them
+  int tile = blockIdx.x, sl = blockIdx.y;
+  {
+    const int tiles = gridDim.x, gx = 8 / S;
+    if (S > 1 && S <= 8 && 8 % S == 0 && tiles % gx == 0) {
+      const int id = blockIdx.x + tiles * blockIdx.y, xcd = id % 8, slot = id / 8;
+      sl = xcd / gx;
+      tile = xcd % gx + gx * slot;
+    }
+  }
+  const int kt0 = sl * kps, nks = min(kps, G - kt0);
   const int cnt = nks > ks ? (nks - ks + KW - 1) / KW : 0;  // this wave's k-steps
-  const int n0 = blockIdx.x * MID_BN;
-  const int P = kps | 1;
+  const int n0 = tile * MID_BN;
 
   MidTab L;
   L.j = lane & 15;
@@ -302,15 +365,19 @@ __global__ __launch_bounds__(64 * midt_kw(TT)) void k_midt(const uint16_t* __res
     L.xo[r] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(c * 16);
     L.xl[r] = (uint32_t)(rl < M ? rl : M - 1) * (uint32_t)K * 2u + (uint32_t)(c * 16);
   }
+  L.cpar = 0;
 #pragma unroll
-  for (int g = 0; g < NB; ++g) L.rt[g] = (uint32_t)((16 * g + L.j) * P * 16);
+  for (int g = 0; g < NB; ++g) {
+    const int n = n0 + 16 * g + L.j < N ? n0 + 16 * g + L.j : N - 1;
+    L.cpar |= (((uint32_t)n * (uint32_t)G + (uint32_t)L.q0) & 1u) << g;
+  }
   f32x4 acc[TT][NB];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
 #pragma unroll
     for (int g = 0; g < NB; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint8_t* const aring = lds + midt_tab_bytes(kps) + ks * DA * SB;
-#define BRQ_MIDT(C) midt_steps<TT, C>(acc, L, lds, aring, recs, scales, N, G, n0, kt0, nks, P, lane, ks)
+  uint8_t* const aring = lds + MIDT_TAB + ks * DA * SB;
+#define BRQ_MIDT(C) midt_steps<TT, C>(acc, L, lds, aring, recs, scales, N, G, n0, kt0, nks, lane, ks)
   switch (cnt) {  // uniform across the wave; every wave loads its share of the tables
     case 0: BRQ_MIDT(0); break;
     case 1: BRQ_MIDT(1); break;
@@ -323,7 +390,7 @@ __global__ __launch_bounds__(64 * midt_kw(TT)) void k_midt(const uint16_t* __res
     default: if constexpr (KW == 4) BRQ_MIDT(8); break;
   }
 #undef BRQ_MIDT
-  mid_reduce_store<TT, KW>(acc, lds, y, y_bf16, part, M, N, n0, S, lane, ks);
+  mid_reduce_store<TT, KW>(acc, lds, y, y_bf16, part, M, N, n0, sl, S, lane, ks);
 }
 
 // y = the sum of the S partial results part[s][M][np], in slice order
@@ -375,7 +442,7 @@ static hipError_t mid_run(Kern kern, int threads, int lds, const uint16_t* x, in
 template <int TT>
 static hipError_t midt_launch(const uint16_t* x, int M, int N, int K, const uint64_t* signs, const uint16_t* scales,
                               void* y, int y_bf16, float* part, const MidPlan& p, hipStream_t st) {
-  return mid_run(&k_midt<TT>, 64 * midt_kw(TT), midt_lds_bytes(TT, p.kps), x, M, N, K, signs, scales, y, y_bf16, part,
+  return mid_run(&k_midt<TT>, 64 * midt_kw(TT), midt_lds_bytes(TT), x, M, N, K, signs, scales, y, y_bf16, part,
                  p, st);
 }
 
