@@ -305,6 +305,11 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
         sc[t][c] = *reinterpret_cast<const uint2*>(scales + row[t] + (gs < G ? gs : 0));
       }
     __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    // a slot past the last chunk (the last wave when CPW does not divide the
+    // chunk count) holds zeros: no digits, no part in the exponent
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      if (c0 + c >= nchunks) xv[c] = make_uint4(0u, 0u, 0u, 0u);
     // ---- slice exponent: biased exponent of the largest |x| of the wave slice
     uint32_t mx = 0;
 #pragma unroll
@@ -358,9 +363,10 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
     }
     const int prow = j < F4_DIGITS ? j : F4_DIGITS;  // lanes 6..15 read the zero row
     const int sa = (int)ebs - 2 - 4 * prow;
-    // ---- products
+    // ---- products (the last wave's slots past the last chunk take no part)
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
+      if (c0 + c >= nchunks) break;  // uniform across the wave
       const uint8_t* ab = xw + c * F4_CHUNK + prow * 128 + 16 * kb;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {

@@ -133,7 +133,8 @@ def test_gemm_mid_wave_steps(M, N, K):
     check_bf16(yb, o, f"gemm {M}x{N}x{K} bf16")
 
 
-@pytest.mark.parametrize("N,K", [(40, 512), (1000, 1536), (2049, 4096), (48, 23040)])
+@pytest.mark.parametrize("N,K", [(40, 512), (1000, 1536), (2049, 4096), (48, 23040), (40, 8704), (300, 9728),
+                                 (64, 17920)])
 def test_gemm_single_row_wide_range(N, K):
     """A single activation row with K % 512 == 0 runs on the fp8 x fp4 matrix
     cores with the activations as fixed-point digit rows: ragged column tiles,
@@ -144,7 +145,9 @@ def test_gemm_single_row_wide_range(N, K):
     the fp32 bar and, element by element, to the bound single_row_bound
     derives from the representation. K = 23040 is the longest row the digit
     rows fit the LDS for (45 chunks, three per wave); 23552 takes the fp16
-    one-launch path (test_gemm_decode_f32)."""
+    one-launch path (test_gemm_decode_f32). K = 8704, 9728 and 17920 (17, 19
+    and 35 chunks of 512) leave the last wave fewer chunks than the others,
+    whose empty slots must add nothing."""
     say("gemm single row, wide range", N, K)
     w = datagen.normal_f32((73, N, K), (N, K), 0.02)
     ow, osc = oracle.pack_sign1(w)
