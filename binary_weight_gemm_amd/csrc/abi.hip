@@ -384,18 +384,20 @@ brq_status brq_kron_rotate(const uint16_t* x, int64_t M, const float* H, int64_t
                            uint16_t* y, void* stream) {
   if (!x || !H || !R || !y) return fail(BRQ_E_NULL, "brq_kron_rotate: x, H, R and y must not be NULL");
   if (M < 1 || M > kMaxDim) return fail(BRQ_E_SHAPE, "brq_kron_rotate: M=%lld out of range", (long long)M);
-  if (n1 != 64 || n2 != 64)
-    return fail(BRQ_E_SHAPE, "brq_kron_rotate: n1=%lld n2=%lld, only 64 x 64 factors are supported", (long long)n1,
-                (long long)n2);
+  if (!brq::kron_supported(n1, n2))
+    return fail(BRQ_E_SHAPE,
+                "brq_kron_rotate: n1=%lld n2=%lld, factor sizes must be 32, 64 or 96 with n1 * n2 <= 6144",
+                (long long)n1, (long long)n2);
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(H, 4) || !aligned(R, 4))
     return fail(BRQ_E_ALIGN, "brq_kron_rotate: x and y must be 16-byte aligned");
   const char* xb = reinterpret_cast<const char*>(x);
   const char* yb = reinterpret_cast<const char*>(y);
-  const size_t bytes = (size_t)M * 4096 * 2;
+  const size_t bytes = (size_t)M * (size_t)(n1 * n2) * 2;
   if (xb < yb + bytes && yb < xb + bytes) return fail(BRQ_E_SHAPE, "brq_kron_rotate: x and y overlap");
   brq_status s = check_device();
   if (s != BRQ_OK) return s;
-  return hip_result(brq::launch_kron(x, (int)M, H, R, y, (hipStream_t)stream), "brq_kron_rotate");
+  return hip_result(brq::launch_kron(x, (int)M, (int)n1, (int)n2, H, R, y, (hipStream_t)stream),
+                    "brq_kron_rotate");
 }
 
 }  // extern "C"

@@ -99,7 +99,9 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
                       void* ws, hipStream_t st);
 
 // ---- Kronecker rotation ----------------------------------------------------
-hipError_t launch_kron(const uint16_t* x, int M, const float* H, const float* R, uint16_t* y,
+// factor sizes n1, n2 in {32, 64, 96} with n1 * n2 <= 6144
+bool kron_supported(int64_t n1, int64_t n2);
+hipError_t launch_kron(const uint16_t* x, int M, int n1, int n2, const float* H, const float* R, uint16_t* y,
                        hipStream_t st);
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }

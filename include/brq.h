@@ -364,9 +364,13 @@ brq_status brq_moe_dbf_ffn(const uint16_t* x, const float* logits,
  *
  *   x   device, bf16 [M][n1*n2];  H device, fp32 [n1][n1];  R device, fp32 [n2][n2]
  *   y   device, out, bf16 [M][n1*n2]; must not overlap x
- *   M >= 1; n1 == n2 == 64 (the 4096-wide rows of the prefill workload; other
- *   factor sizes, e.g. 32 x 64 or 48 x 64 for hidden sizes 2048 and 3072, are
- *   not built and give BRQ_E_SHAPE).
+ *   M >= 1; n1 and n2 each 32, 64 or 96 with n1 * n2 <= 6144 (rows of 1024,
+ *   2048, 3072, 4096 or 6144 values; the prefill workload is 64 x 64); other
+ *   factor sizes (e.g. 48, which 3072 = 48 x 64 would need, or 96 x 96) give
+ *   BRQ_E_SHAPE.
+ *   Errors: BRQ_E_NULL (a NULL pointer), BRQ_E_SHAPE (M or factor sizes out
+ *   of range, x and y overlapping), BRQ_E_ALIGN (x or y not 16-byte aligned,
+ *   H or R not 4-byte aligned).
  */
 brq_status brq_kron_rotate(const uint16_t* x, int64_t M, const float* H, int64_t n1,
                            const float* R, int64_t n2, uint16_t* y, void* stream);

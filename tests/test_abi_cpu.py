@@ -247,6 +247,9 @@ def test_kron_validation(L):
     f = L.brq_kron_rotate
     assert f(None, 4, P, 64, P, 64, P, None) == E_NULL
     assert f(P, 4, P, 32, P, 128, ctypes.c_void_p(1 << 30), None) == E_SHAPE
+    assert f(P, 4, P, 48, P, 64, ctypes.c_void_p(1 << 30), None) == E_SHAPE   # factor size not 32, 64 or 96
+    assert f(P, 4, P, 96, P, 96, ctypes.c_void_p(1 << 30), None) == E_SHAPE   # n1 * n2 above 6144
+    assert f(P, 4, P, 16, P, 64, ctypes.c_void_p(1 << 30), None) == E_SHAPE
     assert f(P, 4, P, 64, P, 64, P, None) == E_SHAPE         # x and y overlap
     assert f(PMIS, 4, P, 64, P, 64, ctypes.c_void_p(1 << 30), None) == E_ALIGN
 

@@ -67,7 +67,7 @@ assert call("brq_dbf_gemm_q8", None, 1, 16, 128, 128, a, b, c, d, a, b, 0, None,
 assert call("brq_moe_ffn", a, b, 1, 2048, 512, 256, 99, a, b, c, d, a, b, c, 0, None, None, d, 0, None) == 2
 assert call("brq_moe_ffn_noalloc", a, b, 1, 2048, 512, 256, 99, a, b, c, d, a, b, c, 0, None, None, None) == 2
 assert call("brq_moe_dbf_ffn", a, b, 1, 2048, 512, 256, 8, 1024, None, None, None, c, 0, None, None, d, 0, None) == 1
-assert call("brq_kron_rotate", a, 1, b, 32, c, 64, d, None) == 2
+assert call("brq_kron_rotate", a, 1, b, 48, c, 64, d, None) == 2
 assert call("brq_set_decode_fusion", 9, 0) == 2
 assert call("brq_debug_fail_launches", -2) == 2
 # the injected failure, then the device check (no GPU in this process)

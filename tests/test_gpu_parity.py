@@ -956,6 +956,21 @@ def test_kron(M):
     assert l2rel(f64(y), o) <= 2e-3
 
 
+@pytest.mark.parametrize("n1,n2,M", [(32, 64, 9), (64, 32, 300), (32, 32, 5), (96, 32, 7), (32, 96, 66),
+                                    (96, 64, 13), (64, 96, 1030), (64, 64, 3)])
+def test_kron_factor_sizes(n1, n2, M):
+    """Factor sizes 32, 64 and 96 (rows of 1024 .. 6144 values), square and
+    not, token counts that leave the last workgroup's waves partly idle; each
+    element within 1 bf16 ulp of the rounded fp64 result."""
+    say("kron factor sizes", n1, n2, M)
+    d = datagen.C5(M=M, K=n1 * n2, n1=n1, n2=n2)
+    o = oracle.kron_rotate(oracle.bf16_to_f64(d["x"]), d["H"], d["R"])
+    y = brq().kron_rotate(dev(d["x"]), dev(d["H"]), dev(d["R"]))
+    torch.cuda.synchronize()
+    assert bf16_close(host_bits(y), o).all()
+    assert l2rel(f64(y), o) <= 2e-3
+
+
 def test_c5_prefill_sampled_columns():
     say("C5 rotate + prefill gemm, sampled columns")
     d = datagen.C5()
