@@ -338,7 +338,7 @@ brq_status brq_moe_ffn(const uint16_t* x, const float* logits, int64_t T, int64_
 
 size_t brq_moe_dbf_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t top_k, int64_t r) {
   if (T < 1 || T > 256 || E < 1 || E > 1024 || top_k < 1 || top_k > 16 || top_k > E) return 0;
-  if (H < 128 || I < 128 || r < 128 || H % 128 || I % 128 || r % 128 || H > 4096 || I > 2048 || r > 2048) return 0;
+  if (H < 128 || I < 128 || r < 128 || H % 128 || I % 128 || r % 128 || H > 8192 || I > 2048 || r > 2048) return 0;
   return brq::moe_dbf_ws_bytes(T, H, I, E, top_k, r);
 }
 
@@ -356,9 +356,9 @@ brq_status brq_moe_dbf_ffn(const uint16_t* x, const float* logits, int64_t T, in
   if (E < 1 || E > 1024) return fail(BRQ_E_SHAPE, "brq_moe_dbf_ffn: E=%lld must be in [1, 1024]", (long long)E);
   if (top_k < 1 || top_k > 16 || top_k > E)
     return fail(BRQ_E_SHAPE, "brq_moe_dbf_ffn: top_k=%lld must be in [1, min(E, 16)]", (long long)top_k);
-  if (H < 128 || I < 128 || r < 128 || H % 128 || I % 128 || r % 128 || H > 4096 || I > 2048 || r > 2048)
+  if (H < 128 || I < 128 || r < 128 || H % 128 || I % 128 || r % 128 || H > 8192 || I > 2048 || r > 2048)
     return fail(BRQ_E_SHAPE,
-                "brq_moe_dbf_ffn: H=%lld, I=%lld, r=%lld must be multiples of 128 with H <= 4096, I <= 2048, "
+                "brq_moe_dbf_ffn: H=%lld, I=%lld, r=%lld must be multiples of 128 with H <= 8192, I <= 2048, "
                 "r <= 2048",
                 (long long)H, (long long)I, (long long)r);
   if (!dtype_ok(y_dtype)) return fail(BRQ_E_DTYPE, "brq_moe_dbf_ffn: unknown y_dtype %d", enum_value(y_dtype));

@@ -1259,39 +1259,48 @@ size_t moe_dbf_ws_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, i
   return moe_ws_bytes(T, H, I, E, k) + align256((size_t)2 * T * k * r * 4);  // h_s: fp32 [2][T*k][r]
 }
 
-template <int STAGE, int SR, int CB>
+template <int STAGE, int SR, int CB, int CPW = 1>
 static hipError_t moe_dbf_stage_cb(const uint16_t* x, int H, int I, int r, int R, int maxact, const DbfStageArgs& a,
                                    const MoeWs& ws, int waves, hipStream_t st) {
   const int N = STAGE == 1 ? I : STAGE == 3 ? H : r;
   constexpr int NMAT = STAGE < 2 ? 2 : 1;
   constexpr int NIN = STAGE == 1 ? 2 : 1;
   constexpr bool PERK = STAGE == 0 || STAGE == 2;
-  const size_t din = PERK ? (size_t)waves * NMAT * 1024 : 0;
-  const size_t stg = (size_t)waves * NIN * SR * 1024;
+  const size_t din = PERK ? (size_t)waves * NMAT * CPW * 1024 : 0;
+  const size_t stg = (size_t)waves * NIN * CPW * SR * 1024;
   const size_t red = (size_t)(waves - 1) * CB * NMAT * 1024;
   const size_t lds = din + (stg > red ? stg : red);
   const dim3 grid((unsigned)((N + 16 * CB - 1) / (16 * CB)), (unsigned)maxact);
   if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_moe_dbf<STAGE, 1, SR, CB>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_moe_dbf<STAGE, CPW, SR, CB>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_moe_dbf<STAGE, 1, SR, CB>), grid, dim3(64 * waves), lds, st, x, H, I, r, R, a, ws);
+  hipLaunchKernelGGL((k_moe_dbf<STAGE, CPW, SR, CB>), grid, dim3(64 * waves), lds, st, x, H, I, r, R, a, ws);
   return hipGetLastError();
 }
 
-// One chunk (512 of the reduction axis) per wave: the accepted shapes have
-// K <= 4096, so at most 8 waves. CB blocks of 16 columns per workgroup: 4
-// when that still gives about four workgroups per compute unit for the
-// experts that can be active, fewer otherwise (decode at T = 1 has 8).
+// One chunk (512 of the reduction axis) per wave up to K = 4096 (8 waves);
+// the hidden vector of stage 0 may be up to 8192 long (two chunks per wave,
+// token tiles of 4 rows so that the staged rows fit the registers). CB
+// blocks of 16 columns per workgroup: 4 when that still gives about four
+// workgroups per compute unit for the experts that can be active, fewer
+// otherwise (decode at T = 1 has 8).
 template <int STAGE, int SR>
 static hipError_t moe_dbf_stage(const uint16_t* x, int H, int I, int r, int R, int maxact, const DbfStageArgs& a,
                                 const MoeWs& ws, hipStream_t st) {
   const int K = STAGE == 0 ? H : STAGE == 2 ? I : r;
   const int N = STAGE == 1 ? I : STAGE == 3 ? H : r;
   const DecSplit sp = dec_split(K / 128, 8);
-  if (sp.cpw != 1) return hipErrorInvalidValue;  // outside the accepted shapes
   const int64_t blocks = (int64_t)((N + 15) / 16) * maxact;
+  if constexpr (STAGE == 0) {
+    if (sp.cpw == 2) {
+      if (blocks >= 4096) return moe_dbf_stage_cb<STAGE, 4, 4, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
+      if (blocks >= 2048) return moe_dbf_stage_cb<STAGE, 4, 2, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
+      return moe_dbf_stage_cb<STAGE, 4, 1, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
+    }
+  }
+  if (sp.cpw != 1) return hipErrorInvalidValue;  // outside the accepted shapes
   if (blocks >= 4096) return moe_dbf_stage_cb<STAGE, SR, 4>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
   if (blocks >= 2048) return moe_dbf_stage_cb<STAGE, SR, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
   return moe_dbf_stage_cb<STAGE, SR, 1>(x, H, I, r, R, maxact, a, ws, sp.waves, st);

@@ -106,6 +106,10 @@ MOE_GEOMETRIES = {
     "DeepSeek-V4-Flash": dict(E=256, H=4096, I=2048, r=2048),
 }
 
+#: the widest named geometry (hidden 6144 x expert intermediate 2048, 256
+#: experts), kept apart so that the table above keeps its seeds
+MOE_GEOMETRY_WIDE = {"GLM-5.2": dict(E=256, H=6144, I=2048, r=2048)}
+
 #: decode-shaped matrices, stored [N_out, K_in]
 C2_SHAPES = ((4096, 14336), (14336, 4096))
 C2_MS = (1, 4, 16, 64)

@@ -340,7 +340,7 @@ typedef struct {
  *   gate, up   host pointers to records of H -> I chains (m = I, n = H)
  *   down       host pointer to a record of an I -> H chain (m = H, n = I)
  *   ws       device workspace, >= brq_moe_dbf_workspace_bytes(T, H, I, E, top_k, r)
- *   H, I, r multiples of 128 with H <= 4096, I <= 2048, r <= 2048; T, E, top_k
+ *   H, I, r multiples of 128 with H <= 8192, I <= 2048, r <= 2048; T, E, top_k
  *   as for brq_moe_ffn. x, y, the sign planes and d_in 16-byte aligned, d_mid
  *   and d_out 2-byte aligned.
  */

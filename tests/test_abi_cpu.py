@@ -160,7 +160,7 @@ def test_moe_dbf_validation(L):
     assert "record" in _err(L)
     assert call(a2=0) == E_SHAPE                          # T
     assert call(a7=100) == E_SHAPE                        # r % 128
-    assert call(a3=8192) == E_SHAPE                       # H past 4096
+    assert call(a3=8320) == E_SHAPE                       # H past 8192
     assert call(a7=4096) == E_SHAPE                       # r past 2048
     assert call(a6=300) == E_SHAPE                        # top_k past min(E, 16)
     assert call(a12=9) == E_DTYPE

@@ -879,11 +879,13 @@ def _dbf_moe_packed(cfg, experts):
 # the other MoE geometries the DBF post names (its section 9), full projection
 # shapes with top-8 routing and r = 2048 (the most the layer accepts); only
 # the selected experts are built. T = 1 and 3 take the few-token path, T = 5
-# the grouped one.
-@pytest.mark.parametrize("name,T", [("GLM-4.5-Air", 1), ("MiniMax-M2.5", 3), ("DeepSeek-V4-Flash", 5)])
+# and 6 the grouped one; GLM-5.2's hidden 6144 gives the gate/up V factors
+# two 512-wide chunks per wave.
+@pytest.mark.parametrize("name,T", [("GLM-4.5-Air", 1), ("MiniMax-M2.5", 3), ("DeepSeek-V4-Flash", 5),
+                                    ("GLM-5.2", 1), ("GLM-5.2", 6)])
 def test_moe_dbf_named_geometries(name, T):
     say("moe dbf geometry", name, T)
-    g = datagen.MOE_GEOMETRIES[name]
+    g = {**datagen.MOE_GEOMETRIES, **datagen.MOE_GEOMETRY_WIDE}[name]
     cfg = datagen.C4D(E=g["E"], H=g["H"], I=g["I"], r=g["r"], top_k=8, layer=11)
     x, lg = cfg.x(T), cfg.logits(T)
     ids_o, _ = oracle.route_topk(lg, cfg.top_k)
