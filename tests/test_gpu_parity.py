@@ -901,6 +901,50 @@ def test_moe_dbf_named_geometries(name, T):
     check_bf16(yb, o, f"moe dbf {name} T={T} bf16")
 
 
+def _moe_packed_selected(E, H, I, experts, key):
+    """Group-128 experts at full projection shapes with only `experts` built
+    (random sign words, fp16 scales in [0.01, 0.03), near the 0.016 of a
+    packed N(0, 0.02^2) matrix), the others zero: device tensors in the
+    order brq.moe_ffn takes them and the oracle's lookup, from the same arrays."""
+    host = []
+    for p, (n, k) in enumerate(((I, H), (I, H), (H, I))):
+        w = np.zeros((E, n, k // 64), np.uint64)
+        sc = np.zeros((E, n, k // 128), np.float16)
+        for e in experts:
+            w[e] = datagen.sign_words((97, key, e, p, 0), n, k).reshape(n, k // 64)
+            sc[e] = (0.01 + 0.02 * datagen.rng(97, key, e, p, 1).random((n, k // 128))).astype(np.float16)
+        host += [w, sc]
+    return [dev(a) for a in host], (lambda e: tuple(a[e] for a in host))
+
+
+# the group-128 layer at the named geometries, full projection shapes, top-8:
+# the router logits favour ten experts so that the oracle's dense
+# reconstructions stay few; T = 1 takes the few-token path, T = 6 the grouped
+# one; GLM-5.2's hidden 6144 gives the gate/up reductions two chunks per wave
+@pytest.mark.parametrize("name,T", [("GLM-4.5-Air", 6), ("MiniMax-M2.5", 1), ("DeepSeek-V4-Flash", 6),
+                                    ("GLM-5.2", 1), ("GLM-5.2", 6)])
+def test_moe_named_geometries(name, T):
+    say("moe geometry", name, T)
+    geo = {**datagen.MOE_GEOMETRIES, **datagen.MOE_GEOMETRY_WIDE}
+    g = geo[name]
+    E, H, I = g["E"], g["H"], g["I"]
+    key = sorted(geo).index(name)
+    x = datagen.bf16_normal((98, key, T), (T, H))
+    lg = datagen.router_logits((99, key, T), T, E)
+    favoured = datagen.rng(96, key).choice(E, size=10, replace=False)
+    lg[:, favoured] += np.float32(8.0)
+    ids_o, _ = oracle.route_topk(lg, 8)
+    d, ex = _moe_packed_selected(E, H, I, sorted(set(int(e) for e in ids_o.ravel())), key)
+    o, oids, ow = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, H, I, 8)
+    y, ids, w = brq().moe_ffn(dev(x), dev(lg), *d, E, H, I, 8, out_dtype=torch.float32, return_routing=True)
+    yb = brq().moe_ffn(dev(x), dev(lg), *d, E, H, I, 8, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=1e-7)
+    check_f32(f64(y), o, F32_TOL, f"moe {name} T={T}")
+    check_bf16(yb, o, f"moe {name} T={T} bf16")
+
+
 # the ABI limits of the routed layers: T = 256 tokens, E = 1024 experts,
 # top-16, with small projections (H = I = r = 128) so that every expert fits
 def test_moe_limits():
