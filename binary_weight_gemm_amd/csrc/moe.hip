@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "dec_core.h"
+#include "f4.h"
 #include "kernels.h"
 
 namespace brq {
@@ -371,6 +372,143 @@ __global__ __launch_bounds__(512) void k_moe_gateup(const uint16_t* __restrict__
   run_tile(0);  // an active expert has at least one route
   for (int tb = MAXR; tb < cnt; tb += MAXR) run_tile(tb);
   (void)nw;
+}
+
+// gate/up on the fp8 x fp4 matrix cores (grouped path, H % 512 == 0): the
+// expert's token rows as fixed-point digit rows (f4.h), two routes per
+// product (digit rows 0..5 and 8..13, the zero row for the others), the +-1
+// weights as +-6 fp4 operands built by one shift-or per eight weights. One
+// workgroup per (NT blocks of 16 intermediate columns, active expert), one
+// 512-wide chunk of the hidden vector per wave (CPW per wave beyond 8
+// chunks); the routes are taken in pairs, each pair's digits rebuilt in the
+// wave's LDS region chunk by chunk; the waves' sums meet in LDS in wave
+// order, and SwiGLU (fp32) writes the routes' intermediate rows.
+constexpr int MOE_F4_ROWS = 13;  // digit rows of a route pair, then the zero row
+constexpr int MOE_F4_GROUP = MOE_F4_ROWS * 128;
+constexpr int MOE_F4_CHUNK = 4 * MOE_F4_GROUP;
+
+template <int CPW, int NT>
+__global__ __launch_bounds__(512) void k_moe_gateup_f4(const uint16_t* __restrict__ x, int H, int I,
+                                                       const uint4* __restrict__ gs, const uint16_t* __restrict__ gsc,
+                                                       const uint4* __restrict__ us, const uint16_t* __restrict__ usc,
+                                                       MoeWs ws) {
+  extern __shared__ uint4 smem[];
+  const int4 bk = ws.blk[blockIdx.y];
+  const int e = bk.x, r0 = bk.y, cnt = bk.z;
+  if (cnt == 0) return;  // past the last active expert
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int G = H >> 7, nchunks = G >> 2;
+  const int c0 = wave * CPW;
+  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * MOE_F4_CHUNK;
+  float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * MOE_F4_CHUNK);
+  // the first pair's token rows, then every weight word, all before any wait
+  auto load_x = [&](int q0, uint4 (&xv)[2][CPW]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rr = q0 + h < cnt ? q0 + h : cnt - 1;  // a missing second route: zeroed below
+      const uint16_t* xr = x + (size_t)ws.route_tok[r0 + rr] * H;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int k0 = (c0 + c) * 512 + 8 * lane;
+        xv[h][c] = *reinterpret_cast<const uint4*>(xr + (k0 < H ? k0 : 0));
+      }
+    }
+  };
+  uint4 xv[2][CPW];
+  load_x(0, xv);
+  uint4 sg[2][NT][CPW];
+  uint2 sc[2][NT][CPW];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = (blockIdx.x * NT + t) * 16 + j;
+    const size_t row = ((size_t)e * I + (n < I ? n : 0)) * G;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int g = 4 * (c0 + c) + kb, g4 = 4 * (c0 + c);
+      sg[0][t][c] = gs[row + (g < G ? g : 0)];
+      sg[1][t][c] = us[row + (g < G ? g : 0)];
+      sc[0][t][c] = *reinterpret_cast<const uint2*>(gsc + row + (g4 < G ? g4 : 0));
+      sc[1][t][c] = *reinterpret_cast<const uint2*>(usc + row + (g4 < G ? g4 : 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (lane < 32)  // the zero row of each group: 16 bytes per lane, never overwritten
+    *reinterpret_cast<uint4*>(xw + (lane >> 3) * MOE_F4_GROUP + 12 * 128 + 16 * (lane & 7)) =
+        make_uint4(0u, 0u, 0u, 0u);
+  // MFMA row j reads digit row j of the pair's first route (j < 6), digit row
+  // j - 8 of its second (8 <= j < 14, LDS rows 6..11) or the zero row
+  const int prow = j < 6 ? j : (j >= 8 && j < 14) ? j - 2 : 12;
+  uint8_t* base = xw + (lane >> 4) * MOE_F4_GROUP + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
+  for (int q0 = 0; q0 < cnt; q0 += 2) {
+    if (q0 > 0) load_x(q0, xv);
+    // slots past the last chunk, and a missing second route, hold zeros
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        if (c0 + c >= nchunks || q0 + h >= cnt) xv[h][c] = make_uint4(0u, 0u, 0u, 0u);
+    float S0, S1;
+    const uint32_t e0 = f4_slice_exponent<CPW>(xv[0], S0), e1 = f4_slice_exponent<CPW>(xv[1], S1);
+    const int sa = j < 8 ? (int)e0 - 2 - 4 * min(j, 6) : (int)e1 - 2 - 4 * min(j - 8, 6);
+    float acc[2][NT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      if (c0 + c >= nchunks) break;  // uniform across the wave
+      f4_digits(xv[0][c], S0, base, 0);
+      f4_digits(xv[1][c], S1, base, 6);
+      const uint8_t* ab = xw + prow * 128 + 16 * kb;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          uint32_t w0 = sg[m][t][c].x, w1 = sg[m][t][c].y, w2 = sg[m][t][c].z, w3 = sg[m][t][c].w;
+          f4_transpose4(w0, w1, w2, w3);
+          const uint32_t wi[4] = {w0, w1, w2, w3};
+          const uint32_t s4[4] = {sc[m][t][c].x & 0xffffu, sc[m][t][c].x >> 16, sc[m][t][c].y & 0xffffu,
+                                  sc[m][t][c].y >> 16};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 d = f4_group_mfma(ab + i * MOE_F4_GROUP, wi[i], sa);
+            acc[m][t] = fmaf(f16_bits_to_f32(s4[i]), (d[0] + d[1]) + (d[2] + d[3]), acc[m][t]);
+          }
+        }
+    }
+    // digit rows 4 and 5 join rows 0..3: lanes 0..15 hold the first route's
+    // sums, lanes 32..47 the second's
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] += __shfl_down(acc[m][t], 16, 64);
+    const bool holds = (kb & 1) == 0;
+    if (wave > 0 && holds) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) red[(((wave - 1) * 2 + m) * NT + t) * 32 + (kb >> 1) * 16 + j] = acc[m][t];
+    }
+    __syncthreads();
+    if (wave == 0 && holds) {
+      const int p = q0 + (kb >> 1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float v[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          v[m] = acc[m][t];
+          for (int w = 1; w < nw; ++w) v[m] += red[(((w - 1) * 2 + m) * NT + t) * 32 + (kb >> 1) * 16 + j];
+          v[m] = v[m] / 6.0f;
+        }
+        const int n = (blockIdx.x * NT + t) * 16 + j;
+        if (p < cnt && n < I) ws.ap[(size_t)(r0 + p) * I + n] = v[0] / (1.0f + expf(-v[0])) * v[1];
+      }
+    }
+    __syncthreads();  // red and the digit regions are free for the next pair
+  }
 }
 
 // down: one workgroup per (CB blocks of 16 hidden columns, active expert); the
@@ -969,6 +1107,19 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
   size_t ld = (size_t)sd.waves * sd.cpw * 2 * rt * 1024, rd = (size_t)(sd.waves - 1) * cbd * 64 * 16;
   const unsigned gx = (unsigned)((I + 16 * cbg - 1) / (16 * cbg));
   const unsigned dx = (unsigned)((H + 16 * cbd - 1) / (16 * cbd));
+  // gate/up on the digit path where the hidden vector comes in whole 512-wide
+  // chunks, at most two per wave (H <= 8192)
+  if (H % 512 == 0 && sg.cpw <= 2) {
+    constexpr int NT = 2;
+    const size_t lf = (size_t)sg.waves * MOE_F4_CHUNK + (size_t)(sg.waves - 1) * 2 * NT * 32 * 4;
+    const dim3 gf((unsigned)((I + 16 * NT - 1) / (16 * NT)), maxact), bf(64 * sg.waves);
+    const uint4* g4 = reinterpret_cast<const uint4*>(gate_s);
+    const uint4* u4 = reinterpret_cast<const uint4*>(up_s);
+    if (sg.cpw == 1)
+      hipLaunchKernelGGL((k_moe_gateup_f4<1, NT>), gf, bf, lf, st, x, H, I, g4, gate_sc, u4, up_sc, ws);
+    else
+      hipLaunchKernelGGL((k_moe_gateup_f4<2, NT>), gf, bf, lf, st, x, H, I, g4, gate_sc, u4, up_sc, ws);
+  } else {
 #define BRQ_GATEUP(TR)                                                                                       \
   BRQ_CPW_SWITCH(sg.cpw, hipLaunchKernelGGL((k_moe_gateup<CPW, TR, moe_cb_gu(CPW)>), dim3(gx, maxact),           \
                                             dim3(64 * sg.waves), lg > rg ? lg : rg, st, x, H, I,                \
@@ -982,6 +1133,7 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
     BRQ_GATEUP(1);
   }
 #undef BRQ_GATEUP
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 #define BRQ_DOWN(RT)                                                                                         \
