@@ -79,6 +79,54 @@ __device__ __forceinline__ void f4_digits(const uint4 v, float S, uint8_t* base,
   }
 }
 
+// biased exponent of the largest |v| of a wave's slice of fp32 values (8 per
+// lane per chunk), at least 24, and 2^(150 - ebs)
+template <int C>
+__device__ __forceinline__ uint32_t f4_slice_exponent_f32(const f32x4 (&v)[C][2], float& S) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = max(mx, __float_as_uint(v[c][h][i]) & 0x7fffffffu);
+  mx = wave_max_u32(mx);
+  const uint32_t ebs = max(mx >> 23, 24u);
+  S = __uint_as_float((277u - ebs) << 23);
+  return ebs;
+}
+
+// as f4_digits for 8 fp32 values (v[0] holds values 0..3, v[1] 4..7): each
+// |v| becomes trunc(|v| * 2^(150 - ebs)), the bits below 2^-23 of the slice
+// maximum dropped
+__device__ __forceinline__ void f4_digits_f32(const f32x4 (&v)[2], float S, uint8_t* base, int row0) {
+  uint32_t lo[8], hi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = v[e >> 2][e & 3];
+    const uint32_t X = (uint32_t)(fabsf(f) * S);
+    const uint32_t sr = (__float_as_uint(f) >> 31) * 0x808080u;
+    lo[e] = (X & 0x0f0f0fu) | sr;
+    hi[e] = ((X >> 4) & 0x0f0f0fu) | sr;
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t l02 = __builtin_amdgcn_perm(lo[t + 4], lo[t], 0x05010400u);
+    const uint32_t l4 = __builtin_amdgcn_perm(lo[t + 4], lo[t], 0x0c0c0602u);
+    const uint32_t h13 = __builtin_amdgcn_perm(hi[t + 4], hi[t], 0x05010400u);
+    const uint32_t h5 = __builtin_amdgcn_perm(hi[t + 4], hi[t], 0x0c0c0602u);
+    auto put = [&](int nib, uint32_t v16) {
+      *reinterpret_cast<uint16_t*>(base + (row0 + 5 - nib) * 128 + 8 * t) = (uint16_t)v16;
+    };
+    put(0, l02);
+    put(2, l02 >> 16);
+    put(4, l4);
+    put(1, h13);
+    put(3, h13 >> 16);
+    put(5, h5);
+  }
+}
+
 // one scale group of 16 columns: A from LDS (32 bytes per lane at ab, digit
 // row of the lane), B the +-6 operands of sign word w, block exponent sa
 __device__ __forceinline__ f32x4 f4_group_mfma(const uint8_t* ab, uint32_t w, int sa) {

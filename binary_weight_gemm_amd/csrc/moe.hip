@@ -1323,6 +1323,147 @@ __global__ __launch_bounds__(512) void k_moe_dbf(const uint16_t* __restrict__ x,
   for (int tb = RT; tb < cnt; tb += RT) run_tile(tb);
 }
 
+// Stage 0 on the fp8 x fp4 matrix cores (H % 512 == 0, at most two chunks
+// per wave): the gate and up V factors against x_s = d_in (.) x of the
+// routes (bf16 times fp16, exact in fp32), carried as fixed-point digit rows
+// of the 24-bit field under each wave slice's largest power of two (bits
+// below 2^-23 of the slice maximum dropped, f4.h), two routes per product,
+// the V signs as +-6 fp4 operands. One workgroup per (NT blocks of 16 rank
+// rows, active expert); h_s = d_mid (.) (the sum / 6) in fp32.
+template <int CPW, int NT>
+__global__ __launch_bounds__(512) void k_moe_dbf0_f4(const uint16_t* __restrict__ x, int H, int r, int R,
+                                                     DbfStageArgs a, MoeWs ws) {
+  extern __shared__ uint4 smem[];
+  const int4 bk = ws.blk[blockIdx.y];
+  const int e = bk.x, r0 = bk.y, cnt = bk.z;
+  if (cnt == 0) return;  // past the last active expert
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int G = H >> 7, nchunks = G >> 2;
+  const int c0 = wave * CPW;
+  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * MOE_F4_CHUNK;
+  float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * MOE_F4_CHUNK);
+  auto load_x = [&](int q0, uint4 (&xv)[2][CPW]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rr = q0 + h < cnt ? q0 + h : cnt - 1;
+      const uint16_t* xr = x + (size_t)ws.route_tok[r0 + rr] * H;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int k0 = (c0 + c) * 512 + 8 * lane;
+        xv[h][c] = *reinterpret_cast<const uint4*>(xr + (k0 < H ? k0 : 0));
+      }
+    }
+  };
+  uint4 xv[2][CPW];
+  load_x(0, xv);
+  uint4 dv[2][CPW];  // d_in of the gate and up chains, the lane's 8 values per chunk
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int k0 = (c0 + c) * 512 + 8 * lane;
+      dv[m][c] = *reinterpret_cast<const uint4*>(a.din[m] + (size_t)e * H + (k0 < H ? k0 : 0));
+    }
+  uint4 sg[2][NT][CPW];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = (blockIdx.x * NT + t) * 16 + j;
+    const size_t row = ((size_t)e * r + (n < r ? n : 0)) * G;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int g = 4 * (c0 + c) + kb;
+        sg[m][t][c] = a.sig[m][row + (g < G ? g : 0)];
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (lane < 32)
+    *reinterpret_cast<uint4*>(xw + (lane >> 3) * MOE_F4_GROUP + 12 * 128 + 16 * (lane & 7)) =
+        make_uint4(0u, 0u, 0u, 0u);
+  const int prow = j < 6 ? j : (j >= 8 && j < 14) ? j - 2 : 12;
+  uint8_t* base = xw + (lane >> 4) * MOE_F4_GROUP + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
+  for (int q0 = 0; q0 < cnt; q0 += 2) {
+    if (q0 > 0) load_x(q0, xv);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        if (c0 + c >= nchunks || q0 + h >= cnt) xv[h][c] = make_uint4(0u, 0u, 0u, 0u);
+    float acc[2][NT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      // x_s = d_in (.) x of both routes for chain m
+      f32x4 xs[2][CPW][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+          const uint32_t xw4[4] = {xv[h][c].x, xv[h][c].y, xv[h][c].z, xv[h][c].w};
+          const uint32_t dw4[4] = {dv[m][c].x, dv[m][c].y, dv[m][c].z, dv[m][c].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t xb = (i & 1) ? (xw4[i >> 1] >> 16) : (xw4[i >> 1] & 0xffffu);
+            const uint32_t db = (i & 1) ? (dw4[i >> 1] >> 16) : (dw4[i >> 1] & 0xffffu);
+            xs[h][c][i >> 2][i & 3] = bf16_to_f32(xb) * f16_bits_to_f32(db);
+          }
+        }
+      float S0, S1;
+      const uint32_t e0 = f4_slice_exponent_f32<CPW>(xs[0], S0), e1 = f4_slice_exponent_f32<CPW>(xs[1], S1);
+      const int sa = j < 8 ? (int)e0 - 2 - 4 * min(j, 6) : (int)e1 - 2 - 4 * min(j - 8, 6);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        if (c0 + c >= nchunks) break;  // uniform across the wave
+        f4_digits_f32(xs[0][c], S0, base, 0);
+        f4_digits_f32(xs[1][c], S1, base, 6);
+        const uint8_t* ab = xw + prow * 128 + 16 * kb;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          uint32_t w0 = sg[m][t][c].x, w1 = sg[m][t][c].y, w2 = sg[m][t][c].z, w3 = sg[m][t][c].w;
+          f4_transpose4(w0, w1, w2, w3);
+          const uint32_t wi[4] = {w0, w1, w2, w3};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 d = f4_group_mfma(ab + i * MOE_F4_GROUP, wi[i], sa);
+            acc[m][t] += (d[0] + d[1]) + (d[2] + d[3]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] += __shfl_down(acc[m][t], 16, 64);
+    const bool holds = (kb & 1) == 0;
+    if (wave > 0 && holds) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) red[(((wave - 1) * 2 + m) * NT + t) * 32 + (kb >> 1) * 16 + j] = acc[m][t];
+    }
+    __syncthreads();
+    if (wave == 0 && holds) {
+      const int p = q0 + (kb >> 1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = (blockIdx.x * NT + t) * 16 + j;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float v = acc[m][t];
+          for (int w = 1; w < nw; ++w) v += red[(((w - 1) * 2 + m) * NT + t) * 32 + (kb >> 1) * 16 + j];
+          if (p < cnt && n < r)
+            a.out[(size_t)m * R * r + (size_t)(r0 + p) * r + n] =
+                (v / 6.0f) * f16_bits_to_f32(a.dg[m][(size_t)e * r + n]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---- DBF experts, few tokens (T <= 4): five launches ----------------------
 //  route: one workgroup, one wave per token: top-k, then one block record per
 //         route in token-major order (route i = t*k + j forms its own block of
@@ -1446,6 +1587,16 @@ static hipError_t moe_dbf_stage(const uint16_t* x, int H, int I, int r, int R, i
   const DecSplit sp = dec_split(K / 128, 8);
   const int64_t blocks = (int64_t)((N + 15) / 16) * maxact;
   if constexpr (STAGE == 0) {
+    // the V factors of gate and up on the digit path where the hidden vector
+    // comes in whole 512-wide chunks
+    if (H % 512 == 0 && sp.cpw <= 2) {
+      constexpr int NT = 2;
+      const size_t lf = (size_t)sp.waves * MOE_F4_CHUNK + (size_t)(sp.waves - 1) * 2 * NT * 32 * 4;
+      const dim3 gf((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)maxact), bf(64 * sp.waves);
+      if (sp.cpw == 1) hipLaunchKernelGGL((k_moe_dbf0_f4<1, NT>), gf, bf, lf, st, x, H, r, R, a, ws);
+      else hipLaunchKernelGGL((k_moe_dbf0_f4<2, NT>), gf, bf, lf, st, x, H, r, R, a, ws);
+      return hipGetLastError();
+    }
     if (sp.cpw == 2) {
       if (blocks >= 4096) return moe_dbf_stage_cb<STAGE, 4, 4, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);
       if (blocks >= 2048) return moe_dbf_stage_cb<STAGE, 4, 2, 2>(x, H, I, r, R, maxact, a, ws, sp.waves, st);

@@ -39,6 +39,11 @@
  *    of its slice of the row (a change of less than 2^-23 of that slice's
  *    maximum; bf16 subnormals count as zero), split into six 4-bit digits
  *    whose products and partial sums are exact;
+ *  - the gate/up products of brq_moe_ffn on its grouped path (T > 4, H a
+ *    multiple of 512 up to 8192): the same digit scheme per route and wave
+ *    slice; the gate/up V factors of brq_moe_dbf_ffn (H a multiple of 512 up
+ *    to 8192): the digit scheme on x_s = d_in * x (exact in fp32), so that
+ *    bits below 2^-23 of the slice's largest |x_s| are dropped;
  *  - brq_gemm with 9 <= M <= 64: bf16 matrix cores with +-1 weights (bf16
  *    activations as they are), each scale group's sum scaled in fp32;
  *  - every other product on the fp16 matrix cores takes the activations as
