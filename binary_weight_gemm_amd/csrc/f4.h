@@ -6,7 +6,10 @@
 // its six 4-bit digits (most significant first) are sign-magnitude e4m3 codes
 // (code c <= 15 is c * 2^-9) with block exponent ebs - 2 - 4p for digit p,
 // against weights +-6 in fp4: every product and partial sum is an integer
-// times one power of two, exact in fp32.
+// times one power of two, exact in fp32. The single-row kernel in dec.hip
+// keeps its own inline form of these steps: built on these helpers it
+// compiled to the same instructions in another order and measured about 1 %
+// slower on one of the decode launch shapes.
 #pragma once
 
 #include "common.h"
