@@ -187,8 +187,13 @@ __global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logi
 // One workgroup of 1024 threads builds the expert-major lists from the ids.
 // Routes of one expert are ordered by token (slots of one token name distinct
 // experts): the rank of route (t, j) inside its expert is the number of earlier
-// tokens in the expert's token bitmap.
-__global__ __launch_bounds__(1024) void k_moe_route(int T, int E, int k, MoeWs ws) {
+// tokens in the expert's token bitmap. TOPK: the workgroup's sixteen waves
+// first route the tokens themselves (T <= MOE_ROUTE_T, one token per wave, as
+// k_moe_topk does), so that routing and lists take one launch.
+constexpr int MOE_ROUTE_T = 8;
+template <bool TOPK>
+__global__ __launch_bounds__(1024) void k_moe_route(const float* __restrict__ logits, int T, int E, int k, MoeWs ws,
+                                                    int32_t* __restrict__ ids_user, float* __restrict__ w_user) {
   __shared__ int s_ids[MOE_MAX_R];
   __shared__ int s_cnt[MOE_MAX_E];
   __shared__ int s_off[MOE_MAX_E];
@@ -196,14 +201,36 @@ __global__ __launch_bounds__(1024) void k_moe_route(int T, int E, int k, MoeWs w
   __shared__ int s_part[16];
   const int tid = threadIdx.x;
   const int words = (T + 63) >> 6;
+  if constexpr (TOPK) {
+    const int lane = tid & 63, t = tid >> 6;
+    if (t < T) {
+      int id;
+      float w;
+      if (E <= 256) wave_route<4>(logits + (size_t)t * E, E, k, id, w);
+      else wave_route<16>(logits + (size_t)t * E, E, k, id, w);
+      if (lane < k) {
+        s_ids[t * k + lane] = id;
+        ws.ids[t * k + lane] = id;
+        ws.wts[t * k + lane] = w;
+        if (ids_user) ids_user[t * k + lane] = id;
+        if (w_user) w_user[t * k + lane] = w;
+      }
+    }
+  }
   for (int e = tid; e < E; e += blockDim.x) {
     s_cnt[e] = 0;
     for (int q = 0; q < words; ++q) s_map[e * words + q] = 0ull;
   }
   __syncthreads();
   for (int r = tid; r < T * k; r += blockDim.x) {
-    const int id = ws.ids[r], t = r / k;
-    s_ids[r] = id;
+    const int t = r / k;
+    int id;
+    if constexpr (TOPK) {
+      id = s_ids[r];
+    } else {
+      id = ws.ids[r];
+      s_ids[r] = id;
+    }
     atomicAdd(&s_cnt[id], 1);
     atomicOr(&s_map[id * words + (t >> 6)], 1ull << (t & 63));
   }
@@ -231,6 +258,18 @@ __global__ __launch_bounds__(1024) void k_moe_route(int T, int E, int k, MoeWs w
     const int pos = s_off[e] + rank;
     ws.route_tok[pos] = t;
     ws.route_pos[r] = pos;
+  }
+}
+
+// top-k and expert-major lists: one launch for up to MOE_ROUTE_T tokens,
+// else a wave per token in k_moe_topk and the lists in a second launch
+static void moe_route(const float* logits, int T, int E, int k, const MoeWs& ws, int32_t* ids, float* w,
+                      hipStream_t st) {
+  if (T <= MOE_ROUTE_T) {
+    hipLaunchKernelGGL(k_moe_route<true>, dim3(1), dim3(1024), 0, st, logits, T, E, k, ws, ids, w);
+  } else {
+    hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, k, ws, ids, w);
+    hipLaunchKernelGGL(k_moe_route<false>, dim3(1), dim3(1024), 0, st, nullptr, T, E, k, ws, nullptr, nullptr);
   }
 }
 
@@ -1095,8 +1134,7 @@ hipError_t launch_moe(const uint16_t* x, const float* logits, int T, int H, int 
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, T, E, top_k, ws);
+  moe_route(logits, T, E, top_k, ws, ids, w, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const DecSplit sg = dec_split(H / 128, 8), sd = dec_split(I / 128, 8);
@@ -1622,8 +1660,7 @@ hipError_t launch_moe_dbf(const uint16_t* x, const float* logits, int T, int H, 
   if (tok) {
     hipLaunchKernelGGL(k_moe_route_tok, dim3(1), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
   } else {
-    hipLaunchKernelGGL(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ws, ids, w);
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, T, E, top_k, ws);
+    moe_route(logits, T, E, top_k, ws, ids, w, st);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
