@@ -738,6 +738,22 @@ def test_moe_small_intermediates(T):
     check_f32(f64(y), o, F32_TOL, f"moe small a T={T}")
 
 
+# hidden sizes on the digit path of the grouped gate/up (a multiple of 512):
+# one wave (H = 512) and three (H = 1536), routes in pairs with an odd count
+@pytest.mark.parametrize("T,H,I,k", [(24, 512, 256, 4), (9, 1536, 128, 3), (40, 512, 128, 1), (6, 512, 256, 4)])
+def test_moe_digit_gateup_shapes(T, H, I, k):
+    say("moe digit gate/up", T, H, I, k)
+    cfg = datagen.C4(E=16, H=H, I=I, top_k=k, layer=13)
+    ex = _Experts(cfg)
+    x, lg = cfg.x(T), cfg.logits(T)
+    o, oids, _ = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, cfg.top_k)
+    y, ids, _ = brq().moe_ffn(dev(x), dev(lg), *ex.d, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32,
+                              return_routing=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+    check_f32(f64(y), o, F32_TOL, f"moe digit gate/up T={T} H={H}")
+
+
 def test_moe_c4_bf16_and_fresh_logits(c4_experts):
     say("C4 moe bf16, several logit draws")
     for it in range(3):
@@ -807,7 +823,9 @@ def _dbf_moe_case(cfg, T, out=torch.float32, it=0):
 # ragged blocks
 @pytest.mark.parametrize("T,E,H,I,r,k", [(1, 16, 256, 128, 128, 4), (3, 16, 256, 128, 640, 4),
                                          (4, 8, 256, 128, 128, 3), (5, 16, 256, 128, 128, 4),
-                                         (64, 16, 256, 128, 128, 4), (7, 8, 384, 256, 256, 3)])
+                                         (64, 16, 256, 128, 128, 4), (7, 8, 384, 256, 256, 3),
+                                         (2, 16, 512, 128, 256, 4), (24, 16, 512, 128, 256, 4),
+                                         (9, 8, 1536, 256, 128, 3)])
 def test_moe_dbf_small(T, E, H, I, r, k):
     say("moe dbf", T, E, H, I, r, k)
     cfg = datagen.C4D(E=E, H=H, I=I, r=r, top_k=k, layer=1)
