@@ -13,10 +13,13 @@
 //  1. top-k per token (descending fp32 logit, ties to the lower expert index)
 //     and the softmax over the k selected logits, one wave per token.
 //  2. route: per-expert counts and offsets, one record per active expert and
-//     the expert-major route list (one workgroup).
-//  3. gate/up: one workgroup per (4 blocks of 16 intermediate columns, active
+//     the expert-major route list (one workgroup; for T <= 8 the same
+//     workgroup does step 1 first, in one launch).
+//  3. gate/up: one workgroup per (blocks of 16 intermediate columns, active
 //     expert); both products share every activation operand; SwiGLU in fp32;
-//     the result is stored as an fp32 row per route.
+//     the result is stored as an fp32 row per route. Where H is a multiple
+//     of 512 (up to 8192) on the fp8 x fp4 matrix cores with the routes as
+//     fixed-point digit rows (k_moe_gateup_f4, f4.h), else on fp16 tiles.
 //  4. down: one workgroup per (4 blocks of 16 hidden columns, active expert);
 //     stages the fp32 rows as scaled fp16 hi/lo pieces (WaveStageF32) and
 //     writes the route's fp32 output.
