@@ -362,7 +362,9 @@ __global__ __launch_bounds__(1024) void k_gemm_dec_f4(const uint16_t* __restrict
       }
     }
     const int prow = j < F4_DIGITS ? j : F4_DIGITS;  // lanes 6..15 read the zero row
-    const int sa = (int)ebs - 2 - 4 * prow;
+    // the zero row takes scale 2^0: at ebs = 25 its digit form ebs - 26
+    // would be the E8M0 NaN code 0xff
+    const int sa = prow < F4_DIGITS ? (int)ebs - 2 - 4 * prow : 127;
     // ---- products (the last wave's slots past the last chunk take no part)
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {

@@ -4,7 +4,8 @@
 // per wave slice of a row, 2^e the largest power of two (biased exponent
 // ebs), every |x| becomes the 24-bit integer X = trunc(|x| * 2^(150 - ebs));
 // its six 4-bit digits (most significant first) are sign-magnitude e4m3 codes
-// (code c <= 15 is c * 2^-9) with block exponent ebs - 2 - 4p for digit p,
+// (code c <= 15 is c * 2^-9) with block exponent ebs - 2 - 4p for digit p
+// (the zero row takes exponent 0: ebs - 26 would reach the E8M0 NaN code),
 // against weights +-6 in fp4: every product and partial sum is an integer
 // times one power of two, exact in fp32. The single-row kernel in dec.hip
 // keeps its own inline form of these steps: built on these helpers it

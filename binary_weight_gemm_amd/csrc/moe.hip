@@ -492,7 +492,8 @@ __global__ __launch_bounds__(512) void k_moe_gateup_f4(const uint16_t* __restric
         if (c0 + c >= nchunks || q0 + h >= cnt) xv[h][c] = make_uint4(0u, 0u, 0u, 0u);
     float S0, S1;
     const uint32_t e0 = f4_slice_exponent<CPW>(xv[0], S0), e1 = f4_slice_exponent<CPW>(xv[1], S1);
-    const int sa = j < 8 ? (int)e0 - 2 - 4 * min(j, 6) : (int)e1 - 2 - 4 * min(j - 8, 6);
+    // the zero row (prow 12) takes scale 2^0 (ebs - 26 is the E8M0 NaN code at ebs = 25)
+    const int sa = prow == 12 ? 127 : j < 8 ? (int)e0 - 2 - 4 * j : (int)e1 - 2 - 4 * (j - 8);
     float acc[2][NT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -1452,7 +1453,8 @@ __global__ __launch_bounds__(512) void k_moe_dbf0_f4(const uint16_t* __restrict_
         }
       float S0, S1;
       const uint32_t e0 = f4_slice_exponent_f32<CPW>(xs[0], S0), e1 = f4_slice_exponent_f32<CPW>(xs[1], S1);
-      const int sa = j < 8 ? (int)e0 - 2 - 4 * min(j, 6) : (int)e1 - 2 - 4 * min(j - 8, 6);
+      // the zero row (prow 12) takes scale 2^0 (ebs - 26 is the E8M0 NaN code at ebs = 25)
+      const int sa = prow == 12 ? 127 : j < 8 ? (int)e0 - 2 - 4 * j : (int)e1 - 2 - 4 * (j - 8);
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
 #pragma unroll

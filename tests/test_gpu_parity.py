@@ -281,6 +281,66 @@ def test_dbf_and_moe_activation_range():
                 assert not np.any(ym[t])
 
 
+def _exp25_rows(M, K, key):
+    """Rows whose every value lies in [2^-102, 1.9 * 2^-102] with a random
+    sign: every wave slice's largest |x| has biased exponent 25, where the
+    digit operands' zero row would read the E8M0 NaN code if it took the
+    digit rows' exponent formula."""
+    g = datagen.rng(83, M, K, key)
+    mag = (1.0 + 0.9 * g.random((M, K))) * 2.0 ** -102
+    sgn = np.where(g.random((M, K)) < 0.5, -1.0, 1.0)
+    return datagen.bf16_bits_from_f32((sgn * mag).astype(np.float32))
+
+
+@pytest.mark.parametrize("N,K", [(96, 512), (520, 4096)])
+def test_digit_paths_slice_exponent_25(N, K):
+    """The fp8 x fp4 digit paths on activations whose slice maxima sit at
+    biased exponent 25: the single-row product matches the oracle to the fp32
+    bar; a routed token at that scale gives finite outputs (its SwiGLU product
+    underflows fp32, so it is checked for finiteness and size) and leaves the
+    other tokens' results at the bar, on the plain and the DBF-expert layers."""
+    say("digit paths at slice exponent 25", N, K)
+    w = datagen.normal_f32((83, N, K), (N, K), 0.02)
+    ow, osc = oracle.pack_sign1(w)
+    xb = _exp25_rows(1, K, 0)
+    o = oracle.bin_gemm(oracle.bf16_to_f64(xb), ow, osc, N, K)
+    y = f64(brq().gemm(dev(xb), dev(ow), dev(osc), N, K, out_dtype=torch.float32))
+    assert np.all(np.isfinite(y))
+    check_f32(y, o, F32_TOL, f"single row at 2^-102, {N}x{K}")
+    if K != 512:
+        return
+
+    def mixed(cfg, T):
+        x = cfg.x(T).copy()
+        x[1] = _exp25_rows(1, cfg.H, T)[0]
+        return x
+
+    def check(y, o, T, what):
+        assert np.all(np.isfinite(y)), f"{what} T={T}: non-finite output"
+        assert np.abs(y[1]).max() <= 2.0 ** -120, f"{what} T={T}: tiny token's output too large"
+        keep = [t for t in range(T) if t != 1]
+        check_f32(y[keep], o[keep], F32_TOL, f"{what} T={T}, other tokens")
+
+    cfg = datagen.C4(E=16, H=512, I=128, top_k=4, layer=83)
+    ex = _Experts(cfg)
+    for T in (3, 9):  # few-token path, grouped path
+        x, lg = mixed(cfg, T), cfg.logits(T)
+        om, oids, _ = oracle.moe_ffn(oracle.bf16_to_f64(x), lg, ex, cfg.H, cfg.I, cfg.top_k)
+        ym, ids, _ = brq().moe_ffn(dev(x), dev(lg), *ex.d, cfg.E, cfg.H, cfg.I, cfg.top_k, out_dtype=torch.float32,
+                                   return_routing=True)
+        assert np.array_equal(ids.cpu().numpy().astype(np.int64), oids)
+        check(f64(ym), om, T, "moe")
+    cfg = datagen.C4D(E=16, H=512, I=128, r=256, top_k=4, layer=83)
+    for T in (2, 24):
+        x, lg = mixed(cfg, T), cfg.logits(T)
+        ids_o, _ = oracle.route_topk(lg, cfg.top_k)
+        recs = _dbf_moe_dev(cfg, sorted(set(int(e) for e in ids_o.ravel())))
+        o, _, _ = oracle.moe_dbf_ffn(oracle.bf16_to_f64(x), lg, _dbf_moe_oracle_experts(cfg), cfg.H, cfg.I, cfg.r,
+                                     cfg.top_k)
+        y = brq().moe_dbf_ffn(dev(x), dev(lg), *recs, cfg.E, cfg.H, cfg.I, cfg.r, cfg.top_k, out_dtype=torch.float32)
+        check(f64(y), o, T, "moe dbf")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 40, 640), (64, 96, 1024)])
 def test_gemm_decode_bf16(M, N, K):
     say("gemm decode bf16", M, N, K)
