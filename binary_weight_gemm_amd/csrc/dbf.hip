@@ -13,6 +13,7 @@
 // slice (decode: per wave; tiled: per row, set by k_dbf_split) near 2^14, so
 // the pieces keep about 22 significant bits whatever the magnitude of D_mid.
 #include "dec_core.h"
+#include "f4.h"
 #include "kernels.h"
 #include "tile.h"
 
@@ -76,6 +77,115 @@ __global__ __launch_bounds__(1024) void k_dbf1_dec(const uint16_t* __restrict__ 
       const int m = 16 * tt + 4 * (lane >> 4) + i;
       if (m < M) hs[(size_t)m * r + col] = acc[0][tt][i] * dm;
     }
+}
+
+// Decode path, stage 1 for one row with n % 512 == 0: x_s = D_in x in fp32
+// (a bf16 times an fp16 value, exact), per wave slice as six fixed-point
+// digit rows under the slice's largest power of two (the single-row scheme
+// of the group-128 product on fp32 values: bits below 2^-23 of the slice
+// maximum are dropped), V as +-6 fp4 operands on the fp8 x fp4 matrix cores,
+// one 512-wide chunk per wave up to 16 waves; D_mid in the epilogue.
+constexpr int DBF_F4_GROUP = 7 * 128;           // six digit rows of 128 codes and a zero row
+constexpr int DBF_F4_CHUNK = 4 * DBF_F4_GROUP;  // four groups of 128
+
+template <int CPW>
+__global__ __launch_bounds__(1024) void k_dbf1_f4(const uint16_t* __restrict__ x, int r, int n,
+                                                  const uint4* __restrict__ v, const uint16_t* __restrict__ d_in,
+                                                  const uint16_t* __restrict__ d_mid, float* __restrict__ hs) {
+  extern __shared__ uint4 smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  const int G = n >> 7, nchunks = G >> 2;
+  const int c0 = wave * CPW;
+  const int col = blockIdx.x * 16 + j;  // row of V = output column of stage 1
+  uint8_t* xw = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * CPW * DBF_F4_CHUNK;
+  float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + (size_t)nw * CPW * DBF_F4_CHUNK);
+  float acc = 0.f;
+  if (c0 < nchunks) {  // uniform across the wave
+    uint4 xv[CPW], dv[CPW], sg[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int k0 = (c0 + c) * 512 + 8 * lane;
+      xv[c] = *reinterpret_cast<const uint4*>(x + (k0 < n ? k0 : 0));
+      dv[c] = *reinterpret_cast<const uint4*>(d_in + (k0 < n ? k0 : 0));
+    }
+    const size_t row = (size_t)(col < r ? col : 0) * G;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int g = 4 * (c0 + c) + kb;
+      sg[c] = v[row + (g < G ? g : 0)];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+    // x_s of the lane's 8 values per chunk; slots past the last chunk hold zeros
+    f32x4 xs[CPW][2];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint32_t xw4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+      const uint32_t dw4[4] = {dv[c].x, dv[c].y, dv[c].z, dv[c].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t xb = (i & 1) ? (xw4[i >> 1] >> 16) : (xw4[i >> 1] & 0xffffu);
+        const uint32_t db = (i & 1) ? (dw4[i >> 1] >> 16) : (dw4[i >> 1] & 0xffffu);
+        xs[c][i >> 2][i & 3] = c0 + c < nchunks ? bf16_to_f32(xb) * f16_bits_to_f32(db) : 0.f;
+      }
+    }
+    float S;
+    const uint32_t ebs = f4_slice_exponent_f32<CPW>(xs, S);
+    uint8_t* base = xw + (lane >> 4) * DBF_F4_GROUP + 32 * ((lane & 15) >> 2) + 2 * (lane & 3);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      if (lane < 32)  // the zero row of each group: 16 bytes per lane
+        *reinterpret_cast<uint4*>(xw + c * DBF_F4_CHUNK + (lane >> 3) * DBF_F4_GROUP + 6 * 128 + 16 * (lane & 7)) =
+            make_uint4(0u, 0u, 0u, 0u);
+      f4_digits_f32(xs[c], S, base + c * DBF_F4_CHUNK, 0);
+    }
+    // MFMA rows 0..5 read the digit rows, 6..15 the zero row (block exponent 0)
+    const int prow = j < 6 ? j : 6;
+    const int sa = prow < 6 ? (int)ebs - 2 - 4 * prow : 127;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      if (c0 + c >= nchunks) break;  // uniform across the wave
+      const uint8_t* ab = xw + c * DBF_F4_CHUNK + prow * 128 + 16 * kb;
+      uint32_t w0 = sg[c].x, w1 = sg[c].y, w2 = sg[c].z, w3 = sg[c].w;
+      f4_transpose4(w0, w1, w2, w3);
+      const uint32_t wi[4] = {w0, w1, w2, w3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 d = f4_group_mfma(ab + i * DBF_F4_GROUP, wi[i], sa);
+        acc += (d[0] + d[1]) + (d[2] + d[3]);
+      }
+    }
+  }
+  // digit rows 4 and 5 (lanes 16..31) join rows 0..3 (lanes 0..15); waves meet in LDS in wave order
+  acc += __shfl_down(acc, 16, 64);
+  if (wave > 0 && kb == 0) red[(wave - 1) * 16 + j] = acc;
+  __syncthreads();
+  if (wave != 0 || kb != 0 || col >= r) return;
+  float s = acc;
+  for (int w = 1; w < nw; ++w) s += red[(w - 1) * 16 + j];
+  hs[col] = (s / 6.0f) * f16_bits_to_f32(d_mid[col]);
+}
+
+// launches k_dbf1_f4 where it applies (one row, n % 512 == 0, at most two
+// chunks per wave over 16 waves); false otherwise
+static bool dbf1_f4(const uint16_t* x, int r, int n, const uint4* v, const uint16_t* d_in, const uint16_t* d_mid,
+                    float* hs, hipStream_t st) {
+  if (n % 512 != 0) return false;
+  const int chunks = n / 512;
+  const int cpw = chunks <= 16 ? 1 : 2;
+  if (chunks > 16 * cpw) return false;
+  const int waves = (chunks + cpw - 1) / cpw;
+  const size_t lds = (size_t)waves * cpw * DBF_F4_CHUNK + (size_t)(waves - 1) * 16 * 4;
+  const dim3 grid((r + 15) / 16), block(64 * waves);
+  if (cpw == 1) {
+    hipLaunchKernelGGL((k_dbf1_f4<1>), grid, block, lds, st, x, r, n, v, d_in, d_mid, hs);
+  } else {
+    if (lds > 64 * 1024)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dbf1_f4<2>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((k_dbf1_f4<2>), grid, block, lds, st, x, r, n, v, d_in, d_mid, hs);
+  }
+  return true;
 }
 
 // Decode path, stage 2: every h_s row is staged in LDS as two scaled fp16
@@ -465,8 +575,9 @@ static hipError_t dbf_decode(const uint16_t* x, int M, int m, int n, int r, cons
   const size_t l2 = (size_t)s2.waves * s2.cpw * MAXR2 * 1024, r2 = (size_t)(s2.waves - 1) * 64 * 16;
   const uint4* v4 = reinterpret_cast<const uint4*>(v);
   const uint4* u4 = reinterpret_cast<const uint4*>(u);
-  BRQ_CPW_SWITCH(s1.cpw, hipLaunchKernelGGL((k_dbf1_dec<1, CPW, MAXR1>), dim3((r + 15) / 16), dim3(64 * s1.waves),
-                                            l1 > r1 ? l1 : r1, st, x, M, r, n, v4, d_in, d_mid, hs));
+  if (!(MAXR1 == 1 && dbf1_f4(x, r, n, v4, d_in, d_mid, hs, st)))
+    BRQ_CPW_SWITCH(s1.cpw, hipLaunchKernelGGL((k_dbf1_dec<1, CPW, MAXR1>), dim3((r + 15) / 16), dim3(64 * s1.waves),
+                                              l1 > r1 ? l1 : r1, st, x, M, r, n, v4, d_in, d_mid, hs));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   BRQ_CPW_SWITCH(s2.cpw, hipLaunchKernelGGL((k_dbf2_dec<1, CPW, MAXR2>), dim3((m + 15) / 16), dim3(64 * s2.waves),

@@ -3,7 +3,9 @@ multi-launch paths and the fp64 oracle.
 
 The one-launch DBF chain (M <= 8) and MoE layer (T <= 4) run the stage bodies
 and sum orders of the multi-launch kernels, so their outputs and routing must
-be the same bits; they are also checked against the oracle directly. The
+be the same bits (save one DBF row with n % 512 == 0, whose two-launch first
+stage runs on the fp8 x fp4 digit path); they are also checked against the
+oracle directly. The
 bounded grid-wide wait is exercised from the host with a spin limit of one
 poll: every workgroup then either finds the others arrived or gives up and
 writes NaN, and each kernel still ends normally.
@@ -14,7 +16,7 @@ import torch
 
 import datagen
 import oracle
-from gpu_util import check_f32, dev, f64, host_bits
+from gpu_util import check_bf16, check_f32, dev, f64, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -62,10 +64,20 @@ def test_dbf_one_launch_same_bits(M, m, n, r):
     say("dbf one launch", M, m, n, r)
     args = _dbf_inputs(M, m, n, r, M + m + n + r)
     o = oracle.dbf_chain(oracle.bf16_to_f64(args[0]), args[1], args[2], args[3], args[4], args[5], m, n, r)
+    # one row with n % 512 == 0: the two-launch chain's first stage runs on the
+    # fp8 x fp4 digit path, the one-launch chain keeps the fp16 stage body, so
+    # there each is held to the oracle's bar instead of to the other's bits
+    digit = M == 1 and n % 512 == 0
     for out in (torch.float32, torch.bfloat16):
         y_on = _dbf_run(args, m, n, r, brq().FUSION_ON, out)
         y_off = _dbf_run(args, m, n, r, brq().FUSION_OFF, out)
-        assert np.array_equal(host_bits(y_on), host_bits(y_off)), f"one launch != two launches ({out})"
+        if not digit:
+            assert np.array_equal(host_bits(y_on), host_bits(y_off)), f"one launch != two launches ({out})"
+        elif out == torch.float32:
+            check_f32(f64(y_off), o, F32_TOL, f"dbf two launches {M},{m},{n},{r}")
+        else:
+            check_bf16(y_on, o, f"dbf one launch bf16 {M},{m},{n},{r}")
+            check_bf16(y_off, o, f"dbf two launches bf16 {M},{m},{n},{r}")
     y32 = _dbf_run(args, m, n, r, brq().FUSION_ON, torch.float32)
     check_f32(f64(y32), o, F32_TOL, f"dbf one launch {M},{m},{n},{r}")
 
@@ -142,13 +154,13 @@ def test_moe_one_launch_named_geometries(name, T):
 def test_one_launch_wait_guard():
     """Spin limit of one poll: every workgroup either sees the wait released
     or gives up and writes NaN over its own outputs; every other output keeps
-    the two-launch bits, the kernels end, and the next default call is
-    unaffected (the wait slots stay consistent)."""
+    the bits of the unguarded one-launch call, the kernels end, and the next
+    call is unaffected (the wait slots stay consistent)."""
     say("one launch wait guard")
     b = brq()
     M, m, n, r = 1, 4096, 4096, 2048
     args = _dbf_inputs(M, m, n, r, 7)
-    ref = host_bits(_dbf_run(args, m, n, r, b.FUSION_OFF, torch.float32)).view(np.float32)
+    ref = host_bits(_dbf_run(args, m, n, r, b.FUSION_ON, torch.float32)).view(np.float32)
     b.set_decode_fusion(b.FUSION_ON, 1)
     x, d_in, vw, d_mid, uw, d_out = args
     y = b.dbf_gemm(dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r, out_dtype=torch.float32)

@@ -533,6 +533,43 @@ def _dbf_case(M, m, n, r, key, out=torch.float32):
     return y, o
 
 
+# one row with n % 512 == 0: the first stage on the fp8 x fp4 matrix cores
+# with x_s = D_in x as digit rows, one wave (n = 512), three (1536), 17 chunks
+# in pairs with the last wave's second slot empty (8704), 16 waves of two
+# (16384, beyond 64 KiB of LDS); ranks of 8 to 24 16-row tiles
+@pytest.mark.parametrize("m,n,r", [(64, 512, 384), (40, 1536, 128), (130, 8704, 256), (48, 16384, 128)])
+def test_dbf_single_row_digit_stage(m, n, r):
+    say("dbf single row digit stage", m, n, r)
+    for out in (torch.float32, torch.bfloat16):
+        y, o = _dbf_case(1, m, n, r, m + n + r, out=out)
+        if out == torch.float32:
+            check_f32(f64(y), o, F32_TOL, f"dbf 1x{m}x{n} r={r}")
+        else:
+            check_bf16(y, o, f"dbf 1x{m}x{n} r={r} bf16")
+
+
+def test_dbf_single_row_activation_range():
+    """Single rows at 1e5, 1e30, 0, 1e-30, 2^-20 on the digit first stage:
+    each matches the oracle to the fp32 bar, the zero row gives zeros."""
+    say("dbf single row activation range")
+    m_, n_, r_ = 64, 1024, 128
+    v = datagen.pm1_f32((79, 2, 0), (r_, n_))
+    u = datagen.pm1_f32((79, 2, 1), (m_, r_))
+    d_in, d_mid, d_out = (datagen.f16_lognormal((79, 2, 2 + i), (s_,)) for i, s_ in enumerate((n_, r_, m_)))
+    vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
+    base = datagen.rng(79, 2, 3).standard_normal(n_).astype(np.float32)
+    for sc in (1e5, 1e30, 0.0, 1e-30, 2.0 ** -20):
+        xb = datagen.bf16_bits_from_f32((base * np.float32(sc))[None, :])
+        o = oracle.dbf_chain(oracle.bf16_to_f64(xb), d_in, vw, d_mid, uw, d_out, m_, n_, r_)
+        y = f64(brq().dbf_gemm(dev(xb), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m_, n_, r_,
+                               out_dtype=torch.float32))
+        assert np.all(np.isfinite(y))
+        if np.any(o):
+            check_f32(y, o, F32_TOL, f"dbf single row at scale {sc:g}")
+        else:
+            assert not np.any(y)
+
+
 @pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (1, 48, 256, 384), (3, 200, 512, 256), (32, 64, 640, 512),
                                      (33, 96, 256, 128), (100, 256, 512, 384)])
 def test_dbf_small(M, m, n, r):
