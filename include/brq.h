@@ -111,7 +111,10 @@ const char* brq_last_error(void);
  * gate/up, SwiGLU and down in one launch). brq_dbf_gemm with M <= 8 and
  * brq_moe_ffn / brq_moe_ffn_noalloc with T <= 4 can each run as one launch
  * whose workgroups (all resident on the device at once) wait for one another
- * once, instead of two launches. The result bits are the same either way.
+ * once, instead of two launches. The result bits are the same either way,
+ * except brq_dbf_gemm with M = 1 and n % 512 == 0, whose multi-launch first
+ * stage takes the fp8 x fp4 digit path (see Numerics) and the single launch
+ * the fp16 one: both meet the same bound, not the same bits.
  *
  *   mode        BRQ_FUSION_DEFAULT: the library's choice per path, the one
  *               that measured faster on MI355X (today the multi-launch path
