@@ -43,8 +43,9 @@
  *    multiple of 512 up to 8192): the same digit scheme per route and wave
  *    slice; the gate/up V factors of brq_moe_dbf_ffn (H a multiple of 512 up
  *    to 8192) and the first stage of brq_dbf_gemm for one row with n % 512
- *    == 0 (n <= 16384): the digit scheme on x_s = d_in * x (exact in fp32),
- *    so that bits below 2^-23 of the slice's largest |x_s| are dropped;
+ *    == 0 (n <= 16384): the digit scheme on x_s = d_in * x (exact in fp32;
+ *    an x_s below 2^-126 counts as zero), so that bits below 2^-23 of the
+ *    slice's largest |x_s| are dropped;
  *  - brq_gemm with 9 <= M <= 64: bf16 matrix cores with +-1 weights (bf16
  *    activations as they are), each scale group's sum scaled in fp32;
  *  - every other product on the fp16 matrix cores takes the activations as
