@@ -6,8 +6,10 @@
 // Episode 01: DBF", section 1). The products here run on the fp16 matrix
 // cores: the weight operand of an MFMA is built in registers as the fp16 value
 // +-c, where c is the group scale (group-128 format), a per-k diagonal entry
-// (the DBF input diagonal) or 1.0. c is never negative, so the operand is the
-// sign bit OR-ed onto c: one shift and one and-or per pair of weights. Both
+// (the DBF input diagonal) or 1.0. A scale is never negative, so the operand
+// is the sign bit OR-ed onto c: one shift and one and-or per pair of weights;
+// a diagonal entry is real-valued and may be negative, so there the weight's
+// sign bit is XOR-ed onto c's (one shift, one and, one xor). Both
 // operands are exact in fp16 and every product is exact in the fp32
 // accumulator.
 //

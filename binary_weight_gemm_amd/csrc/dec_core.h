@@ -109,7 +109,10 @@ __device__ __forceinline__ void b_compute(const BPre<NB, CPW>& bp, const u32x4* 
         for (int t = 0; t < 4; ++t) {
           const int bit = 4 * (i & 3) + t;
           const uint32_t mag = (BMODE == BM_PERK) ? (bp.ok[nb][c] ? mk[t] : 0u) : S;
-          b[t] = ((dw << (15 - bit)) & 0x80008000u) | mag;
+          // a scale is never negative: the weight's sign bit is OR-ed on; a
+          // per-k diagonal value may be, so its sign bit is flipped instead
+          const uint32_t sw = (dw << (15 - bit)) & 0x80008000u;
+          b[t] = (BMODE == BM_PERK) ? (sw ^ mag) : (sw | mag);
         }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {

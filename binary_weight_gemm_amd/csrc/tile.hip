@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
           const uint32_t lw = rk[u][0][t >> 1], hw = rk[u][1][t >> 1];
           mag = (t & 1) ? ((lw >> 16) | (hw & 0xffff0000u)) : ((lw & 0xffffu) | (hw << 16));
         }
-        o[t] = ((dw << (15 - bit)) & 0x80008000u) | mag;
+        // a per-k diagonal value may be negative: flip its sign bit (a scale is OR-ed)
+        const uint32_t sw = (dw << (15 - bit)) & 0x80008000u;
+        o[t] = (BMODE == BM_PERK) ? (sw ^ mag) : (sw | mag);
       }
       uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][col * LDK + 32 * q + 2 * b0]);
       dst[0] = make_uint4(o[0], o[1], o[2], o[3]);

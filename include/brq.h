@@ -225,7 +225,7 @@ brq_status brq_gemm_lr(const uint16_t* x, int64_t M, int64_t N, int64_t K,
  *   x      device, bf16 [M][n]
  *   d_in   device, fp16 [n];  v device, SIGN1 plane of V [r][n]
  *   d_mid  device, fp16 [r];  u device, SIGN1 plane of U [m][r]
- *   d_out  device, fp16 [m]
+ *   d_out  device, fp16 [m]   (the three diagonals are real-valued: either sign)
  *   y      device, out, [M][m] of y_dtype
  *   ws     device workspace, >= brq_dbf_workspace_bytes(M, m, n, r)
  *   M >= 1; m >= 1; n, r >= 128 and multiples of 128.

@@ -570,6 +570,71 @@ def test_dbf_single_row_activation_range():
             assert not np.any(y)
 
 
+def _signed(d, key):
+    """The diagonal d with each entry's sign drawn at random (the diagonals
+    are real-valued, so either sign is valid)."""
+    g = datagen.rng(97, *key)
+    return np.where(g.random(d.shape) < 0.5, -d, d).astype(np.float16)
+
+
+# negative diagonal entries: D_in enters the first product as the weight
+# operand's magnitude on the fp16 paths (one row with n = 640, three rows,
+# the tiled path at M = 100, and the one-launch chain) and as x_s on the
+# digit path (one row, n = 1024); D_mid and D_out scale in fp32
+@pytest.mark.parametrize("M,m,n,r", [(1, 64, 640, 256), (1, 64, 1024, 128), (3, 200, 512, 256),
+                                     (100, 256, 512, 384)])
+def test_dbf_negative_diagonals(M, m, n, r):
+    say("dbf negative diagonals", M, m, n, r)
+    key = (M, m, n, r)
+    v = datagen.pm1_f32((98,) + key + (0,), (r, n))
+    u = datagen.pm1_f32((98,) + key + (1,), (m, r))
+    d_in, d_mid, d_out = (_signed(datagen.f16_lognormal((98,) + key + (2 + i,), (s_,)), key + (i,))
+                          for i, s_ in enumerate((n, r, m)))
+    assert (d_in < 0).any() and (d_mid < 0).any() and (d_out < 0).any()
+    x = datagen.bf16_normal((98,) + key + (5,), (M, n))
+    vw, uw = oracle.pack_sign1_only(v), oracle.pack_sign1_only(u)
+    o = oracle.dbf_chain(oracle.bf16_to_f64(x), d_in, vw, d_mid, uw, d_out, m, n, r)
+    args = (dev(x), dev(d_in), dev(vw), dev(d_mid), dev(uw), dev(d_out), m, n, r)
+    y = brq().dbf_gemm(*args, out_dtype=torch.float32)
+    check_f32(f64(y), o, F32_TOL, f"dbf negative diagonals {key}")
+    if M <= 8:
+        brq().set_decode_fusion(brq().FUSION_ON)
+        try:
+            y1 = brq().dbf_gemm(*args, out_dtype=torch.float32)
+            check_f32(f64(y1), o, F32_TOL, f"dbf negative diagonals, one launch {key}")
+        finally:
+            brq().set_decode_fusion(brq().FUSION_DEFAULT)
+
+
+class _SignedDiagonals:
+    """A DBF-expert configuration whose three diagonals per projection take
+    random signs."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+
+    def __getattr__(self, name):
+        return getattr(self.cfg, name)
+
+    def proj(self, e, p):
+        d = dict(self.cfg.proj(e, p))
+        for i, name in enumerate(("d_in", "d_mid", "d_out")):
+            d[name] = _signed(d[name], (e, p, i))
+        return d
+
+
+# the routed DBF-expert layer with signed diagonals: stage 0 on fp16 tiles
+# (H = 384) and on digit rows (H = 512), the down chain's D_in on the a rows,
+# few-token (T = 2) and grouped (T = 7, 24) paths
+@pytest.mark.parametrize("T,E,H,I,r,k", [(2, 8, 384, 256, 256, 3), (7, 8, 384, 256, 256, 3),
+                                         (24, 16, 512, 128, 256, 4)])
+def test_moe_dbf_negative_diagonals(T, E, H, I, r, k):
+    say("moe dbf negative diagonals", T, E, H, I, r, k)
+    cfg = _SignedDiagonals(datagen.C4D(E=E, H=H, I=I, r=r, top_k=k, layer=9))
+    y, o = _dbf_moe_case(cfg, T)
+    check_f32(f64(y), o, F32_TOL, f"moe dbf negative diagonals T={T} H={H}")
+
+
 @pytest.mark.parametrize("M,m,n,r", [(1, 16, 128, 128), (1, 48, 256, 384), (3, 200, 512, 256), (32, 64, 640, 512),
                                      (33, 96, 256, 128), (100, 256, 512, 384)])
 def test_dbf_small(M, m, n, r):
