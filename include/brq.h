@@ -178,7 +178,9 @@ brq_status brq_pack(const float* w, int64_t rows, int64_t cols,
  * section 1: a binary weight selects x or -x).
  *
  *   x       device, bf16 [M][K]
- *   signs   device, SIGN1 plane of W [N][K]; scales device, fp16 [N][K/128]
+ *   signs   device, SIGN1 plane of W [N][K]; scales device, fp16 [N][K/128],
+ *           each a non-negative finite value (the mean magnitude of its group,
+ *           as brq_pack writes it; the sign of a weight lives in its bit)
  *   y       device, out, [M][N] of y_dtype
  *   ws      device workspace of at least brq_gemm_workspace_bytes(M, N, K)
  *           bytes (may be NULL when that size is 0)
@@ -281,6 +283,7 @@ brq_status brq_dbf_gemm_q8(const uint16_t* x, int64_t M, int64_t m, int64_t n, i
  *   x        device, bf16 [T][H];  logits device, fp32 [T][E]
  *   gate_s / up_s    device, SIGN1 planes [E][I][H/64]; gate_sc / up_sc fp16 [E][I][H/128]
  *   down_s           device, SIGN1 plane [E][H][I/64];   down_sc fp16 [E][H][I/128]
+ *                    (scales non-negative and finite, as for brq_gemm)
  *   y        device, out, [T][H] of y_dtype
  *   ids, w   device, out, [T][top_k] int32 / fp32, or NULL
  *   ws       device workspace, >= brq_moe_workspace_bytes(T, H, I, E, top_k)
@@ -325,7 +328,7 @@ brq_status brq_moe_ffn_noalloc(const uint16_t* x, const float* logits,
  * "LLM binarization, Episode 01: DBF", section 4): for E experts of an m x n
  * projection with inner dimension r,
  *   d_in  fp16 [E][n];  v  SIGN1 [E][r][n/64];  d_mid fp16 [E][r];
- *   u     SIGN1 [E][m][r/64];  d_out fp16 [E][m].
+ *   u     SIGN1 [E][m][r/64];  d_out fp16 [E][m]  (diagonals of either sign).
  */
 typedef struct {
   const uint16_t* d_in;
