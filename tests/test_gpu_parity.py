@@ -604,6 +604,9 @@ def test_dbf_negative_diagonals(M, m, n, r):
             check_f32(f64(y1), o, F32_TOL, f"dbf negative diagonals, one launch {key}")
         finally:
             brq().set_decode_fusion(brq().FUSION_DEFAULT)
+    # the Q8 chain quantises x_s = D_in x and h_s, signs included
+    oq = oracle.dbf_chain_q8(oracle.bf16_to_f64(x), d_in, vw, d_mid, uw, d_out, m, n, r)
+    check_q8(_q8_run(x, d_in, vw, d_mid, uw, d_out, m, n, r), oq, f"dbf q8 negative diagonals {key}")
 
 
 class _SignedDiagonals:
